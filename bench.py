@@ -1,0 +1,272 @@
+"""Benchmark of one decode step of paged attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one pass of the whole hot path over one batch: the cache write of
+each sequence's newest token (reshape_and_cache) followed by decode attention
+of every sequence's query over its paged history.  The default workload is the
+Qwen-7B-shaped GQA batch (64 sequences, 28 query / 4 KV heads, head_dim 128,
+block size 16, context lengths ~ U[512, 4096], bf16).  Inputs are seeded
+synthetic tensors already resident in HBM.  Steps rotate over R copies of the
+KV pool so that no step finds its KV bytes in the 256 MB last-level cache left
+there by the previous one.
+
+Prints ONE JSON line: throughput (decode tokens/s = sequences per second of
+steps), the decode call's achieved KV bandwidth against the 8 TB/s HBM peak
+(HIP events around each decode call, on the stream it runs on), and the
+float64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode attention tokens/s and achieved KV HBM GB/s (% of peak), 1 MI355X"
+KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_generic.hip", "pa_merge.hip",
+                  "pa_finalize.h", "pa_device.h", "pa_api.cpp"]
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_qwen7b_gqa_bf16_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="qwen7b_gqa_bf16")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--kernel", choices=["auto", "generic", "mfma"], default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0,
+                    help="wall-time budget of the oracle sample")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time decode calls only (for counter runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run the plain copy kernel of this size, 5 times")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(HERE, "paged_kv_decode_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(config_name, per_launch_alg_bytes):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources; else None."""
+    if config_name != "qwen7b_gqa_bf16" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle (float64 gather + softmax) on the host, one thread, on a
+    prefix of the batch's sequences bounded by a wall-time budget."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    import oracle
+
+    q = inp.query.float().numpy()
+    kc = inp.key_cache.float().numpy()
+    vc = inp.value_cache.float().numpy()
+    bt = inp.block_tables.numpy().astype(np.int64)
+    cl = inp.context_lens.numpy().astype(np.int64)
+    H = q.shape[1]
+    done, tokens, elapsed = 0, 0, 0.0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        for b in range(q.shape[0]):
+            t0 = time.perf_counter()
+            oracle.decode_contiguous(q, kc, vc, bt, cl, inp.cfg.scale,
+                                     pairs=[(b, h) for h in range(H)])
+            elapsed += time.perf_counter() - t0
+            done += 1
+            tokens += int(cl[b])
+            if elapsed > budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {
+        "value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        "sample": "float64 oracle (contiguous gather + softmax) on the first %d of %d "
+                  "sequences, all %d heads (%d history tokens), %.1f s, 1 BLAS thread"
+                  % (done, q.shape[0], H, tokens, elapsed),
+        "seconds": elapsed,
+        "cpu_model": _cpu_model(),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from paged_kv_decode_attention_amd import inputs as I
+    from paged_kv_decode_attention_amd import ops
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ops.load_library()
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            ops.copy_bytes(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
+
+    cfg = I.CONFIGS[args.config]
+    inp = I.generate(cfg, new_tokens_at="last")
+    S, H, D = inp.query.shape
+    N, H_kv, BS, _ = inp.key_cache.shape
+    W = inp.block_tables.shape[1]
+    lens = inp.context_lens.numpy()
+    alg_bytes = I.kv_bytes_read(cfg, lens)
+
+    q = inp.query.to(dev)
+    bt = inp.block_tables.to(dev)
+    cl = inp.context_lens.to(dev)
+    nk, nv = inp.new_key.to(dev), inp.new_value.to(dev)
+    slots = inp.slot_mapping.to(dev)
+    R = max(1, args.replicas)
+    kcs = [inp.key_cache.to(dev) for _ in range(R)]
+    vcs = [inp.value_cache.to(dev) for _ in range(R)]
+    out = torch.empty_like(q)
+    max_ctx = W * BS
+    ws_bytes = ops.decode_workspace_size(S, H, H_kv, D, BS, max_ctx, args.partition_size,
+                                         q.dtype)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    kind = {"auto": ops.KERNEL_AUTO, "generic": ops.KERNEL_GENERIC, "mfma": ops.KERNEL_MFMA}
+    ops.select_kernel(kind[args.kernel])
+    P = args.partition_size or ops.decode_partition_size(S, H_kv, H // H_kv, D, BS, max_ctx,
+                                                         q.dtype)
+
+    def step(k, ev=None):
+        r = k % R
+        if not args.decode_only:
+            ops.reshape_and_cache(nk, nv, kcs[r], vcs[r], slots)
+        if ev is not None:
+            ev[0].record()
+        ops.paged_attention_decode(q, kcs[r], vcs[r], bt, cl, cfg.scale,
+                                   max_context_len=max_ctx, partition_size=args.partition_size,
+                                   out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k, events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([s.elapsed_time(e) for s, e in events])
+
+    # practical streaming-read ceiling of this GPU (hand-written kernel)
+    rd = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(16 * 65536, dtype=torch.uint8, device=dev)
+    ops.stream_read(rd, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        ops.stream_read(rd, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ceiling_gbps = 5 * rd.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del rd
+
+    dec_s = float(dec_ms.mean()) * 1e-3
+    achieved = alg_bytes / dec_s / 1e9
+    traffic = load_traffic(args.config, alg_bytes)
+    result = {
+        "metric": METRIC,
+        "value": S * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": "%s: Qwen-7B-shaped GQA decode" % cfg.name
+                        if cfg.name == "qwen7b_gqa_bf16" else cfg.name,
+            "num_seqs": S, "num_heads": H, "num_kv_heads": H_kv, "head_dim": D,
+            "block_size": BS, "num_blocks": N, "max_blocks_per_seq": W,
+            "context_lens": "%s %s, seed %d (min %d, mean %.1f, max %d)" % (
+                cfg.lens_kind, list(cfg.lens_args), cfg.seed, lens.min(), lens.mean(),
+                lens.max()),
+            "partition_size": P, "kernel": args.kernel, "kv_pool_replicas": R,
+            "step": "decode only" if args.decode_only else "reshape_and_cache + decode",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "kernel": "paged_attention_decode call (partition kernel + lse merge)",
+            "alg_bytes_per_launch": alg_bytes,
+            "decode_us_mean": float(dec_ms.mean()) * 1e3,
+            "decode_us_p10": float(np.percentile(dec_ms, 10)) * 1e3,
+            "decode_us_p50": float(np.percentile(dec_ms, 50)) * 1e3,
+            "decode_us_p90": float(np.percentile(dec_ms, 90)) * 1e3,
+        },
+        "decode_tokens_per_s": S / dec_s,
+        "hbm_read_ceiling_gbps": ceiling_gbps,
+        "kernel_src_sha": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,225 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged KV decode attention
+ * library, libpagedattn.so.
+ *
+ * Two operations make up one decode step of one attention layer:
+ *
+ *   pa_reshape_and_cache      store the new tokens' K/V into the paged pool at
+ *                             the slots the block manager handed out;
+ *   pa_paged_attention_decode attend each sequence's single new query (one per
+ *                             query head) over its whole paged history.
+ *
+ * Sources, cited by page title and section:
+ *   [MiniPaged-Qwen]  "MiniPaged-Qwen: 把 Paged Attention 讲清楚"
+ *   [PA-source]       "PagedAttention 源码解析: KV Cache 怎么管理"
+ *   [vLLM-paging]     "vLLM 与 PagedAttention: 把 KV Cache 变成分页状态"
+ *
+ * Conventions for every entry point
+ *   - All tensor arguments are DEVICE pointers to dense row-major arrays owned
+ *     by the caller; the library never allocates, frees or keeps them.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously; no call synchronises the device.
+ *   - The return value is a pa_status.  Every argument check happens on the
+ *     host before anything is enqueued, so a non-zero status means nothing was
+ *     launched.  pa_status_string() describes a status; pa_last_error() gives
+ *     the text of the last failure on the calling thread.
+ *   - Preconditions on device-resident data (context lengths, table entries,
+ *     slots) cannot be checked without a sync; they are stated per call with
+ *     what the kernels do when they are broken.  The kernels never access
+ *     memory outside the arrays described here.
+ *   - Thread safety: the library has no mutable global state apart from the
+ *     thread-local error text.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of query, caches, new K/V and output (all the same). */
+typedef enum {
+    PA_F32 = 0,
+    PA_F16 = 1,
+    PA_BF16 = 2
+} pa_dtype;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size, H % H_kv != 0 ... */
+    PA_ERR_UNSUPPORTED = -2,   /* valid but not built: dtype, head_dim, block_size */
+    PA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+    PA_ERR_HIP = -4            /* a HIP runtime call failed (text in pa_last_error) */
+} pa_status;
+
+/* Library ABI version (major*100 + minor). */
+int pa_version(void);
+
+/* Static text for a status code. */
+const char* pa_status_string(int status);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * pa_decode_partition_size -- context partition length (tokens) the decode
+ * call uses for these sizes when called with partition_size = 0.
+ *
+ * Long histories are split into partitions that are reduced independently and
+ * merged by log-sum-exp ([MiniPaged-Qwen] §10.2 (2): shards reduced locally,
+ * then merged globally).  The result is a multiple of 32 and of block_size.
+ * Returns 0 for invalid sizes.
+ */
+int pa_decode_partition_size(int num_seqs, int num_kv_heads, int gqa_group_size,
+                             int head_dim, int block_size, int max_context_len,
+                             pa_dtype dtype);
+
+/*
+ * pa_decode_workspace_size -- bytes of device workspace pa_paged_attention_decode
+ * needs for these sizes (0 if it needs none).  partition_size = 0 selects
+ * pa_decode_partition_size().  The workspace holds float32 per-partition
+ * states (log-sum-exp and normalised output of every (sequence, head,
+ * partition)); contents need no initialisation and are meaningless between
+ * calls.  Returns (size_t)-1 for invalid sizes.
+ */
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                int head_dim, int block_size, int max_context_len,
+                                int partition_size, pa_dtype dtype);
+
+/*
+ * pa_paged_attention_decode -- single-step decode attention over a paged cache.
+ *
+ * Computes, for every sequence b and query head h,
+ *     out[b,h,:] = sum_j softmax_j(scale * q[b,h,:] . k_j) v_j,  j = 0..L_b-1
+ * ([MiniPaged-Qwen] §1, eq. o; normalised over the whole history, §5.2), where
+ * history token j lives at key_cache[pb, kvh, off, :] / value_cache[...] with
+ * pb = block_tables[b, j / block_size], off = j % block_size ([MiniPaged-Qwen]
+ * §6.2 steps 1-4, [vLLM-paging] "Attention kernel 如何读取分页 KV") and
+ * kvh = h / gqa_group_size ([MiniPaged-Qwen] §9.1, 一致点 4).  The sum is
+ * evaluated as an online softmax (running max, rescaled denominator and
+ * accumulator, [MiniPaged-Qwen] §5.2) in float32, with one rounding to the
+ * output dtype at the end.
+ *
+ *   out            [num_seqs, num_heads, head_dim]                dtype, written
+ *   query          [num_seqs, num_heads, head_dim]                dtype
+ *   key_cache      [num_blocks, num_kv_heads, block_size, head_dim] dtype
+ *   value_cache    [num_blocks, num_kv_heads, block_size, head_dim] dtype
+ *                  (layout of [MiniPaged-Qwen] §8.2)
+ *   block_tables   [num_seqs, max_blocks_per_seq] int32; entries j with
+ *                  j*block_size >= L_b are never read (may hold anything)
+ *   context_lens   [num_seqs] int32, L_b
+ *   num_heads      H = num_kv_heads * gqa_group_size
+ *   max_context_len host-side upper bound of every L_b; sizes the launch;
+ *                  must be <= max_blocks_per_seq * block_size
+ *   scale          score scale (1/sqrt(head_dim) in the sources)
+ *   partition_size 0 = pa_decode_partition_size(); else a positive multiple
+ *                  of 32 and of block_size (forces the partitioned path)
+ *   workspace      device buffer of at least pa_decode_workspace_size() bytes,
+ *                  256-byte aligned (may be NULL when that size is 0)
+ *
+ * Supported: dtype f32, f16, bf16; head_dim 64 or 128; block_size 16 or 32;
+ * any gqa_group_size >= 1.  Pointers to query/out/caches must be 16-byte
+ * aligned.
+ *
+ * Device-data preconditions and what happens when they are broken:
+ *   0 <= L_b <= max_context_len      otherwise out[b] is all NaN
+ *   0 <= block_tables[b,j] < num_blocks for j*block_size < L_b
+ *                                    otherwise the rows of the (b, kv-head)
+ *                                    groups whose partitions read it are NaN
+ *   L_b == 0                         out[b] is zero (empty history)
+ */
+int pa_paged_attention_decode(void* out, const void* query,
+                              const void* key_cache, const void* value_cache,
+                              const int32_t* block_tables,
+                              const int32_t* context_lens,
+                              int num_seqs, int num_heads, int num_kv_heads,
+                              int gqa_group_size, int head_dim, int block_size,
+                              int num_blocks, int max_blocks_per_seq,
+                              int max_context_len, float scale, pa_dtype dtype,
+                              int partition_size, void* workspace,
+                              size_t workspace_bytes, void* hip_stream);
+
+/*
+ * pa_reshape_and_cache -- store new tokens' K/V into their cache slots.
+ *
+ * For every token i with s = slot_mapping[i] >= 0:
+ *     key_cache  [s / block_size, h, s % block_size, :] = key  [i, h, :]
+ *     value_cache[s / block_size, h, s % block_size, :] = value[i, h, :]
+ * for all h < num_kv_heads ([MiniPaged-Qwen] §8.1: the block manager returns
+ * the linear slot of each appended token; §8.2: the cache-write kernel stores
+ * its K/V there).  The linear slot is read as pb * block_size + offset.  A
+ * pure copy: bit-exact.
+ *
+ *   key, value     [num_tokens, num_kv_heads, head_dim] dtype
+ *   key_cache,
+ *   value_cache    [num_blocks, num_kv_heads, block_size, head_dim] dtype
+ *   slot_mapping   [num_tokens] int64
+ *
+ * Supported: dtype f32, f16, bf16; head_dim * element size a multiple of 16
+ * bytes; any block_size >= 1.  num_tokens = 0 is a no-op.
+ *
+ * Device-data preconditions:
+ *   slot < 0                      padding: the token is skipped
+ *   slot >= num_blocks*block_size the token is skipped (never written out of
+ *                                 bounds); this is a caller error
+ *   slots distinct                duplicate slots race; the stored row is one
+ *                                 of the candidates
+ */
+int pa_reshape_and_cache(const void* key, const void* value,
+                         void* key_cache, void* value_cache,
+                         const int64_t* slot_mapping,
+                         int num_tokens, int num_kv_heads, int head_dim,
+                         int block_size, int num_blocks, pa_dtype dtype,
+                         void* hip_stream);
+
+/*
+ * pa_debug_gather_kv -- copy one sequence's history into contiguous form,
+ * using the same address translation device code as the decode kernels
+ * ([MiniPaged-Qwen] §6.2; §5: K = [K^(0), ..., K^(T-1)]).  For testing the
+ * index math bit-exactly.
+ *
+ *   k_out, v_out   [num_kv_heads, max_context_len, head_dim] dtype; rows
+ *                  j < L_seq are written, the rest untouched
+ *   seq            sequence index in [0, num_seqs)
+ *
+ * Same device-data preconditions as the decode call; rows of a table entry
+ * outside [0, num_blocks) are filled with 0xFF bytes.
+ */
+int pa_debug_gather_kv(void* k_out, void* v_out,
+                       const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, const int32_t* context_lens,
+                       int seq, int num_seqs, int num_kv_heads, int head_dim,
+                       int block_size, int num_blocks, int max_blocks_per_seq,
+                       int max_context_len, pa_dtype dtype, void* hip_stream);
+
+/*
+ * pa_debug_select_kernel -- choose the decode kernel family for later calls in
+ * this process: 0 = automatic (matrix-core kernel where supported, else the
+ * vector-ALU kernel), 1 = vector-ALU kernel for every shape, 2 = matrix-core
+ * kernel only (calls it does not support return PA_ERR_UNSUPPORTED).  Returns
+ * the previous setting, or PA_ERR_INVALID_ARG for another value.  For tests
+ * that compare the two device paths; process-wide, not synchronised with
+ * calls running on other threads.
+ */
+int pa_debug_select_kernel(int kind);
+
+/*
+ * Measurement helpers (not part of the decode path).
+ *
+ * pa_bench_stream_read -- read `bytes` (multiple of 16) from `src` with 16-byte
+ *   coalesced loads and write one 16-byte value per workgroup to `sink`
+ *   (at least 16 * 65536 bytes); gives the practical HBM read ceiling.
+ * pa_bench_copy -- copy `bytes` (multiple of 16) from src to dst; a kernel of
+ *   known traffic, used to calibrate hardware byte counters.
+ */
+int pa_bench_stream_read(const void* src, size_t bytes, void* sink, void* hip_stream);
+int pa_bench_copy(void* dst, const void* src, size_t bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,297 @@
+// Host side of libpagedattn.so: argument validation, partition sizing,
+// workspace layout and kernel dispatch behind the C ABI of pagedattn.h.
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+std::atomic<int> g_kernel_kind{pa::kAuto};
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(pa_dtype dt) {
+    switch (dt) {
+        case PA_F32: return 4;
+        case PA_F16: return 2;
+        case PA_BF16: return 2;
+        default: return 0;
+    }
+}
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Partition length heuristic.  Histories longer than one partition are
+// reduced in parallel pieces and merged; the launch has
+// num_seqs * num_kv_heads * ceil(max_context_len / P) workgroups (those past a
+// sequence's own length exit at once).  Aim for >= 2048 launched workgroups
+// (8 per compute unit) with partitions no shorter than 128 tokens, so each
+// wavefront still streams at least one 32-token chunk.
+int heuristic_partition(int num_seqs, int num_kv_heads, int block_size, int max_context_len) {
+    const int unit = block_size > 32 ? block_size : 32;
+    int P = 512;
+    const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+    while (P > 128 && pairs * ceil_div(max_context_len, P) < 2048) P /= 2;
+    P = (P + unit - 1) / unit * unit;
+    if (P > 64 * block_size) P = 64 * block_size;
+    return P;
+}
+
+bool valid_partition(int P, int block_size) {
+    return P > 0 && P % 32 == 0 && P % block_size == 0 && P <= 64 * block_size;
+}
+
+struct Layout {
+    int part_len = 0;
+    int num_parts = 0;
+    size_t lse_off = 0, out_off = 0, bytes = 0;
+};
+
+Layout decode_layout(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                     int part_len) {
+    Layout l;
+    l.part_len = part_len;
+    l.num_parts = max_context_len > 0 ? ceil_div(max_context_len, part_len) : 1;
+    if (l.num_parts <= 1) return l;   // single partition: no workspace
+    const size_t rows = (size_t)num_seqs * num_heads * l.num_parts;
+    l.lse_off = 0;
+    l.out_off = align256(rows * sizeof(float));
+    l.bytes = l.out_off + align256(rows * head_dim * sizeof(float));
+    return l;
+}
+
+bool supported_shape(int head_dim, int block_size) {
+    return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return 100; }
+
+const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_INVALID_ARG: return "invalid argument";
+        case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PA_ERR_WORKSPACE: return "workspace missing or too small";
+        case PA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_debug_select_kernel(int kind) {
+    if (kind != pa::kAuto && kind != pa::kGeneric && kind != pa::kMfma)
+        return fail(PA_ERR_INVALID_ARG, "kernel kind %d not in {0,1,2}", kind);
+    return g_kernel_kind.exchange(kind);
+}
+
+int pa_decode_partition_size(int num_seqs, int num_kv_heads, int gqa_group_size, int head_dim,
+                             int block_size, int max_context_len, pa_dtype dtype) {
+    if (num_seqs < 0 || num_kv_heads <= 0 || gqa_group_size <= 0 || max_context_len < 0 ||
+        !supported_shape(head_dim, block_size) || elem_bytes(dtype) == 0)
+        return 0;
+    return heuristic_partition(num_seqs, num_kv_heads, block_size, max_context_len);
+}
+
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                int block_size, int max_context_len, int partition_size,
+                                pa_dtype dtype) {
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
+        max_context_len < 0 || !supported_shape(head_dim, block_size) || elem_bytes(dtype) == 0)
+        return (size_t)-1;
+    int P = partition_size;
+    if (P == 0) P = heuristic_partition(num_seqs, num_kv_heads, block_size, max_context_len);
+    if (!valid_partition(P, block_size)) return (size_t)-1;
+    return decode_layout(num_seqs, num_heads, head_dim, max_context_len, P).bytes;
+}
+
+int pa_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int num_seqs, int num_heads,
+                              int num_kv_heads, int gqa_group_size, int head_dim,
+                              int block_size, int num_blocks, int max_blocks_per_seq,
+                              int max_context_len, float scale, pa_dtype dtype,
+                              int partition_size, void* workspace, size_t workspace_bytes,
+                              void* hip_stream) {
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+    if (num_heads <= 0 || num_kv_heads <= 0)
+        return fail(PA_ERR_INVALID_ARG, "num_heads %d / num_kv_heads %d must be positive",
+                    num_heads, num_kv_heads);
+    if (num_heads % num_kv_heads)
+        return fail(PA_ERR_INVALID_ARG, "num_heads %d not a multiple of num_kv_heads %d",
+                    num_heads, num_kv_heads);
+    if (gqa_group_size != num_heads / num_kv_heads)
+        return fail(PA_ERR_INVALID_ARG, "gqa_group_size %d != num_heads/num_kv_heads = %d",
+                    gqa_group_size, num_heads / num_kv_heads);
+    if (elem_bytes(dtype) == 0) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (num_blocks <= 0 || max_blocks_per_seq <= 0)
+        return fail(PA_ERR_INVALID_ARG, "num_blocks %d / max_blocks_per_seq %d must be positive",
+                    num_blocks, max_blocks_per_seq);
+    if (head_dim <= 0 || block_size <= 0)
+        return fail(PA_ERR_INVALID_ARG, "head_dim %d / block_size %d must be positive",
+                    head_dim, block_size);
+    if (!supported_shape(head_dim, block_size))
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d with block_size %d not built "
+                    "(head_dim 64/128, block_size 16/32)", head_dim, block_size);
+    if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+        return fail(PA_ERR_INVALID_ARG, "max_context_len %d outside [0, %lld]", max_context_len,
+                    (long long)max_blocks_per_seq * block_size);
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if ((int64_t)num_blocks * num_kv_heads * block_size * head_dim > ((int64_t)1 << 46))
+        return fail(PA_ERR_INVALID_ARG, "pool too large");
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+        return fail(PA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
+        return fail(PA_ERR_INVALID_ARG, "query/out/cache pointers must be 16-byte aligned");
+    if (partition_size != 0 && !valid_partition(partition_size, block_size))
+        return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a positive multiple of 32 "
+                    "and of block_size, at most 64*block_size", partition_size);
+
+    const int P = partition_size ? partition_size
+                                 : heuristic_partition(num_seqs, num_kv_heads, block_size,
+                                                       max_context_len);
+    const Layout lay = decode_layout(num_seqs, num_heads, head_dim, max_context_len, P);
+    if (lay.bytes > 0) {
+        if (!workspace || workspace_bytes < lay.bytes)
+            return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.bytes,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(PA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    }
+
+    const int kind = g_kernel_kind.load();
+    const bool mfma_ok = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size);
+    bool use_mfma = mfma_ok && kind != pa::kGeneric;
+    if (kind == pa::kMfma && !mfma_ok)
+        return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
+
+    pa::DecodeArgs a{};
+    a.out = out;
+    a.query = query;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.ws_lse = lay.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off)
+                         : nullptr;
+    a.ws_out = lay.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_off)
+                         : nullptr;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.group = gqa_group_size;
+    a.head_dim = head_dim;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.max_context_len = max_context_len;
+    a.part_len = P;
+    a.num_parts = lay.num_parts;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, s)
+                            : pa::launch_decode_generic(a, dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
+    if (lay.num_parts > 1) {
+        e = pa::launch_lse_merge(a, dtype, s);
+        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    }
+    return PA_OK;
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,
+                         const int64_t* slot_mapping, int num_tokens, int num_kv_heads,
+                         int head_dim, int block_size, int num_blocks, pa_dtype dtype,
+                         void* hip_stream) {
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_tokens >= 0)");
+    if ((head_dim * e) % 16)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16 bytes");
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+        return fail(PA_ERR_INVALID_ARG, "key/value/cache pointers must be 16-byte aligned");
+    hipError_t err = pa::launch_reshape_and_cache(key, value, key_cache, value_cache, slot_mapping,
+                                                  num_tokens, num_kv_heads, head_dim * e,
+                                                  block_size, num_blocks,
+                                                  static_cast<hipStream_t>(hip_stream));
+    if (err != hipSuccess) return hip_fail(err, "cache write kernel launch");
+    return PA_OK;
+}
+
+int pa_debug_gather_kv(void* k_out, void* v_out, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int seq,
+                       int num_seqs, int num_kv_heads, int head_dim, int block_size,
+                       int num_blocks, int max_blocks_per_seq, int max_context_len,
+                       pa_dtype dtype, void* hip_stream) {
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (seq < 0 || seq >= num_seqs)
+        return fail(PA_ERR_INVALID_ARG, "seq %d outside [0, %d)", seq, num_seqs);
+    if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+        max_blocks_per_seq <= 0 || max_context_len < 0 ||
+        (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+        return fail(PA_ERR_INVALID_ARG, "invalid sizes");
+    if ((head_dim * e) % 16)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16 bytes");
+    if (!k_out || !v_out || !key_cache || !value_cache || !block_tables || !context_lens)
+        return fail(PA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned16(k_out) || !aligned16(v_out) || !aligned16(key_cache) || !aligned16(value_cache))
+        return fail(PA_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+    hipError_t err = pa::launch_gather(k_out, v_out, key_cache, value_cache, block_tables,
+                                       context_lens, seq, num_kv_heads, head_dim * e, block_size,
+                                       num_blocks, max_blocks_per_seq, max_context_len,
+                                       static_cast<hipStream_t>(hip_stream));
+    if (err != hipSuccess) return hip_fail(err, "gather kernel launch");
+    return PA_OK;
+}
+
+int pa_bench_stream_read(const void* src, size_t bytes, void* sink, void* hip_stream) {
+    if (!src || !sink || bytes % 16 || !aligned16(src) || !aligned16(sink))
+        return fail(PA_ERR_INVALID_ARG, "stream read needs 16-byte aligned buffers and sizes");
+    hipError_t err = pa::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(hip_stream));
+    if (err != hipSuccess) return hip_fail(err, "stream read kernel launch");
+    return PA_OK;
+}
+
+int pa_bench_copy(void* dst, const void* src, size_t bytes, void* hip_stream) {
+    if (!src || !dst || bytes % 16 || !aligned16(src) || !aligned16(dst))
+        return fail(PA_ERR_INVALID_ARG, "copy needs 16-byte aligned buffers and sizes");
+    hipError_t err = pa::launch_copy(dst, src, bytes, static_cast<hipStream_t>(hip_stream));
+    if (err != hipSuccess) return hip_fail(err, "copy kernel launch");
+    return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Cache write and the debug gather: pure 16-byte copies, bit-exact for every
+// dtype (they move bytes, never values).
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kCopyThreads = 256;
+
+// Token i, KV head h, 16-byte column c:  key[i, h, c] -> key_cache[pb, h, off, c]
+// with pb = slot / block_size, off = slot % block_size ([MiniPaged-Qwen] §8.1
+// linear slot of an appended token; §8.2 pool layout).  Negative slots are
+// padding; slots past the pool are dropped, never written out of bounds.
+__global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, char* key_cache,
+    char* value_cache, const int64_t* __restrict__ slots, int num_tokens, int num_kv_heads,
+    int row_bytes, int block_size, int num_blocks) {
+    const int cols = row_bytes / 16;
+    const uint64_t total = (uint64_t)num_tokens * num_kv_heads * cols;
+    const uint64_t idx = (uint64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    if (idx >= total) return;
+    const int c = (int)(idx % cols);
+    const uint64_t th = idx / cols;              // token * H_kv + h
+    const int h = (int)(th % num_kv_heads);
+    const uint64_t i = th / num_kv_heads;
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
+    const int pb = (int)(slot / block_size);
+    const int off = (int)(slot - (int64_t)pb * block_size);
+    const uint64_t dst = kv_row(pb, h, off, num_kv_heads, block_size) * row_bytes + c * 16;
+    const uint64_t src = th * row_bytes + c * 16;
+    *reinterpret_cast<u32x4*>(key_cache + dst) = load16(key + src);
+    *reinterpret_cast<u32x4*>(value_cache + dst) = load16(value + src);
+}
+
+// History row t of sequence `seq`, KV head h -> k_out[h, t, :], through the
+// decode kernels' address function.
+__global__ __launch_bounds__(kCopyThreads) void gather_kernel(
+    char* k_out, char* v_out, const char* key_cache, const char* value_cache,
+    const int32_t* block_tables, const int32_t* context_lens, int seq, int num_kv_heads,
+    int row_bytes, int block_size, int num_blocks, int max_blocks_per_seq,
+    int max_context_len) {
+    const int cols = row_bytes / 16;
+    const int h = blockIdx.y;
+    const uint64_t idx = (uint64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    const int t = (int)(idx / cols);
+    const int c = (int)(idx % cols);
+    int L = context_lens[seq];
+    L = L < 0 ? 0 : (L > max_context_len ? max_context_len : L);
+    if (t >= L) return;
+    const int pb = block_tables[(uint64_t)seq * max_blocks_per_seq + t / block_size];
+    const uint64_t dst = ((uint64_t)h * max_context_len + t) * row_bytes + c * 16;
+    if ((unsigned)pb >= (unsigned)num_blocks) {
+        const u32x4 ones = {~0u, ~0u, ~0u, ~0u};
+        *reinterpret_cast<u32x4*>(k_out + dst) = ones;
+        *reinterpret_cast<u32x4*>(v_out + dst) = ones;
+        return;
+    }
+    const uint64_t src = kv_row(pb, h, t % block_size, num_kv_heads, block_size) * row_bytes + c * 16;
+    *reinterpret_cast<u32x4*>(k_out + dst) = load16(key_cache + src);
+    *reinterpret_cast<u32x4*>(v_out + dst) = load16(value_cache + src);
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                                    void* value_cache, const int64_t* slots, int num_tokens,
+                                    int num_kv_heads, int row_bytes, int block_size,
+                                    int num_blocks, hipStream_t s) {
+    const uint64_t total = (uint64_t)num_tokens * num_kv_heads * (row_bytes / 16);
+    if (total == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((total + kCopyThreads - 1) / kCopyThreads);
+    hipLaunchKernelGGL(reshape_and_cache_kernel, dim3(grid), dim3(kCopyThreads), 0, s,
+                       static_cast<const char*>(key), static_cast<const char*>(value),
+                       static_cast<char*>(key_cache), static_cast<char*>(value_cache), slots,
+                       num_tokens, num_kv_heads, row_bytes, block_size, num_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(void* k_out, void* v_out, const void* key_cache,
+                         const void* value_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, int seq, int num_kv_heads,
+                         int row_bytes, int block_size, int num_blocks,
+                         int max_blocks_per_seq, int max_context_len, hipStream_t s) {
+    const uint64_t per_head = (uint64_t)max_context_len * (row_bytes / 16);
+    if (per_head == 0) return hipSuccess;
+    dim3 grid((unsigned)((per_head + kCopyThreads - 1) / kCopyThreads), num_kv_heads);
+    hipLaunchKernelGGL(gather_kernel, grid, dim3(kCopyThreads), 0, s, static_cast<char*>(k_out),
+                       static_cast<char*>(v_out), static_cast<const char*>(key_cache),
+                       static_cast<const char*>(value_cache), block_tables, context_lens, seq,
+                       num_kv_heads, row_bytes, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len);
+    return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,196 @@
+// Decode paged attention on the vector ALUs: every supported dtype (f32,
+// f16, bf16), head_dim 64 or 128, block size 16 or 32, any GQA group size.
+// The matrix-core kernel covers the bf16/fp16 head_dim-128 cases; this one
+// covers the rest (and serves as a second, independent device path).
+//
+// One workgroup (4 wavefronts) per (sequence, KV head, head group of up to GT
+// query heads, context partition).  A token row of head_dim elements is
+// D*E/16 lanes wide (16 bytes per lane, one coalesced load); the workgroup
+// holds 256/(D*E/16) such token groups, which walk the partition's tokens in
+// an interleaved order.  Each token group keeps its own online-softmax state
+// per head ([MiniPaged-Qwen] §5.2 applied one token at a time):
+//   m' = max(m, s),  l' = l 2^(m-m') + 2^(s-m'),  o' = o 2^(m-m') + 2^(s-m') v
+// and the groups' states are merged at the end (same update rule applied to
+// whole states), first across lanes, then across wavefronts in LDS.
+#include "pa_finalize.h"
+
+namespace pa {
+namespace {
+
+template <typename Tag, int D, int BS, int GT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeArgs a) {
+    constexpr int E = Tag::kBytes;
+    constexpr int VEC = 16 / E;                  // elements per lane
+    constexpr int TG = D * E / 16;               // lanes per token row
+    constexpr int NG = kDecodeThreads / TG;      // token groups per workgroup
+    constexpr int NW = kDecodeThreads / 64;
+    constexpr int kMaxBlocks = 64;               // part_len <= 64 * BS
+    static_assert(TG >= 1 && TG <= 64 && 64 % TG == 0, "row width");
+
+    __shared__ int sm_pb[kMaxBlocks];
+    __shared__ float sm_m[NW * 16];
+    __shared__ float sm_l[NW * 16];
+    __shared__ float sm_o[NW * GT * D];
+
+    const int part = blockIdx.x;
+    const int hgroups = (a.group + GT - 1) / GT;
+    const int kvh = blockIdx.y / hgroups;
+    const int hg = blockIdx.y - kvh * hgroups;
+    const int b = blockIdx.z;
+    const int g0 = hg * GT;
+    const int nh = min(GT, a.group - g0);
+    const int head0 = kvh * a.group + g0;
+    const int L = a.context_lens[b];
+
+    if (L < 0 || L > a.max_context_len) {
+        if (part == 0) fill_rows<Tag>(a, b, head0, nh, __builtin_nanf(""));
+        return;
+    }
+    if (L == 0) {
+        if (part == 0) fill_rows<Tag>(a, b, head0, nh, 0.0f);
+        return;
+    }
+    const int t_begin = part * a.part_len;
+    if (t_begin >= L) return;
+    const int t_end = min(t_begin + a.part_len, L);
+    const int nparts_b = (L + a.part_len - 1) / a.part_len;
+
+    // Physical blocks of the partition.
+    const int nblk = (t_end - t_begin + BS - 1) / BS;
+    int bad_t = 0;
+    for (int i = threadIdx.x; i < nblk; i += kDecodeThreads) {
+        int pb = a.block_tables[(uint64_t)b * a.max_blocks_per_seq + t_begin / BS + i];
+        if ((unsigned)pb >= (unsigned)a.num_blocks) {
+            bad_t = 1;
+            pb = 0;
+        }
+        sm_pb[i] = pb;
+    }
+    const bool bad = __syncthreads_or(bad_t);
+
+    const int lane = threadIdx.x & 63;
+    const int c = lane % TG;                     // 16-byte column of the row
+    const int grp = threadIdx.x / TG;            // token group
+    const int wave = threadIdx.x >> 6;
+
+    float qf[GT][VEC];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        if (g < nh) {
+            const char* qp = reinterpret_cast<const char*>(a.query) +
+                             (((uint64_t)b * a.num_heads + head0 + g) * D + c * VEC) * E;
+            to_float(Tag(), load16(qp), qf[g]);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) qf[g][e] *= a.scale_log2;
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) qf[g][e] = 0.0f;
+        }
+    }
+
+    float m[GT], l[GT], o[GT][VEC];
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[g][e] = 0.0f;
+    }
+
+    const char* kbase = reinterpret_cast<const char*>(a.key_cache);
+    const char* vbase = reinterpret_cast<const char*>(a.value_cache);
+    for (int t = t_begin + grp; t < t_end; t += NG) {
+        const int pb = sm_pb[(t - t_begin) / BS];
+        const uint64_t byte = (kv_row(pb, kvh, t % BS, a.num_kv_heads, BS) * D + c * VEC) * E;
+        float kf[VEC], vf[VEC];
+        to_float(Tag(), load16(kbase + byte), kf);
+        to_float(Tag(), load16(vbase + byte), vf);
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            float dot = 0.0f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) dot += qf[g][e] * kf[e];
+#pragma unroll
+            for (int s = 1; s < TG; s <<= 1) dot += __shfl_xor(dot, s);
+            const float m_new = fmaxf(m[g], dot);
+            const float al = fast_exp2(m[g] - m_new);
+            const float pe = fast_exp2(dot - m_new);
+            l[g] = l[g] * al + pe;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o[g][e] = o[g][e] * al + pe * vf[e];
+            m[g] = m_new;
+        }
+    }
+
+    // Merge the token groups of each wavefront (lanes TG apart).
+#pragma unroll
+    for (int s = TG; s < 64; s <<= 1) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            const float m2 = __shfl_xor(m[g], s);
+            const float l2 = __shfl_xor(l[g], s);
+            const float M = fmaxf(m[g], m2);
+            const float e1 = rescale_weight(m[g], M);
+            const float e2 = rescale_weight(m2, M);
+            l[g] = e1 * l[g] + e2 * l2;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const float o2 = __shfl_xor(o[g][e], s);
+                o[g][e] = e1 * o[g][e] + e2 * o2;
+            }
+            m[g] = M;
+        }
+    }
+    if (lane < TG) {
+#pragma unroll
+        for (int g = 0; g < GT; ++g) {
+            if (c == 0) {
+                sm_m[wave * 16 + g] = m[g];
+                sm_l[wave * 16 + g] = l[g];
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) sm_o[(wave * GT + g) * D + c * VEC + e] = o[g][e];
+        }
+    }
+    __syncthreads();
+    finalize_partition<Tag>(a, sm_m, sm_l, sm_o, NW, GT * D, D, head0, nh, b, part,
+                            nparts_b, bad);
+}
+
+template <typename Tag, int D, int BS, int GT>
+hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
+    const int hgroups = (a.group + GT - 1) / GT;
+    dim3 grid(a.num_parts, a.num_kv_heads * hgroups, a.num_seqs);
+    hipLaunchKernelGGL((decode_generic_kernel<Tag, D, BS, GT>), grid, dim3(kDecodeThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename Tag, int D, int BS>
+hipError_t launch3(const DecodeArgs& a, hipStream_t s) {
+    if (a.group == 1) return launch4<Tag, D, BS, 1>(a, s);
+    if (a.group == 2) return launch4<Tag, D, BS, 2>(a, s);
+    if (a.group <= 4) return launch4<Tag, D, BS, 4>(a, s);
+    return launch4<Tag, D, BS, 8>(a, s);
+}
+
+template <typename Tag, int D>
+hipError_t launch2(const DecodeArgs& a, hipStream_t s) {
+    return a.block_size == 16 ? launch3<Tag, D, 16>(a, s) : launch3<Tag, D, 32>(a, s);
+}
+
+template <typename Tag>
+hipError_t launch1(const DecodeArgs& a, hipStream_t s) {
+    return a.head_dim == 64 ? launch2<Tag, 64>(a, s) : launch2<Tag, 128>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s) {
+    switch (dt) {
+        case PA_F32: return launch1<F32>(a, s);
+        case PA_F16: return launch1<F16>(a, s);
+        default: return launch1<BF16>(a, s);
+    }
+}
+
+}  // namespace pa

@@ -1,0 +1,110 @@
+// Device-side helpers shared by the kernels of libpagedattn.so: element
+// conversions, 16-byte vector loads and the paged-cache address function.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Row index (in units of head_dim elements) of token slot `off` of physical
+// block `pb`, KV head `kvh`, in a [num_blocks, num_kv_heads, block_size,
+// head_dim] pool: key_cache[pb, kvh, off, :] of [MiniPaged-Qwen] §8.2, the
+// last step of the position -> block -> slot translation of §6.2.  64-bit so
+// pools beyond 4 GiB address correctly.
+__device__ __forceinline__ uint64_t kv_row(int pb, int kvh, int off,
+                                           int num_kv_heads, int block_size) {
+    return ((uint64_t)(uint32_t)pb * (uint32_t)num_kv_heads + (uint32_t)kvh) *
+               (uint32_t)block_size + (uint32_t)off;
+}
+
+// ---- element types -------------------------------------------------------
+// Tags for the three storage types; 16-bit types travel as raw bits.
+struct F32 {
+    static constexpr int kBytes = 4;
+};
+struct F16 {
+    static constexpr int kBytes = 2;
+};
+struct BF16 {
+    static constexpr int kBytes = 2;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// Two float32 -> two 16-bit values packed in one dword (low = a), rounded to
+// nearest even.
+__device__ __forceinline__ uint32_t pack2(BF16, float a, float b) {
+    bf16x2 v = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pack2(F16, float a, float b) {
+    f16x2 v = __builtin_convertvector((f32x2){a, b}, f16x2);
+    return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float unpack_lo(BF16, uint32_t w) { return bf16_lo(w); }
+__device__ __forceinline__ float unpack_hi(BF16, uint32_t w) { return bf16_hi(w); }
+__device__ __forceinline__ float unpack_lo(F16, uint32_t w) { return f16_lo(w); }
+__device__ __forceinline__ float unpack_hi(F16, uint32_t w) { return f16_hi(w); }
+
+// Store one float32 as the storage type (round to nearest even).
+__device__ __forceinline__ void store_elem(F32, void* base, uint64_t i, float v) {
+    reinterpret_cast<float*>(base)[i] = v;
+}
+__device__ __forceinline__ void store_elem(BF16, void* base, uint64_t i, float v) {
+    reinterpret_cast<__bf16*>(base)[i] = (__bf16)v;
+}
+__device__ __forceinline__ void store_elem(F16, void* base, uint64_t i, float v) {
+    reinterpret_cast<_Float16*>(base)[i] = (_Float16)v;
+}
+
+// 16 bytes -> float32 values (4 for F32, 8 for the 16-bit types).
+__device__ __forceinline__ void to_float(F32, u32x4 w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(w[i]);
+}
+__device__ __forceinline__ void to_float(BF16, u32x4 w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_lo(w[i]);
+        f[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+__device__ __forceinline__ void to_float(F16, u32x4 w, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = f16_lo(w[i]);
+        f[2 * i + 1] = f16_hi(w[i]);
+    }
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// exp2 on the hardware transcendental unit; exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Weight of a partial state with running max m against the merged max M,
+// 0 for an empty state (m = -inf).
+__device__ __forceinline__ float rescale_weight(float m, float M) {
+    return m == -INFINITY ? 0.0f : fast_exp2(m - M);
+}
+
+}  // namespace pa

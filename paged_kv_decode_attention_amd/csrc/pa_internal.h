@@ -1,0 +1,59 @@
+// Internal declarations shared by the host API and the kernel launchers of
+// libpagedattn.so.  Not part of the public ABI (that is include/pagedattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "pagedattn.h"
+
+namespace pa {
+
+// Everything a decode launch needs; passed to the kernels by value.
+struct DecodeArgs {
+    void* out;                 // [S, H, D] dtype
+    const void* query;         // [S, H, D] dtype
+    const void* key_cache;     // [N, H_kv, BS, D] dtype
+    const void* value_cache;   // [N, H_kv, BS, D] dtype
+    const int32_t* block_tables;   // [S, W]
+    const int32_t* context_lens;   // [S]
+    float* ws_lse;             // [S, H, num_parts] float32 (log2 units)
+    float* ws_out;             // [S, H, num_parts, D] float32
+    int num_seqs, num_heads, num_kv_heads, group, head_dim, block_size;
+    int num_blocks, max_blocks_per_seq, max_context_len;
+    int part_len;              // tokens per context partition
+    int num_parts;             // ceil(max_context_len / part_len)
+    float scale_log2;          // scale * log2(e): scores kept in log2 units
+};
+
+constexpr int kDecodeThreads = 256;   // 4 wavefronts per workgroup
+constexpr int kChunk = 32;            // tokens a wavefront handles per step
+
+// Kernel families.
+enum KernelKind { kAuto = 0, kGeneric = 1, kMfma = 2 };
+
+bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group);
+hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_lse_merge(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value,
+                                    void* key_cache, void* value_cache,
+                                    const int64_t* slots, int num_tokens,
+                                    int num_kv_heads, int row_bytes,
+                                    int block_size, int num_blocks,
+                                    hipStream_t s);
+
+hipError_t launch_gather(void* k_out, void* v_out, const void* key_cache,
+                         const void* value_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, int seq,
+                         int num_kv_heads, int row_bytes, int block_size,
+                         int num_blocks, int max_blocks_per_seq,
+                         int max_context_len, hipStream_t s);
+
+hipError_t launch_stream_read(const void* src, size_t bytes, void* sink, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+}  // namespace pa

@@ -25,8 +25,10 @@ read-only prefix blocks [MiniPaged-Qwen §9.2 差异 3; vLLM-paging
 "Copy-on-write 是共享的正确性边界"].
 """
 
+import concurrent.futures as cf
 from dataclasses import dataclass, field, replace
 import math
+import os
 
 import numpy as np
 import torch
@@ -140,16 +142,28 @@ def _draw_lens(rng, cfg):
     raise ValueError(cfg.lens_kind)
 
 
-def _draw_pool(rng, shape, std, dtype, chunk_blocks=512):
-    """Normal(0, std) pool drawn block-chunk by chunk (fixed chunking)."""
+def _draw_pool(rng, shape, std, dtype, chunk_blocks=256):
+    """Normal(0, std) pool.  One 63-bit seed is drawn from `rng`; chunk k of
+    `chunk_blocks` blocks then comes from its own child stream
+    SeedSequence(seed).spawn(...)[k], so chunks can be drawn in parallel and
+    the result does not depend on the thread count."""
     out = torch.empty(shape, dtype=DTYPES[dtype])
     n = shape[0]
-    for s in range(0, n, chunk_blocks):
+    starts = list(range(0, n, chunk_blocks))
+    children = np.random.SeedSequence(int(rng.integers(0, 2**63 - 1))).spawn(len(starts))
+
+    def fill(k):
+        s = starts[k]
         e = min(n, s + chunk_blocks)
-        x = rng.standard_normal((e - s,) + tuple(shape[1:]), dtype=np.float32)
+        g = np.random.Generator(np.random.PCG64(children[k]))
+        x = g.standard_normal((e - s,) + tuple(shape[1:]), dtype=np.float32)
         if std != 1.0:
             x *= np.float32(std)
         out[s:e] = torch.from_numpy(x).to(DTYPES[dtype])
+
+    workers = max(1, min(16, os.cpu_count() or 1))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fill, range(len(starts))))
     return out
 
 

@@ -1,0 +1,235 @@
+"""Thin ctypes binding of libpagedattn.so (argument marshalling only).
+
+Every function takes torch tensors that live on the GPU, checks their dtype,
+shape and layout against each other, and passes their device pointers, the
+sizes and torch's current HIP stream to the C ABI of ``include/pagedattn.h``.
+All computation happens in the library's HIP kernels; there is no other path.
+If the shared library has not been built, ``load_library`` raises.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+
+KERNEL_AUTO, KERNEL_GENERIC, KERNEL_MFMA = 0, 1, 2
+
+_lib = None
+
+_VP = ctypes.c_void_p
+_I = ctypes.c_int
+_SIGNATURES = {
+    "pa_version": (_I, []),
+    "pa_status_string": (ctypes.c_char_p, [_I]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_debug_select_kernel": (_I, [_I]),
+    "pa_decode_partition_size": (_I, [_I, _I, _I, _I, _I, _I, _I]),
+    "pa_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "pa_paged_attention_decode": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _VP,
+             _I, _I, _I, _I, _I, _I, _I, _I, _I,
+             ctypes.c_float, _I, _I, _VP, ctypes.c_size_t, _VP]),
+    "pa_reshape_and_cache": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP]),
+    "pa_debug_gather_kv": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _VP]),
+    "pa_bench_stream_read": (_I, [_VP, ctypes.c_size_t, _VP, _VP]),
+    "pa_bench_copy": (_I, [_VP, _VP, ctypes.c_size_t, _VP]),
+}
+
+
+def load_library(path=None):
+    """Load libpagedattn.so (once) and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libpagedattn.so not found at %s; build it with "
+            "`python -m paged_kv_decode_attention_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status, what):
+    if status != 0:
+        lib = load_library()
+        raise RuntimeError("%s failed: %s (%s)" % (
+            what, lib.pa_status_string(status).decode(), lib.pa_last_error().decode()))
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _gpu(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def dtype_code(dtype):
+    if dtype not in _DTYPE_CODE:
+        raise ValueError("unsupported dtype %s" % dtype)
+    return _DTYPE_CODE[dtype]
+
+
+def select_kernel(kind):
+    """Pick the decode kernel family (KERNEL_AUTO / _GENERIC / _MFMA); returns
+    the previous choice.  For comparing the two device paths in tests."""
+    prev = load_library().pa_debug_select_kernel(int(kind))
+    if prev < 0:
+        _check(prev, "select_kernel")
+    return prev
+
+
+def decode_partition_size(num_seqs, num_kv_heads, gqa_group_size, head_dim, block_size,
+                          max_context_len, dtype):
+    return load_library().pa_decode_partition_size(
+        num_seqs, num_kv_heads, gqa_group_size, head_dim, block_size, max_context_len,
+        dtype_code(dtype))
+
+
+def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                          max_context_len, partition_size, dtype):
+    n = load_library().pa_decode_workspace_size(
+        num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len,
+        partition_size, dtype_code(dtype))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes for the decode workspace")
+    return n
+
+
+def paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens,
+                           scale=None, *, max_context_len=None, partition_size=0,
+                           out=None, workspace=None):
+    """Single-step decode attention over a paged KV cache.
+
+    query [S, H, D]; key_cache/value_cache [N, H_kv, BS, D] (same dtype);
+    block_tables [S, W] int32; context_lens [S] int32.  The GQA group size is
+    H / H_kv.  max_context_len defaults to W * BS (no device sync).  Returns
+    out [S, H, D] in the query dtype.
+    """
+    for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _gpu(t, n)
+    if query.dim() != 3 or key_cache.dim() != 4 or key_cache.shape != value_cache.shape:
+        raise ValueError("query must be [S,H,D] and caches [N,H_kv,BS,D] of one shape")
+    S, H, D = query.shape
+    N, H_kv, BS, D2 = key_cache.shape
+    if D2 != D:
+        raise ValueError("head_dim of query (%d) and caches (%d) differ" % (D, D2))
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise ValueError("query and caches must share one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, W] and context_lens [S]")
+    if H_kv == 0 or H % H_kv:
+        raise ValueError("num_heads %d is not a multiple of num_kv_heads %d" % (H, H_kv))
+    W = block_tables.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if max_context_len is None:
+        max_context_len = W * BS
+    if out is None:
+        out = torch.empty_like(query)
+    else:
+        _gpu(out, "out")
+        if out.shape != query.shape or out.dtype != query.dtype:
+            raise ValueError("out must match query in shape and dtype")
+    code = dtype_code(query.dtype)
+    lib = load_library()
+    ws_bytes = decode_workspace_size(S, H, H_kv, D, BS, max_context_len, partition_size,
+                                     query.dtype)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=query.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    status = lib.pa_paged_attention_decode(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), S, H, H_kv, H // H_kv, D, BS, N, W, int(max_context_len),
+        float(scale), code, int(partition_size), ws_ptr, ws_len, _stream(query.device))
+    _check(status, "paged_attention_decode")
+    return out
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
+    """Store key/value [T, H_kv, D] into the caches at slot_mapping [T] (int64;
+    negative = skip).  In place on the caches."""
+    for t, n in ((key, "key"), (value, "value"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache"), (slot_mapping, "slot_mapping")):
+        _gpu(t, n)
+    if key.shape != value.shape or key.dim() != 3:
+        raise ValueError("key and value must be [T, H_kv, D] of one shape")
+    if key_cache.shape != value_cache.shape or key_cache.dim() != 4:
+        raise ValueError("caches must be [N, H_kv, BS, D] of one shape")
+    T, H_kv, D = key.shape
+    N, H_kv2, BS, D2 = key_cache.shape
+    if (H_kv, D) != (H_kv2, D2):
+        raise ValueError("new tokens and caches disagree in KV heads or head_dim")
+    if len({key.dtype, value.dtype, key_cache.dtype, value_cache.dtype}) != 1:
+        raise ValueError("key, value and caches must share one dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    status = load_library().pa_reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping),
+        T, H_kv, D, BS, N, dtype_code(key.dtype), _stream(key.device))
+    _check(status, "reshape_and_cache")
+
+
+def debug_gather_kv(key_cache, value_cache, block_tables, context_lens, seq,
+                    max_context_len=None, k_out=None, v_out=None):
+    """Contiguous [H_kv, max_context_len, D] copies of sequence `seq`'s history
+    (rows >= its length are left as given), via the kernels' address code."""
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _gpu(t, n)
+    N, H_kv, BS, D = key_cache.shape
+    S, W = block_tables.shape
+    if max_context_len is None:
+        max_context_len = W * BS
+    if k_out is None:
+        k_out = torch.zeros((H_kv, max_context_len, D), dtype=key_cache.dtype,
+                            device=key_cache.device)
+    if v_out is None:
+        v_out = torch.zeros_like(k_out)
+    status = load_library().pa_debug_gather_kv(
+        _ptr(k_out), _ptr(v_out), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), int(seq), S, H_kv, D, BS, N, W, int(max_context_len),
+        dtype_code(key_cache.dtype), _stream(key_cache.device))
+    _check(status, "debug_gather_kv")
+    return k_out, v_out
+
+
+def stream_read(src, sink):
+    """Read all of `src` (a GPU tensor, bytes multiple of 16) once."""
+    _check(load_library().pa_bench_stream_read(
+        _ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src.device)),
+        "stream_read")
+
+
+def copy_bytes(dst, src):
+    """Copy src to dst (same byte size, multiple of 16) with a plain kernel."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst too small")
+    _check(load_library().pa_bench_copy(_ptr(dst), _ptr(src), n, _stream(src.device)),
+           "copy_bytes")

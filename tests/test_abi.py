@@ -1,0 +1,137 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol
+include/pagedattn.h declares, and rejects invalid arguments on the host with
+the documented status before anything is launched (no GPU needed; these
+calls never reach a kernel)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_decode_attention_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+FAKE = 0x10000            # a 16-byte aligned non-null address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ops.LIB_PATH):
+        from paged_kv_decode_attention_amd import build
+        build.build()
+    return ops.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(ops._SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pa_version() == 100
+    for s, text in ((OK, b"ok"), (INVALID, b"invalid argument"),
+                    (UNSUPPORTED, b"unsupported configuration")):
+        assert lib.pa_status_string(s) == text
+    assert lib.pa_status_string(12345) == b"unknown status"
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, query=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, S=2, H=28, H_kv=4,
+             G=7, D=128, BS=16, N=100, W=8, max_ctx=128, scale=0.088, dtype=ops.PA_BF16,
+             P=0, ws=0, ws_bytes=0, stream=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return lib.pa_paged_attention_decode(
+        vp(a["out"]), vp(a["query"]), vp(a["kc"]), vp(a["vc"]), vp(a["bt"]), vp(a["cl"]),
+        a["S"], a["H"], a["H_kv"], a["G"], a["D"], a["BS"], a["N"], a["W"], a["max_ctx"],
+        a["scale"], a["dtype"], a["P"], vp(a["ws"]), a["ws_bytes"], vp(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=30, H_kv=4, G=7), INVALID),          # H % H_kv != 0
+    (dict(G=4), INVALID),                        # group size mismatch
+    (dict(H_kv=0), INVALID),
+    (dict(S=-1), INVALID),
+    (dict(dtype=7), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(BS=8), UNSUPPORTED),
+    (dict(max_ctx=129), INVALID),                # > W * BS
+    (dict(max_ctx=-1), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(N=0), INVALID),
+    (dict(query=0), INVALID),                    # null pointer
+    (dict(kc=FAKE + 8), INVALID),                # misaligned
+    (dict(P=48), INVALID),                       # not a multiple of 32
+    (dict(P=2048), INVALID),                     # > 64 * block_size
+    (dict(max_ctx=128, P=32), WORKSPACE),        # 4 partitions, no workspace
+    (dict(max_ctx=128, P=32, ws=FAKE, ws_bytes=16), WORKSPACE),
+    (dict(max_ctx=128, P=32, ws=FAKE + 16, ws_bytes=1 << 30), INVALID),  # not 256-aligned
+])
+def test_decode_rejects_on_host(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    assert lib.pa_last_error() != b""
+
+
+def test_decode_empty_batch_is_noop(lib):
+    assert _decode(lib, S=0, out=0, query=0) == OK
+
+
+def test_workspace_size_arithmetic(lib):
+    f = lib.pa_decode_workspace_size
+    # one partition: no workspace
+    assert f(4, 2, 2, 64, 16, 64, 0, ops.PA_F32) == 0
+    # S=2, H=4, P=32, max 128 -> 4 partitions: lse 2*4*4 floats, out *D floats
+    rows = 2 * 4 * 4
+    want = ((rows * 4 + 255) // 256) * 256 + ((rows * 128 * 4 + 255) // 256) * 256
+    assert f(2, 4, 2, 128, 16, 128, 32, ops.PA_BF16) == want
+    assert f(2, 4, 3, 128, 16, 128, 32, ops.PA_BF16) == ctypes.c_size_t(-1).value
+    assert f(2, 4, 2, 128, 16, 128, 40, ops.PA_BF16) == ctypes.c_size_t(-1).value
+
+
+def test_partition_heuristic_is_valid(lib):
+    for S, H_kv, BS, L in ((64, 4, 16, 4096), (32, 32, 16, 4096), (4, 8, 32, 131072),
+                           (128, 8, 16, 8192), (4, 2, 16, 64), (1, 1, 32, 1)):
+        P = lib.pa_decode_partition_size(S, H_kv, 7, 128, BS, L, ops.PA_BF16)
+        assert P > 0 and P % 32 == 0 and P % BS == 0 and P <= 64 * BS
+    assert lib.pa_decode_partition_size(4, 0, 1, 128, 16, 64, ops.PA_BF16) == 0
+
+
+def test_reshape_and_cache_rejects_on_host(lib):
+    vp = ctypes.c_void_p
+    f = lib.pa_reshape_and_cache
+    assert f(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 0, 2, 64, 16, 4, ops.PA_F32,
+             vp(0)) == OK                                               # no tokens
+    assert f(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(0), 4, 2, 64, 16, 4, ops.PA_F32,
+             vp(0)) == INVALID                                          # null slots
+    assert f(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 4, 2, 6, 16, 4, ops.PA_F16,
+             vp(0)) == UNSUPPORTED                                      # 12-byte rows
+    assert f(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 4, 2, 64, 16, 4, 9,
+             vp(0)) == INVALID
+
+
+def test_select_kernel_validates(lib):
+    assert lib.pa_debug_select_kernel(5) == INVALID
+    prev = lib.pa_debug_select_kernel(1)
+    assert lib.pa_debug_select_kernel(prev) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(2, 4, 64)
+    kc = torch.zeros(8, 2, 16, 64)
+    with pytest.raises(ValueError):
+        ops.paged_attention_decode(q, kc, kc, torch.zeros(2, 1, dtype=torch.int32),
+                                   torch.zeros(2, dtype=torch.int32))

@@ -1,0 +1,88 @@
+"""reshape_and_cache on the GPU: bit-exact against the oracle's assignment,
+whole pool compared as raw bits; and the write-then-attend decode step."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, compare, oracle_inputs, small_config, upload
+from paged_kv_decode_attention_amd import inputs as I
+from paged_kv_decode_attention_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+BITS = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16}
+
+
+def bits(t):
+    return t.detach().cpu().view(BITS[t.dtype]).numpy()
+
+
+@pytest.mark.parametrize("dtype,H_kv,D,BS", [("f32", 2, 64, 16), ("bf16", 8, 128, 16),
+                                              ("f16", 4, 128, 32), ("bf16", 2, 64, 32)])
+def test_cache_write_bit_exact(dtype, H_kv, D, BS):
+    cfg = small_config(dtype, H_kv, 1, D, BS, (40, 300, 17), extra_blocks=40)
+    inp = I.generate(cfg)
+    rng = np.random.default_rng(5)
+    N = inp.num_blocks
+    T = 300
+    slots = rng.choice(N * BS, size=T, replace=False).astype(np.int64)
+    slots[::17] = -1                      # padding entries
+    slots[5] = N * BS + 3                 # past the pool: dropped
+    key = torch.randn(T, H_kv, D).to(inp.key_cache.dtype)
+    val = torch.randn(T, H_kv, D).to(inp.key_cache.dtype)
+    kc, vc = inp.key_cache.to(DEV), inp.value_cache.to(DEV)
+    ops.reshape_and_cache(key.to(DEV), val.to(DEV), kc, vc, torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    keep = slots < N * BS
+    rk, rv = oracle.reshape_and_cache(bits(key)[keep], bits(val)[keep], bits(inp.key_cache),
+                                      bits(inp.value_cache), slots[keep])
+    assert np.array_equal(bits(kc), rk)
+    assert np.array_equal(bits(vc), rv)
+
+
+def test_write_then_attend_tiny():
+    """The append flow: each sequence's next token goes to position L_b (a
+    free block when L_b is a multiple of the block size), then decode attends
+    over L_b + 1 tokens."""
+    cfg = I.CONFIGS["tiny_fp32"]
+    inp = I.generate(cfg)
+    BS = cfg.block_size
+    L = inp.context_lens.numpy().copy()
+    bt = inp.block_tables.numpy().copy()
+    free = list(inp.free_blocks)
+    slots = []
+    for b in range(cfg.num_seqs):
+        pos = int(L[b])
+        if pos % BS == 0:
+            bt[b, pos // BS] = free.pop(0)
+        slots.append(int(bt[b, pos // BS]) * BS + pos % BS)
+    slots = np.array(slots, dtype=np.int64)
+    key = inp.new_key[:cfg.num_seqs]
+    val = inp.new_value[:cfg.num_seqs]
+    d = upload(inp)
+    ops.reshape_and_cache(key.to(DEV), val.to(DEV), d["key_cache"], d["value_cache"],
+                          torch.from_numpy(slots).to(DEV))
+    bt_t = torch.from_numpy(bt.astype(np.int32)).to(DEV)
+    lens_t = torch.from_numpy((L + 1).astype(np.int32)).to(DEV)
+    out = ops.paged_attention_decode(d["query"], d["key_cache"], d["value_cache"], bt_t, lens_t)
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(key.numpy(), val.numpy(), inp.key_cache.numpy(),
+                                      inp.value_cache.numpy(), slots)
+    assert np.array_equal(d["key_cache"].cpu().numpy(), kc)
+    ref = oracle.decode_contiguous(inp.query.numpy(), kc, vc, bt, L + 1, cfg.scale)
+    compare(out, ref, "f32", what="write then attend")
+
+
+def test_tiny_config_cache_write():
+    inp = I.generate(I.CONFIGS["tiny_fp32"])
+    d = upload(inp)
+    ops.reshape_and_cache(d["new_key"], d["new_value"], d["key_cache"], d["value_cache"],
+                          d["slot_mapping"])
+    torch.cuda.synchronize()
+    rk, rv = oracle.reshape_and_cache(bits(inp.new_key), bits(inp.new_value),
+                                      bits(inp.key_cache), bits(inp.value_cache),
+                                      inp.slot_mapping.numpy())
+    assert np.array_equal(bits(d["key_cache"]), rk)
+    assert np.array_equal(bits(d["value_cache"]), rv)

@@ -1,0 +1,188 @@
+"""Decode parity on the GPU: the HIP kernels, called through the C ABI,
+against the float64 oracle, element by element, on the same seeded inputs.
+
+Every pool slot no history token occupies is NaN (tail slots of last blocks,
+blocks no table references) and unused table entries are -1, so any read
+past the history shows up as a non-finite output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, compare, oracle_inputs, same_history_other_layout, small_config, upload
+from paged_kv_decode_attention_amd import inputs as I
+from paged_kv_decode_attention_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = (1, 15, 16, 17, 31, 33, 100, 513)
+
+
+def run_decode(d, kernel=ops.KERNEL_AUTO, partition_size=0, **kw):
+    prev = ops.select_kernel(kernel)
+    try:
+        out = ops.paged_attention_decode(d["query"], d["key_cache"], d["value_cache"],
+                                         d["block_tables"], d["context_lens"],
+                                         partition_size=partition_size, **kw)
+        torch.cuda.synchronize()
+    finally:
+        ops.select_kernel(prev)
+    return out
+
+
+def oracle_ref(inp, pairs=None):
+    return oracle.decode_contiguous(*oracle_inputs(inp), pairs=pairs)
+
+
+# ---------------------------------------------------------------- small shapes
+
+SMALL_CASES = [
+    # dtype, H_kv, G, D, BS, kernel
+    ("bf16", 2, 7, 128, 16, ops.KERNEL_MFMA),
+    ("bf16", 2, 7, 128, 16, ops.KERNEL_GENERIC),
+    ("f16", 2, 4, 128, 16, ops.KERNEL_MFMA),
+    ("f16", 2, 4, 128, 32, ops.KERNEL_MFMA),
+    ("bf16", 3, 1, 128, 32, ops.KERNEL_MFMA),
+    ("bf16", 1, 16, 128, 16, ops.KERNEL_MFMA),
+    ("bf16", 2, 8, 128, 32, ops.KERNEL_MFMA),
+    ("bf16", 2, 20, 128, 16, ops.KERNEL_AUTO),      # G > 16: vector-ALU kernel
+    ("f16", 2, 3, 64, 16, ops.KERNEL_AUTO),         # head_dim 64: vector-ALU kernel
+    ("bf16", 2, 5, 64, 32, ops.KERNEL_GENERIC),
+    ("f32", 2, 1, 64, 16, ops.KERNEL_AUTO),
+    ("f32", 2, 4, 128, 32, ops.KERNEL_GENERIC),
+    ("f32", 1, 12, 128, 16, ops.KERNEL_GENERIC),
+]
+
+
+@pytest.mark.parametrize("partition_size", [0, 32, 64, 256])
+@pytest.mark.parametrize("case", SMALL_CASES, ids=lambda c: "%s-hkv%d-g%d-d%d-bs%d-k%d" % c)
+def test_small_parity(case, partition_size):
+    dtype, H_kv, G, D, BS, kernel = case
+    if partition_size and partition_size % BS:
+        pytest.skip("partition not a multiple of the block size")
+    inp = I.poison_unread(I.generate(small_config(dtype, H_kv, G, D, BS, RAGGED)))
+    out = run_decode(upload(inp), kernel, partition_size)
+    compare(out, oracle_ref(inp), dtype, what="small %s P=%d" % (case, partition_size))
+
+
+def test_kernels_agree():
+    inp = I.poison_unread(I.generate(small_config("bf16", 4, 7, 128, 16, RAGGED, seed=3)))
+    d = upload(inp)
+    a = run_decode(d, ops.KERNEL_MFMA).float()
+    b = run_decode(d, ops.KERNEL_GENERIC).float()
+    assert torch.all(torch.abs(a - b) <= 2e-2 + 1e-2 * torch.abs(b))
+
+
+def test_single_token_history_is_v0_exactly():
+    for dtype, D, kernel in (("bf16", 128, ops.KERNEL_MFMA), ("f16", 128, ops.KERNEL_MFMA),
+                             ("f32", 64, ops.KERNEL_GENERIC), ("bf16", 128, ops.KERNEL_GENERIC)):
+        inp = I.generate(small_config(dtype, 2, 4, D, 16, (1, 1, 1)))
+        out = run_decode(upload(inp), kernel).cpu()
+        for b in range(3):
+            pb = int(inp.block_tables[b, 0])
+            for h in range(8):
+                v0 = inp.value_cache[pb, h // 4, 0]
+                assert torch.equal(out[b, h], v0), (dtype, kernel, b, h)
+
+
+def test_empty_history_gives_zeros():
+    for kernel in (ops.KERNEL_MFMA, ops.KERNEL_GENERIC):
+        inp = I.generate(small_config("bf16", 2, 7, 128, 16, (5, 40, 3)))
+        inp.context_lens[1] = 0
+        out = run_decode(upload(inp), kernel).cpu()
+        assert torch.all(out[1] == 0)
+        ref = oracle_ref(inp)
+        compare(out, ref, "bf16", what="with empty row")
+
+
+def test_invalid_device_data_gives_nan_rows():
+    for kernel in (ops.KERNEL_MFMA, ops.KERNEL_GENERIC):
+        inp = I.generate(small_config("bf16", 2, 7, 128, 16, (40, 40, 40, 40)))
+        inp.context_lens[1] = 10_000          # > max_context_len
+        inp.context_lens[2] = -3
+        inp.block_tables[3, 1] = 10_000_000   # outside the pool
+        out = run_decode(upload(inp), kernel).cpu().float()
+        assert torch.isnan(out[1]).all() and torch.isnan(out[2]).all()
+        assert torch.isnan(out[3]).all()
+        assert torch.isfinite(out[0]).all()
+
+
+def test_permutation_and_block_size_invariance_bitwise():
+    inp = I.generate(small_config("bf16", 2, 7, 128, 16, RAGGED, seed=11))
+    base = run_decode(upload(inp), ops.KERNEL_MFMA, 256).cpu()
+    for bs, seed in ((16, 1), (16, 2), (32, 3)):
+        kc, vc, bt = same_history_other_layout(inp, bs, seed)
+        d = dict(query=inp.query.to(DEV), key_cache=kc.to(DEV), value_cache=vc.to(DEV),
+                 block_tables=bt.to(DEV), context_lens=inp.context_lens.to(DEV))
+        out = run_decode(d, ops.KERNEL_MFMA, 256).cpu()
+        assert torch.equal(out, base), "layout (bs=%d, seed=%d) changed the result" % (bs, seed)
+
+
+def test_partition_size_invariance():
+    inp = I.poison_unread(I.generate(small_config("bf16", 2, 7, 128, 32, (700, 1000, 64))))
+    d = upload(inp)
+    ref = oracle_ref(inp)
+    outs = [run_decode(d, ops.KERNEL_MFMA, P) for P in (32, 64, 128, 512, 1024, 2048)]
+    for o in outs:
+        compare(o, ref, "bf16", what="partition sweep")
+
+
+def test_shared_blocks_across_sequences():
+    # two sequences read the same physical blocks (a shared prefix)
+    inp = I.generate(small_config("bf16", 2, 7, 128, 16, (100, 100, 50)))
+    inp.block_tables[1, :4] = inp.block_tables[0, :4]
+    out = run_decode(upload(inp), ops.KERNEL_MFMA)
+    compare(out, oracle_ref(inp), "bf16", what="shared prefix")
+
+
+def test_gather_index_math_bit_exact():
+    for cfg in (small_config("bf16", 2, 7, 128, 16, RAGGED),
+                small_config("f32", 3, 1, 64, 32, (5, 64, 65))):
+        inp = I.generate(cfg)
+        d = upload(inp)
+        kc16 = inp.key_cache.view(torch.int16 if cfg.dtype != "f32" else torch.int32).numpy()
+        vc16 = inp.value_cache.view(torch.int16 if cfg.dtype != "f32" else torch.int32).numpy()
+        for b, L in enumerate(inp.context_lens.tolist()):
+            k, v = ops.debug_gather_kv(d["key_cache"], d["value_cache"], d["block_tables"],
+                                       d["context_lens"], b)
+            torch.cuda.synchronize()
+            view = torch.int16 if cfg.dtype != "f32" else torch.int32
+            gk = k.cpu().view(view).numpy()[:, :L]
+            gv = v.cpu().view(view).numpy()[:, :L]
+            rk, rv = oracle.gather_sequence_kv(kc16, vc16, inp.block_tables[b].numpy(), L)
+            assert np.array_equal(gk, rk) and np.array_equal(gv, rv), (cfg.dtype, b)
+
+
+# ------------------------------------------------ full workloads, bench launch
+
+_FULL = {}
+
+
+def full_inputs(name):
+    if name not in _FULL:
+        _FULL.clear()
+        inp = I.generate(I.CONFIGS[name])
+        _FULL[name] = (inp, upload(inp))
+    return _FULL[name]
+
+
+@pytest.mark.parametrize("name", I.CONFIG_ORDER)
+def test_full_config_parity(name):
+    inp, d = full_inputs(name)
+    out = run_decode(d)
+    ref = oracle_ref(inp)
+    compare(out, ref, inp.cfg.dtype, what="config %s" % name)
+
+
+def test_long_context_ragged_tails():
+    cfg = I.CONFIGS["long_ctx_bf16"]
+    lens = [L - r for L, r in zip(cfg.lens_args, (1, 7, 13, 31))]
+    inp = I.poison_unread(I.generate(cfg, lens=lens))
+    d = upload(inp)
+    pairs = [(b, h) for b in range(4) for h in (0, 5, 13, 31)]
+    ref = oracle_ref(inp, pairs)
+    for P in (0, 512, 2048):
+        out = run_decode(d, partition_size=P)
+        compare(out, ref, "bf16", pairs=pairs, what="long ragged P=%d" % P)
