@@ -172,7 +172,7 @@ def main():
     max_ctx = W * BS
     ws_bytes = ops.decode_workspace_size(S, H, H_kv, D, BS, max_ctx, args.partition_size,
                                          q.dtype)
-    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     kind = {"auto": ops.KERNEL_AUTO, "generic": ops.KERNEL_GENERIC, "mfma": ops.KERNEL_MFMA}
     ops.select_kernel(kind[args.kernel])
     P = args.partition_size or ops.decode_partition_size(S, H_kv, H // H_kv, D, BS, max_ctx,
@@ -252,7 +252,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
-            "kernel": "paged_attention_decode call (partition kernel + lse merge)",
+            "kernel": "paged_attention_decode call (partition kernel + lse merge kernel)",
             "alg_bytes_per_launch": alg_bytes,
             "decode_us_mean": float(dec_ms.mean()) * 1e3,
             "decode_us_p10": float(np.percentile(dec_ms, 10)) * 1e3,

@@ -28,7 +28,7 @@
  *     what the kernels do when they are broken.  The kernels never access
  *     memory outside the arrays described here.
  *   - Thread safety: the library has no mutable global state apart from the
- *     thread-local error text.
+ *     thread-local error text and the test-only kernel selection below.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -80,10 +80,11 @@ int pa_decode_partition_size(int num_seqs, int num_kv_heads, int gqa_group_size,
 /*
  * pa_decode_workspace_size -- bytes of device workspace pa_paged_attention_decode
  * needs for these sizes (0 if it needs none).  partition_size = 0 selects
- * pa_decode_partition_size().  The workspace holds float32 per-partition
- * states (log-sum-exp and normalised output of every (sequence, head,
- * partition)); contents need no initialisation and are meaningless between
- * calls.  Returns (size_t)-1 for invalid sizes.
+ * pa_decode_partition_size().  The workspace holds the float32
+ * per-partition states (log-sum-exp and normalised output of every (sequence,
+ * head, partition)); contents need no initialisation and are meaningless
+ * between calls.  Calls that share one workspace must not overlap in time
+ * (use one per stream).  Returns (size_t)-1 for invalid sizes.
  */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
                                 int head_dim, int block_size, int max_context_len,

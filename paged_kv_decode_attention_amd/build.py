@@ -33,8 +33,9 @@ SOURCES = [
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# -amdgpu-mfma-vgpr-form: keep matrix-core results in VGPRs (no AGPR copies)
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops"]
+          "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 
 
 def hipcc():

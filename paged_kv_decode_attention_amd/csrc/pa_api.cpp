@@ -70,8 +70,9 @@ struct Layout {
     size_t lse_off = 0, out_off = 0, bytes = 0;
 };
 
-Layout decode_layout(int num_seqs, int num_heads, int head_dim, int max_context_len,
-                     int part_len) {
+// Fixed schedule: states [S, H, num_parts] (lse) and [S, H, num_parts, D].
+Layout fixed_layout(int num_seqs, int num_heads, int head_dim, int max_context_len,
+                    int part_len) {
     Layout l;
     l.part_len = part_len;
     l.num_parts = max_context_len > 0 ? ceil_div(max_context_len, part_len) : 1;
@@ -81,6 +82,40 @@ Layout decode_layout(int num_seqs, int num_heads, int head_dim, int max_context_
     l.out_off = align256(rows * sizeof(float));
     l.bytes = l.out_off + align256(rows * head_dim * sizeof(float));
     return l;
+}
+
+// Balanced schedule: two slots per workgroup of kMaxGroup heads each.
+Layout balanced_layout(int head_dim) {
+    Layout l;
+    const size_t rows = (size_t)pa::kMaxBalancedWg * 2 * pa::kMaxGroup;
+    l.lse_off = 0;
+    l.out_off = align256(rows * sizeof(float));
+    l.bytes = l.out_off + align256(rows * head_dim * sizeof(float));
+    return l;
+}
+
+// Workgroups of the balanced schedule: two per compute unit of the current
+// device (the matrix-core kernel's occupancy), so all are resident at once.
+int balanced_workgroups() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = cus * 2 > pa::kMaxBalancedWg ? pa::kMaxBalancedWg : cus * 2;
+    }
+    return cached[dev];
+}
+
+// The balanced schedule serves the matrix-core kernel when no partition
+// size is forced, the prefix table of context lengths fits in LDS and there
+// can be history to read.
+bool use_balanced(bool mfma, int partition_size, int num_seqs, int max_context_len) {
+    return mfma && partition_size == 0 && num_seqs <= pa::kMaxBalancedSeqs &&
+           max_context_len > 0;
 }
 
 bool supported_shape(int head_dim, int block_size) {
@@ -129,7 +164,14 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
     int P = partition_size;
     if (P == 0) P = heuristic_partition(num_seqs, num_kv_heads, block_size, max_context_len);
     if (!valid_partition(P, block_size)) return (size_t)-1;
-    return decode_layout(num_seqs, num_heads, head_dim, max_context_len, P).bytes;
+    size_t bytes = fixed_layout(num_seqs, num_heads, head_dim, max_context_len, P).bytes;
+    // enough for either kernel family (pa_debug_select_kernel may force one)
+    const bool mfma = pa::mfma_supported(dtype, head_dim, block_size, num_heads / num_kv_heads);
+    if (use_balanced(mfma, partition_size, num_seqs, max_context_len)) {
+        const size_t bal = balanced_layout(head_dim).bytes;
+        if (bal > bytes) bytes = bal;
+    }
+    return bytes;
 }
 
 int pa_paged_attention_decode(void* out, const void* query, const void* key_cache,
@@ -175,23 +217,26 @@ int pa_paged_attention_decode(void* out, const void* query, const void* key_cach
         return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a positive multiple of 32 "
                     "and of block_size, at most 64*block_size", partition_size);
 
+    const int kind = g_kernel_kind.load();
+    const bool mfma_ok = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size);
+    const bool use_mfma = mfma_ok && kind != pa::kGeneric;
+    if (kind == pa::kMfma && !mfma_ok)
+        return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
+    const bool balanced = use_balanced(use_mfma, partition_size, num_seqs, max_context_len);
+
     const int P = partition_size ? partition_size
                                  : heuristic_partition(num_seqs, num_kv_heads, block_size,
                                                        max_context_len);
-    const Layout lay = decode_layout(num_seqs, num_heads, head_dim, max_context_len, P);
-    if (lay.bytes > 0) {
+    const Layout lay = balanced ? balanced_layout(head_dim)
+                                : fixed_layout(num_seqs, num_heads, head_dim, max_context_len, P);
+    const bool needs_ws = lay.bytes > 0;
+    if (needs_ws) {
         if (!workspace || workspace_bytes < lay.bytes)
             return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", lay.bytes,
                         workspace ? workspace_bytes : (size_t)0);
         if (reinterpret_cast<uintptr_t>(workspace) & 255u)
             return fail(PA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
     }
-
-    const int kind = g_kernel_kind.load();
-    const bool mfma_ok = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size);
-    bool use_mfma = mfma_ok && kind != pa::kGeneric;
-    if (kind == pa::kMfma && !mfma_ok)
-        return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
 
     pa::DecodeArgs a{};
     a.out = out;
@@ -200,10 +245,10 @@ int pa_paged_attention_decode(void* out, const void* query, const void* key_cach
     a.value_cache = value_cache;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
-    a.ws_lse = lay.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off)
-                         : nullptr;
-    a.ws_out = lay.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_off)
-                         : nullptr;
+    a.ws_lse = needs_ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off)
+                        : nullptr;
+    a.ws_out = needs_ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_off)
+                        : nullptr;
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
@@ -214,14 +259,16 @@ int pa_paged_attention_decode(void* out, const void* query, const void* key_cach
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.max_context_len = max_context_len;
     a.part_len = P;
-    a.num_parts = lay.num_parts;
+    a.num_parts = balanced ? 1 : lay.num_parts;
+    a.schedule = balanced ? pa::kBalanced : pa::kFixed;
+    a.num_wg = balanced ? balanced_workgroups() : 0;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, s)
                             : pa::launch_decode_generic(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
-    if (lay.num_parts > 1) {
+    if (balanced || lay.num_parts > 1) {
         e = pa::launch_lse_merge(a, dtype, s);
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     }

@@ -32,11 +32,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
     __shared__ float sm_l[NW * 16];
     __shared__ float sm_o[NW * GT * D];
 
-    const int part = blockIdx.x;
     const int hgroups = (a.group + GT - 1) / GT;
-    const int kvh = blockIdx.y / hgroups;
-    const int hg = blockIdx.y - kvh * hgroups;
-    const int b = blockIdx.z;
+    const int kvh = blockIdx.x / hgroups;
+    const int hg = blockIdx.x - kvh * hgroups;
+    const int b = blockIdx.y;
+    const int part = blockIdx.z;     // slowest: full partitions dispatch first
     const int g0 = hg * GT;
     const int nh = min(GT, a.group - g0);
     const int head0 = kvh * a.group + g0;
@@ -153,14 +153,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
         }
     }
     __syncthreads();
-    finalize_partition<Tag>(a, sm_m, sm_l, sm_o, NW, GT * D, D, head0, nh, b, part,
-                            nparts_b, bad);
+    if (nparts_b == 1) {
+        finalize_state<Tag>(a, sm_m, sm_l, sm_o, NW, GT * D, D, head0, nh, b, bad, nullptr, 0,
+                            nullptr, 0);
+    } else {
+        const uint64_t row = ((uint64_t)b * a.num_heads + head0) * a.num_parts + part;
+        finalize_state<Tag>(a, sm_m, sm_l, sm_o, NW, GT * D, D, head0, nh, b, bad,
+                            a.ws_lse + row, a.num_parts, a.ws_out + row * D, a.num_parts * D);
+    }
 }
 
 template <typename Tag, int D, int BS, int GT>
 hipError_t launch4(const DecodeArgs& a, hipStream_t s) {
     const int hgroups = (a.group + GT - 1) / GT;
-    dim3 grid(a.num_parts, a.num_kv_heads * hgroups, a.num_seqs);
+    dim3 grid(a.num_kv_heads * hgroups, a.num_seqs, a.num_parts);
     hipLaunchKernelGGL((decode_generic_kernel<Tag, D, BS, GT>), grid, dim3(kDecodeThreads), 0, s, a);
     return hipGetLastError();
 }

@@ -12,7 +12,13 @@
 //   m'  = max(m, max_t s),  p = 2^(s - m'),  l' = l 2^(m-m') + sum p
 //   O^T = 2^(m-m') O^T + V^T P^T   (d x heads)  8 MFMA 16x16x32
 // with scores in log2 units (scale * log2 e folded in), so exp is a single
-// v_exp_f32.
+// v_exp_f32.  The reference max m is only moved (and O, l rescaled) when a
+// chunk's max exceeds it by more than 2^8; in between, weights 2^(s - m) are
+// at most 2^8, and the final o = O / l does not depend on the choice of m.
+// l is summed on the matrix core (P times a ones operand).  While one
+// chunk is computed, the next chunk's loads are in flight (two register
+// buffers).  Histories longer than one partition leave float32 partition
+// states that the merge kernel (pa_merge.hip) combines.
 //
 // Lane layout (lane = 16 q + n): in every MFMA the column index (lane % 16)
 // is the query head n of the group, so the running max / denominator of head
@@ -42,56 +48,181 @@ __device__ __forceinline__ f32x4 mfma16x16x32(F16, u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// Two 16-bit 1.0 values packed in one dword.
+template <typename Tag>
+constexpr uint32_t kOnePair();
+template <>
+constexpr uint32_t kOnePair<BF16>() { return 0x3f803f80u; }
+template <>
+constexpr uint32_t kOnePair<F16>() { return 0x3c003c00u; }
+
+// One 32-token chunk's K and V operands, as loaded (two 16-token tiles).
+struct ChunkRegs {
+    u32x4 k0[4], k1[4];   // K tile 0 / tile 1: row n, d = 32 kk + 8 q .. +8
+    u32x4 v[8];           // V rows of this lane's 8 tokens, d = 8 n .. +8
+};
+
+// Physical blocks of chunk c's two 16-token tiles, read from the sequence's
+// table row (wave-uniform scalar loads).  A tile past the end of the history
+// reuses tile 0's block, so its table entry is never read.  Entries outside
+// the pool set `bad` and are replaced by block 0 (never an out-of-bounds read).
+// The block table is read-only for the whole launch: read it through the
+// constant address space, which lets uniform reads become scalar loads.
+typedef __attribute__((address_space(4))) const int32_t ConstI32;
+
+template <int BS>
+__device__ __forceinline__ int2 chunk_blocks(const ConstI32* row, int c, int L, int num_blocks,
+                                             int& bad) {
+    const int j0 = c * (kChunk / BS);
+    int pb0 = row[j0];
+    int pb1 = pb0;
+    if constexpr (BS == 16) {
+        if (c * kChunk + 16 < L) pb1 = row[j0 + 1];
+    }
+    if ((unsigned)pb0 >= (unsigned)num_blocks) { bad = 1; pb0 = 0; }
+    if ((unsigned)pb1 >= (unsigned)num_blocks) { bad = 1; pb1 = 0; }
+    return make_int2(pb0, pb1);
+}
+
+// Issue the 16 loads of one chunk (always 16, so the in-order load counter
+// the compiler waits on is the same on every path and the next chunk's
+// loads stay in flight while this one is computed).  KV is streamed once:
+// nontemporal loads.
+template <int BS>
+__device__ __forceinline__ void load_chunk(ChunkRegs& r, const char* kbase, const char* vbase,
+                                           int2 pb, int kvh, int num_kv_heads, uint32_t koff,
+                                           uint32_t voff) {
+    constexpr int RB = 128 * 2;   // bytes per token row
+    const uint64_t row0 = kv_row(pb.x, kvh, 0, num_kv_heads, BS) * RB;
+    const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : 16, num_kv_heads, BS) * RB;
+    const u32x4* k0 = reinterpret_cast<const u32x4*>(kbase + row0 + koff);
+    const u32x4* k1 = reinterpret_cast<const u32x4*>(kbase + row1 + koff);
+    const u32x4* v0 = reinterpret_cast<const u32x4*>(vbase + row0 + voff);
+    const u32x4* v1 = reinterpret_cast<const u32x4*>(vbase + row1 + voff);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) r.k0[kk] = __builtin_nontemporal_load(k0 + kk * 4);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) r.k1[kk] = __builtin_nontemporal_load(k1 + kk * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(v0 + i * (RB / 16));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[4 + i] = __builtin_nontemporal_load(v1 + i * (RB / 16));
+}
+
+// Running state of one wavefront: for head n (lane % 16), the reference max
+// m_ref (log2 units), the accumulators O^T and the denominator l (computed
+// on the matrix core as P times a ones operand, so it sums exactly the
+// rounded weights the PV product uses).
+struct WaveState {
+    float m_ref;
+    f32x4 acc[8];
+    f32x4 acc_l;
+};
+
+// Scores may exceed the reference max by up to 2^kLazy before the
+// accumulators are rescaled (weights stay <= 2^8; float32 accumulators and
+// 16-bit weights hold that range with no loss of relative precision).
+constexpr float kLazy = 8.0f;
+
+template <typename Tag>
+__device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const u32x4* qop,
+                                              float sl2, int tc, int t_end, int q) {
+    // Scores: S^T[token][head] for the two 16-token tiles.
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) s0 = mfma16x16x32(Tag(), r.k0[kk], qop[kk], s0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) s1 = mfma16x16x32(Tag(), r.k1[kk], qop[kk], s1);
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s[i] = s0[i] * sl2;
+        s[4 + i] = s1[i] * sl2;
+    }
+    if (tc + kChunk > t_end) {
+        // Tokens at or past the end of the history are excluded (the last
+        // block is masked past the context length): score -inf, and the V
+        // row zeroed so stale slot contents cannot reach the accumulator.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (tc + 4 * q + i >= t_end) {
+                s[i] = -INFINITY;
+                r.v[i] = (u32x4){0u, 0u, 0u, 0u};
+            }
+            if (tc + 16 + 4 * q + i >= t_end) {
+                s[4 + i] = -INFINITY;
+                r.v[4 + i] = (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    float cmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    // Online softmax update ([MiniPaged-Qwen] §5.2), with the rescale of the
+    // accumulators deferred until the running max has grown by 2^kLazy.
+    if (__any(cmax > st.m_ref + kLazy)) {
+        const float m_new = fmaxf(st.m_ref, cmax);
+        const float alpha = fast_exp2(st.m_ref - m_new);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
+        st.acc_l *= alpha;
+        st.m_ref = m_new;
+    }
+    u32x4 pop;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        pop[u] = pack2(Tag(), fast_exp2(s[2 * u] - st.m_ref), fast_exp2(s[2 * u + 1] - st.m_ref));
+    const u32x4 ones = {kOnePair<Tag>(), kOnePair<Tag>(), kOnePair<Tag>(), kOnePair<Tag>()};
+    st.acc_l = mfma16x16x32(Tag(), ones, pop, st.acc_l);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        // V^T operand for d = 8 n + j: 16-bit element j of each of the 8 rows.
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 w;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            w[u] = __builtin_amdgcn_perm(r.v[2 * u + 1][j >> 1], r.v[2 * u][j >> 1], sel);
+        st.acc[j] = mfma16x16x32(Tag(), w, pop, st.acc[j]);
+    }
+}
+
+constexpr int kNW = kDecodeThreads / 64;   // wavefronts per workgroup
+constexpr int kOS = 128 + 4;               // padded LDS row of one head (floats)
+
+struct SegmentLds {
+    float m[kNW * 16];
+    float l[kNW * 16];
+    __attribute__((aligned(16))) float o[kNW * 16 * kOS];
+};
+
+// All wavefronts of the workgroup attend chunks [c0, c1) of (sequence b,
+// KV head kvh) -- chunk c covers history tokens [32 c, 32 c + 32) -- with
+// the chunks dealt round-robin to the wavefronts, then merge their states
+// and write the result: the final output rows when the segment is the whole
+// history, else a partial state at (plse, po) with head strides
+// (plse_hs, po_hs).
 template <typename Tag, int BS>
-__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs a) {
+__device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& sm, int b, int kvh,
+                                               int L, int c0, int c1, float* plse, int plse_hs,
+                                               float* po, int po_hs) {
     constexpr int D = 128;
-    constexpr int E = 2;                         // bytes per element
-    constexpr int NW = kDecodeThreads / 64;      // wavefronts per workgroup
-    constexpr int OS = D + 4;                    // padded LDS row (floats)
-    static_assert(BS == 16 || BS == 32, "block size");
-
-    __shared__ float sm_m[NW * 16];
-    __shared__ float sm_l[NW * 16];
-    __shared__ __attribute__((aligned(16))) float sm_o[NW * 16 * OS];
-
-    const int part = blockIdx.x;
-    const int kvh = blockIdx.y;
-    const int b = blockIdx.z;
+    constexpr int E = 2;
+    // The segment is the same for every lane; say so, so that block numbers
+    // are fetched with scalar loads (which do not share the vector loads'
+    // in-order counter) and addresses are computed once per wavefront.
+    b = __builtin_amdgcn_readfirstlane(b);
+    kvh = __builtin_amdgcn_readfirstlane(kvh);
+    L = __builtin_amdgcn_readfirstlane(L);
+    c0 = __builtin_amdgcn_readfirstlane(c0);
+    c1 = __builtin_amdgcn_readfirstlane(c1);
     const int G = a.group;
     const int head0 = kvh * G;
-    const int L = a.context_lens[b];
-
-    if (L < 0 || L > a.max_context_len) {
-        if (part == 0) fill_rows<Tag>(a, b, head0, G, __builtin_nanf(""));
-        return;
-    }
-    if (L == 0) {
-        if (part == 0) fill_rows<Tag>(a, b, head0, G, 0.0f);
-        return;
-    }
-    const int t_begin = part * a.part_len;
-    if (t_begin >= L) return;
-    const int t_end = min(t_begin + a.part_len, L);
-    const int nparts_b = (L + a.part_len - 1) / a.part_len;
-    const int nchunks = (t_end - t_begin + kChunk - 1) / kChunk;
-
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
     const int q = lane >> 4;
-
-    // Physical blocks of this partition, one per lane (part_len <= 64 * BS).
-    const int nblk = (t_end - t_begin + BS - 1) / BS;
-    int my_pb = 0;
-    int bad_lane = 0;
-    if (lane < nblk) {
-        my_pb = a.block_tables[(uint64_t)b * a.max_blocks_per_seq + t_begin / BS + lane];
-        if ((unsigned)my_pb >= (unsigned)a.num_blocks) {
-            bad_lane = 1;
-            my_pb = 0;
-        }
-    }
-    const bool bad = __any(bad_lane);
+    const int t_end = min(c1 * kChunk, L);
 
     // Query operand: Q[head n][32 kk + 8 q .. +8]; zero for padding heads.
     u32x4 qop[4];
@@ -107,136 +238,153 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
 
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
+    const ConstI32* row =
+        (const ConstI32*)(a.block_tables) + (uint64_t)b * a.max_blocks_per_seq;
     const uint32_t koff = (uint32_t)(n * D + 8 * q) * E;        // K row n, d 8q
     const uint32_t voff = (uint32_t)(4 * q * D + 8 * n) * E;    // V row 4q, d 8n
     const float sl2 = a.scale_log2;
 
-    float m_run = -INFINITY;
-    float l_run = 0.0f;
-    f32x4 acc[8];
+    WaveState st;
+    st.m_ref = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) st.acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    st.acc_l = (f32x4){0.f, 0.f, 0.f, 0.f};
+    int bad = 0;
 
-    for (int c = wave; c < nchunks; c += NW) {
-        const int tc = t_begin + c * kChunk;
-        int pb0, pb1, off1;
-        if constexpr (BS == 16) {
-            pb0 = __builtin_amdgcn_readlane(my_pb, 2 * c);
-            pb1 = __builtin_amdgcn_readlane(my_pb, 2 * c + 1);
-            off1 = 0;
-        } else {
-            pb0 = __builtin_amdgcn_readlane(my_pb, c);
-            pb1 = pb0;
-            off1 = 16;
-        }
-        const uint64_t base0 = kv_row(pb0, kvh, 0, a.num_kv_heads, BS) * (D * E);
-        const uint64_t base1 = kv_row(pb1, kvh, off1, a.num_kv_heads, BS) * (D * E);
-        const bool tile1 = tc + 16 < t_end;
-
-        u32x4 k0[4], k1[4], v[8];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) k0[kk] = load16(kbase + base0 + koff + kk * 64);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = load16(vbase + base0 + voff + i * (D * E));
-        if (tile1) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) k1[kk] = load16(kbase + base1 + koff + kk * 64);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[4 + i] = load16(vbase + base1 + voff + i * (D * E));
-        } else {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) k1[kk] = (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[4 + i] = (u32x4){0u, 0u, 0u, 0u};
-        }
-
-        // Scores: S^T[token][head] for the two 16-token tiles.
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) s0 = mfma16x16x32(Tag(), k0[kk], qop[kk], s0);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) s1 = mfma16x16x32(Tag(), k1[kk], qop[kk], s1);
-
-        float s[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s[i] = s0[i] * sl2;
-            s[4 + i] = s1[i] * sl2;
-        }
-        if (tc + kChunk > t_end) {
-            // Last chunk of the partition: tokens at or past the end of the
-            // history are excluded (score -inf, V row zero so that stale
-            // slot contents cannot reach the accumulator).
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (tc + 4 * q + i >= t_end) {
-                    s[i] = -INFINITY;
-                    v[i] = (u32x4){0u, 0u, 0u, 0u};
-                }
-                if (tc + 16 + 4 * q + i >= t_end) {
-                    s[4 + i] = -INFINITY;
-                    v[4 + i] = (u32x4){0u, 0u, 0u, 0u};
-                }
-            }
-        }
-
-        // Online softmax update for head n over this chunk.
-        float cmax = s[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) cmax = fmaxf(cmax, s[i]);
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        const float m_new = fmaxf(m_run, cmax);
-        const float alpha = fast_exp2(m_run - m_new);
-        u32x4 pop;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            pop[u] = pack2(Tag(), fast_exp2(s[2 * u] - m_new), fast_exp2(s[2 * u + 1] - m_new));
-        // The denominator sums the same rounded weights the MFMA consumes.
-        float psum = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) psum += unpack_lo(Tag(), pop[u]) + unpack_hi(Tag(), pop[u]);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            acc[j] *= alpha;
-            // V^T operand for d = 8 n + j: element j of each of the 8 rows.
-            u32x4 w;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t r0 = v[2 * u][j >> 1];
-                const uint32_t r1 = v[2 * u + 1][j >> 1];
-                w[u] = (j & 1) ? ((r0 >> 16) | (r1 & 0xffff0000u))
-                               : ((r0 & 0xffffu) | (r1 << 16));
-            }
-            acc[j] = mfma16x16x32(Tag(), w, pop, acc[j]);
+    // This wave's chunks are c0 + wave + kNW k, k < K.  Two register buffers:
+    // while chunk k is computed, chunk k+1's loads are in flight and chunk
+    // k+2's block numbers are being fetched.  Past the last chunk the
+    // prefetch repeats the last chunk (its registers are never used).
+    const int first = c0 + wave;
+    const int K = first < c1 ? (c1 - first + kNW - 1) / kNW : 0;
+    if (K > 0) {
+        auto chunk_of = [&](int k) { return first + kNW * min(k, K - 1); };
+        ChunkRegs bufA, bufB;
+        int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
+        int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
+        load_chunk<BS>(bufA, kbase, vbase, idsA, kvh, a.num_kv_heads, koff, voff);
+        int k = 0;
+        // The scheduling barriers keep each phase's loads after the previous
+        // chunk's math and before this chunk's: the load counter is in
+        // order, so a load hoisted above the math would make it wait for
+        // the prefetch too.
+        for (;;) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_chunk<BS>(bufB, kbase, vbase, idsB, kvh, a.num_kv_heads, koff, voff);
+            idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_chunk<Tag>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+            if (++k >= K) break;
+            __builtin_amdgcn_sched_barrier(0);
+            load_chunk<BS>(bufA, kbase, vbase, idsA, kvh, a.num_kv_heads, koff, voff);
+            idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_chunk<Tag>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+            if (++k >= K) break;
         }
     }
 
-    // Denominator of head n: sum the four lane groups' partial sums.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
     if (q == 0) {
-        sm_m[wave * 16 + n] = m_run;
-        sm_l[wave * 16 + n] = l_run;
+        sm.m[wave * 16 + n] = st.m_ref;
+        sm.l[wave * 16 + n] = st.acc_l[0];
     }
-    float* ow = sm_o + (wave * 16 + n) * OS + 32 * q;
+    float* ow = sm.o + (wave * 16 + n) * kOS + 32 * q;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<f32x4*>(ow + 8 * i) = (f32x4){acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-        *reinterpret_cast<f32x4*>(ow + 8 * i + 4) = (f32x4){acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+        *reinterpret_cast<f32x4*>(ow + 8 * i) =
+            (f32x4){st.acc[0][i], st.acc[1][i], st.acc[2][i], st.acc[3][i]};
+        *reinterpret_cast<f32x4*>(ow + 8 * i + 4) =
+            (f32x4){st.acc[4][i], st.acc[5][i], st.acc[6][i], st.acc[7][i]};
     }
-    __syncthreads();
-    finalize_partition<Tag>(a, sm_m, sm_l, sm_o, NW, 16 * OS, OS, head0, G, b, part,
-                            nparts_b, bad);
+    const bool any_bad = __syncthreads_or(bad);
+    finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, 16 * kOS, kOS, head0, G, b, any_bad, plse,
+                        plse_hs, po, po_hs);
+    __syncthreads();   // LDS is reused by the next segment
+}
+
+// Fixed schedule: workgroup (kvh, b, part) takes tokens [part P, part P + P).
+// The partition index varies slowest, so every sequence's first (full)
+// partition is dispatched before any shorter trailing one.
+template <typename Tag, int BS>
+__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a) {
+    __shared__ SegmentLds sm;
+    const int kvh = blockIdx.x;
+    const int b = blockIdx.y;
+    const int part = blockIdx.z;
+    const int G = a.group;
+    const int L = a.context_lens[b];
+    if (L < 0 || L > a.max_context_len) {
+        if (part == 0) fill_rows<Tag>(a, b, kvh * G, G, __builtin_nanf(""));
+        return;
+    }
+    if (L == 0) {
+        if (part == 0) fill_rows<Tag>(a, b, kvh * G, G, 0.0f);
+        return;
+    }
+    const int t_begin = part * a.part_len;
+    if (t_begin >= L) return;
+    const int nparts_b = (L + a.part_len - 1) / a.part_len;
+    const int c0 = t_begin / kChunk;
+    const int c1 = min(L, t_begin + a.part_len);
+    const int c1c = (c1 + kChunk - 1) / kChunk;
+    if (nparts_b == 1) {
+        attend_segment<Tag, BS>(a, sm, b, kvh, L, c0, c1c, nullptr, 0, nullptr, 0);
+    } else {
+        const uint64_t row = ((uint64_t)b * a.num_heads + kvh * G) * a.num_parts + part;
+        attend_segment<Tag, BS>(a, sm, b, kvh, L, c0, c1c, a.ws_lse + row, a.num_parts,
+                                a.ws_out + row * 128, a.num_parts * 128);
+    }
+}
+
+// Balanced schedule: the flattened (sequence, kv head, chunk) work list is
+// cut into gridDim.x equal ranges, one per workgroup (all resident at once).
+// Each workgroup walks the segments of its range; a segment that is a whole
+// history writes its output rows, one cut by the range boundary writes a
+// partial state into slot [w][0] (continues from the previous range) or
+// [w][1] (continues into the next) for the merge kernel.
+template <typename Tag, int BS>
+__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
+    __shared__ SegmentLds sm;
+    __shared__ int pref[kMaxBalancedSeqs + 1];
+    __shared__ int wsum[kNW];
+    chunk_prefix(a, pref, wsum);
+    const int H_kv = a.num_kv_heads;
+    const int64_t T = (int64_t)H_kv * pref[a.num_seqs];
+    if (T == 0) return;
+    const int w = blockIdx.x;
+    const int64_t xb = range_start(w, T, a.num_wg);
+    const int64_t xe = range_start(w + 1, T, a.num_wg);
+    int64_t x = xb;
+    while (x < xe) {
+        const int b = __builtin_amdgcn_readfirstlane(find_seq(pref, a.num_seqs, H_kv, x));
+        const int nb = pref[b + 1] - pref[b];
+        const int64_t off = x - (int64_t)H_kv * pref[b];
+        const int kvh = (int)(off / nb);
+        const int c0 = (int)(off - (int64_t)kvh * nb);
+        const int c1 = (int)min((int64_t)nb, c0 + (xe - x));
+        const bool head = c0 > 0;          // continues from the previous range
+        const bool tail = c1 < nb;         // continues into the next range
+        const int L = a.context_lens[b];
+        if (!head && !tail) {
+            attend_segment<Tag, BS>(a, sm, b, kvh, L, c0, c1, nullptr, 0, nullptr, 0);
+        } else {
+            const uint64_t slot = (uint64_t)w * 2 + (head ? 0 : 1);
+            attend_segment<Tag, BS>(a, sm, b, kvh, L, c0, c1, a.ws_lse + slot * kMaxGroup, 1,
+                                    a.ws_out + slot * kMaxGroup * 128, 128);
+        }
+        x += c1 - c0;
+    }
 }
 
 template <typename Tag, int BS>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
-    dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_mfma_kernel<Tag, BS>), grid, dim3(kDecodeThreads), 0, s, a);
+    if (a.schedule == kBalanced) {
+        hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS>), dim3(a.num_wg), dim3(kDecodeThreads),
+                           0, s, a);
+    } else {
+        dim3 grid(a.num_kv_heads, a.num_seqs, a.num_parts);
+        hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS>), grid, dim3(kDecodeThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -23,10 +23,26 @@ struct DecodeArgs {
     float* ws_out;             // [S, H, num_parts, D] float32
     int num_seqs, num_heads, num_kv_heads, group, head_dim, block_size;
     int num_blocks, max_blocks_per_seq, max_context_len;
-    int part_len;              // tokens per context partition
+    int part_len;              // tokens per context partition (fixed schedule)
     int num_parts;             // ceil(max_context_len / part_len)
+    int schedule;              // kFixed or kBalanced
+    int num_wg;                // workgroups of the balanced schedule
     float scale_log2;          // scale * log2(e): scores kept in log2 units
 };
+
+// Work schedules of the decode kernels.
+//   kFixed: workgroup (kv head, sequence, p) takes tokens [p P, (p+1) P);
+//     partition states are indexed [S, H, num_parts].
+//   kBalanced: the (sequence, kv head, 32-token chunk) work list, in that
+//     order, is cut into num_wg equal contiguous ranges, one per workgroup;
+//     a (sequence, kv head) cut by a range boundary leaves one state per
+//     piece in slot [w][0] (the piece that continues from workgroup w-1) or
+//     [w][1] (the piece that continues into w+1), each slot holding up to
+//     kMaxGroup heads.
+enum Schedule { kFixed = 0, kBalanced = 1 };
+constexpr int kMaxGroup = 16;          // heads per slot (matrix-core kernel)
+constexpr int kMaxBalancedWg = 1024;   // workspace is sized for this many
+constexpr int kMaxBalancedSeqs = 2048; // LDS prefix table of the balanced schedule
 
 constexpr int kDecodeThreads = 256;   // 4 wavefronts per workgroup
 constexpr int kChunk = 32;            // tokens a wavefront handles per step

@@ -1,81 +1,79 @@
-// Log-sum-exp merge of context partitions ("reduce locally, then merge
-// globally", [MiniPaged-Qwen] §10.2 (2)).  Partition p of (b, h) left
-// lse_p = m_p + log2 l_p and o_p = o~_p / l_p (float32, log2 units); the
-// online update of [MiniPaged-Qwen] §5.2 applied to whole partitions gives
-//   o = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),  M = max_p lse_p,
-// summed in partition order (deterministic).
-#include "pa_device.h"
-#include "pa_internal.h"
+// Log-sum-exp merge of partial decode states: the "merge globally" half of
+// the partitioned reduction ([MiniPaged-Qwen] §10.2 (2)).  One workgroup per
+// (sequence, KV head) combines, in token order, the float32 states (lse, o)
+// the decode workgroups left for the G query heads of that group
+// (merge_pieces in pa_finalize.h).
+#include "pa_finalize.h"
 
 namespace pa {
 namespace {
 
-constexpr int kMergeThreads = 128;
+constexpr int kMergeThreads = 256;
 
+// Fixed schedule: partitions [p P, p P + P); histories of one partition were
+// written directly by the decode kernel.
 template <typename Tag>
-__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(DecodeArgs a) {
-    __shared__ float sm_w[kMergeThreads];
-    __shared__ float sm_red[kMergeThreads / 64];
-    __shared__ int sm_nan[kMergeThreads / 64];
-
-    const int h = blockIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
+    const int kvh = blockIdx.x;
     const int b = blockIdx.y;
     const int L = a.context_lens[b];
-    // One partition (or an invalid length): the partition kernel wrote out.
     if (L <= a.part_len || L > a.max_context_len) return;
-    const int np = (L + a.part_len - 1) / a.part_len;
-    const uint64_t row0 = ((uint64_t)b * a.num_heads + h) * a.num_parts;
-    const float* lse = a.ws_lse + row0;
-    const int tid = threadIdx.x;
+    const int nparts = (L + a.part_len - 1) / a.part_len;
+    const int head0 = kvh * a.group;
+    const FixedPieces pc{a.ws_lse, a.ws_out,
+                         ((uint64_t)b * a.num_heads + head0) * a.num_parts, a.num_parts,
+                         a.head_dim};
+    merge_pieces<Tag>(a, pc, b, head0, a.group, nparts);
+}
 
-    float M = -INFINITY;
-    int has_nan = 0;
-    for (int p = tid; p < np; p += kMergeThreads) {
-        const float x = lse[p];
-        has_nan |= (x != x);
-        M = fmaxf(M, x);
+// Balanced schedule: the pieces of (b, kvh) are the slots of the workgroup
+// ranges its chunks fall in.  Also writes the rows the decode kernel skips:
+// zeros for an empty history, NaN for an invalid context length.
+template <typename Tag>
+__global__ __launch_bounds__(kMergeThreads) void merge_balanced(DecodeArgs a) {
+    __shared__ int pref[kMaxBalancedSeqs + 1];
+    __shared__ int wsum[kMergeThreads / 64];
+    __shared__ int slots[kMaxBalancedWg + 1];
+    __shared__ int npieces;
+    const int kvh = blockIdx.x;
+    const int b = blockIdx.y;
+    const int head0 = kvh * a.group;
+    const int L = a.context_lens[b];
+    if (L < 0 || L > a.max_context_len) {
+        fill_rows<Tag>(a, b, head0, a.group, __builtin_nanf(""));
+        return;
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        M = fmaxf(M, __shfl_xor(M, s));
-        has_nan |= __shfl_xor(has_nan, s);
+    if (L == 0) {
+        fill_rows<Tag>(a, b, head0, a.group, 0.0f);
+        return;
     }
-    if ((tid & 63) == 0) {
-        sm_red[tid >> 6] = M;
-        sm_nan[tid >> 6] = has_nan;
+    chunk_prefix(a, pref, wsum);
+    const int H_kv = a.num_kv_heads;
+    const int64_t T = (int64_t)H_kv * pref[a.num_seqs];
+    const int nb = pref[b + 1] - pref[b];
+    const int64_t x0 = (int64_t)H_kv * pref[b] + (int64_t)kvh * nb;
+    const int w0 = range_owner(x0, T, a.num_wg);
+    const int w1 = range_owner(x0 + nb - 1, T, a.num_wg);
+    if (w0 == w1) return;   // one range held the whole history
+    if (threadIdx.x == 0) {
+        int k = 0;
+        slots[k++] = 2 * w0 + 1;
+        for (int w = w0 + 1; w <= w1; ++w)
+            if (range_start(w, T, a.num_wg) < range_start(w + 1, T, a.num_wg)) slots[k++] = 2 * w;
+        npieces = k;
     }
     __syncthreads();
-    M = sm_red[0];
-    has_nan = sm_nan[0];
-#pragma unroll
-    for (int w = 1; w < kMergeThreads / 64; ++w) {
-        M = fmaxf(M, sm_red[w]);
-        has_nan |= sm_nan[w];
-    }
-
-    const int D = a.head_dim;
-    float num = 0.0f, den = 0.0f;
-    for (int p0 = 0; p0 < np; p0 += kMergeThreads) {
-        __syncthreads();
-        if (p0 + tid < np) sm_w[tid] = fast_exp2(lse[p0 + tid] - M);
-        __syncthreads();
-        const int cnt = min(kMergeThreads, np - p0);
-        for (int k = 0; k < cnt; ++k) {
-            const float w = sm_w[k];
-            den += w;
-            if (tid < D) num += w * a.ws_out[(row0 + p0 + k) * D + tid];
-        }
-    }
-    if (tid < D) {
-        const float o = has_nan ? __builtin_nanf("") : num / den;
-        store_elem(Tag(), a.out, ((uint64_t)b * a.num_heads + h) * D + tid, o);
-    }
+    const BalancedPieces pc{a.ws_lse, a.ws_out, slots, a.head_dim};
+    merge_pieces<Tag>(a, pc, b, head0, a.group, npieces);
 }
 
 template <typename Tag>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
-    dim3 grid(a.num_heads, a.num_seqs);
-    hipLaunchKernelGGL((lse_merge_kernel<Tag>), grid, dim3(kMergeThreads), 0, s, a);
+    dim3 grid(a.num_kv_heads, a.num_seqs);
+    if (a.schedule == kBalanced)
+        hipLaunchKernelGGL((merge_balanced<Tag>), grid, dim3(kMergeThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((merge_fixed<Tag>), grid, dim3(kMergeThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -93,9 +93,11 @@ def test_workspace_size_arithmetic(lib):
     f = lib.pa_decode_workspace_size
     # one partition: no workspace
     assert f(4, 2, 2, 64, 16, 64, 0, ops.PA_F32) == 0
-    # S=2, H=4, P=32, max 128 -> 4 partitions: lse 2*4*4 floats, out *D floats
+    # S=2, H=4, P=32, max 128 -> 4 partitions: lse 2*4*4 floats, out
+    # 2*4*4*D floats, each region 256-byte aligned
+    up = lambda x: (x + 255) // 256 * 256
     rows = 2 * 4 * 4
-    want = ((rows * 4 + 255) // 256) * 256 + ((rows * 128 * 4 + 255) // 256) * 256
+    want = up(rows * 4) + up(rows * 128 * 4)
     assert f(2, 4, 2, 128, 16, 128, 32, ops.PA_BF16) == want
     assert f(2, 4, 3, 128, 16, 128, 32, ops.PA_BF16) == ctypes.c_size_t(-1).value
     assert f(2, 4, 2, 128, 16, 128, 40, ops.PA_BF16) == ctypes.c_size_t(-1).value
