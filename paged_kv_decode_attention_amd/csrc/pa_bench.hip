@@ -14,13 +14,15 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
     u32x4 x = {0u, 0u, 0u, 0u};
     const uint64_t stride = (uint64_t)gridDim.x * kThreads;
     uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    // four independent loads in flight per iteration
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride],
-                    d = src[i + 3 * stride];
-        x ^= a ^ b ^ c ^ d;
+    // eight independent nontemporal loads in flight per iteration
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&src[i + u * stride]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x ^= v[u];
     }
-    for (; i < n16; i += stride) x ^= src[i];
+    for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(&src[i]);
     // reduce so the loads cannot be dropped; one write per workgroup
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) {

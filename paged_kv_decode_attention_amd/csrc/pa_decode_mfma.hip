@@ -84,29 +84,46 @@ __device__ __forceinline__ int2 chunk_blocks(const ConstI32* row, int c, int L, 
     return make_int2(pb0, pb1);
 }
 
-// Issue the 16 loads of one chunk (always 16, so the in-order load counter
-// the compiler waits on is the same on every path and the next chunk's
-// loads stay in flight while this one is computed).  KV is streamed once:
-// nontemporal loads.
+// Buffer descriptor of one 16-token tile (4 KB): base address, size.  A
+// size of 0 makes every load from it return zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, bool live) {
+    constexpr int kTileBytes = 16 * 128 * 2;
+    constexpr int kRawBufferFlags = 0x00020000;   // 32-bit data format: raw loads return data
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, live ? kTileBytes : 0,
+                                             kRawBufferFlags);
+}
+
+// Issue the 16 loads of one chunk: always 16, so the in-order load counter
+// the compiler waits on is the same on every path and the next chunk's loads
+// stay in flight while this one is computed.  KV is streamed once: loads are
+// nontemporal.  A tile that is not live (past the end of the history, or a
+// prefetch past the wave's last chunk) is read through an empty descriptor:
+// the loads return zeros and move no bytes.
+constexpr int kNonTemporal = 2;   // buffer cache-policy bit: nt
+
 template <int BS>
 __device__ __forceinline__ void load_chunk(ChunkRegs& r, const char* kbase, const char* vbase,
-                                           int2 pb, int kvh, int num_kv_heads, uint32_t koff,
-                                           uint32_t voff) {
+                                           int2 pb, bool live0, bool live1, int kvh,
+                                           int num_kv_heads, uint32_t koff, uint32_t voff) {
     constexpr int RB = 128 * 2;   // bytes per token row
     const uint64_t row0 = kv_row(pb.x, kvh, 0, num_kv_heads, BS) * RB;
     const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : 16, num_kv_heads, BS) * RB;
-    const u32x4* k0 = reinterpret_cast<const u32x4*>(kbase + row0 + koff);
-    const u32x4* k1 = reinterpret_cast<const u32x4*>(kbase + row1 + koff);
-    const u32x4* v0 = reinterpret_cast<const u32x4*>(vbase + row0 + voff);
-    const u32x4* v1 = reinterpret_cast<const u32x4*>(vbase + row1 + voff);
+    const __amdgpu_buffer_rsrc_t k0 = tile_rsrc(kbase + row0, live0);
+    const __amdgpu_buffer_rsrc_t k1 = tile_rsrc(kbase + row1, live1);
+    const __amdgpu_buffer_rsrc_t v0 = tile_rsrc(vbase + row0, live0);
+    const __amdgpu_buffer_rsrc_t v1 = tile_rsrc(vbase + row1, live1);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) r.k0[kk] = __builtin_nontemporal_load(k0 + kk * 4);
+    for (int kk = 0; kk < 4; ++kk)
+        r.k0[kk] = __builtin_amdgcn_raw_buffer_load_b128(k0, koff + kk * 64, 0, kNonTemporal);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) r.k1[kk] = __builtin_nontemporal_load(k1 + kk * 4);
+    for (int kk = 0; kk < 4; ++kk)
+        r.k1[kk] = __builtin_amdgcn_raw_buffer_load_b128(k1, koff + kk * 64, 0, kNonTemporal);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = __builtin_nontemporal_load(v0 + i * (RB / 16));
+    for (int i = 0; i < 4; ++i)
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(v0, voff + i * RB, 0, kNonTemporal);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[4 + i] = __builtin_nontemporal_load(v1 + i * (RB / 16));
+    for (int i = 0; i < 4; ++i)
+        r.v[4 + i] = __builtin_amdgcn_raw_buffer_load_b128(v1, voff + i * RB, 0, kNonTemporal);
 }
 
 // Running state of one wavefront: for head n (lane % 16), the reference max
@@ -253,30 +270,35 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
 
     // This wave's chunks are c0 + wave + kNW k, k < K.  Two register buffers:
     // while chunk k is computed, chunk k+1's loads are in flight and chunk
-    // k+2's block numbers are being fetched.  Past the last chunk the
-    // prefetch repeats the last chunk (its registers are never used).
+    // k+2's block numbers are being fetched (scalar loads of the table).
     const int first = c0 + wave;
     const int K = first < c1 ? (c1 - first + kNW - 1) / kNW : 0;
     if (K > 0) {
         auto chunk_of = [&](int k) { return first + kNW * min(k, K - 1); };
+        // tile 1 of chunk c is live when it holds history tokens
+        auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
         ChunkRegs bufA, bufB;
         int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
         int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
-        load_chunk<BS>(bufA, kbase, vbase, idsA, kvh, a.num_kv_heads, koff, voff);
+        load_chunk<BS>(bufA, kbase, vbase, idsA, true, tile1_live(0), kvh, a.num_kv_heads, koff,
+                       voff);
         int k = 0;
         // The scheduling barriers keep each phase's loads after the previous
         // chunk's math and before this chunk's: the load counter is in
         // order, so a load hoisted above the math would make it wait for
-        // the prefetch too.
+        // the prefetch too.  A prefetch past the wave's last chunk is issued
+        // dead (no bytes move) so that every path has 16 loads in flight.
         for (;;) {
             __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS>(bufB, kbase, vbase, idsB, kvh, a.num_kv_heads, koff, voff);
+            load_chunk<BS>(bufB, kbase, vbase, idsB, k + 1 < K, k + 1 < K && tile1_live(k + 1),
+                           kvh, a.num_kv_heads, koff, voff);
             idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
             compute_chunk<Tag>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
             if (++k >= K) break;
             __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS>(bufA, kbase, vbase, idsA, kvh, a.num_kv_heads, koff, voff);
+            load_chunk<BS>(bufA, kbase, vbase, idsA, k + 1 < K, k + 1 < K && tile1_live(k + 1),
+                           kvh, a.num_kv_heads, koff, voff);
             idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
             compute_chunk<Tag>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, q);
