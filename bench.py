@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
 A step is one pass of the whole hot path over one batch: the cache write of
-each sequence's newest token (reshape_and_cache) followed by decode attention
-of every sequence's query over its paged history.  The default workload is the
+each sequence's newest token followed by decode attention of every
+sequence's query over its paged history (one pa_decode_append call; with
+--unfused, reshape_and_cache then pa_paged_attention_decode).  The default workload is the
 Qwen-7B-shaped GQA batch (64 sequences, 28 query / 4 KV heads, head_dim 128,
 block size 16, context lengths ~ U[512, 4096], bf16).  Inputs are seeded
 synthetic tensors already resident in HBM.  Steps rotate over R copies of the
@@ -53,6 +54,8 @@ def parse():
                     help="time decode calls only (for counter runs)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="cache write and decode as two calls instead of pa_decode_append")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run the plain copy kernel of this size, 5 times")
     return ap.parse_args()
@@ -187,13 +190,19 @@ def main():
 
     def step(k, ev=None, decode_only=args.decode_only):
         r = k % R
-        if not decode_only:
+        if not decode_only and args.unfused:
             ops.reshape_and_cache(nk, nv, kcs[r], vcs[r], slots)
         if ev is not None:
             ev[0].record()
-        ops.paged_attention_decode(q, kcs[r], vcs[r], bt, cl, cfg.scale,
-                                   max_context_len=max_ctx, partition_size=args.partition_size,
-                                   out=out, workspace=ws)
+        if not decode_only and not args.unfused:
+            # the cache write of each sequence's newest token, fused
+            ops.decode_append(q, nk, nv, kcs[r], vcs[r], bt, cl, cfg.scale,
+                              max_context_len=max_ctx, partition_size=args.partition_size,
+                              out=out, workspace=ws)
+        else:
+            ops.paged_attention_decode(q, kcs[r], vcs[r], bt, cl, cfg.scale,
+                                       max_context_len=max_ctx,
+                                       partition_size=args.partition_size, out=out, workspace=ws)
         if ev is not None:
             ev[1].record()
 
@@ -280,7 +289,9 @@ def main():
                 lens.max()),
             "partition_size": P if args.partition_size else "balanced schedule",
             "kernel": args.kernel, "kv_pool_replicas": R,
-            "step": "decode only" if args.decode_only else "reshape_and_cache + decode",
+            "step": "decode only" if args.decode_only else (
+                "reshape_and_cache + decode" if args.unfused
+                else "decode_append (cache write of the newest token + decode)"),
             "launch": "eager" if args.eager else "hip graph of the K steps",
         },
         "roofline": {

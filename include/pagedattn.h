@@ -144,6 +144,41 @@ int pa_paged_attention_decode(void* out, const void* query,
                               size_t workspace_bytes, void* hip_stream);
 
 /*
+ * pa_decode_append -- one decode step: append each sequence's newest token to
+ * its paged history, then attend over the whole history (the step of
+ * [MiniPaged-Qwen] §8.1 -- append_token gives the new token's slot, the
+ * cache-write kernel stores it -- followed by §8.3's decode attention).
+ *
+ * context_lens already count the new token: sequence b's new token is its
+ * history position L_b - 1, stored at
+ *     key_cache  [block_tables[b, (L_b-1)/block_size], h, (L_b-1) % block_size, :] = key  [b, h, :]
+ *     value_cache[...]                                                       = value[b, h, :]
+ * for every KV head h, and then out is exactly what pa_paged_attention_decode
+ * returns on the updated caches (bit for bit).  Equivalent to
+ * pa_reshape_and_cache with those slots followed by pa_paged_attention_decode;
+ * the matrix-core path does both in one launch.
+ *
+ *   key, value     [num_seqs, num_kv_heads, head_dim] dtype, 16-byte aligned
+ *   key_cache,
+ *   value_cache    written at the new tokens' slots
+ *   all other arguments as for pa_paged_attention_decode.
+ *
+ * Precondition: the block that receives a sequence's new token is not read by
+ * any other sequence in the same call (the tail block of a sequence being
+ * appended to is private to it -- copy-on-write, [vLLM-paging]
+ * "Copy-on-write 是共享的正确性边界").  L_b = 0 appends nothing; an invalid
+ * length or a table entry outside the pool writes nothing and yields NaN
+ * rows, as for the decode call.
+ */
+int pa_decode_append(void* out, const void* query, const void* key, const void* value,
+                     void* key_cache, void* value_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                     int gqa_group_size, int head_dim, int block_size, int num_blocks,
+                     int max_blocks_per_seq, int max_context_len, float scale, pa_dtype dtype,
+                     int partition_size, void* workspace, size_t workspace_bytes,
+                     void* hip_stream);
+
+/*
  * pa_reshape_and_cache -- store new tokens' K/V into their cache slots.
  *
  * For every token i with s = slot_mapping[i] >= 0:

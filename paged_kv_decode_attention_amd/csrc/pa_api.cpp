@@ -174,14 +174,15 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
     return bytes;
 }
 
-int pa_paged_attention_decode(void* out, const void* query, const void* key_cache,
-                              const void* value_cache, const int32_t* block_tables,
-                              const int32_t* context_lens, int num_seqs, int num_heads,
-                              int num_kv_heads, int gqa_group_size, int head_dim,
-                              int block_size, int num_blocks, int max_blocks_per_seq,
-                              int max_context_len, float scale, pa_dtype dtype,
-                              int partition_size, void* workspace, size_t workspace_bytes,
-                              void* hip_stream) {
+}  // extern "C"
+
+static int decode_impl(void* out, const void* query, const void* new_key,
+                       const void* new_value, const void* key_cache, const void* value_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                       int num_heads, int num_kv_heads, int gqa_group_size, int head_dim,
+                       int block_size, int num_blocks, int max_blocks_per_seq,
+                       int max_context_len, float scale, pa_dtype dtype, int partition_size,
+                       void* workspace, size_t workspace_bytes, void* hip_stream) {
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
     if (num_heads <= 0 || num_kv_heads <= 0)
         return fail(PA_ERR_INVALID_ARG, "num_heads %d / num_kv_heads %d must be positive",
@@ -213,6 +214,9 @@ int pa_paged_attention_decode(void* out, const void* query, const void* key_cach
         return fail(PA_ERR_INVALID_ARG, "null tensor pointer");
     if (!aligned16(out) || !aligned16(query) || !aligned16(key_cache) || !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "query/out/cache pointers must be 16-byte aligned");
+    const bool append = new_key != nullptr || new_value != nullptr;
+    if (append && (!new_key || !new_value || !aligned16(new_key) || !aligned16(new_value)))
+        return fail(PA_ERR_INVALID_ARG, "new key/value must be non-null and 16-byte aligned");
     if (partition_size != 0 && !valid_partition(partition_size, block_size))
         return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a positive multiple of 32 "
                     "and of block_size, at most 64*block_size", partition_size);
@@ -265,14 +269,57 @@ int pa_paged_attention_decode(void* out, const void* query, const void* key_cach
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, s)
-                            : pa::launch_decode_generic(a, dtype, s);
+    hipError_t e = hipSuccess;
+    if (append && use_mfma) {
+        // the matrix-core kernel stores each newest token itself
+        a.new_key = new_key;
+        a.new_value = new_value;
+    } else if (append) {
+        e = pa::launch_append_tokens(new_key, new_value, const_cast<void*>(key_cache),
+                                     const_cast<void*>(value_cache), block_tables, context_lens,
+                                     num_seqs, num_kv_heads, head_dim * elem_bytes(dtype),
+                                     block_size, num_blocks, max_blocks_per_seq,
+                                     max_context_len, s);
+        if (e != hipSuccess) return hip_fail(e, "append kernel launch");
+    }
+    e = use_mfma ? pa::launch_decode_mfma(a, dtype, s) : pa::launch_decode_generic(a, dtype, s);
     if (e != hipSuccess) return hip_fail(e, "decode partition kernel launch");
     if (balanced || lay.num_parts > 1) {
         e = pa::launch_lse_merge(a, dtype, s);
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     }
     return PA_OK;
+}
+
+extern "C" {
+
+int pa_paged_attention_decode(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int num_seqs, int num_heads,
+                              int num_kv_heads, int gqa_group_size, int head_dim,
+                              int block_size, int num_blocks, int max_blocks_per_seq,
+                              int max_context_len, float scale, pa_dtype dtype,
+                              int partition_size, void* workspace, size_t workspace_bytes,
+                              void* hip_stream) {
+    return decode_impl(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                       context_lens, num_seqs, num_heads, num_kv_heads, gqa_group_size, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                       partition_size, workspace, workspace_bytes, hip_stream);
+}
+
+int pa_decode_append(void* out, const void* query, const void* key, const void* value,
+                     void* key_cache, void* value_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, int num_seqs, int num_heads, int num_kv_heads,
+                     int gqa_group_size, int head_dim, int block_size, int num_blocks,
+                     int max_blocks_per_seq, int max_context_len, float scale, pa_dtype dtype,
+                     int partition_size, void* workspace, size_t workspace_bytes,
+                     void* hip_stream) {
+    if (num_seqs > 0 && (!key || !value))
+        return fail(PA_ERR_INVALID_ARG, "null key/value pointer");
+    return decode_impl(out, query, key, value, key_cache, value_cache, block_tables,
+                       context_lens, num_seqs, num_heads, num_kv_heads, gqa_group_size, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                       partition_size, workspace, workspace_bytes, hip_stream);
 }
 
 int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,

@@ -24,14 +24,48 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
     const uint64_t th = idx / cols;              // token * H_kv + h
     const int h = (int)(th % num_kv_heads);
     const uint64_t i = th / num_kv_heads;
+    // the row loads do not depend on the slot: issue all three together
+    const uint64_t src = th * row_bytes + c * 16;
+    const u32x4 kv = load16(key + src);
+    const u32x4 vv = load16(value + src);
     const int64_t slot = slots[i];
     if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
     const int pb = (int)(slot / block_size);
     const int off = (int)(slot - (int64_t)pb * block_size);
     const uint64_t dst = kv_row(pb, h, off, num_kv_heads, block_size) * row_bytes + c * 16;
+    *reinterpret_cast<u32x4*>(key_cache + dst) = kv;
+    *reinterpret_cast<u32x4*>(value_cache + dst) = vv;
+}
+
+// Sequence b's newest token (history position L_b - 1): key[b, h, c] ->
+// key_cache[pb, h, off, c] with pb = block_tables[b, (L_b-1) / block_size],
+// off = (L_b-1) % block_size -- the append step of [MiniPaged-Qwen] §8.1 with
+// the slot taken from the table.  Empty or invalid lengths and table entries
+// outside the pool write nothing.
+__global__ __launch_bounds__(kCopyThreads) void append_tokens_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, char* key_cache,
+    char* value_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int num_seqs, int num_kv_heads, int row_bytes,
+    int block_size, int num_blocks, int max_blocks_per_seq, int max_context_len) {
+    const int cols = row_bytes / 16;
+    const uint64_t total = (uint64_t)num_seqs * num_kv_heads * cols;
+    const uint64_t idx = (uint64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    if (idx >= total) return;
+    const int c = (int)(idx % cols);
+    const uint64_t th = idx / cols;              // sequence * H_kv + h
+    const int h = (int)(th % num_kv_heads);
+    const uint64_t b = th / num_kv_heads;
     const uint64_t src = th * row_bytes + c * 16;
-    *reinterpret_cast<u32x4*>(key_cache + dst) = load16(key + src);
-    *reinterpret_cast<u32x4*>(value_cache + dst) = load16(value + src);
+    const u32x4 kv = load16(key + src);
+    const u32x4 vv = load16(value + src);
+    const int L = context_lens[b];
+    if (L <= 0 || L > max_context_len) return;
+    const int pos = L - 1;
+    const int pb = block_tables[b * max_blocks_per_seq + pos / block_size];
+    if ((unsigned)pb >= (unsigned)num_blocks) return;
+    const uint64_t dst = kv_row(pb, h, pos % block_size, num_kv_heads, block_size) * row_bytes + c * 16;
+    *reinterpret_cast<u32x4*>(key_cache + dst) = kv;
+    *reinterpret_cast<u32x4*>(value_cache + dst) = vv;
 }
 
 // History row t of sequence `seq`, KV head h -> k_out[h, t, :], through the
@@ -75,6 +109,22 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
                        static_cast<const char*>(key), static_cast<const char*>(value),
                        static_cast<char*>(key_cache), static_cast<char*>(value_cache), slots,
                        num_tokens, num_kv_heads, row_bytes, block_size, num_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_tokens(const void* key, const void* value, void* key_cache,
+                                void* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, int num_seqs, int num_kv_heads,
+                                int row_bytes, int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_context_len, hipStream_t s) {
+    const uint64_t total = (uint64_t)num_seqs * num_kv_heads * (row_bytes / 16);
+    if (total == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((total + kCopyThreads - 1) / kCopyThreads);
+    hipLaunchKernelGGL(append_tokens_kernel, dim3(grid), dim3(kCopyThreads), 0, s,
+                       static_cast<const char*>(key), static_cast<const char*>(value),
+                       static_cast<char*>(key_cache), static_cast<char*>(value_cache),
+                       block_tables, context_lens, num_seqs, num_kv_heads, row_bytes, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len);
     return hipGetLastError();
 }
 

@@ -261,6 +261,28 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
     const uint32_t voff = (uint32_t)(4 * q * D + 8 * n) * E;    // V row 4q, d 8n
     const float sl2 = a.scale_log2;
 
+    // Append step: the wave that will read the chunk holding the newest
+    // history position (L - 1) first stores that token's K/V row there.  Its
+    // own later load of the row follows in program order; no other
+    // wavefront reads the slot in this launch (the tail block of a sequence
+    // being appended to is private to it).
+    if (a.new_key != nullptr) {
+        const int c_last = (L - 1) / kChunk;
+        if (c_last >= c0 && c_last < c1 && (c_last - c0) % kNW == wave) {
+            const int pos = L - 1;
+            const int pb = row[pos / BS];
+            if ((unsigned)pb < (unsigned)a.num_blocks && lane < 32) {
+                const uint64_t dst =
+                    kv_row(pb, kvh, pos % BS, a.num_kv_heads, BS) * (D * E) + (lane & 15) * 16;
+                const uint64_t src = ((uint64_t)b * a.num_kv_heads + kvh) * (D * E) + (lane & 15) * 16;
+                const char* from = reinterpret_cast<const char*>(lane < 16 ? a.new_key : a.new_value);
+                char* to = reinterpret_cast<char*>(const_cast<void*>(lane < 16 ? a.key_cache
+                                                                               : a.value_cache));
+                *reinterpret_cast<u32x4*>(to + dst) = load16(from + src);
+            }
+        }
+    }
+
     WaveState st;
     st.m_ref = -INFINITY;
 #pragma unroll

@@ -90,30 +90,47 @@ struct BalancedPieces {
 // nheads - 1 of sequence b ("reduce locally, then merge globally",
 // [MiniPaged-Qwen] §10.2 (2)):
 //   o = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),  M = max_p lse_p,
-// the online update of §5.2 applied to whole pieces.  Summed in piece
-// (token) order, so the result is deterministic.
+// the online update of §5.2 applied to whole pieces: batches of kBatch
+// pieces are loaded together (one memory round trip per batch) and folded
+// into a running (max, denominator, numerator).  Always in piece (token)
+// order, so the result is deterministic.
 template <typename Tag, typename Pieces>
 __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const Pieces& pc, int b,
                                              int head0, int nheads, int npieces) {
+    constexpr int kBatch = 8;
     const int D = a.head_dim;
     const int D4 = D / 4;
     for (int it = threadIdx.x; it < nheads * D4; it += blockDim.x) {
         const int g = it / D4;
         const int d4 = it - g * D4;
-        float M = -INFINITY;
-        int has_nan = 0;
-        for (int p = 0; p < npieces; ++p) {
-            const float x = pc.lse_at(p, g);
-            has_nan |= (x != x);
-            M = fmaxf(M, x);
-        }
-        float den = 0.0f;
+        float M = -INFINITY, den = 0.0f;
         f32x4 num = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int p = 0; p < npieces; ++p) {
-            const float w = fast_exp2(pc.lse_at(p, g) - M);
-            den += w;
-            num += w * pc.o_at(p, g)[d4];
+        int has_nan = 0;
+        for (int p0 = 0; p0 < npieces; p0 += kBatch) {
+            f32x4 o[kBatch];
+            float lse[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const int p = min(p0 + k, npieces - 1);
+                o[k] = pc.o_at(p, g)[d4];
+                lse[k] = p0 + k < npieces ? pc.lse_at(p, g) : -INFINITY;
+            }
+            float mb = M;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                has_nan |= (lse[k] != lse[k]);
+                mb = fmaxf(mb, lse[k]);
+            }
+            const float keep = rescale_weight(M, mb);
+            den *= keep;
+            num *= keep;
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const float w = rescale_weight(lse[k], mb);
+                den += w;
+                num += w * o[k];
+            }
+            M = mb;
         }
         const uint64_t out0 = ((uint64_t)b * a.num_heads + head0 + g) * D + 4 * d4;
 #pragma unroll

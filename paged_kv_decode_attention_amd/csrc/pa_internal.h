@@ -19,6 +19,8 @@ struct DecodeArgs {
     const void* value_cache;   // [N, H_kv, BS, D] dtype
     const int32_t* block_tables;   // [S, W]
     const int32_t* context_lens;   // [S]
+    const void* new_key;       // [S, H_kv, D] appended token per sequence, or null
+    const void* new_value;     // [S, H_kv, D]
     float* ws_lse;             // [S, H, num_parts] float32 (log2 units)
     float* ws_out;             // [S, H, num_parts, D] float32
     int num_seqs, num_heads, num_kv_heads, group, head_dim, block_size;
@@ -61,6 +63,14 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value,
                                     int num_kv_heads, int row_bytes,
                                     int block_size, int num_blocks,
                                     hipStream_t s);
+
+// Store the newest token of every sequence (history position L_b - 1) into
+// its cache slot, read from the sequence's block table.
+hipError_t launch_append_tokens(const void* key, const void* value, void* key_cache,
+                                void* value_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, int num_seqs, int num_kv_heads,
+                                int row_bytes, int block_size, int num_blocks,
+                                int max_blocks_per_seq, int max_context_len, hipStream_t s);
 
 hipError_t launch_gather(void* k_out, void* v_out, const void* key_cache,
                          const void* value_cache, const int32_t* block_tables,

@@ -28,13 +28,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
 
 // Balanced schedule: the pieces of (b, kvh) are the slots of the workgroup
 // ranges its chunks fall in.  Also writes the rows the decode kernel skips:
-// zeros for an empty history, NaN for an invalid context length.
+// zeros for an empty history, NaN for an invalid context length.  Only two
+// sums over the context lengths are needed (chunks before sequence b, and in
+// total), so they are a single workgroup reduction rather than a prefix table.
 template <typename Tag>
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced(DecodeArgs a) {
-    __shared__ int pref[kMaxBalancedSeqs + 1];
-    __shared__ int wsum[kMergeThreads / 64];
+    constexpr int NW = kMergeThreads / 64;
+    __shared__ int red_before[NW], red_total[NW];
     __shared__ int slots[kMaxBalancedWg + 1];
-    __shared__ int npieces;
+    __shared__ int live[kMaxBalancedWg + 1];
     const int kvh = blockIdx.x;
     const int b = blockIdx.y;
     const int head0 = kvh * a.group;
@@ -47,24 +49,54 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced(DecodeArgs a) {
         fill_rows<Tag>(a, b, head0, a.group, 0.0f);
         return;
     }
-    chunk_prefix(a, pref, wsum);
+    int before = 0, total = 0;
+    for (int i = threadIdx.x; i < a.num_seqs; i += kMergeThreads) {
+        const int c = seq_chunks(a.context_lens[i], a.max_context_len);
+        total += c;
+        if (i < b) before += c;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        before += __shfl_xor(before, off);
+        total += __shfl_xor(total, off);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red_before[threadIdx.x >> 6] = before;
+        red_total[threadIdx.x >> 6] = total;
+    }
+    __syncthreads();
+    before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        before += red_before[w];
+        total += red_total[w];
+    }
     const int H_kv = a.num_kv_heads;
-    const int64_t T = (int64_t)H_kv * pref[a.num_seqs];
-    const int nb = pref[b + 1] - pref[b];
-    const int64_t x0 = (int64_t)H_kv * pref[b] + (int64_t)kvh * nb;
+    const int64_t T = (int64_t)H_kv * total;
+    const int nb = seq_chunks(L, a.max_context_len);
+    const int64_t x0 = (int64_t)H_kv * before + (int64_t)kvh * nb;
     const int w0 = range_owner(x0, T, a.num_wg);
     const int w1 = range_owner(x0 + nb - 1, T, a.num_wg);
     if (w0 == w1) return;   // one range held the whole history
+    // piece k is slot [w0][1] for k = 0, then [w][0] for each non-empty
+    // range w in (w0, w1]
+    const int span = w1 - w0;
+    for (int k = threadIdx.x; k < span; k += kMergeThreads) {
+        const int w = w0 + 1 + k;
+        live[k] = range_start(w, T, a.num_wg) < range_start(w + 1, T, a.num_wg);
+    }
+    __syncthreads();
     if (threadIdx.x == 0) {
-        int k = 0;
-        slots[k++] = 2 * w0 + 1;
-        for (int w = w0 + 1; w <= w1; ++w)
-            if (range_start(w, T, a.num_wg) < range_start(w + 1, T, a.num_wg)) slots[k++] = 2 * w;
-        npieces = k;
+        int n = 0;
+        slots[n++] = 2 * w0 + 1;
+        for (int k = 0; k < span; ++k)
+            if (live[k]) slots[n++] = 2 * (w0 + 1 + k);
+        live[kMaxBalancedWg] = n;
     }
     __syncthreads();
     const BalancedPieces pc{a.ws_lse, a.ws_out, slots, a.head_dim};
-    merge_pieces<Tag>(a, pc, b, head0, a.group, npieces);
+    merge_pieces<Tag>(a, pc, b, head0, a.group, live[kMaxBalancedWg]);
 }
 
 template <typename Tag>

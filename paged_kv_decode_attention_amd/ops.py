@@ -35,6 +35,10 @@ _SIGNATURES = {
         _I, [_VP, _VP, _VP, _VP, _VP, _VP,
              _I, _I, _I, _I, _I, _I, _I, _I, _I,
              ctypes.c_float, _I, _I, _VP, ctypes.c_size_t, _VP]),
+    "pa_decode_append": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+             _I, _I, _I, _I, _I, _I, _I, _I, _I,
+             ctypes.c_float, _I, _I, _VP, ctypes.c_size_t, _VP]),
     "pa_reshape_and_cache": (
         _I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP]),
     "pa_debug_gather_kv": (
@@ -117,16 +121,8 @@ def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_siz
     return n
 
 
-def paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens,
-                           scale=None, *, max_context_len=None, partition_size=0,
-                           out=None, workspace=None):
-    """Single-step decode attention over a paged KV cache.
-
-    query [S, H, D]; key_cache/value_cache [N, H_kv, BS, D] (same dtype);
-    block_tables [S, W] int32; context_lens [S] int32.  The GQA group size is
-    H / H_kv.  max_context_len defaults to W * BS (no device sync).  Returns
-    out [S, H, D] in the query dtype.
-    """
+def _decode_args(query, key_cache, value_cache, block_tables, context_lens, scale,
+                 max_context_len, partition_size, out, workspace):
     for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
                  (block_tables, "block_tables"), (context_lens, "context_lens")):
         _gpu(t, n)
@@ -155,19 +151,56 @@ def paged_attention_decode(query, key_cache, value_cache, block_tables, context_
         _gpu(out, "out")
         if out.shape != query.shape or out.dtype != query.dtype:
             raise ValueError("out must match query in shape and dtype")
-    code = dtype_code(query.dtype)
-    lib = load_library()
     ws_bytes = decode_workspace_size(S, H, H_kv, D, BS, max_context_len, partition_size,
                                      query.dtype)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=query.device)
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    status = lib.pa_paged_attention_decode(
+    sizes = (S, H, H_kv, H // H_kv, D, BS, N, W, int(max_context_len))
+    tail = (float(scale), dtype_code(query.dtype), int(partition_size), ws_ptr, ws_len,
+            _stream(query.device))
+    return out, sizes, tail
+
+
+def paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens,
+                           scale=None, *, max_context_len=None, partition_size=0,
+                           out=None, workspace=None):
+    """Single-step decode attention over a paged KV cache.
+
+    query [S, H, D]; key_cache/value_cache [N, H_kv, BS, D] (same dtype);
+    block_tables [S, W] int32; context_lens [S] int32.  The GQA group size is
+    H / H_kv.  max_context_len defaults to W * BS (no device sync).  Returns
+    out [S, H, D] in the query dtype.
+    """
+    out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
+                                    scale, max_context_len, partition_size, out, workspace)
+    status = load_library().pa_paged_attention_decode(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
-        _ptr(context_lens), S, H, H_kv, H // H_kv, D, BS, N, W, int(max_context_len),
-        float(scale), code, int(partition_size), ws_ptr, ws_len, _stream(query.device))
+        _ptr(context_lens), *sizes, *tail)
     _check(status, "paged_attention_decode")
+    return out
+
+
+def decode_append(query, key, value, key_cache, value_cache, block_tables, context_lens,
+                  scale=None, *, max_context_len=None, partition_size=0, out=None,
+                  workspace=None):
+    """One decode step: store each sequence's newest token key/value [S, H_kv, D]
+    at its history position context_lens[b] - 1 (slot from the block table),
+    then attend.  context_lens count the new token.  In place on the caches."""
+    out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
+                                    scale, max_context_len, partition_size, out, workspace)
+    for t, n in ((key, "key"), (value, "value")):
+        _gpu(t, n)
+    S, H_kv, D = query.shape[0], key_cache.shape[1], query.shape[2]
+    if key.shape != (S, H_kv, D) or value.shape != key.shape:
+        raise ValueError("key and value must be [S, H_kv, D]")
+    if key.dtype != query.dtype or value.dtype != query.dtype:
+        raise ValueError("key/value must share the query dtype")
+    status = load_library().pa_decode_append(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+        _ptr(block_tables), _ptr(context_lens), *sizes, *tail)
+    _check(status, "decode_append")
     return out
 
 

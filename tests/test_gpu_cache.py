@@ -86,3 +86,56 @@ def test_tiny_config_cache_write():
                                       inp.slot_mapping.numpy())
     assert np.array_equal(bits(d["key_cache"]), rk)
     assert np.array_equal(bits(d["value_cache"]), rv)
+
+
+@pytest.mark.parametrize("name,kernel,partition_size", [
+    ("qwen7b_gqa_bf16", ops.KERNEL_AUTO, 0),       # matrix core, balanced schedule
+    ("qwen7b_gqa_bf16", ops.KERNEL_MFMA, 256),     # matrix core, fixed partitions
+    ("qwen7b_gqa_bf16", ops.KERNEL_GENERIC, 0),    # vector ALU: append kernel + decode
+    ("long_ctx_bf16", ops.KERNEL_AUTO, 0),
+    ("tiny_fp32", ops.KERNEL_AUTO, 0),
+])
+def test_decode_append_equals_write_then_decode(name, kernel, partition_size):
+    """The fused step gives bit for bit the caches and output of
+    reshape_and_cache at each sequence's last position followed by decode."""
+    cfg = I.CONFIGS[name]
+    inp = I.generate(cfg, new_tokens_at="last")
+    prev = ops.select_kernel(kernel)
+    try:
+        d1 = upload(inp)
+        ops.reshape_and_cache(d1["new_key"], d1["new_value"], d1["key_cache"],
+                              d1["value_cache"], d1["slot_mapping"])
+        o1 = ops.paged_attention_decode(d1["query"], d1["key_cache"], d1["value_cache"],
+                                        d1["block_tables"], d1["context_lens"],
+                                        partition_size=partition_size)
+        d2 = upload(inp)
+        o2 = ops.decode_append(d2["query"], d2["new_key"], d2["new_value"], d2["key_cache"],
+                               d2["value_cache"], d2["block_tables"], d2["context_lens"],
+                               partition_size=partition_size)
+        torch.cuda.synchronize()
+    finally:
+        ops.select_kernel(prev)
+    assert torch.equal(o1, o2)
+    assert torch.equal(d1["key_cache"], d2["key_cache"])
+    assert torch.equal(d1["value_cache"], d2["value_cache"])
+
+
+def test_decode_append_against_oracle():
+    cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_seqs=6, num_blocks=400,
+                           max_blocks_per_seq=64, lens_kind="list",
+                           lens_args=(1, 16, 17, 33, 500, 1024))
+    inp = I.poison_unread(I.generate(cfg, new_tokens_at="last"))
+    d = upload(inp)
+    out = ops.decode_append(d["query"], d["new_key"], d["new_value"], d["key_cache"],
+                            d["value_cache"], d["block_tables"], d["context_lens"])
+    torch.cuda.synchronize()
+    kc, vc = oracle.reshape_and_cache(bits(inp.new_key), bits(inp.new_value),
+                                      bits(inp.key_cache), bits(inp.value_cache),
+                                      inp.slot_mapping.numpy())
+    assert np.array_equal(bits(d["key_cache"]), kc)
+    assert np.array_equal(bits(d["value_cache"]), vc)
+    kcf = torch.from_numpy(kc).view(torch.bfloat16).float().numpy()
+    vcf = torch.from_numpy(vc).view(torch.bfloat16).float().numpy()
+    ref = oracle.decode_contiguous(inp.query.float().numpy(), kcf, vcf,
+                                   inp.block_tables.numpy(), inp.context_lens.numpy(), cfg.scale)
+    compare(out, ref, "bf16", what="decode_append vs oracle")
