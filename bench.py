@@ -24,7 +24,6 @@ a bounded sample of the same workload.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -33,8 +32,6 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attention tokens/s and achieved KV HBM GB/s (% of peak), 1 MI355X"
-KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_generic.hip", "pa_merge.hip",
-                  "pa_finalize.h", "pa_device.h", "pa_api.cpp"]
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_qwen7b_gqa_bf16_traffic.json")
 
 
@@ -62,11 +59,8 @@ def parse():
 
 
 def kernel_source_hash():
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(HERE, "paged_kv_decode_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+    from paged_kv_decode_attention_amd.build import decode_source_hash
+    return decode_source_hash()
 
 
 def load_traffic(config_name, per_launch_alg_bytes):

@@ -38,6 +38,22 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
 
 
+# Sources whose change changes what the decode call's kernels do; hashed to
+# tell whether stored counter readings still describe the built kernels.
+DECODE_SOURCES = ["pa_decode_mfma.hip", "pa_decode_generic.hip", "pa_merge.hip",
+                  "pa_finalize.h", "pa_device.h", "pa_api.cpp"]
+
+
+def decode_source_hash():
+    """First 16 hex digits of the SHA-256 of the decode sources, in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc():
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):

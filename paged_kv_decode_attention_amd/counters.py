@@ -1,0 +1,124 @@
+"""HBM bytes of one decode call, from rocprofv3 counter runs.
+
+    python -m paged_kv_decode_attention_amd.counters \\
+        --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
+        --copy-bytes N --config NAME --out FILE.json [--command CMD ...]
+
+Each DIR holds the ``*_counter_collection.csv`` of one
+``rocprofv3 --pmc FETCH_SIZE`` (or ``WRITE_SIZE``) ``--output-format csv``
+run.  The decode runs profile ``bench.py --decode-only``; the copy runs
+profile ``bench.py --copy-calibration-mib M``, a plain copy of N = M MiB that
+reads N bytes and writes N bytes.  The counters read in KiB per dispatch
+and are not taken at face value: the copy kernel's reading of each counter
+gives that counter's factor (true bytes per counted KiB), and every decode
+kernel's reading is scaled by it.
+
+The result is the bytes one decode call moves (its partition kernel plus its
+merge kernel, averaged per dispatch), next to the algorithmic K/V bytes of
+the same workload and the hash of the decode sources the runs were taken on.
+"""
+
+import argparse
+import csv
+import glob
+import json
+import os
+import sys
+from collections import defaultdict
+
+# Kernels of a decode call, matched by substring of the demangled name.
+DECODE_KERNELS = ("decode_mfma", "decode_generic", "merge_")
+COPY_KERNEL = "copy_kernel"
+
+
+def read_counter(run_dir, counter):
+    """{kernel name: [per-dispatch values]} of one counter in one run."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError("no counter_collection.csv under " + run_dir)
+    out = defaultdict(list)
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] == counter:
+                    out[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+    return out
+
+
+def short_name(name):
+    n = name.replace("void ", "").replace("pa::(anonymous namespace)::", "")
+    return n.split("(")[0]
+
+
+def per_dispatch(readings, keys):
+    """Mean reading per dispatch of every kernel whose name holds one of keys."""
+    res = {}
+    for name, vals in readings.items():
+        if any(k in name for k in keys):
+            res[short_name(name)] = (sum(vals) / len(vals), len(vals))
+    return res
+
+
+def calibration(run_dir, counter, copy_bytes):
+    vals = per_dispatch(read_counter(run_dir, counter), (COPY_KERNEL,))
+    if len(vals) != 1:
+        raise ValueError("expected one copy kernel in %s, found %s" % (run_dir, list(vals)))
+    kib, _ = next(iter(vals.values()))
+    return copy_bytes / kib
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--copy-fetch", required=True)
+    ap.add_argument("--copy-write", required=True)
+    ap.add_argument("--copy-bytes", type=int, required=True)
+    ap.add_argument("--config", default="qwen7b_gqa_bf16")
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", action="append", default=[],
+                    help="a command the readings came from (repeatable)")
+    a = ap.parse_args(argv)
+
+    from . import inputs as I
+    from .build import decode_source_hash
+
+    f_fetch = calibration(a.copy_fetch, "FETCH_SIZE", a.copy_bytes)
+    f_write = calibration(a.copy_write, "WRITE_SIZE", a.copy_bytes)
+    fetch = per_dispatch(read_counter(a.fetch, "FETCH_SIZE"), DECODE_KERNELS)
+    write = per_dispatch(read_counter(a.write, "WRITE_SIZE"), DECODE_KERNELS)
+    if not fetch or set(fetch) != set(write):
+        raise ValueError("decode kernels differ between runs: %s vs %s"
+                         % (sorted(fetch), sorted(write)))
+    kernels = {}
+    total = 0.0
+    for k in sorted(fetch):
+        fb = fetch[k][0] * f_fetch
+        wb = write[k][0] * f_write
+        kernels[k] = {"dispatches": fetch[k][1], "fetch_kib": fetch[k][0],
+                      "write_kib": write[k][0], "fetch_bytes": fb, "write_bytes": wb}
+        total += fb + wb
+    cfg = I.CONFIGS[a.config]
+    alg = I.kv_bytes_read(cfg, I.draw_context_lens(cfg))
+    rec = {
+        "config": a.config,
+        "kernel_src_sha": decode_source_hash(),
+        "hbm_bytes_per_launch": total,
+        "alg_bytes_per_launch": alg,
+        "traffic_over_alg": total / alg,
+        "fetch_factor_bytes_per_kib": f_fetch,
+        "write_factor_bytes_per_kib": f_write,
+        "copy_calibration_bytes": a.copy_bytes,
+        "kernels": kernels,
+        "commands": a.command,
+    }
+    with open(a.out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps({"hbm_bytes_per_launch": total, "alg": alg, "ratio": total / alg,
+                      "fetch_factor": f_fetch, "write_factor": f_write}))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -282,6 +282,13 @@ def poison_unread(inp, value=float("nan")):
     return inp
 
 
+def draw_context_lens(cfg, seed=None):
+    """The context lengths generate() draws for cfg (the first draw of its
+    stream), without building the rest of the workload."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    return _draw_lens(rng, cfg)
+
+
 def kv_bytes_read(cfg, context_lens):
     """Algorithmic K+V bytes one decode call reads: every history token's K
     and V row of every KV head, once."""
