@@ -1,8 +1,12 @@
-"""HBM bytes of one decode call, from rocprofv3 counter runs.
+"""Summaries of rocprofv3 runs of the decode call.
 
-    python -m paged_kv_decode_attention_amd.counters \\
+    python -m paged_kv_decode_attention_amd.counters traffic \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --copy-bytes N --config NAME --out FILE.json [--command CMD ...]
+    python -m paged_kv_decode_attention_amd.counters trace \\
+        --db FILE.db --out FILE.md --title TEXT --command CMD [--note TEXT ...]
+
+traffic: HBM bytes of one decode call, from counter runs.
 
 Each DIR holds the ``*_counter_collection.csv`` of one
 ``rocprofv3 --pmc FETCH_SIZE`` (or ``WRITE_SIZE``) ``--output-format csv``
@@ -67,8 +71,48 @@ def calibration(run_dir, counter, copy_bytes):
     return copy_bytes / kib
 
 
+def trace_table(db):
+    """(kernel, calls, avg us, min us, max us, share of traced kernel time)
+    per kernel of a rocprofv3 --kernel-trace database, longest total first."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        rows = con.execute(
+            "select name, count(*), avg(end - start), min(end - start), max(end - start), "
+            "sum(end - start) from kernels group by name order by sum(end - start) desc"
+        ).fetchall()
+    finally:
+        con.close()
+    total = sum(r[5] for r in rows) or 1
+    return [(short_name(r[0]), r[1], r[2] / 1e3, r[3] / 1e3, r[4] / 1e3, 100.0 * r[5] / total)
+            for r in rows]
+
+
+def trace_main(a):
+    lines = ["# " + a.title, "", "Command (repository root, one MI355X):", "",
+             "    " + a.command, "",
+             "| kernel | calls | avg us | min us | max us | % of traced kernel time |",
+             "|---|---|---|---|---|---|"]
+    for k, n, avg, lo, hi, share in trace_table(a.db):
+        lines.append("| %s | %d | %.2f | %.2f | %.2f | %.1f |" % (k, n, avg, lo, hi, share))
+    if a.note:
+        lines += [""] + ["- " + t for t in a.note]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    top = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = top.add_subparsers(dest="cmd", required=True)
+    tr = sub.add_parser("trace", help="kernel table of a --kernel-trace database")
+    tr.add_argument("--db", required=True)
+    tr.add_argument("--out", required=True)
+    tr.add_argument("--title", required=True)
+    tr.add_argument("--command", required=True)
+    tr.add_argument("--note", action="append", default=[])
+    ap = sub.add_parser("traffic", help="HBM bytes per decode call from counter runs")
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
     ap.add_argument("--copy-fetch", required=True)
@@ -78,7 +122,9 @@ def main(argv=None):
     ap.add_argument("--out", required=True)
     ap.add_argument("--command", action="append", default=[],
                     help="a command the readings came from (repeatable)")
-    a = ap.parse_args(argv)
+    a = top.parse_args(argv)
+    if a.cmd == "trace":
+        return trace_main(a)
 
     from . import inputs as I
     from .build import decode_source_hash

@@ -40,7 +40,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced(DecodeArgs a) {
     const int kvh = blockIdx.x;
     const int b = blockIdx.y;
     const int head0 = kvh * a.group;
+    // The first batch of lengths is loaded together with L_b: one memory
+    // round trip before the checks below.
     const int L = a.context_lens[b];
+    const int i0 = threadIdx.x;
+    const int len0 = i0 < a.num_seqs ? a.context_lens[i0] : 0;
     if (L < 0 || L > a.max_context_len) {
         fill_rows<Tag>(a, b, head0, a.group, __builtin_nanf(""));
         return;
@@ -49,8 +53,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced(DecodeArgs a) {
         fill_rows<Tag>(a, b, head0, a.group, 0.0f);
         return;
     }
-    int before = 0, total = 0;
-    for (int i = threadIdx.x; i < a.num_seqs; i += kMergeThreads) {
+    int total = seq_chunks(len0, a.max_context_len);
+    int before = i0 < b ? total : 0;
+    for (int i = i0 + kMergeThreads; i < a.num_seqs; i += kMergeThreads) {
         const int c = seq_chunks(a.context_lens[i], a.max_context_len);
         total += c;
         if (i < b) before += c;
