@@ -380,15 +380,202 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
     }
 }
 
-// Balanced schedule: the flattened (sequence, kv head, chunk) work list is
-// cut into gridDim.x equal ranges, one per workgroup (all resident at once).
-// Each workgroup walks the segments of its range; a segment that is a whole
-// history writes its output rows, one cut by the range boundary writes a
-// partial state into slot [w][0] (continues from the previous range) or
-// [w][1] (continues into the next) for the merge kernel.
+// ---- balanced schedule ----------------------------------------------------
+//
+// The flattened (sequence, KV head, chunk) work list is cut into gridDim.x
+// equal ranges, one per workgroup (all resident at once), and each range
+// into kNW contiguous wavefront ranges.  A wavefront walks its own range
+// with no barrier: a (sequence, KV head) segment lying wholly inside it is
+// finished there and its output rows written; the segment the wavefront
+// starts inside and the one it ends inside ("edge pieces", at most two) are
+// staged in LDS.  After one barrier the workgroup merges the edge pieces of
+// each segment and writes either its output rows (the segment lies inside
+// the workgroup's range) or a partial state in slot [w][0] (continues from
+// the previous range) or [w][1] (continues into the next) for the merge
+// kernel.
+
+// Edge pieces of the workgroup's wavefronts, in work-list order: piece
+// 2 v + 0 is the segment wavefront v starts inside (or its only piece),
+// 2 v + 1 the one it ends inside.  key: sequence * num_kv_heads + KV head of
+// the piece's segment, -1 when the piece is absent.
+struct EdgeLds {
+    float m[2 * kNW][16];
+    float l[2 * kNW][16];
+    __attribute__((aligned(16))) float o[2 * kNW][16 * kOS];
+    int key[2 * kNW];
+    int bad[2 * kNW];
+};
+
+// Wavefront state over chunks [cs, ce) of (sequence b, KV head kvh) with a
+// history of L tokens: the two-buffer pipeline of attend_segment with the
+// chunks taken in order.  Includes the append step when the newest history
+// position lies in [cs, ce): this wavefront alone reads that chunk.
+template <typename Tag, int BS>
+__device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh, int L, int cs,
+                                             int ce, WaveState& st, int& bad) {
+    constexpr int D = 128;
+    constexpr int E = 2;
+    const int G = a.group;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int q = lane >> 4;
+    const int t_end = min(ce * kChunk, L);
+
+    u32x4 qop[4];
+    if (n < G) {
+        const char* qp = reinterpret_cast<const char*>(a.query) +
+                         (((uint64_t)b * a.num_heads + kvh * G + n) * D + 8 * q) * E;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qop[kk] = load16(qp + kk * 64);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qop[kk] = (u32x4){0u, 0u, 0u, 0u};
+    }
+
+    const char* kbase = reinterpret_cast<const char*>(a.key_cache);
+    const char* vbase = reinterpret_cast<const char*>(a.value_cache);
+    const ConstI32* row =
+        (const ConstI32*)(a.block_tables) + (uint64_t)b * a.max_blocks_per_seq;
+    const uint32_t koff = (uint32_t)(n * D + 8 * q) * E;        // K row n, d 8q
+    const uint32_t voff = (uint32_t)(4 * q * D + 8 * n) * E;    // V row 4q, d 8n
+    const float sl2 = a.scale_log2;
+
+    if (a.new_key != nullptr) {
+        const int c_last = (L - 1) / kChunk;
+        if (c_last >= cs && c_last < ce) {
+            const int pos = L - 1;
+            const int pb = row[pos / BS];
+            if ((unsigned)pb < (unsigned)a.num_blocks && lane < 32) {
+                const uint64_t dst =
+                    kv_row(pb, kvh, pos % BS, a.num_kv_heads, BS) * (D * E) + (lane & 15) * 16;
+                const uint64_t src =
+                    ((uint64_t)b * a.num_kv_heads + kvh) * (D * E) + (lane & 15) * 16;
+                const char* from =
+                    reinterpret_cast<const char*>(lane < 16 ? a.new_key : a.new_value);
+                char* to = reinterpret_cast<char*>(const_cast<void*>(lane < 16 ? a.key_cache
+                                                                               : a.value_cache));
+                *reinterpret_cast<u32x4*>(to + dst) = load16(from + src);
+            }
+        }
+    }
+
+    const int K = ce - cs;
+    auto chunk_of = [&](int k) { return cs + min(k, K - 1); };
+    auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
+    ChunkRegs bufA, bufB;
+    int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
+    int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
+    load_chunk<BS>(bufA, kbase, vbase, idsA, true, tile1_live(0), kvh, a.num_kv_heads, koff,
+                   voff);
+    int k = 0;
+    for (;;) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk<BS>(bufB, kbase, vbase, idsB, k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
+                       a.num_kv_heads, koff, voff);
+        idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_chunk<Tag>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+        if (++k >= K) break;
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk<BS>(bufA, kbase, vbase, idsA, k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
+                       a.num_kv_heads, koff, voff);
+        idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_chunk<Tag>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+        if (++k >= K) break;
+    }
+}
+
+// Output rows of a whole history held by one wavefront: o = õ / l for the
+// G heads of the group (lane 16 q + n holds head n, d = 32 q + 8 i + j in
+// acc[j][i]), rounded once to the storage type; NaN when a table entry was
+// out of the pool.
+template <typename Tag>
+__device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh,
+                                           const WaveState& st, bool bad) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int q = lane >> 4;
+    if (n >= a.group) return;
+    const float l = st.acc_l[0];
+    char* orow = reinterpret_cast<char*>(a.out) +
+                 (((uint64_t)b * a.num_heads + kvh * a.group + n) * 128 + 32 * q) * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = bad ? __builtin_nanf("") : st.acc[j][i] / l;
+        const u32x4 v = {pack2(Tag(), o[0], o[1]), pack2(Tag(), o[2], o[3]),
+                         pack2(Tag(), o[4], o[5]), pack2(Tag(), o[6], o[7])};
+        *reinterpret_cast<u32x4*>(orow + 16 * i) = v;
+    }
+}
+
+// Merge of the edge pieces in `mask` (bit p: piece p) of one segment (the
+// update of [MiniPaged-Qwen] §5.2 applied to whole states, in piece order)
+// and its write: output rows when plse == nullptr, else the partial state
+// (o~/l, m + log2 l) at (plse, po).  Called by every thread of the
+// workgroup; a thread takes 4 consecutive d of one head.  The pieces are
+// listed by position (absent slots repeat the last piece with weight 0) so
+// that all of a thread's LDS reads are issued together.
+template <typename Tag>
+__device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLds& e,
+                                               unsigned mask, int b, int kvh, bool bad,
+                                               float* plse, float* po) {
+    constexpr int NP = 2 * kNW;
+    const int G = a.group;
+    int idx[NP];
+    bool on[NP];
+    unsigned mm = mask;
+    int last = 0;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        on[k] = mm != 0;
+        idx[k] = on[k] ? __builtin_ctz(mm) : last;
+        last = idx[k];
+        mm &= mm - 1;
+    }
+    for (int it = threadIdx.x; it < G * 32; it += blockDim.x) {
+        const int g = it >> 5;
+        const int d = (it & 31) * 4;
+        float mv[NP], lv[NP];
+        f32x4 ov[NP];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            mv[k] = e.m[idx[k]][g];
+            lv[k] = e.l[idx[k]][g];
+            ov[k] = *reinterpret_cast<const f32x4*>(&e.o[idx[k]][g * kOS + d]);
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NP; ++k) M = fmaxf(M, on[k] ? mv[k] : -INFINITY);
+        float den = 0.0f;
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const float w = on[k] ? rescale_weight(mv[k], M) : 0.0f;
+            den += w * lv[k];
+            num += w * ov[k];
+        }
+        f32x4 o = num / den;
+        if (bad) o = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                             __builtin_nanf("")};
+        if (plse == nullptr) {
+            const uint32_t lo = pack2(Tag(), o[0], o[1]);
+            const uint32_t hi = pack2(Tag(), o[2], o[3]);
+            char* dst = reinterpret_cast<char*>(a.out) +
+                        (((uint64_t)b * a.num_heads + kvh * G + g) * 128 + d) * 2;
+            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        } else {
+            *reinterpret_cast<f32x4*>(po + g * 128 + d) = o;
+            if (d == 0) plse[g] = bad ? __builtin_nanf("") : M + __log2f(den);
+        }
+    }
+}
+
 template <typename Tag, int BS>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
-    __shared__ SegmentLds sm;
+    __shared__ EdgeLds edge;
     __shared__ int pref[kMaxBalancedSeqs + 1];
     __shared__ int wsum[kNW];
     chunk_prefix(a, pref, wsum);
@@ -398,25 +585,90 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     const int w = blockIdx.x;
     const int64_t xb = range_start(w, T, a.num_wg);
     const int64_t xe = range_start(w + 1, T, a.num_wg);
-    int64_t x = xb;
-    while (x < xe) {
+    if (xb >= xe) return;
+
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int q = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t ws = xb + wave * (xe - xb) / kNW;       // this wavefront's range
+    const int64_t we = xb + (wave + 1) * (xe - xb) / kNW;
+    if (lane < 2) edge.key[2 * wave + lane] = -1;
+
+    for (int64_t x = ws; x < we;) {
         const int b = __builtin_amdgcn_readfirstlane(find_seq(pref, a.num_seqs, H_kv, x));
-        const int nb = pref[b + 1] - pref[b];
+        const int nb = __builtin_amdgcn_readfirstlane(pref[b + 1] - pref[b]);
         const int64_t off = x - (int64_t)H_kv * pref[b];
-        const int kvh = (int)(off / nb);
-        const int c0 = (int)(off - (int64_t)kvh * nb);
-        const int c1 = (int)min((int64_t)nb, c0 + (xe - x));
-        const bool head = c0 > 0;          // continues from the previous range
-        const bool tail = c1 < nb;         // continues into the next range
-        const int L = a.context_lens[b];
-        if (!head && !tail) {
-            attend_segment<Tag, BS>(a, sm, b, kvh, L, c0, c1, nullptr, 0, nullptr, 0);
+        const int kvh = __builtin_amdgcn_readfirstlane((int)(off / nb));
+        const int c0 = __builtin_amdgcn_readfirstlane((int)(off - (int64_t)kvh * nb));
+        const int c1 = __builtin_amdgcn_readfirstlane((int)min((int64_t)nb, c0 + (we - x)));
+        const int L = __builtin_amdgcn_readfirstlane(a.context_lens[b]);
+
+        WaveState st;
+        st.m_ref = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        st.acc_l = (f32x4){0.f, 0.f, 0.f, 0.f};
+        int bad = 0;
+        attend_piece<Tag, BS>(a, b, kvh, L, c0, c1, st, bad);
+
+        const bool starts_before = c0 > 0;    // the segment began before this range
+        const bool ends_after = c1 < nb;      // it continues past this range
+        if (!starts_before && !ends_after) {
+            write_rows<Tag>(a, b, kvh, st, bad != 0);
         } else {
-            const uint64_t slot = (uint64_t)w * 2 + (head ? 0 : 1);
-            attend_segment<Tag, BS>(a, sm, b, kvh, L, c0, c1, a.ws_lse + slot * kMaxGroup, 1,
-                                    a.ws_out + slot * kMaxGroup * 128, 128);
+            const int p = 2 * wave + (starts_before ? 0 : 1);
+            if (q == 0) {
+                edge.m[p][n] = st.m_ref;
+                edge.l[p][n] = st.acc_l[0];
+            }
+            float* ow = &edge.o[p][n * kOS + 32 * q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                *reinterpret_cast<f32x4*>(ow + 8 * i) =
+                    (f32x4){st.acc[0][i], st.acc[1][i], st.acc[2][i], st.acc[3][i]};
+                *reinterpret_cast<f32x4*>(ow + 8 * i + 4) =
+                    (f32x4){st.acc[4][i], st.acc[5][i], st.acc[6][i], st.acc[7][i]};
+            }
+            if (lane == 0) {
+                edge.key[p] = b * H_kv + kvh;
+                edge.bad[p] = bad;
+            }
         }
         x += c1 - c0;
+    }
+    __syncthreads();
+
+    // The edge pieces of one segment are consecutive in work-list order
+    // (absent pieces aside): gather each segment's as a bit mask and go on
+    // after its last piece.
+    for (int p = 0; p < 2 * kNW;) {
+        const int k = edge.key[p];
+        if (k < 0) { ++p; continue; }
+        unsigned mask = 0;
+        int bad = 0;
+#pragma unroll
+        for (int p1 = 0; p1 < 2 * kNW; ++p1) {
+            if (edge.key[p1] == k) {
+                mask |= 1u << p1;
+                bad |= edge.bad[p1];
+            }
+        }
+        const int p1 = 32 - __builtin_clz(mask);
+        const int b = k / H_kv;
+        const int kvh = k - b * H_kv;
+        const int nb = pref[b + 1] - pref[b];
+        const int64_t xs = (int64_t)H_kv * pref[b] + (int64_t)kvh * nb;
+        const bool head = xs < xb;            // continues from the previous range
+        const bool tail = xs + nb > xe;       // continues into the next range
+        if (!head && !tail) {
+            finalize_edges<Tag>(a, edge, mask, b, kvh, bad != 0, nullptr, nullptr);
+        } else {
+            const uint64_t slot = (uint64_t)w * 2 + (head ? 0 : 1);
+            finalize_edges<Tag>(a, edge, mask, b, kvh, bad != 0, a.ws_lse + slot * kMaxGroup,
+                                a.ws_out + slot * kMaxGroup * 128);
+        }
+        p = p1;
     }
 }
 
