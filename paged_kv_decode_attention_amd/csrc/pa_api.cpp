@@ -67,7 +67,7 @@ bool valid_partition(int P, int block_size) {
 struct Layout {
     int part_len = 0;
     int num_parts = 0;
-    size_t lse_off = 0, out_off = 0, bytes = 0;
+    size_t lse_off = 0, out_off = 0, meta_off = 0, bytes = 0;
 };
 
 // Fixed schedule: states [S, H, num_parts] (lse) and [S, H, num_parts, D].
@@ -84,13 +84,15 @@ Layout fixed_layout(int num_seqs, int num_heads, int head_dim, int max_context_l
     return l;
 }
 
-// Balanced schedule: two slots per workgroup of kMaxGroup heads each.
+// Balanced schedule: two slots per workgroup of kMaxGroup heads each, and
+// one 16-byte record per workgroup.
 Layout balanced_layout(int head_dim) {
     Layout l;
     const size_t rows = (size_t)pa::kMaxBalancedWg * 2 * pa::kMaxGroup;
     l.lse_off = 0;
     l.out_off = align256(rows * sizeof(float));
-    l.bytes = l.out_off + align256(rows * head_dim * sizeof(float));
+    l.meta_off = l.out_off + align256(rows * head_dim * sizeof(float));
+    l.bytes = l.meta_off + align256((size_t)pa::kMaxBalancedWg * 4 * sizeof(int));
     return l;
 }
 
@@ -253,6 +255,9 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                         : nullptr;
     a.ws_out = needs_ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_off)
                         : nullptr;
+    a.ws_meta = needs_ws && balanced
+                    ? reinterpret_cast<int*>(static_cast<char*>(workspace) + lay.meta_off)
+                    : nullptr;
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;

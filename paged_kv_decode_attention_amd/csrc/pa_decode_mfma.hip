@@ -581,11 +581,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     chunk_prefix(a, pref, wsum);
     const int H_kv = a.num_kv_heads;
     const int64_t T = (int64_t)H_kv * pref[a.num_seqs];
-    if (T == 0) return;
     const int w = blockIdx.x;
-    const int64_t xb = range_start(w, T, a.num_wg);
-    const int64_t xe = range_start(w + 1, T, a.num_wg);
-    if (xb >= xe) return;
+    // record of the segment whose first piece this range leaves in [w][1]
+    int4 meta = make_int4(-1, 0, (int)(uint32_t)T, (int)(T >> 32));
+    const int64_t xb = T > 0 ? range_start(w, T, a.num_wg) : 0;
+    const int64_t xe = T > 0 ? range_start(w + 1, T, a.num_wg) : 0;
+    if (xb >= xe) {
+        if (threadIdx.x == 0) reinterpret_cast<int4*>(a.ws_meta)[w] = meta;
+        return;
+    }
 
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
@@ -667,9 +671,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
             const uint64_t slot = (uint64_t)w * 2 + (head ? 0 : 1);
             finalize_edges<Tag>(a, edge, mask, b, kvh, bad != 0, a.ws_lse + slot * kMaxGroup,
                                 a.ws_out + slot * kMaxGroup * 128);
+            if (!head) meta.x = k, meta.y = range_owner(xs + nb - 1, T, a.num_wg);
         }
         p = p1;
     }
+    if (threadIdx.x == 0) reinterpret_cast<int4*>(a.ws_meta)[w] = meta;
 }
 
 template <typename Tag, int BS>

@@ -72,20 +72,6 @@ struct FixedPieces {
     }
 };
 
-// Partial states of the balanced schedule: piece p lives in slot slots[p].
-struct BalancedPieces {
-    const float* lse;    // a.ws_lse, [slot][kMaxGroup]
-    const float* o;      // a.ws_out, [slot][kMaxGroup][D]
-    const int* slots;    // LDS list of slot indices, in token order
-    int D;
-    __device__ __forceinline__ float lse_at(int p, int g) const {
-        return lse[(uint64_t)slots[p] * kMaxGroup + g];
-    }
-    __device__ __forceinline__ const f32x4* o_at(int p, int g) const {
-        return reinterpret_cast<const f32x4*>(o + ((uint64_t)slots[p] * kMaxGroup + g) * D);
-    }
-};
-
 // Log-sum-exp merge of npieces partial states of heads head0 .. head0 +
 // nheads - 1 of sequence b ("reduce locally, then merge globally",
 // [MiniPaged-Qwen] §10.2 (2)):

@@ -23,6 +23,7 @@ struct DecodeArgs {
     const void* new_value;     // [S, H_kv, D]
     float* ws_lse;             // [S, H, num_parts] float32 (log2 units)
     float* ws_out;             // [S, H, num_parts, D] float32
+    int* ws_meta;              // balanced schedule: [num_wg][4] tail-segment records
     int num_seqs, num_heads, num_kv_heads, group, head_dim, block_size;
     int num_blocks, max_blocks_per_seq, max_context_len;
     int part_len;              // tokens per context partition (fixed schedule)
@@ -40,7 +41,10 @@ struct DecodeArgs {
 //     a (sequence, kv head) cut by a range boundary leaves one state per
 //     piece in slot [w][0] (the piece that continues from workgroup w-1) or
 //     [w][1] (the piece that continues into w+1), each slot holding up to
-//     kMaxGroup heads.
+//     kMaxGroup heads.  Record ws_meta[w] = {key, w1, T lo, T hi} names the
+//     segment whose first piece is slot [w][1] (key = sequence * H_kv + KV
+//     head, -1 if none), the last range w1 holding it, and the work-list
+//     size T; the decode kernel writes every record on every launch.
 enum Schedule { kFixed = 0, kBalanced = 1 };
 constexpr int kMaxGroup = 16;          // heads per slot (matrix-core kernel)
 constexpr int kMaxBalancedWg = 1024;   // workspace is sized for this many

@@ -1,8 +1,7 @@
 // Log-sum-exp merge of partial decode states: the "merge globally" half of
-// the partitioned reduction ([MiniPaged-Qwen] §10.2 (2)).  One workgroup per
-// (sequence, KV head) combines, in token order, the float32 states (lse, o)
-// the decode workgroups left for the G query heads of that group
-// (merge_pieces in pa_finalize.h).
+// the partitioned reduction ([MiniPaged-Qwen] §10.2 (2)).  The float32
+// states (lse, o) the decode workgroups left for the G query heads of a
+// (sequence, KV head) are combined in token order.
 #include "pa_finalize.h"
 
 namespace pa {
@@ -26,91 +25,125 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
     merge_pieces<Tag>(a, pc, b, head0, a.group, nparts);
 }
 
-// Balanced schedule: the pieces of (b, kvh) are the slots of the workgroup
-// ranges its chunks fall in.  Also writes the rows the decode kernel skips:
-// zeros for an empty history, NaN for an invalid context length.  Only two
-// sums over the context lengths are needed (chunks before sequence b, and in
-// total), so they are a single workgroup reduction rather than a prefix table.
+// Balanced schedule.  Workgroup w < num_wg merges the segment whose first
+// piece range w left in slot [w][1], as named by record ws_meta[w]: the
+// pieces are [w][1] and [w'][0] for every non-empty range w' in (w, w1], in
+// token order.  The record and the first kSpec candidate pieces are loaded
+// together (one memory round trip for the common case of a segment spread
+// over at most kSpec ranges).  Workgroup num_wg + b writes the rows of
+// sequence b when the decode kernel has none to write: zeros for an empty
+// history, NaN for an invalid context length.  A thread takes 4
+// consecutive d of one head (head_dim 128, at most kMaxGroup heads).
+constexpr int kMergeBalancedThreads = kMaxGroup * 32;
+
 template <typename Tag>
-__global__ __launch_bounds__(kMergeThreads) void merge_balanced(DecodeArgs a) {
-    constexpr int NW = kMergeThreads / 64;
-    __shared__ int red_before[NW], red_total[NW];
-    __shared__ int slots[kMaxBalancedWg + 1];
-    __shared__ int live[kMaxBalancedWg + 1];
-    const int kvh = blockIdx.x;
-    const int b = blockIdx.y;
-    const int head0 = kvh * a.group;
-    // The first batch of lengths is loaded together with L_b: one memory
-    // round trip before the checks below.
-    const int L = a.context_lens[b];
-    const int i0 = threadIdx.x;
-    const int len0 = i0 < a.num_seqs ? a.context_lens[i0] : 0;
-    if (L < 0 || L > a.max_context_len) {
-        fill_rows<Tag>(a, b, head0, a.group, __builtin_nanf(""));
+__global__ __launch_bounds__(kMergeBalancedThreads) void merge_balanced(DecodeArgs a) {
+    constexpr int kSpec = 4;
+    constexpr int D = 128;
+    const int w = blockIdx.x;
+    if (w >= a.num_wg) {
+        const int b = w - a.num_wg;
+        const int L = a.context_lens[b];
+        if (L < 0 || L > a.max_context_len)
+            fill_rows<Tag>(a, b, 0, a.num_heads, __builtin_nanf(""));
+        else if (L == 0)
+            fill_rows<Tag>(a, b, 0, a.num_heads, 0.0f);
         return;
     }
-    if (L == 0) {
-        fill_rows<Tag>(a, b, head0, a.group, 0.0f);
+    const int g = threadIdx.x >> 5;
+    const int d = (threadIdx.x & 31) * 4;
+    const int nwg = a.num_wg;
+    auto slot_row = [&](int slot) { return (uint64_t)slot * kMaxGroup + g; };
+    const int4 meta = reinterpret_cast<const int4*>(a.ws_meta)[w];
+    f32x4 o[kSpec];
+    float lse[kSpec];
+#pragma unroll
+    for (int k = 0; k < kSpec; ++k) {
+        const int slot = k == 0 ? 2 * w + 1 : 2 * min(w + k, nwg - 1);
+        o[k] = *reinterpret_cast<const f32x4*>(a.ws_out + slot_row(slot) * D + d);
+        lse[k] = a.ws_lse[slot_row(slot)];
+    }
+    const int key = meta.x;
+    const int w1 = meta.y;
+    // (a record outside these bounds cannot come from the decode kernel)
+    if (key < 0 || key >= a.num_seqs * a.num_kv_heads || w1 <= w || w1 >= nwg ||
+        g >= a.group)
         return;
-    }
-    int total = seq_chunks(len0, a.max_context_len);
-    int before = i0 < b ? total : 0;
-    for (int i = i0 + kMergeThreads; i < a.num_seqs; i += kMergeThreads) {
-        const int c = seq_chunks(a.context_lens[i], a.max_context_len);
-        total += c;
-        if (i < b) before += c;
-    }
+    const int64_t T = (int64_t)(uint32_t)meta.z | ((int64_t)meta.w << 32);
+    const int b = key / a.num_kv_heads;
+    const int kvh = key - b * a.num_kv_heads;
+    // every range is non-empty when T >= num_wg: pieces are then [w][1],
+    // [w+1][0], ..., [w1][0]
+    const int npieces = w1 - w + 1;
+    float M = -INFINITY, den = 0.0f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    bool has_nan = false;
+    auto fold = [&](float l, f32x4 v) {     // the update of [MiniPaged-Qwen] §5.2
+        has_nan |= (l != l);
+        const float m = fmaxf(M, l);
+        const float keep = rescale_weight(M, m);
+        const float wgt = rescale_weight(l, m);
+        den = den * keep + wgt;
+        num = num * keep + wgt * v;
+        M = m;
+    };
+    if (T >= nwg && npieces <= kSpec) {
+        float m = -INFINITY;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        before += __shfl_xor(before, off);
-        total += __shfl_xor(total, off);
-    }
-    if ((threadIdx.x & 63) == 0) {
-        red_before[threadIdx.x >> 6] = before;
-        red_total[threadIdx.x >> 6] = total;
-    }
-    __syncthreads();
-    before = 0;
-    total = 0;
+        for (int k = 0; k < kSpec; ++k) m = fmaxf(m, k < npieces ? lse[k] : -INFINITY);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        before += red_before[w];
-        total += red_total[w];
+        for (int k = 0; k < kSpec; ++k) {
+            if (k >= npieces) continue;
+            has_nan |= (lse[k] != lse[k]);
+            const float wgt = rescale_weight(lse[k], m);
+            den += wgt;
+            num += wgt * o[k];
+        }
+        M = m;
+    } else if (T >= nwg) {
+        // contiguous pieces beyond the first kSpec: batches of kBatch loaded
+        // together, folded in order
+        constexpr int kBatch = 8;
+#pragma unroll
+        for (int k = 0; k < kSpec; ++k) fold(lse[k], o[k]);
+        for (int k0 = kSpec; k0 < npieces; k0 += kBatch) {
+            f32x4 ob[kBatch];
+            float lb[kBatch];
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k) {
+                const int slot = 2 * (w + min(k0 + k, npieces - 1));
+                ob[k] = *reinterpret_cast<const f32x4*>(a.ws_out + slot_row(slot) * D + d);
+                lb[k] = a.ws_lse[slot_row(slot)];
+            }
+#pragma unroll
+            for (int k = 0; k < kBatch; ++k)
+                if (k0 + k < npieces) fold(lb[k], ob[k]);
+        }
+    } else {
+        // fewer work items than workgroups: skip the empty ranges
+        fold(lse[0], o[0]);
+        for (int w2 = w + 1; w2 <= w1; ++w2) {
+            if (range_start(w2, T, nwg) >= range_start(w2 + 1, T, nwg)) continue;
+            const int slot = 2 * w2;
+            fold(a.ws_lse[slot_row(slot)],
+                 *reinterpret_cast<const f32x4*>(a.ws_out + slot_row(slot) * D + d));
+        }
     }
-    const int H_kv = a.num_kv_heads;
-    const int64_t T = (int64_t)H_kv * total;
-    const int nb = seq_chunks(L, a.max_context_len);
-    const int64_t x0 = (int64_t)H_kv * before + (int64_t)kvh * nb;
-    const int w0 = range_owner(x0, T, a.num_wg);
-    const int w1 = range_owner(x0 + nb - 1, T, a.num_wg);
-    if (w0 == w1) return;   // one range held the whole history
-    // piece k is slot [w0][1] for k = 0, then [w][0] for each non-empty
-    // range w in (w0, w1]
-    const int span = w1 - w0;
-    for (int k = threadIdx.x; k < span; k += kMergeThreads) {
-        const int w = w0 + 1 + k;
-        live[k] = range_start(w, T, a.num_wg) < range_start(w + 1, T, a.num_wg);
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int n = 0;
-        slots[n++] = 2 * w0 + 1;
-        for (int k = 0; k < span; ++k)
-            if (live[k]) slots[n++] = 2 * (w0 + 1 + k);
-        live[kMaxBalancedWg] = n;
-    }
-    __syncthreads();
-    const BalancedPieces pc{a.ws_lse, a.ws_out, slots, a.head_dim};
-    merge_pieces<Tag>(a, pc, b, head0, a.group, live[kMaxBalancedWg]);
+    const uint64_t out0 = ((uint64_t)b * a.num_heads + kvh * a.group + g) * D + d;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        store_elem(Tag(), a.out, out0 + e, has_nan ? __builtin_nanf("") : num[e] / den);
 }
 
 template <typename Tag>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
-    dim3 grid(a.num_kv_heads, a.num_seqs);
-    if (a.schedule == kBalanced)
-        hipLaunchKernelGGL((merge_balanced<Tag>), grid, dim3(kMergeThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((merge_fixed<Tag>), grid, dim3(kMergeThreads), 0, s, a);
+    if (a.schedule == kBalanced) {
+        hipLaunchKernelGGL((merge_balanced<Tag>), dim3(a.num_wg + a.num_seqs),
+                           dim3(kMergeBalancedThreads), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((merge_fixed<Tag>), dim3(a.num_kv_heads, a.num_seqs),
+                           dim3(kMergeThreads), 0, s, a);
+    }
     return hipGetLastError();
 }
 

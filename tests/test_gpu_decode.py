@@ -120,6 +120,42 @@ def test_permutation_and_block_size_invariance_bitwise():
         assert torch.equal(out, base), "layout (bs=%d, seed=%d) changed the result" % (bs, seed)
 
 
+def test_balanced_schedule_layout_invariance_bitwise():
+    """The balanced schedule's work split depends on lengths only, so moving
+    the history to other physical blocks, or to blocks of 32, changes no bit."""
+    inp = I.generate(small_config("bf16", 2, 7, 128, 16, RAGGED + (2000, 3000), seed=12))
+    base = run_decode(upload(inp), ops.KERNEL_MFMA, 0).cpu()
+    for bs, seed in ((16, 4), (32, 5)):
+        kc, vc, bt = same_history_other_layout(inp, bs, seed)
+        d = dict(query=inp.query.to(DEV), key_cache=kc.to(DEV), value_cache=vc.to(DEV),
+                 block_tables=bt.to(DEV), context_lens=inp.context_lens.to(DEV))
+        out = run_decode(d, ops.KERNEL_MFMA, 0).cpu()
+        assert torch.equal(out, base), "layout (bs=%d, seed=%d) changed the result" % (bs, seed)
+
+
+def test_balanced_workspace_reuse_and_all_empty():
+    """One workspace, first filled with a junk byte pattern, serves a batch
+    with no history at all (every row 0), a full batch and the empty batch
+    again: nothing a call leaves behind leaks into the next."""
+    cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_seqs=16, num_blocks=4200)
+    inp = I.poison_unread(I.generate(cfg))
+    d = upload(inp)
+    S, H, D = inp.query.shape
+    n = ops.decode_workspace_size(S, H, cfg.num_kv_heads, D, cfg.block_size,
+                                  cfg.max_blocks_per_seq * cfg.block_size, 0, inp.query.dtype)
+    ws = torch.full((n,), 1, dtype=torch.uint8, device=DEV)
+    empty = torch.zeros_like(d["context_lens"])
+    for lens, want in ((empty, "zeros"), (d["context_lens"], "oracle"), (empty, "zeros")):
+        out = torch.full_like(d["query"], float("nan"))
+        ops.paged_attention_decode(d["query"], d["key_cache"], d["value_cache"],
+                                   d["block_tables"], lens, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        if want == "zeros":
+            assert torch.all(out == 0)
+        else:
+            compare(out, oracle_ref(inp), "bf16", what="after an empty batch")
+
+
 def test_partition_size_invariance():
     inp = I.poison_unread(I.generate(small_config("bf16", 2, 7, 128, 32, (700, 1000, 64))))
     d = upload(inp)
