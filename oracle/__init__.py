@@ -18,7 +18,9 @@ source pages it follows:
 
 Parity status: every function here is pinned by ``tests/test_oracle.py``
 (closed forms, invariants, brute force, a library special case and the
-worked examples the pages print); none is "parity unpinned".
+worked examples the pages print) or, for the block pool and the block copy
+(``block_pool.py``), by ``tests/test_block_pool_oracle.py`` (the printed
+copy-on-write example and invariants); none is "parity unpinned".
 """
 
 from .paged_attention import (  # noqa: F401
@@ -36,3 +38,4 @@ from .paged_attention import (  # noqa: F401
     kv_cache_bytes,
     kv_cache_bytes_hidden_form,
 )
+from .block_pool import BlockPool, PoolExhausted, copy_blocks  # noqa: F401,E402
