@@ -117,6 +117,37 @@ def cpu_baseline(inp, budget_s):
     }
 
 
+def copy_blocks_rate(kcs, vcs, dev, pairs=2048, calls=8):
+    """The copy-on-write block copy (pa_copy_blocks) on the same pools:
+    `pairs` distinct (src, dst) blocks per call, a fresh set each call and
+    the pool replicas in turn, so no call finds its blocks in the last-level
+    cache.  Bytes moved = blocks read + blocks written, both caches."""
+    import numpy as np
+    import torch
+    from paged_kv_decode_attention_amd import ops
+
+    N = kcs[0].shape[0]
+    rng = np.random.default_rng(99)
+    sets = []
+    for _ in range(calls):
+        perm = rng.permutation(N)[:2 * pairs].astype(np.int32)
+        sets.append(torch.from_numpy(perm.reshape(2, pairs).T.copy()).to(dev))
+    ops.copy_blocks(kcs[0], vcs[0], sets[0])                 # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(calls):
+        ops.copy_blocks(kcs[k % len(kcs)], vcs[k % len(vcs)], sets[k])
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / calls
+    block_bytes = kcs[0][0].numel() * kcs[0].element_size()
+    moved = 2 * 2 * pairs * block_bytes
+    return {"pairs_per_call": pairs, "bytes_moved_per_call": moved, "us_per_call": t * 1e6,
+            "achieved_gbps": moved / t / 1e9, "frac": moved / t / 1e9 / HBM_PEAK_GBPS,
+            "bound": "hbm"}
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -257,6 +288,8 @@ def main():
     ceiling_gbps = 5 * rd.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del rd
 
+    copy = copy_blocks_rate(kcs, vcs, dev)
+
     dec_s = float(dec_ms.mean()) * 1e-3
     achieved = alg_bytes / dec_s / 1e9
     traffic = load_traffic(args.config, alg_bytes)
@@ -303,6 +336,7 @@ def main():
         },
         "decode_tokens_per_s": S / dec_s,
         "hbm_read_ceiling_gbps": ceiling_gbps,
+        "copy_blocks": copy,
         "kernel_src_sha": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

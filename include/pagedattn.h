@@ -7,7 +7,14 @@
  *   pa_reshape_and_cache      store the new tokens' K/V into the paged pool at
  *                             the slots the block manager handed out;
  *   pa_paged_attention_decode attend each sequence's single new query (one per
- *                             query head) over its whole paged history.
+ *                             query head) over its whole paged history;
+ *
+ * (pa_decode_append does both in one call), and the write side of shared
+ * blocks:
+ *
+ *   pa_pool_*                 a host-side block pool with reference counts
+ *                             and copy-on-write of shared partial blocks;
+ *   pa_copy_blocks            the device copy that copy-on-write asks for.
  *
  * Sources, cited by page title and section:
  *   [MiniPaged-Qwen]  "MiniPaged-Qwen: 把 Paged Attention 讲清楚"
@@ -52,7 +59,8 @@ typedef enum {
     PA_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size, H % H_kv != 0 ... */
     PA_ERR_UNSUPPORTED = -2,   /* valid but not built: dtype, head_dim, block_size */
     PA_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
-    PA_ERR_HIP = -4            /* a HIP runtime call failed (text in pa_last_error) */
+    PA_ERR_HIP = -4,           /* a HIP runtime call failed (text in pa_last_error) */
+    PA_ERR_POOL_EXHAUSTED = -5 /* the block pool has too few free blocks */
 } pa_status;
 
 /* Library ABI version (major*100 + minor). */
@@ -210,6 +218,103 @@ int pa_reshape_and_cache(const void* key, const void* value,
                          int num_tokens, int num_kv_heads, int head_dim,
                          int block_size, int num_blocks, pa_dtype dtype,
                          void* hip_stream);
+
+/*
+ * pa_copy_blocks -- copy whole physical blocks of both caches:
+ *     key_cache  [dst_i, :, :, :] = key_cache  [src_i, :, :, :]
+ *     value_cache[dst_i, :, :, :] = value_cache[src_i, :, :, :]
+ * for every pair i (all KV heads and slots of the block): the copy behind
+ * copy-on-write, when a sequence must write into a partially filled block
+ * that other sequences still share ([vLLM-paging] "Copy-on-write 是共享的正确
+ * 性边界": the branch copies the block and writes its new token into the
+ * private copy).  A pure copy: bit-exact.
+ *
+ *   key_cache,
+ *   value_cache    [num_blocks, num_kv_heads, block_size, head_dim] dtype
+ *   block_pairs    DEVICE [num_pairs][2] int32 (src, dst), as pa_pool_append
+ *                  returns them
+ *
+ * Supported: dtype f32, f16, bf16; head_dim * element size a multiple of 16
+ * bytes; any block_size >= 1.  num_pairs = 0 is a no-op.
+ *
+ * Device-data preconditions: no dst is also a src or another pair's dst in
+ * the same call (a copy-on-write destination is a freshly taken block), so
+ * the pairs are independent.  A pair with an index outside [0, num_blocks),
+ * or with src == dst, is skipped.
+ */
+int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs,
+                   int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                   int num_blocks, pa_dtype dtype, void* hip_stream);
+
+/*
+ * Block pool -- host-side ownership of the physical blocks of a paged cache,
+ * with sharing ([vLLM-paging] "Copy-on-write 是共享的正确性边界" and its
+ * "最小分页与 COW 模拟"; [MiniPaged-Qwen] §9 "差异 3", §10.1: shared
+ * prefixes, branch sharing, reference counting, copy-on-write).  The pool
+ * keeps no device memory: it hands out block tables, slots and copy pairs
+ * for the cache write, the decode call and pa_copy_blocks.
+ *
+ *   - A block is taken from the END of the free list (blocks start as the
+ *     list 0, 1, ..., num_blocks - 1) and starts with one reference.
+ *   - A sequence is a block table; its tokens fill the blocks in order,
+ *     block_size per block, the last block possibly partial.
+ *   - pa_pool_fork: a new sequence naming the same blocks; each gains one
+ *     reference.
+ *   - pa_pool_append: one new token for each listed sequence, in list order.
+ *     Empty table or full last block: a fresh block is taken.  Partial last
+ *     block shared with another sequence: the sequence drops that reference,
+ *     takes a fresh block and a copy pair (shared, fresh) is reported; the
+ *     token goes into the copy.  Otherwise the token goes into the last block.
+ *     slots[i] = block * block_size + position of the new token, the linear
+ *     slot of pa_reshape_and_cache.  Before storing the new tokens, the caller
+ *     runs pa_copy_blocks on the copy pairs (in the same stream order).
+ *   - pa_pool_release: the sequence's blocks each lose one reference; blocks
+ *     with none left return to the free list; the sequence id is retired.
+ *
+ * A pool is not thread-safe: calls on one pool must not overlap.  Distinct
+ * pools are independent.
+ */
+typedef struct pa_block_pool pa_block_pool;
+
+/* New pool of num_blocks blocks of block_size tokens; NULL for non-positive
+ * sizes or when host memory runs out (pa_last_error says which).  Destroyed
+ * by pa_pool_destroy (NULL is ignored). */
+pa_block_pool* pa_pool_create(int num_blocks, int block_size);
+void pa_pool_destroy(pa_block_pool* pool);
+
+/* New empty sequence; returns its id (>= 0) or a negative status. */
+int pa_pool_add_sequence(pa_block_pool* pool);
+
+/* New sequence sharing every block of `seq`; returns its id or a negative
+ * status (PA_ERR_INVALID_ARG for an unknown or retired id). */
+int pa_pool_fork(pa_block_pool* pool, int seq);
+
+/*
+ * One new token for each of seqs[0..n) (distinct, live ids), as described
+ * above.  HOST arrays: slots [n] int64 receives each token's slot;
+ * copy_pairs [n][2] int32 receives the copy pairs (at most one per token),
+ * *num_copies their count.  All or nothing: if the free blocks do not
+ * suffice, returns PA_ERR_POOL_EXHAUSTED ("KV pool exhausted") and changes
+ * nothing; PA_ERR_INVALID_ARG for a bad id, a repeated id or null arrays.
+ */
+int pa_pool_append(pa_block_pool* pool, const int* seqs, int n, int64_t* slots,
+                   int32_t* copy_pairs, int* num_copies);
+
+/* Drop a sequence (see above); PA_OK or PA_ERR_INVALID_ARG. */
+int pa_pool_release(pa_block_pool* pool, int seq);
+
+/* Tokens in a sequence, or a negative status. */
+int pa_pool_length(const pa_block_pool* pool, int seq);
+
+/* Number of blocks in the sequence's table (or a negative status); the first
+ * min(capacity, that number) entries are written to the HOST array table. */
+int pa_pool_table(const pa_block_pool* pool, int seq, int32_t* table, int capacity);
+
+/* References to a block (0 = free), or a negative status. */
+int pa_pool_refcount(const pa_block_pool* pool, int block);
+
+/* Blocks on the free list. */
+int pa_pool_free_blocks(const pa_block_pool* pool);
 
 /*
  * pa_debug_gather_kv -- copy one sequence's history into contiguous form,

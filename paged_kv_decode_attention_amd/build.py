@@ -29,6 +29,7 @@ SOURCES = [
     "pa_merge.hip",
     "pa_cache.hip",
     "pa_bench.hip",
+    "pa_pool.cpp",
 ]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -25,6 +25,15 @@ int fail(int status, const char* fmt, ...) {
     return status;
 }
 
+}  // namespace
+
+int pa::report_error(int status, const char* msg) {
+    g_last_error = msg;
+    return status;
+}
+
+namespace {
+
 int hip_fail(hipError_t e, const char* what) {
     return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -137,6 +146,7 @@ const char* pa_status_string(int status) {
         case PA_ERR_UNSUPPORTED: return "unsupported configuration";
         case PA_ERR_WORKSPACE: return "workspace missing or too small";
         case PA_ERR_HIP: return "HIP runtime error";
+        case PA_ERR_POOL_EXHAUSTED: return "KV pool exhausted";
         default: return "unknown status";
     }
 }
@@ -347,6 +357,30 @@ int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, vo
                                                   block_size, num_blocks,
                                                   static_cast<hipStream_t>(hip_stream));
     if (err != hipSuccess) return hip_fail(err, "cache write kernel launch");
+    return PA_OK;
+}
+
+int pa_copy_blocks(void* key_cache, void* value_cache, const int32_t* block_pairs,
+                   int num_pairs, int num_kv_heads, int head_dim, int block_size,
+                   int num_blocks, pa_dtype dtype, void* hip_stream) {
+    const int e = elem_bytes(dtype);
+    if (e == 0) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return fail(PA_ERR_INVALID_ARG, "sizes must be positive (num_pairs >= 0)");
+    if ((head_dim * e) % 16)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim * element size must be a multiple of 16 bytes");
+    const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * e;
+    if (block_bytes > (int64_t)1 << 30)
+        return fail(PA_ERR_UNSUPPORTED, "blocks of %lld bytes are too large", (long long)block_bytes);
+    if (num_pairs == 0) return PA_OK;
+    if (!key_cache || !value_cache || !block_pairs)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(key_cache) || !aligned16(value_cache))
+        return fail(PA_ERR_INVALID_ARG, "cache pointers must be 16-byte aligned");
+    hipError_t err = pa::launch_copy_blocks(key_cache, value_cache, block_pairs, num_pairs,
+                                            (int)block_bytes, num_blocks,
+                                            static_cast<hipStream_t>(hip_stream));
+    if (err != hipSuccess) return hip_fail(err, "block copy kernel launch");
     return PA_OK;
 }
 

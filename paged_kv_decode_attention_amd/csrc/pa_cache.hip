@@ -1,5 +1,5 @@
-// Cache write and the debug gather: pure 16-byte copies, bit-exact for every
-// dtype (they move bytes, never values).
+// Cache write, block copy and the debug gather: pure 16-byte copies,
+// bit-exact for every dtype (they move bytes, never values).
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -68,6 +68,29 @@ __global__ __launch_bounds__(kCopyThreads) void append_tokens_kernel(
     *reinterpret_cast<u32x4*>(value_cache + dst) = vv;
 }
 
+// Block copy for copy-on-write: 16-byte column c of pair i's block slab
+// (num_kv_heads * block_size * head_dim elements, contiguous in the
+// [N, H_kv, BS, D] layout), for the key cache (blockIdx.y = 0) or the value
+// cache (blockIdx.y = 1).  Pairs with an index outside the pool, or with
+// src == dst, are skipped.
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
+    char* key_cache, char* value_cache, const int32_t* __restrict__ pairs, int num_pairs,
+    int block_bytes, int num_blocks) {
+    const int cols = block_bytes / 16;
+    const uint64_t idx = (uint64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    if (idx >= (uint64_t)num_pairs * cols) return;
+    const int i = (int)(idx / cols);
+    const int c = (int)(idx - (uint64_t)i * cols);
+    const int src = pairs[2 * i];
+    const int dst = pairs[2 * i + 1];
+    if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks ||
+        src == dst)
+        return;
+    char* base = blockIdx.y == 0 ? key_cache : value_cache;
+    const u32x4 v = load16(base + (uint64_t)src * block_bytes + c * 16);
+    *reinterpret_cast<u32x4*>(base + (uint64_t)dst * block_bytes + c * 16) = v;
+}
+
 // History row t of sequence `seq`, KV head h -> k_out[h, t, :], through the
 // decode kernels' address function.
 __global__ __launch_bounds__(kCopyThreads) void gather_kernel(
@@ -125,6 +148,17 @@ hipError_t launch_append_tokens(const void* key, const void* value, void* key_ca
                        static_cast<char*>(key_cache), static_cast<char*>(value_cache),
                        block_tables, context_lens, num_seqs, num_kv_heads, row_bytes, block_size,
                        num_blocks, max_blocks_per_seq, max_context_len);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                              int num_pairs, int block_bytes, int num_blocks, hipStream_t s) {
+    const uint64_t total = (uint64_t)num_pairs * (block_bytes / 16);
+    if (total == 0) return hipSuccess;
+    dim3 grid((unsigned)((total + kCopyThreads - 1) / kCopyThreads), 2);
+    hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, s,
+                       static_cast<char*>(key_cache), static_cast<char*>(value_cache), pairs,
+                       num_pairs, block_bytes, num_blocks);
     return hipGetLastError();
 }
 

@@ -76,6 +76,13 @@ hipError_t launch_append_tokens(const void* key, const void* value, void* key_ca
                                 int row_bytes, int block_size, int num_blocks,
                                 int max_blocks_per_seq, int max_context_len, hipStream_t s);
 
+// Copy whole blocks of both caches: pair i = (src, dst) in device memory.
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,
+                              int num_pairs, int block_bytes, int num_blocks, hipStream_t s);
+
+// Record `msg` as the calling thread's pa_last_error text and return status.
+int report_error(int status, const char* msg);
+
 hipError_t launch_gather(void* k_out, void* v_out, const void* key_cache,
                          const void* value_cache, const int32_t* block_tables,
                          const int32_t* context_lens, int seq,

@@ -43,6 +43,17 @@ _SIGNATURES = {
         _I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP]),
     "pa_debug_gather_kv": (
         _I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _VP]),
+    "pa_copy_blocks": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP]),
+    "pa_pool_create": (_VP, [_I, _I]),
+    "pa_pool_destroy": (None, [_VP]),
+    "pa_pool_add_sequence": (_I, [_VP]),
+    "pa_pool_fork": (_I, [_VP, _I]),
+    "pa_pool_append": (_I, [_VP, _VP, _I, _VP, _VP, _VP]),
+    "pa_pool_release": (_I, [_VP, _I]),
+    "pa_pool_length": (_I, [_VP, _I]),
+    "pa_pool_table": (_I, [_VP, _I, _VP, _I]),
+    "pa_pool_refcount": (_I, [_VP, _I]),
+    "pa_pool_free_blocks": (_I, [_VP]),
     "pa_bench_stream_read": (_I, [_VP, ctypes.c_size_t, _VP, _VP]),
     "pa_bench_copy": (_I, [_VP, _VP, ctypes.c_size_t, _VP]),
 }
@@ -266,3 +277,93 @@ def copy_bytes(dst, src):
         raise ValueError("dst too small")
     _check(load_library().pa_bench_copy(_ptr(dst), _ptr(src), n, _stream(src.device)),
            "copy_bytes")
+
+
+def copy_blocks(key_cache, value_cache, block_pairs):
+    """key_cache[dst] = key_cache[src] and the same for value_cache, for each
+    row (src, dst) of block_pairs ([n, 2] int32 on the GPU): the copy behind
+    copy-on-write (see BlockPool.append)."""
+    _gpu(key_cache, "key_cache")
+    _gpu(value_cache, "value_cache")
+    _gpu(block_pairs, "block_pairs")
+    if key_cache.shape != value_cache.shape or key_cache.dtype != value_cache.dtype:
+        raise ValueError("key_cache and value_cache must match")
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2] int32")
+    N, H_kv, BS, D = key_cache.shape
+    _check(load_library().pa_copy_blocks(
+        _ptr(key_cache), _ptr(value_cache), _ptr(block_pairs), block_pairs.shape[0], H_kv, D,
+        BS, N, dtype_code(key_cache.dtype), _stream(key_cache.device)), "copy_blocks")
+
+
+class BlockPool:
+    """The library's host-side block pool (pa_pool_* of pagedattn.h): block
+    tables with reference counts and copy-on-write of shared partial blocks.
+    Arrays cross the boundary as NumPy host arrays."""
+
+    def __init__(self, num_blocks, block_size):
+        import numpy as np
+        self._np = np
+        lib = load_library()
+        self._lib = lib
+        self._h = lib.pa_pool_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise RuntimeError("pa_pool_create failed: " + lib.pa_last_error().decode())
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self._h:
+            self._lib.pa_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _ok(self, r, what):
+        if r < 0:
+            _check(r, what)
+        return r
+
+    def add_sequence(self):
+        return self._ok(self._lib.pa_pool_add_sequence(self._h), "pool add_sequence")
+
+    def fork(self, seq):
+        return self._ok(self._lib.pa_pool_fork(self._h, int(seq)), "pool fork")
+
+    def append(self, seqs):
+        """One new token for each sequence id in seqs, in order.  Returns
+        (slots int64 [n], copy pairs int32 [c, 2]); run copy_blocks on the
+        pairs before storing the tokens at the slots."""
+        np = self._np
+        ids = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = len(ids)
+        slots = np.zeros(n, dtype=np.int64)
+        pairs = np.zeros((max(n, 1), 2), dtype=np.int32)
+        count = ctypes.c_int(0)
+        _check(self._lib.pa_pool_append(
+            self._h, ids.ctypes.data_as(_VP), n, slots.ctypes.data_as(_VP),
+            pairs.ctypes.data_as(_VP), ctypes.byref(count)), "pool append")
+        return slots, pairs[:count.value].copy()
+
+    def release(self, seq):
+        _check(self._lib.pa_pool_release(self._h, int(seq)), "pool release")
+
+    def length(self, seq):
+        return self._ok(self._lib.pa_pool_length(self._h, int(seq)), "pool length")
+
+    def table(self, seq):
+        np = self._np
+        n = self._ok(self._lib.pa_pool_table(self._h, int(seq), None, 0), "pool table")
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        self._lib.pa_pool_table(self._h, int(seq), out.ctypes.data_as(_VP), n)
+        return out[:n].copy()
+
+    def refcount(self, block):
+        return self._ok(self._lib.pa_pool_refcount(self._h, int(block)), "pool refcount")
+
+    def free_blocks(self):
+        return self._ok(self._lib.pa_pool_free_blocks(self._h), "pool free_blocks")

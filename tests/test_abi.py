@@ -43,7 +43,8 @@ def test_every_declared_symbol_is_exported(lib):
 def test_version_and_status_strings(lib):
     assert lib.pa_version() == 100
     for s, text in ((OK, b"ok"), (INVALID, b"invalid argument"),
-                    (UNSUPPORTED, b"unsupported configuration")):
+                    (UNSUPPORTED, b"unsupported configuration"),
+                    (-5, b"KV pool exhausted")):
         assert lib.pa_status_string(s) == text
     assert lib.pa_status_string(12345) == b"unknown status"
 
@@ -122,6 +123,17 @@ def test_reshape_and_cache_rejects_on_host(lib):
              vp(0)) == UNSUPPORTED                                      # 12-byte rows
     assert f(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 4, 2, 64, 16, 4, 9,
              vp(0)) == INVALID
+
+
+def test_copy_blocks_rejects_on_host(lib):
+    vp = ctypes.c_void_p
+    f = lib.pa_copy_blocks
+    assert f(vp(FAKE), vp(FAKE), vp(FAKE), 0, 2, 64, 16, 4, ops.PA_F32, vp(0)) == OK   # no pairs
+    assert f(vp(FAKE), vp(FAKE), vp(0), 3, 2, 64, 16, 4, ops.PA_F32, vp(0)) == INVALID
+    assert f(vp(FAKE), vp(FAKE), vp(FAKE), -1, 2, 64, 16, 4, ops.PA_F32, vp(0)) == INVALID
+    assert f(vp(FAKE), vp(FAKE), vp(FAKE), 3, 2, 6, 16, 4, ops.PA_F16, vp(0)) == UNSUPPORTED
+    assert f(vp(FAKE + 8), vp(FAKE), vp(FAKE), 3, 2, 64, 16, 4, ops.PA_F32, vp(0)) == INVALID
+    assert f(vp(FAKE), vp(FAKE), vp(FAKE), 3, 2, 64, 16, 0, ops.PA_F32, vp(0)) == INVALID
 
 
 def test_select_kernel_validates(lib):
