@@ -20,7 +20,10 @@ Parity status: every function here is pinned by ``tests/test_oracle.py``
 (closed forms, invariants, brute force, a library special case and the
 worked examples the pages print) or, for the block pool and the block copy
 (``block_pool.py``), by ``tests/test_block_pool_oracle.py`` (the printed
-copy-on-write example and invariants); none is "parity unpinned".
+copy-on-write example and invariants), or, for the FP8 KV cache
+(``fp8.py``), by ``tests/test_fp8_oracle.py`` (the E4M3 definition,
+PyTorch's float8_e4m3fn cast where it is defined, exhaustive round trips,
+ties and saturation); none is "parity unpinned".
 """
 
 from .paged_attention import (  # noqa: F401
@@ -39,3 +42,4 @@ from .paged_attention import (  # noqa: F401
     kv_cache_bytes_hidden_form,
 )
 from .block_pool import BlockPool, PoolExhausted, copy_blocks  # noqa: F401,E402
+from . import fp8  # noqa: F401,E402
