@@ -117,6 +117,53 @@ def cpu_baseline(inp, budget_s):
     }
 
 
+def fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
+                    timed_replay):
+    """The same decode calls on OCP FP8 E4M3 caches (pa_paged_attention_decode_fp8):
+    each pool replica quantised once by the library's own FP8 cache write
+    (every slot written as one token, per-cache scales), then K decode calls
+    replayed from a HIP graph.  Algorithmic bytes are half the 16-bit ones."""
+    import numpy as np
+    import torch
+    from paged_kv_decode_attention_amd import ops
+
+    k_scale, v_scale = 1.0 / 64, 1.0 / 64
+    N, H_kv, BS, D = kcs[0].shape
+    slots = torch.arange(N * BS, dtype=torch.int64, device=dev)
+    k8s, v8s = [], []
+    for kc, vc in zip(kcs, vcs):
+        k8 = torch.empty(N, H_kv, BS, D, dtype=torch.uint8, device=dev)
+        v8 = torch.empty_like(k8)
+        # pool rows as tokens: [N, BS, H_kv, D] -> [N*BS, H_kv, D], slot = row
+        ops.reshape_and_cache_fp8(kc.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous(),
+                                  vc.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous(),
+                                  k8, v8, slots, k_scale, v_scale)
+        k8s.append(k8)
+        v8s.append(v8)
+    out = torch.empty_like(q)
+    S, H = q.shape[0], q.shape[1]
+    ws = torch.zeros(max(ops.decode_workspace_size(S, H, H_kv, D, BS, max_ctx, 0, q.dtype), 256),
+                     dtype=torch.uint8, device=dev)
+
+    def call(k):
+        r = k % len(k8s)
+        ops.paged_attention_decode_fp8(q, k8s[r], v8s[r], bt, cl, k_scale, v_scale, cfg.scale,
+                                       max_context_len=max_ctx, out=out, workspace=ws)
+    for k in range(10):
+        call(k)
+    torch.cuda.synchronize()
+    g = capture(lambda: [call(k) for k in range(args.steps)])
+    g.replay()
+    us = np.array([timed_replay(g)[1] / args.steps * 1e6 for _ in range(3)])
+    t = float(us.mean()) * 1e-6
+    alg8 = alg_bytes // 2
+    del k8s, v8s
+    return {"kv_format": "OCP FP8 E4M3, per-cache scales", "decode_us_mean": t * 1e6,
+            "decode_tokens_per_s": S / t, "alg_bytes_per_launch": alg8,
+            "achieved_gbps": alg8 / t / 1e9, "frac": alg8 / t / 1e9 / HBM_PEAK_GBPS,
+            "bound": "hbm"}
+
+
 def copy_blocks_rate(kcs, vcs, dev, pairs=2048, calls=8):
     """The copy-on-write block copy (pa_copy_blocks) on the same pools:
     `pairs` distinct (src, dst) blocks per call, a fresh set each call and
@@ -289,6 +336,8 @@ def main():
     del rd
 
     copy = copy_blocks_rate(kcs, vcs, dev)
+    fp8_kv = fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
+                             capture, timed_replay) if cfg.dtype in ("bf16", "f16") else None
 
     dec_s = float(dec_ms.mean()) * 1e-3
     achieved = alg_bytes / dec_s / 1e9
@@ -337,6 +386,7 @@ def main():
         "decode_tokens_per_s": S / dec_s,
         "hbm_read_ceiling_gbps": ceiling_gbps,
         "copy_blocks": copy,
+        "fp8_kv": fp8_kv,
         "kernel_src_sha": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

@@ -20,6 +20,7 @@
  *   [MiniPaged-Qwen]  "MiniPaged-Qwen: 把 Paged Attention 讲清楚"
  *   [PA-source]       "PagedAttention 源码解析: KV Cache 怎么管理"
  *   [vLLM-paging]     "vLLM 与 PagedAttention: 把 KV Cache 变成分页状态"
+ *   [KV-principles]   "2.1 KV Cache 与 PagedAttention 原理"
  *
  * Conventions for every entry point
  *   - All tensor arguments are DEVICE pointers to dense row-major arrays owned
@@ -218,6 +219,56 @@ int pa_reshape_and_cache(const void* key, const void* value,
                          int num_tokens, int num_kv_heads, int head_dim,
                          int block_size, int num_blocks, pa_dtype dtype,
                          void* hip_stream);
+
+/*
+ * FP8 KV cache.  The caches hold OCP FP8 E4M3 codes (one byte per value:
+ * sign, 4 exponent bits of bias 7, 3 mantissa bits; no infinities; 0x7F and
+ * 0xFF are NaN; largest finite 448), in the same [num_blocks, num_kv_heads,
+ * block_size, head_dim] layout, with ONE scale per cache: code c of the key
+ * cache stands for value(c) * k_scale, of the value cache for
+ * value(c) * v_scale.  Storing x gives E4M3(fp32(x) * fp32(1 / scale)):
+ * nearest value, ties to the even code, saturating to +-448, NaN kept.
+ * ([KV-principles] §3.3 and its tuning Q&A: a quantised, e.g. FP8, KV cache
+ * when KV memory binds; [vLLM-paging] "Kernel metadata": the KV dtype and
+ * quantisation scales are passed explicitly.  The pages fix neither format
+ * nor scale granularity; per-cache scales are the reading taken here.)
+ * Halving the KV bytes nearly doubles decode throughput at the same
+ * bandwidth.
+ *
+ * pa_paged_attention_decode_fp8 -- pa_paged_attention_decode over E4M3
+ *   caches: the attention of each query over the dequantised history.  Same
+ *   arguments, plus k_scale and v_scale (finite, > 0); dtype is that of query
+ *   and out (bf16 or f16).  Supported: head_dim 128, block_size 16 or 32,
+ *   gqa_group_size <= 16 (the matrix-core kernel); other shapes return
+ *   PA_ERR_UNSUPPORTED.  The workspace is sized by pa_decode_workspace_size
+ *   with the query dtype.
+ * pa_decode_append_fp8 -- pa_decode_append over E4M3 caches: each newest
+ *   token's key/value (query dtype) is quantised as it is stored.
+ * pa_reshape_and_cache_fp8 -- pa_reshape_and_cache into E4M3 caches: key and
+ *   value [num_tokens, num_kv_heads, head_dim] of dtype f32, f16 or bf16 are
+ *   quantised with k_scale / v_scale; head_dim a multiple of 16; slot rules
+ *   as for pa_reshape_and_cache.
+ * Cache pointers must be 16-byte aligned.
+ */
+int pa_paged_attention_decode_fp8(void* out, const void* query, const void* key_cache,
+                                  const void* value_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int num_seqs, int num_heads,
+                                  int num_kv_heads, int gqa_group_size, int head_dim,
+                                  int block_size, int num_blocks, int max_blocks_per_seq,
+                                  int max_context_len, float scale, pa_dtype dtype, float k_scale,
+                                  float v_scale, int partition_size, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream);
+int pa_decode_append_fp8(void* out, const void* query, const void* key, const void* value,
+                         void* key_cache, void* value_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, int num_seqs, int num_heads,
+                         int num_kv_heads, int gqa_group_size, int head_dim, int block_size,
+                         int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+                         pa_dtype dtype, float k_scale, float v_scale, int partition_size,
+                         void* workspace, size_t workspace_bytes, void* hip_stream);
+int pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                             void* value_cache, const int64_t* slot_mapping, int num_tokens,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             pa_dtype dtype, float k_scale, float v_scale, void* hip_stream);
 
 /*
  * pa_copy_blocks -- copy whole physical blocks of both caches:

@@ -72,7 +72,8 @@ def inverse_scale(scale):
 
 def quantize(x, scale):
     """E4M3 codes of fp32(x) * fp32(1 / scale) (x: float32-exact values)."""
-    prod = np.asarray(x, dtype=np.float32) * inverse_scale(scale)   # one fp32 rounding
+    with np.errstate(over="ignore", invalid="ignore"):      # inf/NaN inputs are legal
+        prod = np.asarray(x, dtype=np.float32) * inverse_scale(scale)   # one fp32 rounding
     return e4m3_encode(prod.astype(np.float32))
 
 

@@ -37,6 +37,56 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
     *reinterpret_cast<u32x4*>(value_cache + dst) = vv;
 }
 
+// Cache write into OCP FP8 E4M3 caches: 8 consecutive values of token i,
+// KV head h (column group c) -> 8 codes at key_cache[pb, h, off, 8c .. +8],
+// each E4M3(fp32(x) * inv_scale) -- the quantised form of the cache write
+// above, with one scale per cache.
+template <typename Tag>
+__device__ __forceinline__ void load8_f32(const char* src, float* f) {
+    if constexpr (Tag::kBytes == 4) {
+        to_float(Tag(), load16(src), f);
+        to_float(Tag(), load16(src + 16), f + 4);
+    } else {
+        to_float(Tag(), load16(src), f);
+    }
+}
+
+template <typename Tag>
+__global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, uint8_t* key_cache,
+    uint8_t* value_cache, const int64_t* __restrict__ slots, int num_tokens, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks, float k_inv, float v_inv) {
+    const int cols = head_dim / 8;
+    const uint64_t total = (uint64_t)num_tokens * num_kv_heads * cols;
+    const uint64_t idx = (uint64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+    if (idx >= total) return;
+    const int c = (int)(idx % cols);
+    const uint64_t th = idx / cols;              // token * H_kv + h
+    const int h = (int)(th % num_kv_heads);
+    const uint64_t i = th / num_kv_heads;
+    const uint64_t src = (th * head_dim + 8 * c) * Tag::kBytes;
+    float fk[8], fv[8];
+    load8_f32<Tag>(key + src, fk);
+    load8_f32<Tag>(value + src, fv);
+    const int64_t slot = slots[i];
+    if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
+    const int pb = (int)(slot / block_size);
+    const int off = (int)(slot - (int64_t)pb * block_size);
+    uint32_t ck[8], cv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        ck[e] = e4m3_encode(fk[e] * k_inv);
+        cv[e] = e4m3_encode(fv[e] * v_inv);
+    }
+    const uint64_t dst = kv_row(pb, h, off, num_kv_heads, block_size) * head_dim + 8 * c;
+    *reinterpret_cast<u32x2*>(key_cache + dst) =
+        (u32x2){ck[0] | ck[1] << 8 | ck[2] << 16 | ck[3] << 24,
+                ck[4] | ck[5] << 8 | ck[6] << 16 | ck[7] << 24};
+    *reinterpret_cast<u32x2*>(value_cache + dst) =
+        (u32x2){cv[0] | cv[1] << 8 | cv[2] << 16 | cv[3] << 24,
+                cv[4] | cv[5] << 8 | cv[6] << 16 | cv[7] << 24};
+}
+
 // Sequence b's newest token (history position L_b - 1): key[b, h, c] ->
 // key_cache[pb, h, off, c] with pb = block_tables[b, (L_b-1) / block_size],
 // off = (L_b-1) % block_size -- the append step of [MiniPaged-Qwen] §8.1 with
@@ -132,6 +182,29 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
                        static_cast<const char*>(key), static_cast<const char*>(value),
                        static_cast<char*>(key_cache), static_cast<char*>(value_cache), slots,
                        num_tokens, num_kv_heads, row_bytes, block_size, num_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                        void* value_cache, const int64_t* slots, int num_tokens,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, pa_dtype src_dtype, float k_inv_scale,
+                                        float v_inv_scale, hipStream_t s) {
+    const uint64_t total = (uint64_t)num_tokens * num_kv_heads * (head_dim / 8);
+    if (total == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((total + kCopyThreads - 1) / kCopyThreads);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kCopyThreads), 0, s,
+                           static_cast<const char*>(key), static_cast<const char*>(value),
+                           static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache),
+                           slots, num_tokens, num_kv_heads, head_dim, block_size, num_blocks,
+                           k_inv_scale, v_inv_scale);
+    };
+    switch (src_dtype) {
+        case PA_F32: go(reshape_and_cache_fp8_kernel<F32>); break;
+        case PA_F16: go(reshape_and_cache_fp8_kernel<F16>); break;
+        default: go(reshape_and_cache_fp8_kernel<BF16>); break;
+    }
     return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@
 //   O^T acc  : lane holds O[head n][d = 32 q + 8 i + j] for MFMA j, reg i.
 // The address of every row is kv_row(): block_tables[b, t / BS] gives the
 // physical block, t % BS the slot ([MiniPaged-Qwen] §6.2).
+#include <type_traits>
+
 #include "pa_finalize.h"
 
 namespace pa {
@@ -84,10 +86,11 @@ __device__ __forceinline__ int2 chunk_blocks(const ConstI32* row, int c, int L, 
     return make_int2(pb0, pb1);
 }
 
-// Buffer descriptor of one 16-token tile (4 KB): base address, size.  A
-// size of 0 makes every load from it return zero without touching memory.
+// Buffer descriptor of one 16-token tile (4 KB of 16-bit values, 2 KB of
+// 8-bit codes): base address, size.  A size of 0 makes every load from it
+// return zero without touching memory.
+template <int kTileBytes = 16 * 128 * 2>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, bool live) {
-    constexpr int kTileBytes = 16 * 128 * 2;
     constexpr int kRawBufferFlags = 0x00020000;   // 32-bit data format: raw loads return data
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, live ? kTileBytes : 0,
                                              kRawBufferFlags);
@@ -124,6 +127,149 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& r, const char* kbase, cons
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         r.v[4 + i] = __builtin_amdgcn_raw_buffer_load_b128(v1, voff + i * RB, 0, kNonTemporal);
+}
+
+// ---- KV storage formats -----------------------------------------------------
+// KvSame: the caches hold the query's 16-bit type.  KvE4M3: they hold OCP FP8
+// E4M3 codes (one scale per cache; the value of a code is decode(code) *
+// scale).  For E4M3 a lane takes a contiguous 32-element slice of d for K:
+// in MFMA step kk it supplies K[token n][d = 32 q + 8 kk .. +8] and Q uses
+// the same d, so the contraction over d is the same sum in another order.
+struct KvSame {
+    static constexpr bool kE4M3 = false;
+};
+struct KvE4M3 {
+    static constexpr bool kE4M3 = true;
+};
+
+// One 32-token chunk of E4M3 codes, as loaded.
+struct ChunkRegs8 {
+    u32x4 k0[2], k1[2];   // K tile 0 / 1: row n, d = 32 q .. 32 q + 32
+    u32x2 v[8];           // V rows of this lane's 8 tokens, d = 8 n .. +8
+};
+
+// The 12 loads of one E4M3 chunk (same rules as load_chunk: always issued,
+// dead tiles through an empty descriptor, nontemporal).
+template <int BS>
+__device__ __forceinline__ void load_chunk(ChunkRegs8& r, const char* kbase, const char* vbase,
+                                           int2 pb, bool live0, bool live1, int kvh,
+                                           int num_kv_heads, uint32_t koff, uint32_t voff) {
+    constexpr int RB = 128;       // bytes per token row
+    constexpr int kTile = 16 * RB;
+    const uint64_t row0 = kv_row(pb.x, kvh, 0, num_kv_heads, BS) * RB;
+    const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : 16, num_kv_heads, BS) * RB;
+    const __amdgpu_buffer_rsrc_t k0 = tile_rsrc<kTile>(kbase + row0, live0);
+    const __amdgpu_buffer_rsrc_t k1 = tile_rsrc<kTile>(kbase + row1, live1);
+    const __amdgpu_buffer_rsrc_t v0 = tile_rsrc<kTile>(vbase + row0, live0);
+    const __amdgpu_buffer_rsrc_t v1 = tile_rsrc<kTile>(vbase + row1, live1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        r.k0[h] = __builtin_amdgcn_raw_buffer_load_b128(k0, koff + h * 16, 0, kNonTemporal);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        r.k1[h] = __builtin_amdgcn_raw_buffer_load_b128(k1, koff + h * 16, 0, kNonTemporal);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r.v[i] = __builtin_amdgcn_raw_buffer_load_b64(v0, voff + i * RB, 0, kNonTemporal);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r.v[4 + i] = __builtin_amdgcn_raw_buffer_load_b64(v1, voff + i * RB, 0, kNonTemporal);
+}
+
+// Two E4M3 codes (the low or the high half of w) -> two 16-bit values,
+// exactly (every E4M3 value is representable in bf16 and in fp16).
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3_pair(BF16, uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh));
+}
+template <bool kHigh>
+__device__ __forceinline__ uint32_t e4m3_pair(F16, uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHigh));
+}
+template <typename Tag>
+__device__ __forceinline__ u32x4 e4m3_eight(uint32_t w0, uint32_t w1) {
+    return (u32x4){e4m3_pair<false>(Tag(), w0), e4m3_pair<true>(Tag(), w0),
+                   e4m3_pair<false>(Tag(), w1), e4m3_pair<true>(Tag(), w1)};
+}
+
+// E4M3 chunk -> the 16-bit operands compute_chunk takes (K step kk holds
+// d = 32 q + 8 kk .. +8; V rows as for the 16-bit format).
+template <typename Tag>
+__device__ __forceinline__ ChunkRegs expand(const ChunkRegs8& r8) {
+    ChunkRegs r;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const u32x4 a = r8.k0[kk >> 1], b = r8.k1[kk >> 1];
+        r.k0[kk] = e4m3_eight<Tag>(a[2 * (kk & 1)], a[2 * (kk & 1) + 1]);
+        r.k1[kk] = e4m3_eight<Tag>(b[2 * (kk & 1)], b[2 * (kk & 1) + 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.v[i] = e4m3_eight<Tag>(r8.v[i][0], r8.v[i][1]);
+    return r;
+}
+
+template <typename Kv>
+using KvRegs = typename std::conditional<Kv::kE4M3, ChunkRegs8, ChunkRegs>::type;
+
+// Byte offsets of this lane's K and V data inside a tile.
+template <typename Kv>
+__device__ __forceinline__ uint32_t lane_koff(int n, int q) {
+    return Kv::kE4M3 ? (uint32_t)(n * 128 + 32 * q) : (uint32_t)(n * 128 + 8 * q) * 2;
+}
+template <typename Kv>
+__device__ __forceinline__ uint32_t lane_voff(int n, int q) {
+    return Kv::kE4M3 ? (uint32_t)(4 * q * 128 + 8 * n) : (uint32_t)(4 * q * 128 + 8 * n) * 2;
+}
+
+// Query operand: Q[head n][d] for the d each MFMA step contracts (see the
+// K layouts above); zero for padding heads n >= G.
+template <typename Kv>
+__device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, int n, int q,
+                                           u32x4* qop) {
+    constexpr int D = 128;
+    const int G = a.group;
+    if (n < G) {
+        const char* qp = reinterpret_cast<const char*>(a.query) +
+                         ((uint64_t)b * a.num_heads + kvh * G + n) * D * 2;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            qop[kk] = load16(qp + (Kv::kE4M3 ? 32 * q + 8 * kk : 32 * kk + 8 * q) * 2);
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) qop[kk] = (u32x4){0u, 0u, 0u, 0u};
+    }
+}
+
+// Append step: lanes 0-15 store the newest token's K row, lanes 16-31 its V
+// row, into slot pos of the sequence's tail block (row: its table row).  For
+// E4M3 each value is quantised: E4M3(fp32(x) * fp32(1 / scale)), nearest,
+// ties to even, saturating at +-448.
+template <typename Tag, typename Kv, int BS>
+__device__ __forceinline__ void append_token(const DecodeArgs& a, const ConstI32* row, int b,
+                                             int kvh, int pos, int lane) {
+    constexpr int D = 128;
+    const int pb = row[pos / BS];
+    if ((unsigned)pb >= (unsigned)a.num_blocks || lane >= 32) return;
+    const bool is_k = lane < 16;
+    const char* from = reinterpret_cast<const char*>(is_k ? a.new_key : a.new_value) +
+                       (((uint64_t)b * a.num_kv_heads + kvh) * D + (lane & 15) * 8) * 2;
+    char* to = reinterpret_cast<char*>(const_cast<void*>(is_k ? a.key_cache : a.value_cache));
+    const uint64_t r = kv_row(pb, kvh, pos % BS, a.num_kv_heads, BS);
+    const u32x4 x = load16(from);
+    if constexpr (Kv::kE4M3) {
+        const float inv = is_k ? a.k_inv_scale : a.v_inv_scale;
+        uint32_t c[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            c[2 * u] = e4m3_encode(unpack_lo(Tag(), x[u]) * inv);
+            c[2 * u + 1] = e4m3_encode(unpack_hi(Tag(), x[u]) * inv);
+        }
+        const u32x2 w = {c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                         c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24};
+        *reinterpret_cast<u32x2*>(to + r * D + (lane & 15) * 8) = w;
+    } else {
+        *reinterpret_cast<u32x4*>(to + r * D * 2 + (lane & 15) * 16) = x;
+    }
 }
 
 // Running state of one wavefront: for head n (lane % 16), the reference max
@@ -204,6 +350,18 @@ __device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const
     }
 }
 
+// One chunk's math on either storage format.
+template <typename Tag, typename Kv>
+__device__ __forceinline__ void compute(WaveState& st, KvRegs<Kv>& r, const u32x4* qop,
+                                        float sl2, int tc, int t_end, int q) {
+    if constexpr (Kv::kE4M3) {
+        ChunkRegs ops = expand<Tag>(r);
+        compute_chunk<Tag>(st, ops, qop, sl2, tc, t_end, q);
+    } else {
+        compute_chunk<Tag>(st, r, qop, sl2, tc, t_end, q);
+    }
+}
+
 constexpr int kNW = kDecodeThreads / 64;   // wavefronts per workgroup
 constexpr int kOS = 128 + 4;               // padded LDS row of one head (floats)
 
@@ -219,7 +377,7 @@ struct SegmentLds {
 // and write the result: the final output rows when the segment is the whole
 // history, else a partial state at (plse, po) with head strides
 // (plse_hs, po_hs).
-template <typename Tag, int BS>
+template <typename Tag, int BS, typename Kv>
 __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& sm, int b, int kvh,
                                                int L, int c0, int c1, float* plse, int plse_hs,
                                                float* po, int po_hs) {
@@ -241,24 +399,15 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
     const int q = lane >> 4;
     const int t_end = min(c1 * kChunk, L);
 
-    // Query operand: Q[head n][32 kk + 8 q .. +8]; zero for padding heads.
     u32x4 qop[4];
-    if (n < G) {
-        const char* qp = reinterpret_cast<const char*>(a.query) +
-                         (((uint64_t)b * a.num_heads + head0 + n) * D + 8 * q) * E;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qop[kk] = load16(qp + kk * 64);
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qop[kk] = (u32x4){0u, 0u, 0u, 0u};
-    }
+    load_query<Kv>(a, b, kvh, n, q, qop);
 
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
         (const ConstI32*)(a.block_tables) + (uint64_t)b * a.max_blocks_per_seq;
-    const uint32_t koff = (uint32_t)(n * D + 8 * q) * E;        // K row n, d 8q
-    const uint32_t voff = (uint32_t)(4 * q * D + 8 * n) * E;    // V row 4q, d 8n
+    const uint32_t koff = lane_koff<Kv>(n, q);
+    const uint32_t voff = lane_voff<Kv>(n, q);
     const float sl2 = a.scale_log2;
 
     // Append step: the wave that will read the chunk holding the newest
@@ -268,19 +417,8 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
     // being appended to is private to it).
     if (a.new_key != nullptr) {
         const int c_last = (L - 1) / kChunk;
-        if (c_last >= c0 && c_last < c1 && (c_last - c0) % kNW == wave) {
-            const int pos = L - 1;
-            const int pb = row[pos / BS];
-            if ((unsigned)pb < (unsigned)a.num_blocks && lane < 32) {
-                const uint64_t dst =
-                    kv_row(pb, kvh, pos % BS, a.num_kv_heads, BS) * (D * E) + (lane & 15) * 16;
-                const uint64_t src = ((uint64_t)b * a.num_kv_heads + kvh) * (D * E) + (lane & 15) * 16;
-                const char* from = reinterpret_cast<const char*>(lane < 16 ? a.new_key : a.new_value);
-                char* to = reinterpret_cast<char*>(const_cast<void*>(lane < 16 ? a.key_cache
-                                                                               : a.value_cache));
-                *reinterpret_cast<u32x4*>(to + dst) = load16(from + src);
-            }
-        }
+        if (c_last >= c0 && c_last < c1 && (c_last - c0) % kNW == wave)
+            append_token<Tag, Kv, BS>(a, row, b, kvh, L - 1, lane);
     }
 
     WaveState st;
@@ -299,7 +437,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
         auto chunk_of = [&](int k) { return first + kNW * min(k, K - 1); };
         // tile 1 of chunk c is live when it holds history tokens
         auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
-        ChunkRegs bufA, bufB;
+        KvRegs<Kv> bufA, bufB;
         int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
         int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
         load_chunk<BS>(bufA, kbase, vbase, idsA, true, tile1_live(0), kvh, a.num_kv_heads, koff,
@@ -316,14 +454,14 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
                            kvh, a.num_kv_heads, koff, voff);
             idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
-            compute_chunk<Tag>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+            compute<Tag, Kv>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
             if (++k >= K) break;
             __builtin_amdgcn_sched_barrier(0);
             load_chunk<BS>(bufA, kbase, vbase, idsA, k + 1 < K, k + 1 < K && tile1_live(k + 1),
                            kvh, a.num_kv_heads, koff, voff);
             idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
-            compute_chunk<Tag>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+            compute<Tag, Kv>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, q);
             if (++k >= K) break;
         }
     }
@@ -349,7 +487,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
 // Fixed schedule: workgroup (kvh, b, part) takes tokens [part P, part P + P).
 // The partition index varies slowest, so every sequence's first (full)
 // partition is dispatched before any shorter trailing one.
-template <typename Tag, int BS>
+template <typename Tag, int BS, typename Kv>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a) {
     __shared__ SegmentLds sm;
     const int kvh = blockIdx.x;
@@ -372,10 +510,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
     const int c1 = min(L, t_begin + a.part_len);
     const int c1c = (c1 + kChunk - 1) / kChunk;
     if (nparts_b == 1) {
-        attend_segment<Tag, BS>(a, sm, b, kvh, L, c0, c1c, nullptr, 0, nullptr, 0);
+        attend_segment<Tag, BS, Kv>(a, sm, b, kvh, L, c0, c1c, nullptr, 0, nullptr, 0);
     } else {
         const uint64_t row = ((uint64_t)b * a.num_heads + kvh * G) * a.num_parts + part;
-        attend_segment<Tag, BS>(a, sm, b, kvh, L, c0, c1c, a.ws_lse + row, a.num_parts,
+        attend_segment<Tag, BS, Kv>(a, sm, b, kvh, L, c0, c1c, a.ws_lse + row, a.num_parts,
                                 a.ws_out + row * 128, a.num_parts * 128);
     }
 }
@@ -410,7 +548,7 @@ struct EdgeLds {
 // history of L tokens: the two-buffer pipeline of attend_segment with the
 // chunks taken in order.  Includes the append step when the newest history
 // position lies in [cs, ce): this wavefront alone reads that chunk.
-template <typename Tag, int BS>
+template <typename Tag, int BS, typename Kv>
 __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh, int L, int cs,
                                              int ce, WaveState& st, int& bad) {
     constexpr int D = 128;
@@ -422,47 +560,25 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
     const int t_end = min(ce * kChunk, L);
 
     u32x4 qop[4];
-    if (n < G) {
-        const char* qp = reinterpret_cast<const char*>(a.query) +
-                         (((uint64_t)b * a.num_heads + kvh * G + n) * D + 8 * q) * E;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qop[kk] = load16(qp + kk * 64);
-    } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qop[kk] = (u32x4){0u, 0u, 0u, 0u};
-    }
+    load_query<Kv>(a, b, kvh, n, q, qop);
 
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
         (const ConstI32*)(a.block_tables) + (uint64_t)b * a.max_blocks_per_seq;
-    const uint32_t koff = (uint32_t)(n * D + 8 * q) * E;        // K row n, d 8q
-    const uint32_t voff = (uint32_t)(4 * q * D + 8 * n) * E;    // V row 4q, d 8n
+    const uint32_t koff = lane_koff<Kv>(n, q);
+    const uint32_t voff = lane_voff<Kv>(n, q);
     const float sl2 = a.scale_log2;
 
     if (a.new_key != nullptr) {
         const int c_last = (L - 1) / kChunk;
-        if (c_last >= cs && c_last < ce) {
-            const int pos = L - 1;
-            const int pb = row[pos / BS];
-            if ((unsigned)pb < (unsigned)a.num_blocks && lane < 32) {
-                const uint64_t dst =
-                    kv_row(pb, kvh, pos % BS, a.num_kv_heads, BS) * (D * E) + (lane & 15) * 16;
-                const uint64_t src =
-                    ((uint64_t)b * a.num_kv_heads + kvh) * (D * E) + (lane & 15) * 16;
-                const char* from =
-                    reinterpret_cast<const char*>(lane < 16 ? a.new_key : a.new_value);
-                char* to = reinterpret_cast<char*>(const_cast<void*>(lane < 16 ? a.key_cache
-                                                                               : a.value_cache));
-                *reinterpret_cast<u32x4*>(to + dst) = load16(from + src);
-            }
-        }
+        if (c_last >= cs && c_last < ce) append_token<Tag, Kv, BS>(a, row, b, kvh, L - 1, lane);
     }
 
     const int K = ce - cs;
     auto chunk_of = [&](int k) { return cs + min(k, K - 1); };
     auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
-    ChunkRegs bufA, bufB;
+    KvRegs<Kv> bufA, bufB;
     int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
     int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
     load_chunk<BS>(bufA, kbase, vbase, idsA, true, tile1_live(0), kvh, a.num_kv_heads, koff,
@@ -474,14 +590,14 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
                        a.num_kv_heads, koff, voff);
         idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
         __builtin_amdgcn_sched_barrier(0);
-        compute_chunk<Tag>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+        compute<Tag, Kv>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
         if (++k >= K) break;
         __builtin_amdgcn_sched_barrier(0);
         load_chunk<BS>(bufA, kbase, vbase, idsA, k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
                        a.num_kv_heads, koff, voff);
         idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
         __builtin_amdgcn_sched_barrier(0);
-        compute_chunk<Tag>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+        compute<Tag, Kv>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, q);
         if (++k >= K) break;
     }
 }
@@ -498,13 +614,14 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh,
     const int q = lane >> 4;
     if (n >= a.group) return;
     const float l = st.acc_l[0];
+    const float vs = a.out_scale;
     char* orow = reinterpret_cast<char*>(a.out) +
                  (((uint64_t)b * a.num_heads + kvh * a.group + n) * 128 + 32 * q) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float o[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = bad ? __builtin_nanf("") : st.acc[j][i] / l;
+        for (int j = 0; j < 8; ++j) o[j] = bad ? __builtin_nanf("") : vs * (st.acc[j][i] / l);
         const u32x4 v = {pack2(Tag(), o[0], o[1]), pack2(Tag(), o[2], o[3]),
                          pack2(Tag(), o[4], o[5]), pack2(Tag(), o[6], o[7])};
         *reinterpret_cast<u32x4*>(orow + 16 * i) = v;
@@ -561,8 +678,9 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
         if (bad) o = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                              __builtin_nanf("")};
         if (plse == nullptr) {
-            const uint32_t lo = pack2(Tag(), o[0], o[1]);
-            const uint32_t hi = pack2(Tag(), o[2], o[3]);
+            const f32x4 os = a.out_scale * o;
+            const uint32_t lo = pack2(Tag(), os[0], os[1]);
+            const uint32_t hi = pack2(Tag(), os[2], os[3]);
             char* dst = reinterpret_cast<char*>(a.out) +
                         (((uint64_t)b * a.num_heads + kvh * G + g) * 128 + d) * 2;
             *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
@@ -573,7 +691,7 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
     }
 }
 
-template <typename Tag, int BS>
+template <typename Tag, int BS, typename Kv>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
     __shared__ EdgeLds edge;
     __shared__ int pref[kMaxBalancedSeqs + 1];
@@ -614,7 +732,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         for (int j = 0; j < 8; ++j) st.acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
         st.acc_l = (f32x4){0.f, 0.f, 0.f, 0.f};
         int bad = 0;
-        attend_piece<Tag, BS>(a, b, kvh, L, c0, c1, st, bad);
+        attend_piece<Tag, BS, Kv>(a, b, kvh, L, c0, c1, st, bad);
 
         const bool starts_before = c0 > 0;    // the segment began before this range
         const bool ends_after = c1 < nb;      // it continues past this range
@@ -678,16 +796,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     if (threadIdx.x == 0) reinterpret_cast<int4*>(a.ws_meta)[w] = meta;
 }
 
-template <typename Tag, int BS>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
+template <typename Tag, int BS, typename Kv>
+hipError_t launch_kv(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
-        hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS>), dim3(a.num_wg), dim3(kDecodeThreads),
-                           0, s, a);
+        hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv>), dim3(a.num_wg),
+                           dim3(kDecodeThreads), 0, s, a);
     } else {
         dim3 grid(a.num_kv_heads, a.num_seqs, a.num_parts);
-        hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS>), grid, dim3(kDecodeThreads), 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS, Kv>), grid, dim3(kDecodeThreads), 0, s, a);
     }
     return hipGetLastError();
+}
+
+template <typename Tag, int BS>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
+    return a.kv_format == kKvE4M3 ? launch_kv<Tag, BS, KvE4M3>(a, s)
+                                  : launch_kv<Tag, BS, KvSame>(a, s);
 }
 
 }  // namespace

@@ -9,6 +9,7 @@
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -72,6 +73,29 @@ __device__ __forceinline__ void store_elem(BF16, void* base, uint64_t i, float v
 }
 __device__ __forceinline__ void store_elem(F16, void* base, uint64_t i, float v) {
     reinterpret_cast<_Float16*>(base)[i] = (_Float16)v;
+}
+
+// OCP FP8 E4M3 code of a float32 (sign, 4 exponent bits of bias 7, 3
+// mantissa bits; no infinities; 0x7F is NaN; largest finite 448): nearest
+// representable value, ties to the even code, saturating to +-448.
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (!(a == a)) return 0x7Fu;                       // NaN
+    uint32_t code;
+    if (a >= 448.0f) {
+        code = 0x7Eu;
+    } else if (a < 0.015625f) {
+        // below the least normal 2^-6: multiples of 2^-9 (8 is 2^-6 itself)
+        code = (uint32_t)__builtin_rintf(a * 512.0f);
+    } else {
+        // keep 3 mantissa bits, rounding the 20 dropped ones to nearest even;
+        // exponent bias 127 -> 7
+        const uint32_t u = __float_as_uint(a);
+        code = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+        if (code > 0x7Eu) code = 0x7Eu;
+    }
+    return code | sign;
 }
 
 // 16 bytes -> float32 values (4 for F32, 8 for the 16-bit types).

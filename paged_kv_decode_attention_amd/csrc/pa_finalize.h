@@ -49,7 +49,8 @@ __device__ __forceinline__ void finalize_state(
         float o = num / den;
         if (bad) o = __builtin_nanf("");
         if (plse == nullptr) {
-            store_elem(Tag(), a.out, ((uint64_t)b * a.num_heads + head0 + g) * D + d, o);
+            store_elem(Tag(), a.out, ((uint64_t)b * a.num_heads + head0 + g) * D + d,
+                       a.out_scale * o);
         } else {
             po[(uint64_t)g * po_hs + d] = o;
             if (d == 0) plse[(uint64_t)g * plse_hs] = bad ? __builtin_nanf("") : M + __log2f(den);
@@ -121,7 +122,8 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const Pieces& 
         const uint64_t out0 = ((uint64_t)b * a.num_heads + head0 + g) * D + 4 * d4;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            store_elem(Tag(), a.out, out0 + e, has_nan ? __builtin_nanf("") : num[e] / den);
+            store_elem(Tag(), a.out, out0 + e,
+                       has_nan ? __builtin_nanf("") : a.out_scale * (num[e] / den));
     }
 }
 

@@ -30,8 +30,16 @@ struct DecodeArgs {
     int num_parts;             // ceil(max_context_len / part_len)
     int schedule;              // kFixed or kBalanced
     int num_wg;                // workgroups of the balanced schedule
-    float scale_log2;          // scale * log2(e): scores kept in log2 units
+    float scale_log2;          // scale * log2(e) (* k_scale): scores in log2 units
+    int kv_format;             // kKvSame or kKvE4M3
+    float out_scale;           // v_scale for E4M3 caches, else 1: output = out_scale * o
+    float k_inv_scale;         // fp32(1 / k_scale), fp32(1 / v_scale): the appended
+    float v_inv_scale;         //   token's quantisation (E4M3 caches)
 };
+
+// Storage of the caches: the query's 16-bit type, or OCP FP8 E4M3 codes with
+// one scale per cache.
+enum KvFormat { kKvSame = 0, kKvE4M3 = 1 };
 
 // Work schedules of the decode kernels.
 //   kFixed: workgroup (kv head, sequence, p) takes tokens [p P, (p+1) P);
@@ -75,6 +83,14 @@ hipError_t launch_append_tokens(const void* key, const void* value, void* key_ca
                                 const int32_t* context_lens, int num_seqs, int num_kv_heads,
                                 int row_bytes, int block_size, int num_blocks,
                                 int max_blocks_per_seq, int max_context_len, hipStream_t s);
+
+// Cache write into E4M3 caches: each value x of key/value (dtype src_dtype)
+// is stored as E4M3(fp32(x) * inv_scale).
+hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                        void* value_cache, const int64_t* slots, int num_tokens,
+                                        int num_kv_heads, int head_dim, int block_size,
+                                        int num_blocks, pa_dtype src_dtype, float k_inv_scale,
+                                        float v_inv_scale, hipStream_t s);
 
 // Copy whole blocks of both caches: pair i = (src, dst) in device memory.
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,

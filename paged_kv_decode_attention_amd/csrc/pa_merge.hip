@@ -132,7 +132,8 @@ __global__ __launch_bounds__(kMergeBalancedThreads) void merge_balanced(DecodeAr
     const uint64_t out0 = ((uint64_t)b * a.num_heads + kvh * a.group + g) * D + d;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        store_elem(Tag(), a.out, out0 + e, has_nan ? __builtin_nanf("") : num[e] / den);
+        store_elem(Tag(), a.out, out0 + e,
+                   has_nan ? __builtin_nanf("") : a.out_scale * (num[e] / den));
 }
 
 template <typename Tag>

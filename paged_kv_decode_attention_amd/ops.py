@@ -44,6 +44,17 @@ _SIGNATURES = {
     "pa_debug_gather_kv": (
         _I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _VP]),
     "pa_copy_blocks": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP]),
+    "pa_paged_attention_decode_fp8": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _VP,
+             _I, _I, _I, _I, _I, _I, _I, _I, _I,
+             ctypes.c_float, _I, ctypes.c_float, ctypes.c_float, _I, _VP, ctypes.c_size_t, _VP]),
+    "pa_decode_append_fp8": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+             _I, _I, _I, _I, _I, _I, _I, _I, _I,
+             ctypes.c_float, _I, ctypes.c_float, ctypes.c_float, _I, _VP, ctypes.c_size_t, _VP]),
+    "pa_reshape_and_cache_fp8": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, ctypes.c_float, ctypes.c_float,
+             _VP]),
     "pa_pool_create": (_VP, [_I, _I]),
     "pa_pool_destroy": (None, [_VP]),
     "pa_pool_add_sequence": (_I, [_VP]),
@@ -132,8 +143,11 @@ def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_siz
     return n
 
 
+FP8_CACHE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
 def _decode_args(query, key_cache, value_cache, block_tables, context_lens, scale,
-                 max_context_len, partition_size, out, workspace):
+                 max_context_len, partition_size, out, workspace, kv_fp8=False):
     for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
                  (block_tables, "block_tables"), (context_lens, "context_lens")):
         _gpu(t, n)
@@ -143,7 +157,10 @@ def _decode_args(query, key_cache, value_cache, block_tables, context_lens, scal
     N, H_kv, BS, D2 = key_cache.shape
     if D2 != D:
         raise ValueError("head_dim of query (%d) and caches (%d) differ" % (D, D2))
-    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+    if kv_fp8:
+        if key_cache.dtype not in FP8_CACHE_DTYPES or value_cache.dtype not in FP8_CACHE_DTYPES:
+            raise ValueError("FP8 caches must be uint8 or float8_e4m3fn tensors of E4M3 codes")
+    elif key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
         raise ValueError("query and caches must share one dtype")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
         raise ValueError("block_tables and context_lens must be int32")
@@ -172,6 +189,12 @@ def _decode_args(query, key_cache, value_cache, block_tables, context_lens, scal
     tail = (float(scale), dtype_code(query.dtype), int(partition_size), ws_ptr, ws_len,
             _stream(query.device))
     return out, sizes, tail
+
+
+def _fp8_tail(tail, k_scale, v_scale):
+    # (scale, dtype, partition_size, ws, ws_len, stream) ->
+    # (scale, dtype, k_scale, v_scale, partition_size, ws, ws_len, stream)
+    return tail[:2] + (float(k_scale), float(v_scale)) + tail[2:]
 
 
 def paged_attention_decode(query, key_cache, value_cache, block_tables, context_lens,
@@ -277,6 +300,69 @@ def copy_bytes(dst, src):
         raise ValueError("dst too small")
     _check(load_library().pa_bench_copy(_ptr(dst), _ptr(src), n, _stream(src.device)),
            "copy_bytes")
+
+
+def paged_attention_decode_fp8(query, key_cache, value_cache, block_tables, context_lens,
+                               k_scale, v_scale, scale=None, *, max_context_len=None,
+                               partition_size=0, out=None, workspace=None):
+    """paged_attention_decode over caches of OCP FP8 E4M3 codes (uint8 or
+    float8_e4m3fn [N, H_kv, BS, D]); a code stands for decode(code) * k_scale
+    (keys) or * v_scale (values).  query/out bf16 or f16, head_dim 128."""
+    out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
+                                    scale, max_context_len, partition_size, out, workspace,
+                                    kv_fp8=True)
+    status = load_library().pa_paged_attention_decode_fp8(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), *sizes, *_fp8_tail(tail, k_scale, v_scale))
+    _check(status, "paged_attention_decode_fp8")
+    return out
+
+
+def decode_append_fp8(query, key, value, key_cache, value_cache, block_tables, context_lens,
+                      k_scale, v_scale, scale=None, *, max_context_len=None, partition_size=0,
+                      out=None, workspace=None):
+    """decode_append on E4M3 caches: the newest token's key/value (query
+    dtype) are quantised with k_scale / v_scale as they are stored."""
+    out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
+                                    scale, max_context_len, partition_size, out, workspace,
+                                    kv_fp8=True)
+    for t, n in ((key, "key"), (value, "value")):
+        _gpu(t, n)
+    S, H_kv, D = query.shape[0], key_cache.shape[1], query.shape[2]
+    if key.shape != (S, H_kv, D) or value.shape != key.shape:
+        raise ValueError("key and value must be [S, H_kv, D]")
+    if key.dtype != query.dtype or value.dtype != query.dtype:
+        raise ValueError("key/value must share the query dtype")
+    status = load_library().pa_decode_append_fp8(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+        _ptr(block_tables), _ptr(context_lens), *sizes, *_fp8_tail(tail, k_scale, v_scale))
+    _check(status, "decode_append_fp8")
+    return out
+
+
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale):
+    """Quantise key/value [T, H_kv, D] (f32, f16 or bf16) to E4M3 with the
+    given scales and store them at slot_mapping [T] in the uint8 /
+    float8_e4m3fn caches [N, H_kv, BS, D]."""
+    for t, n in ((key, "key"), (value, "value"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache"), (slot_mapping, "slot_mapping")):
+        _gpu(t, n)
+    if key.shape != value.shape or key.dim() != 3 or key.dtype != value.dtype:
+        raise ValueError("key and value must be [T, H_kv, D] of one shape and dtype")
+    if key_cache.shape != value_cache.shape or key_cache.dim() != 4:
+        raise ValueError("caches must be [N, H_kv, BS, D] of one shape")
+    if key_cache.dtype not in FP8_CACHE_DTYPES or value_cache.dtype not in FP8_CACHE_DTYPES:
+        raise ValueError("FP8 caches must be uint8 or float8_e4m3fn")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
+        raise ValueError("slot_mapping must be [T] int64")
+    T, H_kv, D = key.shape
+    N, H_kv2, BS, D2 = key_cache.shape
+    if (H_kv, D) != (H_kv2, D2):
+        raise ValueError("new tokens and caches disagree in KV heads or head_dim")
+    _check(load_library().pa_reshape_and_cache_fp8(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T, H_kv,
+        D, BS, N, dtype_code(key.dtype), float(k_scale), float(v_scale),
+        _stream(key.device)), "reshape_and_cache_fp8")
 
 
 def copy_blocks(key_cache, value_cache, block_pairs):

@@ -136,6 +136,30 @@ def test_copy_blocks_rejects_on_host(lib):
     assert f(vp(FAKE), vp(FAKE), vp(FAKE), 3, 2, 64, 16, 0, ops.PA_F32, vp(0)) == INVALID
 
 
+def test_fp8_entry_points_reject_on_host(lib):
+    vp, f32 = ctypes.c_void_p, ctypes.c_float
+    f = lib.pa_reshape_and_cache_fp8
+    args = lambda ks, vs, T=4, D=128: (vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), T, 2, D,
+                                       16, 4, ops.PA_BF16, f32(ks), f32(vs), vp(0))
+    assert f(*args(1.0, 1.0, T=0)) == OK                       # no tokens
+    assert f(*args(0.0, 1.0)) == INVALID                       # scale must be > 0
+    assert f(*args(1.0, float("inf"))) == INVALID
+    assert f(*args(1.0, 1.0, D=24)) == UNSUPPORTED             # head_dim not a multiple of 16
+    d = lib.pa_paged_attention_decode_fp8
+    base = dict(S=2, H=28, H_kv=4, G=7, D=128, BS=16, dtype=ops.PA_BF16, ks=0.5, vs=0.5)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return d(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), a["S"], a["H"],
+                 a["H_kv"], a["G"], a["D"], a["BS"], 64, 16, 256, f32(0.1), a["dtype"],
+                 f32(a["ks"]), f32(a["vs"]), 0, vp(FAKE), ctypes.c_size_t(1 << 30), vp(0))
+    assert call(ks=-1.0) == INVALID
+    assert call(vs=float("nan")) == INVALID
+    assert call(D=64) == UNSUPPORTED                           # matrix-core kernel: head_dim 128
+    assert call(dtype=ops.PA_F32) == UNSUPPORTED               # f32 queries: vector-ALU only
+    assert call(S=0) == OK
+
+
 def test_select_kernel_validates(lib):
     assert lib.pa_debug_select_kernel(5) == INVALID
     prev = lib.pa_debug_select_kernel(1)
