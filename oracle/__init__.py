@@ -35,6 +35,7 @@ from .paged_attention import (  # noqa: F401
     decode_contiguous,
     decode_online,
     decode_partitioned,
+    decode_verify,
     partition_state,
     lse_merge,
     reshape_and_cache,

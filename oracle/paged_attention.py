@@ -312,3 +312,35 @@ def kv_cache_bytes_hidden_form(num_layers, seq_len, hidden, batch, bytes_per_ele
     """2 x layers x seq x hidden x batch x bytes  [KV-principles §2.2]."""
     return 2 * int(num_layers) * int(seq_len) * int(hidden) * int(batch) \
         * int(bytes_per_elem)
+
+
+def decode_verify(query, key_cache, value_cache, block_tables, context_lens, query_start,
+                  scale):
+    """Decode with several new query tokens per sequence (the verify step of
+    speculative decoding; [vLLM-paging] "Kernel metadata" lists each
+    sequence's query range and the verify semantics, "Prefix、beam 与
+    speculative": candidate tokens are written to the cache and checked).
+
+    Sequence b owns query rows query_start[b] .. query_start[b+1] - 1 of
+    query [total_q, H, D]: its q_b newest tokens, already in the cache as
+    history positions L_b - q_b .. L_b - 1.  Row i attends positions
+    t <= L_b - q_b + i (causal among the new tokens): the plain decode of
+    eq. o over that prefix of the history.  q_b > L_b (a query token outside
+    the history) gives NaN rows.
+    """
+    total_q, H, D = query.shape
+    out = np.full((total_q, H, D), np.nan)
+    qs = np.asarray(query_start, dtype=np.int64)
+    for b in range(len(qs) - 1):
+        q_b = int(qs[b + 1] - qs[b])
+        L = int(context_lens[b])
+        if q_b <= 0 or q_b > L:
+            continue
+        for i in range(q_b):
+            r = int(qs[b]) + i
+            Li = L - q_b + i + 1
+            one = decode_contiguous(query[r:r + 1], key_cache, value_cache,
+                                    np.asarray(block_tables)[b:b + 1],
+                                    np.array([Li]), scale)
+            out[r] = one[0]
+    return out
