@@ -164,6 +164,43 @@ def fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, cap
             "bound": "hbm"}
 
 
+def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
+                timed_replay, q_len=4):
+    """Verify step (pa_paged_attention_verify) on the same workload: q_len new
+    query tokens per sequence, K calls replayed from a HIP graph.  Each query
+    token is reduced as its own decode row, so the KV bytes read are q_len
+    times the algorithmic ones."""
+    import numpy as np
+    import torch
+    from paged_kv_decode_attention_amd import ops
+
+    S, H, D = q.shape
+    qv = q.repeat_interleave(q_len, dim=0).contiguous()
+    qs = torch.arange(0, S * q_len + 1, q_len, dtype=torch.int32, device=dev)
+    out = torch.empty_like(qv)
+    N, H_kv, BS, _ = kcs[0].shape
+    ws = torch.zeros(max(ops.load_library().pa_verify_workspace_size(
+        S * q_len, H, H_kv, D, BS, max_ctx, 0, ops.dtype_code(q.dtype)), 256),
+        dtype=torch.uint8, device=dev)
+
+    def call(k):
+        r = k % len(kcs)
+        ops.paged_attention_verify(qv, kcs[r], vcs[r], bt, cl, qs, q_len, cfg.scale,
+                                   max_context_len=max_ctx, out=out, workspace=ws)
+    for k in range(10):
+        call(k)
+    torch.cuda.synchronize()
+    g = capture(lambda: [call(k) for k in range(args.steps)])
+    g.replay()
+    us = np.array([timed_replay(g)[1] / args.steps * 1e6 for _ in range(3)])
+    t = float(us.mean()) * 1e-6
+    read = alg_bytes * q_len        # histories re-read per query token (to first order)
+    return {"query_tokens_per_seq": q_len, "call_us_mean": t * 1e6,
+            "verified_tokens_per_s": S * q_len / t, "alg_bytes_per_launch": alg_bytes,
+            "kv_bytes_read_approx": read, "read_gbps": read / t / 1e9,
+            "note": "each query token reduced as its own decode row"}
+
+
 def copy_blocks_rate(kcs, vcs, dev, pairs=2048, calls=8):
     """The copy-on-write block copy (pa_copy_blocks) on the same pools:
     `pairs` distinct (src, dst) blocks per call, a fresh set each call and
@@ -336,6 +373,8 @@ def main():
     del rd
 
     copy = copy_blocks_rate(kcs, vcs, dev)
+    verify = verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
+                         timed_replay)
     fp8_kv = fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
                              capture, timed_replay) if cfg.dtype in ("bf16", "f16") else None
 
@@ -387,6 +426,7 @@ def main():
         "hbm_read_ceiling_gbps": ceiling_gbps,
         "copy_blocks": copy,
         "fp8_kv": fp8_kv,
+        "verify": verify,
         "kernel_src_sha": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:

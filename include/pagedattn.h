@@ -221,6 +221,43 @@ int pa_reshape_and_cache(const void* key, const void* value,
                          void* hip_stream);
 
 /*
+ * pa_paged_attention_verify -- decode with several new query tokens per
+ * sequence: the verify step of speculative decoding, or multi-token decode
+ * ([vLLM-paging] "Kernel metadata": each sequence's query range and the
+ * verify semantics are passed explicitly; "Prefix、beam 与 speculative":
+ * candidate tokens are written to the cache, then checked).
+ *
+ * Sequence b owns the query rows query_start[b] .. query_start[b+1] - 1 of
+ * query and out [total_queries, num_heads, head_dim]: its q_b newest tokens,
+ * already stored in the caches as history positions L_b - q_b .. L_b - 1
+ * (context_lens count them).  Row i of the sequence attends positions
+ * t <= L_b - q_b + i: causal among the new tokens, the plain decode of
+ * pa_paged_attention_decode over that prefix.
+ *
+ *   query_start    DEVICE [num_seqs + 1] int32, non-decreasing, starting at 0
+ *   max_query_len  host-side bound on every q_b
+ *   block_tables   [num_seqs, max_blocks_per_seq]; context_lens [num_seqs]
+ *   workspace      at least pa_verify_workspace_size() bytes, 256-byte aligned
+ *   other arguments as for pa_paged_attention_decode (same support matrix).
+ *
+ * Rows of a sequence with q_b > max_query_len, q_b > L_b or an invalid L_b,
+ * and rows outside every sequence's range, are NaN.  Each query row is
+ * reduced as its own decode row: the K/V of a sequence is read once per
+ * query token.
+ */
+size_t pa_verify_workspace_size(int total_queries, int num_heads, int num_kv_heads,
+                                int head_dim, int block_size, int max_context_len,
+                                int partition_size, pa_dtype dtype);
+int pa_paged_attention_verify(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const int32_t* query_start,
+                              int num_seqs, int total_queries, int max_query_len, int num_heads,
+                              int num_kv_heads, int gqa_group_size, int head_dim, int block_size,
+                              int num_blocks, int max_blocks_per_seq, int max_context_len,
+                              float scale, pa_dtype dtype, int partition_size, void* workspace,
+                              size_t workspace_bytes, void* hip_stream);
+
+/*
  * FP8 KV cache.  The caches hold OCP FP8 E4M3 codes (one byte per value:
  * sign, 4 exponent bits of bias 7, 3 mantissa bits; no infinities; 0x7F and
  * 0xFF are NaN; largest finite 448), in the same [num_blocks, num_kv_heads,

@@ -195,7 +195,8 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                        int block_size, int num_blocks, int max_blocks_per_seq,
                        int max_context_len, float scale, pa_dtype dtype, int partition_size,
                        void* workspace, size_t workspace_bytes, void* hip_stream,
-                       int kv_format = pa::kKvSame, float k_scale = 1.0f, float v_scale = 1.0f) {
+                       int kv_format = pa::kKvSame, float k_scale = 1.0f, float v_scale = 1.0f,
+                       const int32_t* table_rows = nullptr) {
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
     const bool e4m3 = kv_format == pa::kKvE4M3;
     if (e4m3 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
@@ -269,6 +270,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     a.value_cache = value_cache;
     a.block_tables = block_tables;
     a.context_lens = context_lens;
+    a.table_rows = table_rows;
     a.ws_lse = needs_ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off)
                         : nullptr;
     a.ws_out = needs_ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_off)
@@ -403,6 +405,57 @@ int pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache
         (float)(1.0 / (double)v_scale), static_cast<hipStream_t>(hip_stream));
     if (err != hipSuccess) return hip_fail(err, "fp8 cache write kernel launch");
     return PA_OK;
+}
+
+size_t pa_verify_workspace_size(int total_queries, int num_heads, int num_kv_heads,
+                                int head_dim, int block_size, int max_context_len,
+                                int partition_size, pa_dtype dtype) {
+    if (total_queries < 0) return (size_t)-1;
+    const size_t dec = pa_decode_workspace_size(total_queries, num_heads, num_kv_heads, head_dim,
+                                                block_size, max_context_len, partition_size,
+                                                dtype);
+    if (dec == (size_t)-1) return dec;
+    return align256(dec) + 2 * align256((size_t)total_queries * sizeof(int32_t));
+}
+
+int pa_paged_attention_verify(void* out, const void* query, const void* key_cache,
+                              const void* value_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, const int32_t* query_start,
+                              int num_seqs, int total_queries, int max_query_len, int num_heads,
+                              int num_kv_heads, int gqa_group_size, int head_dim, int block_size,
+                              int num_blocks, int max_blocks_per_seq, int max_context_len,
+                              float scale, pa_dtype dtype, int partition_size, void* workspace,
+                              size_t workspace_bytes, void* hip_stream) {
+    if (num_seqs < 0 || total_queries < 0 || max_query_len < 1)
+        return fail(PA_ERR_INVALID_ARG, "num_seqs, total_queries >= 0 and max_query_len >= 1");
+    if (total_queries > 0 && num_seqs == 0)
+        return fail(PA_ERR_INVALID_ARG, "query rows without sequences");
+    if (total_queries == 0) return PA_OK;
+    if (!query_start) return fail(PA_ERR_INVALID_ARG, "null query_start");
+    const size_t need = pa_verify_workspace_size(total_queries, num_heads, num_kv_heads,
+                                                 head_dim, block_size, max_context_len,
+                                                 partition_size, dtype);
+    if (need == (size_t)-1) return fail(PA_ERR_INVALID_ARG, "invalid sizes");
+    if (!workspace || workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(PA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    const size_t dec = need - 2 * align256((size_t)total_queries * sizeof(int32_t));
+    char* base = static_cast<char*>(workspace);
+    int32_t* rows = reinterpret_cast<int32_t*>(base + dec);
+    int32_t* lens = reinterpret_cast<int32_t*>(base + dec +
+                                               align256((size_t)total_queries * sizeof(int32_t)));
+    if (!context_lens) return fail(PA_ERR_INVALID_ARG, "null context_lens");
+    hipError_t e = pa::launch_verify_rows(query_start, context_lens, num_seqs, total_queries,
+                                          max_query_len, max_context_len, rows, lens,
+                                          static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "verify row kernel launch");
+    return decode_impl(out, query, nullptr, nullptr, key_cache, value_cache, block_tables, lens,
+                       total_queries, num_heads, num_kv_heads, gqa_group_size, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                       partition_size, dec > 0 ? workspace : nullptr, dec, hip_stream,
+                       pa::kKvSame, 1.0f, 1.0f, rows);
 }
 
 int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,

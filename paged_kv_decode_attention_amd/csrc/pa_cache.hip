@@ -87,6 +87,34 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
                 cv[4] | cv[5] << 8 | cv[6] << 16 | cv[7] << 24};
 }
 
+// Verify mode: query row r belongs to the sequence b with query_start[b] <=
+// r < query_start[b+1]; it is that sequence's token i = r - query_start[b]
+// of q_b, at history position L_b - q_b + i, and attends the L_b - q_b + i + 1
+// positions up to it.  Every row is written on every call: rows whose
+// sequence cannot be found, whose q_b exceeds max_query_len or L_b, or whose
+// L_b is invalid get length -1 (the decode kernels give them NaN rows) and
+// table row 0.
+__global__ __launch_bounds__(kCopyThreads) void verify_rows_kernel(
+    const int32_t* __restrict__ query_start, const int32_t* __restrict__ context_lens,
+    int num_seqs, int total_queries, int max_query_len, int max_context_len,
+    int32_t* table_rows, int32_t* lens) {
+    const int r = blockIdx.x * kCopyThreads + threadIdx.x;
+    if (r >= total_queries) return;
+    int lo = 0, hi = num_seqs - 1;   // largest b with query_start[b] <= r
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (query_start[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int q0 = query_start[b];
+    const int q1 = query_start[b + 1];
+    const int L = context_lens[b];
+    const int qb = q1 - q0;
+    const bool ok = q0 <= r && r < q1 && qb <= max_query_len && L >= qb && L <= max_context_len;
+    table_rows[r] = ok ? b : 0;
+    lens[r] = ok ? L - qb + (r - q0) + 1 : -1;
+}
+
 // Sequence b's newest token (history position L_b - 1): key[b, h, c] ->
 // key_cache[pb, h, off, c] with pb = block_tables[b, (L_b-1) / block_size],
 // off = (L_b-1) % block_size -- the append step of [MiniPaged-Qwen] §8.1 with
@@ -205,6 +233,18 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
         case PA_F16: go(reshape_and_cache_fp8_kernel<F16>); break;
         default: go(reshape_and_cache_fp8_kernel<BF16>); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_verify_rows(const int32_t* query_start, const int32_t* context_lens,
+                              int num_seqs, int total_queries, int max_query_len,
+                              int max_context_len, int32_t* table_rows, int32_t* lens,
+                              hipStream_t s) {
+    if (total_queries == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((total_queries + kCopyThreads - 1) / kCopyThreads);
+    hipLaunchKernelGGL(verify_rows_kernel, dim3(grid), dim3(kCopyThreads), 0, s, query_start,
+                       context_lens, num_seqs, total_queries, max_query_len, max_context_len,
+                       table_rows, lens);
     return hipGetLastError();
 }
 

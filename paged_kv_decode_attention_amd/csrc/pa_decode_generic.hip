@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
     const int nblk = (t_end - t_begin + BS - 1) / BS;
     int bad_t = 0;
     for (int i = threadIdx.x; i < nblk; i += kDecodeThreads) {
-        int pb = a.block_tables[(uint64_t)b * a.max_blocks_per_seq + t_begin / BS + i];
+        int pb = a.block_tables[table_row_offset(a, b) + t_begin / BS + i];
         if ((unsigned)pb >= (unsigned)a.num_blocks) {
             bad_t = 1;
             pb = 0;

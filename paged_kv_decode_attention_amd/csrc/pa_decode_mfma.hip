@@ -405,7 +405,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
-        (const ConstI32*)(a.block_tables) + (uint64_t)b * a.max_blocks_per_seq;
+        (const ConstI32*)(a.block_tables) + table_row_offset(a, b);
     const uint32_t koff = lane_koff<Kv>(n, q);
     const uint32_t voff = lane_voff<Kv>(n, q);
     const float sl2 = a.scale_log2;
@@ -565,7 +565,7 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
-        (const ConstI32*)(a.block_tables) + (uint64_t)b * a.max_blocks_per_seq;
+        (const ConstI32*)(a.block_tables) + table_row_offset(a, b);
     const uint32_t koff = lane_koff<Kv>(n, q);
     const uint32_t voff = lane_voff<Kv>(n, q);
     const float sl2 = a.scale_log2;

@@ -127,6 +127,18 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const Pieces& 
     }
 }
 
+// Offset of decode row b's block-table row (rows of several decode rows may
+// be one sequence's in verify mode).
+// b is the same in every lane of the wavefront (read through the constant
+// address space, so the read is a scalar load and the row stays uniform).
+__device__ __forceinline__ uint64_t table_row_offset(const DecodeArgs& a, int b) {
+    typedef __attribute__((address_space(4))) const int32_t ConstRow;
+    int r = b;
+    if (a.table_rows != nullptr)
+        r = __builtin_amdgcn_readfirstlane(((const ConstRow*)a.table_rows)[b]);
+    return (uint64_t)r * a.max_blocks_per_seq;
+}
+
 // ---- arithmetic of the balanced schedule (shared by decode and merge) ----
 
 // 32-token chunks of a history of L tokens; 0 for an empty or invalid length.

@@ -19,6 +19,7 @@ struct DecodeArgs {
     const void* value_cache;   // [N, H_kv, BS, D] dtype
     const int32_t* block_tables;   // [S, W]
     const int32_t* context_lens;   // [S]
+    const int32_t* table_rows;     // [S]: block-table row of decode row b, or null (row b)
     const void* new_key;       // [S, H_kv, D] appended token per sequence, or null
     const void* new_value;     // [S, H_kv, D]
     float* ws_lse;             // [S, H, num_parts] float32 (log2 units)
@@ -91,6 +92,13 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         int num_kv_heads, int head_dim, int block_size,
                                         int num_blocks, pa_dtype src_dtype, float k_inv_scale,
                                         float v_inv_scale, hipStream_t s);
+
+// Verify mode: for every query row r < total_q, the block-table row of its
+// sequence and its effective history length (-1 for an invalid row).
+hipError_t launch_verify_rows(const int32_t* query_start, const int32_t* context_lens,
+                              int num_seqs, int total_queries, int max_query_len,
+                              int max_context_len, int32_t* table_rows, int32_t* lens,
+                              hipStream_t s);
 
 // Copy whole blocks of both caches: pair i = (src, dst) in device memory.
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,

@@ -44,6 +44,11 @@ _SIGNATURES = {
     "pa_debug_gather_kv": (
         _I, [_VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, _I, _I, _VP]),
     "pa_copy_blocks": (_I, [_VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _VP]),
+    "pa_verify_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "pa_paged_attention_verify": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP,
+             _I, _I, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+             ctypes.c_float, _I, _I, _VP, ctypes.c_size_t, _VP]),
     "pa_paged_attention_decode_fp8": (
         _I, [_VP, _VP, _VP, _VP, _VP, _VP,
              _I, _I, _I, _I, _I, _I, _I, _I, _I,
@@ -300,6 +305,57 @@ def copy_bytes(dst, src):
         raise ValueError("dst too small")
     _check(load_library().pa_bench_copy(_ptr(dst), _ptr(src), n, _stream(src.device)),
            "copy_bytes")
+
+
+def paged_attention_verify(query, key_cache, value_cache, block_tables, context_lens,
+                           query_start, max_query_len, scale=None, *, max_context_len=None,
+                           partition_size=0, out=None, workspace=None):
+    """Decode with several new query tokens per sequence (speculative verify).
+
+    query [total_q, H, D]: sequence b owns rows query_start[b] ..
+    query_start[b+1] - 1 (query_start [S+1] int32 on the GPU), its q_b newest
+    tokens, already in the caches; row i attends history positions
+    t <= context_lens[b] - q_b + i.  max_query_len bounds every q_b.
+    """
+    for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (query_start, "query_start")):
+        _gpu(t, n)
+    if query.dim() != 3 or key_cache.dim() != 4 or key_cache.shape != value_cache.shape:
+        raise ValueError("query must be [total_q,H,D] and caches [N,H_kv,BS,D] of one shape")
+    if key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
+        raise ValueError("query and caches must share one dtype")
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (query_start, "query_start")):
+        if t.dtype != torch.int32:
+            raise ValueError("%s must be int32" % n)
+    TQ, H, D = query.shape
+    N, H_kv, BS, D2 = key_cache.shape
+    S = context_lens.shape[0]
+    if D2 != D or block_tables.dim() != 2 or block_tables.shape[0] != S or \
+            query_start.shape != (S + 1,):
+        raise ValueError("shapes disagree: block_tables [S, W], query_start [S+1]")
+    if H_kv == 0 or H % H_kv:
+        raise ValueError("num_heads %d is not a multiple of num_kv_heads %d" % (H, H_kv))
+    W = block_tables.shape[1]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    max_context_len = W * BS if max_context_len is None else max_context_len
+    if out is None:
+        out = torch.empty_like(query)
+    lib = load_library()
+    need = lib.pa_verify_workspace_size(TQ, H, H_kv, D, BS, int(max_context_len),
+                                        int(partition_size), dtype_code(query.dtype))
+    if need == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid sizes for the verify workspace")
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=query.device)
+    _check(lib.pa_paged_attention_verify(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start), S, TQ, int(max_query_len), H, H_kv, H // H_kv, D,
+        BS, N, W, int(max_context_len), float(scale), dtype_code(query.dtype),
+        int(partition_size), _ptr(workspace), workspace.numel(), _stream(query.device)),
+        "paged_attention_verify")
+    return out
 
 
 def paged_attention_decode_fp8(query, key_cache, value_cache, block_tables, context_lens,

@@ -1,0 +1,103 @@
+"""Verify mode on the GPU (several new query tokens per sequence, causal
+among them) against the float64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, compare, small_config
+from paged_kv_decode_attention_amd import inputs as I
+from paged_kv_decode_attention_amd import ops
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = (1, 15, 16, 17, 31, 33, 100, 513)
+
+
+def verify_inputs(cfg, qlens, seed=3):
+    inp = I.poison_unread(I.generate(cfg))
+    rng = np.random.default_rng(seed)
+    qs = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    H, D = cfg.num_heads, cfg.head_dim
+    q = torch.from_numpy(rng.standard_normal((int(qs[-1]), H, D)).astype(np.float32)).to(
+        inp.query.dtype)
+    return inp, q, qs
+
+
+def oracle_verify(inp, q, qs):
+    return oracle.decode_verify(q.float().numpy(), inp.key_cache.float().numpy(),
+                                inp.value_cache.float().numpy(),
+                                inp.block_tables.numpy().astype(np.int64),
+                                inp.context_lens.numpy().astype(np.int64), qs, inp.cfg.scale)
+
+
+def run_verify(inp, q, qs, max_q, kernel=ops.KERNEL_AUTO, partition_size=0):
+    prev = ops.select_kernel(kernel)
+    try:
+        out = ops.paged_attention_verify(
+            q.to(DEV), inp.key_cache.to(DEV), inp.value_cache.to(DEV), inp.block_tables.to(DEV),
+            inp.context_lens.to(DEV), torch.from_numpy(qs).to(DEV), max_q,
+            partition_size=partition_size)
+        torch.cuda.synchronize()
+    finally:
+        ops.select_kernel(prev)
+    return out
+
+
+CASES = [("bf16", 2, 7, 128, 16, ops.KERNEL_MFMA), ("f16", 2, 4, 128, 32, ops.KERNEL_MFMA),
+         ("bf16", 2, 7, 128, 16, ops.KERNEL_GENERIC), ("f32", 2, 1, 64, 16, ops.KERNEL_AUTO)]
+
+
+@pytest.mark.parametrize("partition_size", [0, 64])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-hkv%d-g%d-d%d-bs%d-k%d" % c)
+def test_verify_parity(case, partition_size):
+    dtype, H_kv, G, D, BS, kernel = case
+    cfg = small_config(dtype, H_kv, G, D, BS, RAGGED)
+    # q_b <= L_b, except the first sequence (L = 1, q = 2): its rows are NaN
+    qlens = [2, 4, 1, 6, 3, 5, 8, 4]
+    inp, q, qs = verify_inputs(cfg, qlens)
+    out = run_verify(inp, q, qs, 8, kernel, partition_size)
+    ref = oracle_verify(inp, q, qs)
+    assert torch.isnan(out[:2].float()).all()
+    compare(out[2:], ref[2:], dtype, what="verify %s P=%d" % (case, partition_size))
+
+
+def test_verify_single_query_equals_decode():
+    cfg = small_config("bf16", 2, 7, 128, 16, RAGGED)
+    inp, _, _ = verify_inputs(cfg, [1] * len(RAGGED))
+    qs = np.arange(len(RAGGED) + 1, dtype=np.int32)
+    d = dict(q=inp.query.to(DEV), kc=inp.key_cache.to(DEV), vc=inp.value_cache.to(DEV),
+             bt=inp.block_tables.to(DEV), cl=inp.context_lens.to(DEV))
+    a = ops.paged_attention_decode(d["q"], d["kc"], d["vc"], d["bt"], d["cl"])
+    b = ops.paged_attention_verify(d["q"], d["kc"], d["vc"], d["bt"], d["cl"],
+                                   torch.from_numpy(qs).to(DEV), 1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_verify_rows_beyond_max_query_len_are_nan():
+    cfg = small_config("bf16", 2, 7, 128, 16, (100, 200))
+    inp, q, qs = verify_inputs(cfg, [3, 5])
+    out = run_verify(inp, q, qs, 4)           # the second sequence has q = 5 > 4
+    ref = oracle_verify(inp, q, qs)
+    assert torch.isnan(out[3:].float()).all()
+    compare(out[:3], ref[:3], "bf16", what="verify within bound")
+
+
+def test_verify_bench_workload_q4_sampled():
+    cfg = I.CONFIGS["qwen7b_gqa_bf16"]
+    inp, q, qs = verify_inputs(cfg, [4] * cfg.num_seqs)
+    out = run_verify(inp, q, qs, 4)
+    rows = list(range(0, 256, 17))
+    ref = np.full((q.shape[0], cfg.num_heads, cfg.head_dim), np.nan)
+    sub_q = q.float().numpy()
+    kc, vc = inp.key_cache.float().numpy(), inp.value_cache.float().numpy()
+    for r in rows:
+        b = r // 4
+        sel = oracle.decode_verify(sub_q[4 * b:4 * b + 4], kc, vc,
+                                   inp.block_tables.numpy()[b:b + 1].astype(np.int64),
+                                   inp.context_lens.numpy()[b:b + 1].astype(np.int64),
+                                   np.array([0, 4]), cfg.scale)
+        ref[r] = sel[r - 4 * b]
+    compare(out[rows], ref[rows], "bf16", what="verify bench workload q=4")
