@@ -55,6 +55,10 @@ def parse():
                     help="cache write and decode as two calls instead of pa_decode_append")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run the plain copy kernel of this size, 5 times")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the block-size x head-dim sweep (one JSON line per shape)")
+    ap.add_argument("--sweep-out", default=None,
+                    help="with --sweep: also write the table as markdown to this file")
     return ap.parse_args()
 
 
@@ -201,6 +205,105 @@ def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture
             "note": "each query token reduced as its own decode row"}
 
 
+def shape_sweep(args, dev):
+    """Decode-call rate over block sizes 8/16/32/64 and head dims 64/128/256:
+    the bench batch (64 sequences, 28 query / 4 KV heads, the same seeded
+    context lengths), bf16, shuffled tables, random pools on the GPU, pool
+    replicas rotated so the last-level cache cannot hold the working set;
+    K calls replayed from a HIP graph, HIP events around each replay."""
+    import numpy as np
+    import torch
+    from paged_kv_decode_attention_amd import inputs as I
+    from paged_kv_decode_attention_amd import ops
+
+    base = I.CONFIGS["qwen7b_gqa_bf16"]
+    lens = I.draw_context_lens(base).astype(np.int64)
+    S, H, H_kv = base.num_seqs, base.num_heads, base.num_kv_heads
+    G = H // H_kv
+    K = min(args.steps, 100)
+    rows = []
+    for D in (64, 128, 256):
+        for BS in (8, 16, 32, 64):
+            rng = np.random.default_rng(7)
+            nblk = -(-lens // BS)
+            N = int(nblk.sum()) + 64
+            W = -(-4096 // BS)
+            perm = rng.permutation(N).astype(np.int32)
+            bt = np.full((S, W), -1, dtype=np.int32)
+            k = 0
+            for b in range(S):
+                bt[b, :nblk[b]] = perm[k:k + nblk[b]]
+                k += nblk[b]
+            pool = N * H_kv * BS * D * 2
+            R = max(2, int(np.ceil(600e6 / (2 * pool))))
+            g = torch.Generator(device=dev).manual_seed(11)
+            kcs = [torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(R)]
+            vcs = [torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(torch.bfloat16)
+                   for _ in range(R)]
+            q = torch.randn(S, H, D, generator=g, device=dev).to(torch.bfloat16)
+            btd = torch.from_numpy(bt).to(dev)
+            cld = torch.from_numpy(lens.astype(np.int32)).to(dev)
+            out = torch.empty_like(q)
+            max_ctx = W * BS
+            ws = torch.zeros(max(ops.decode_workspace_size(S, H, H_kv, D, BS, max_ctx, 0,
+                                                           q.dtype), 256),
+                             dtype=torch.uint8, device=dev)
+
+            def call(j):
+                ops.paged_attention_decode(q, kcs[j % R], vcs[j % R], btd, cld,
+                                           max_context_len=max_ctx, out=out, workspace=ws)
+            for j in range(5):
+                call(j)
+            torch.cuda.synchronize()
+            gr = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(gr, stream=st):
+                    for j in range(K):
+                        call(j)
+            torch.cuda.current_stream().wait_stream(st)
+            gr.replay()
+            torch.cuda.synchronize()
+            us = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                gr.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us.append(e0.elapsed_time(e1) * 1e3 / K)
+            t = float(np.mean(us)) * 1e-6
+            alg = int(lens.sum()) * H_kv * D * 2 * 2
+            mfma = D == 128 and BS in (16, 32, 64) and G <= 16
+            row = {"head_dim": D, "block_size": BS,
+                   "kernel": "matrix-core, balanced" if mfma else "vector-ALU, partitions",
+                   "decode_us": t * 1e6, "alg_bytes": alg, "achieved_gbps": alg / t / 1e9,
+                   "frac": alg / t / 1e9 / HBM_PEAK_GBPS, "decode_tokens_per_s": S / t,
+                   "pool_replicas": R}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+            del kcs, vcs, gr
+            torch.cuda.empty_cache()
+    if args.sweep_out:
+        L = ["# Decode shape sweep: block size x head dim (bf16, 64 sequences, 28/4 heads, "
+             "L~U[512,4096] seed 2)", "",
+             "Command (repository root, one MI355X):", "",
+             "    python bench.py --sweep --sweep-out <file>", "",
+             "| head_dim | block_size | kernel | decode call us | KV TB/s | % of 8 TB/s | "
+             "decode tokens/s |", "|---|---|---|---|---|---|---|"]
+        for r in rows:
+            L.append("| %d | %d | %s | %.1f | %.2f | %.1f | %.0f |" % (
+                r["head_dim"], r["block_size"], r["kernel"], r["decode_us"],
+                r["achieved_gbps"] / 1e3, 100 * r["frac"], r["decode_tokens_per_s"]))
+        L += ["", "Algorithmic bytes: sum_b L_b x 4 KV heads x head_dim x 2 B x 2 (K and V).  "
+              "Timing: K decode calls replayed from a HIP graph, HIP events around each "
+              "replay, mean of 3."]
+        with open(args.sweep_out, "w") as fh:
+            fh.write("\n".join(L) + "\n")
+
+
 def copy_blocks_rate(kcs, vcs, dev, pairs=2048, calls=8):
     """The copy-on-write block copy (pa_copy_blocks) on the same pools:
     `pairs` distinct (src, dst) blocks per call, a fresh set each call and
@@ -260,6 +363,10 @@ def main():
         sys.exit(1)
     ops.load_library()
     dev = torch.device("cuda:0")
+
+    if args.sweep:
+        shape_sweep(args, dev)
+        return
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20

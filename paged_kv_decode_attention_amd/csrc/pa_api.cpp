@@ -130,7 +130,8 @@ bool use_balanced(bool mfma, int partition_size, int num_seqs, int max_context_l
 }
 
 bool supported_shape(int head_dim, int block_size) {
-    return (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32);
+    return (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
+           (block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64);
 }
 
 }  // namespace
@@ -220,7 +221,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                     head_dim, block_size);
     if (!supported_shape(head_dim, block_size))
         return fail(PA_ERR_UNSUPPORTED, "head_dim %d with block_size %d not built "
-                    "(head_dim 64/128, block_size 16/32)", head_dim, block_size);
+                    "(head_dim 64/128/256, block_size 8/16/32/64)", head_dim, block_size);
     if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
         return fail(PA_ERR_INVALID_ARG, "max_context_len %d outside [0, %lld]", max_context_len,
                     (long long)max_blocks_per_seq * block_size);

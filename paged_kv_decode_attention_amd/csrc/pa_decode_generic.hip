@@ -1,5 +1,6 @@
 // Decode paged attention on the vector ALUs: every supported dtype (f32,
-// f16, bf16), head_dim 64 or 128, block size 16 or 32, any GQA group size.
+// f16, bf16), head_dim 64, 128 or 256, block size 8, 16, 32 or 64, any GQA
+// group size.
 // The matrix-core kernel covers the bf16/fp16 head_dim-128 cases; this one
 // covers the rest (and serves as a second, independent device path).
 //
@@ -181,12 +182,21 @@ hipError_t launch3(const DecodeArgs& a, hipStream_t s) {
 
 template <typename Tag, int D>
 hipError_t launch2(const DecodeArgs& a, hipStream_t s) {
-    return a.block_size == 16 ? launch3<Tag, D, 16>(a, s) : launch3<Tag, D, 32>(a, s);
+    switch (a.block_size) {
+        case 8: return launch3<Tag, D, 8>(a, s);
+        case 16: return launch3<Tag, D, 16>(a, s);
+        case 32: return launch3<Tag, D, 32>(a, s);
+        default: return launch3<Tag, D, 64>(a, s);
+    }
 }
 
 template <typename Tag>
 hipError_t launch1(const DecodeArgs& a, hipStream_t s) {
-    return a.head_dim == 64 ? launch2<Tag, 64>(a, s) : launch2<Tag, 128>(a, s);
+    switch (a.head_dim) {
+        case 64: return launch2<Tag, 64>(a, s);
+        case 128: return launch2<Tag, 128>(a, s);
+        default: return launch2<Tag, 256>(a, s);
+    }
 }
 
 }  // namespace

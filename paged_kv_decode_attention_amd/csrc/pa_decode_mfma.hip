@@ -72,10 +72,17 @@ struct ChunkRegs {
 // constant address space, which lets uniform reads become scalar loads.
 typedef __attribute__((address_space(4))) const int32_t ConstI32;
 
+// Row of chunk c's first tile inside its block: blocks of 16 or 32 tokens
+// start a chunk at row 0; a 64-token block holds two chunks.
+template <int BS>
+__device__ __forceinline__ int tile_row(int c) {
+    return BS == 64 ? (c & 1) * 32 : 0;
+}
+
 template <int BS>
 __device__ __forceinline__ int2 chunk_blocks(const ConstI32* row, int c, int L, int num_blocks,
                                              int& bad) {
-    const int j0 = c * (kChunk / BS);
+    const int j0 = c * kChunk / BS;
     int pb0 = row[j0];
     int pb1 = pb0;
     if constexpr (BS == 16) {
@@ -106,11 +113,11 @@ constexpr int kNonTemporal = 2;   // buffer cache-policy bit: nt
 
 template <int BS>
 __device__ __forceinline__ void load_chunk(ChunkRegs& r, const char* kbase, const char* vbase,
-                                           int2 pb, bool live0, bool live1, int kvh,
+                                           int2 pb, int r0, bool live0, bool live1, int kvh,
                                            int num_kv_heads, uint32_t koff, uint32_t voff) {
     constexpr int RB = 128 * 2;   // bytes per token row
-    const uint64_t row0 = kv_row(pb.x, kvh, 0, num_kv_heads, BS) * RB;
-    const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : 16, num_kv_heads, BS) * RB;
+    const uint64_t row0 = kv_row(pb.x, kvh, r0, num_kv_heads, BS) * RB;
+    const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : r0 + 16, num_kv_heads, BS) * RB;
     const __amdgpu_buffer_rsrc_t k0 = tile_rsrc(kbase + row0, live0);
     const __amdgpu_buffer_rsrc_t k1 = tile_rsrc(kbase + row1, live1);
     const __amdgpu_buffer_rsrc_t v0 = tile_rsrc(vbase + row0, live0);
@@ -152,12 +159,12 @@ struct ChunkRegs8 {
 // dead tiles through an empty descriptor, nontemporal).
 template <int BS>
 __device__ __forceinline__ void load_chunk(ChunkRegs8& r, const char* kbase, const char* vbase,
-                                           int2 pb, bool live0, bool live1, int kvh,
+                                           int2 pb, int r0, bool live0, bool live1, int kvh,
                                            int num_kv_heads, uint32_t koff, uint32_t voff) {
     constexpr int RB = 128;       // bytes per token row
     constexpr int kTile = 16 * RB;
-    const uint64_t row0 = kv_row(pb.x, kvh, 0, num_kv_heads, BS) * RB;
-    const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : 16, num_kv_heads, BS) * RB;
+    const uint64_t row0 = kv_row(pb.x, kvh, r0, num_kv_heads, BS) * RB;
+    const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : r0 + 16, num_kv_heads, BS) * RB;
     const __amdgpu_buffer_rsrc_t k0 = tile_rsrc<kTile>(kbase + row0, live0);
     const __amdgpu_buffer_rsrc_t k1 = tile_rsrc<kTile>(kbase + row1, live1);
     const __amdgpu_buffer_rsrc_t v0 = tile_rsrc<kTile>(vbase + row0, live0);
@@ -440,7 +447,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
         KvRegs<Kv> bufA, bufB;
         int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
         int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
-        load_chunk<BS>(bufA, kbase, vbase, idsA, true, tile1_live(0), kvh, a.num_kv_heads, koff,
+        load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true, tile1_live(0), kvh, a.num_kv_heads, koff,
                        voff);
         int k = 0;
         // The scheduling barriers keep each phase's loads after the previous
@@ -450,14 +457,14 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
         // dead (no bytes move) so that every path has 16 loads in flight.
         for (;;) {
             __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS>(bufB, kbase, vbase, idsB, k + 1 < K, k + 1 < K && tile1_live(k + 1),
+            load_chunk<BS>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1),
                            kvh, a.num_kv_heads, koff, voff);
             idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
             compute<Tag, Kv>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
             if (++k >= K) break;
             __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS>(bufA, kbase, vbase, idsA, k + 1 < K, k + 1 < K && tile1_live(k + 1),
+            load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1),
                            kvh, a.num_kv_heads, koff, voff);
             idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
@@ -581,19 +588,19 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
     KvRegs<Kv> bufA, bufB;
     int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
     int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
-    load_chunk<BS>(bufA, kbase, vbase, idsA, true, tile1_live(0), kvh, a.num_kv_heads, koff,
+    load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true, tile1_live(0), kvh, a.num_kv_heads, koff,
                    voff);
     int k = 0;
     for (;;) {
         __builtin_amdgcn_sched_barrier(0);
-        load_chunk<BS>(bufB, kbase, vbase, idsB, k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
+        load_chunk<BS>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
                        a.num_kv_heads, koff, voff);
         idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
         __builtin_amdgcn_sched_barrier(0);
         compute<Tag, Kv>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
         if (++k >= K) break;
         __builtin_amdgcn_sched_barrier(0);
-        load_chunk<BS>(bufA, kbase, vbase, idsA, k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
+        load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
                        a.num_kv_heads, koff, voff);
         idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
         __builtin_amdgcn_sched_barrier(0);
@@ -818,14 +825,21 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
 
 bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group) {
     return (dt == PA_BF16 || dt == PA_F16) && head_dim == 128 &&
-           (block_size == 16 || block_size == 32) && group >= 1 && group <= 16;
+           (block_size == 16 || block_size == 32 || block_size == 64) && group >= 1 &&
+           group <= 16;
+}
+
+template <typename Tag>
+hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
+    switch (a.block_size) {
+        case 16: return launch_typed<Tag, 16>(a, s);
+        case 32: return launch_typed<Tag, 32>(a, s);
+        default: return launch_typed<Tag, 64>(a, s);
+    }
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s) {
-    if (dt == PA_BF16) {
-        return a.block_size == 16 ? launch_typed<BF16, 16>(a, s) : launch_typed<BF16, 32>(a, s);
-    }
-    return a.block_size == 16 ? launch_typed<F16, 16>(a, s) : launch_typed<F16, 32>(a, s);
+    return dt == PA_BF16 ? launch_bs<BF16>(a, s) : launch_bs<F16>(a, s);
 }
 
 }  // namespace pa

@@ -68,7 +68,7 @@ def _decode(lib, **kw):
     (dict(S=-1), INVALID),
     (dict(dtype=7), INVALID),
     (dict(D=96), UNSUPPORTED),
-    (dict(BS=8), UNSUPPORTED),
+    (dict(BS=12), UNSUPPORTED),
     (dict(max_ctx=129), INVALID),                # > W * BS
     (dict(max_ctx=-1), INVALID),
     (dict(scale=float("inf")), INVALID),

@@ -53,6 +53,13 @@ SMALL_CASES = [
     ("f32", 2, 1, 64, 16, ops.KERNEL_AUTO),
     ("f32", 2, 4, 128, 32, ops.KERNEL_GENERIC),
     ("f32", 1, 12, 128, 16, ops.KERNEL_GENERIC),
+    # block sizes 8 and 64, head_dim 256
+    ("bf16", 2, 7, 128, 64, ops.KERNEL_MFMA),
+    ("f16", 2, 4, 128, 8, ops.KERNEL_AUTO),         # block size 8: vector-ALU kernel
+    ("bf16", 2, 4, 256, 16, ops.KERNEL_AUTO),       # head_dim 256: vector-ALU kernel
+    ("f32", 2, 2, 256, 64, ops.KERNEL_GENERIC),
+    ("bf16", 1, 8, 64, 8, ops.KERNEL_GENERIC),
+    ("f16", 2, 3, 64, 64, ops.KERNEL_GENERIC),
 ]
 
 

@@ -81,7 +81,7 @@ def test_fp8_cache_write_bit_exact(src, scales):
 
 
 CASES = [("bf16", 2, 7, 16), ("bf16", 2, 4, 32), ("f16", 2, 4, 16), ("bf16", 1, 16, 16),
-         ("f16", 3, 1, 32)]
+         ("f16", 3, 1, 32), ("bf16", 2, 7, 64)]
 
 
 @pytest.mark.parametrize("partition_size", [0, 64, 256])
