@@ -479,11 +479,16 @@ def main():
     ceiling_gbps = 5 * rd.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del rd
 
-    copy = copy_blocks_rate(kcs, vcs, dev)
-    verify = verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
-                         timed_replay)
-    fp8_kv = fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
-                             capture, timed_replay) if cfg.dtype in ("bf16", "f16") else None
+    # the other operations' figures (not in --decode-only runs, which the
+    # hardware-counter passes profile)
+    copy = fp8_kv = verify = None
+    if not args.decode_only:
+        copy = copy_blocks_rate(kcs, vcs, dev)
+        verify = verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
+                             timed_replay)
+        if cfg.dtype in ("bf16", "f16"):
+            fp8_kv = fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
+                                     capture, timed_replay)
 
     dec_s = float(dec_ms.mean()) * 1e-3
     achieved = alg_bytes / dec_s / 1e9

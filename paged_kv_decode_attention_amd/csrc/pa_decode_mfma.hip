@@ -384,7 +384,7 @@ struct SegmentLds {
 // and write the result: the final output rows when the segment is the whole
 // history, else a partial state at (plse, po) with head strides
 // (plse_hs, po_hs).
-template <typename Tag, int BS, typename Kv>
+template <typename Tag, int BS, typename Kv, int kRows>
 __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& sm, int b, int kvh,
                                                int L, int c0, int c1, float* plse, int plse_hs,
                                                float* po, int po_hs) {
@@ -412,7 +412,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
-        (const ConstI32*)(a.block_tables) + table_row_offset(a, b);
+        (const ConstI32*)(a.block_tables) + table_row_offset<kRows>(a, b);
     const uint32_t koff = lane_koff<Kv>(n, q);
     const uint32_t voff = lane_voff<Kv>(n, q);
     const float sl2 = a.scale_log2;
@@ -494,7 +494,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
 // Fixed schedule: workgroup (kvh, b, part) takes tokens [part P, part P + P).
 // The partition index varies slowest, so every sequence's first (full)
 // partition is dispatched before any shorter trailing one.
-template <typename Tag, int BS, typename Kv>
+template <typename Tag, int BS, typename Kv, int kRows>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a) {
     __shared__ SegmentLds sm;
     const int kvh = blockIdx.x;
@@ -517,10 +517,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
     const int c1 = min(L, t_begin + a.part_len);
     const int c1c = (c1 + kChunk - 1) / kChunk;
     if (nparts_b == 1) {
-        attend_segment<Tag, BS, Kv>(a, sm, b, kvh, L, c0, c1c, nullptr, 0, nullptr, 0);
+        attend_segment<Tag, BS, Kv, kRows>(a, sm, b, kvh, L, c0, c1c, nullptr, 0, nullptr, 0);
     } else {
         const uint64_t row = ((uint64_t)b * a.num_heads + kvh * G) * a.num_parts + part;
-        attend_segment<Tag, BS, Kv>(a, sm, b, kvh, L, c0, c1c, a.ws_lse + row, a.num_parts,
+        attend_segment<Tag, BS, Kv, kRows>(a, sm, b, kvh, L, c0, c1c, a.ws_lse + row, a.num_parts,
                                 a.ws_out + row * 128, a.num_parts * 128);
     }
 }
@@ -555,7 +555,7 @@ struct EdgeLds {
 // history of L tokens: the two-buffer pipeline of attend_segment with the
 // chunks taken in order.  Includes the append step when the newest history
 // position lies in [cs, ce): this wavefront alone reads that chunk.
-template <typename Tag, int BS, typename Kv>
+template <typename Tag, int BS, typename Kv, int kRows>
 __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh, int L, int cs,
                                              int ce, WaveState& st, int& bad) {
     constexpr int D = 128;
@@ -572,7 +572,7 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
-        (const ConstI32*)(a.block_tables) + table_row_offset(a, b);
+        (const ConstI32*)(a.block_tables) + table_row_offset<kRows>(a, b);
     const uint32_t koff = lane_koff<Kv>(n, q);
     const uint32_t voff = lane_voff<Kv>(n, q);
     const float sl2 = a.scale_log2;
@@ -698,7 +698,7 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
     }
 }
 
-template <typename Tag, int BS, typename Kv>
+template <typename Tag, int BS, typename Kv, int kRows>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
     __shared__ EdgeLds edge;
     __shared__ int pref[kMaxBalancedSeqs + 1];
@@ -739,7 +739,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         for (int j = 0; j < 8; ++j) st.acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
         st.acc_l = (f32x4){0.f, 0.f, 0.f, 0.f};
         int bad = 0;
-        attend_piece<Tag, BS, Kv>(a, b, kvh, L, c0, c1, st, bad);
+        attend_piece<Tag, BS, Kv, kRows>(a, b, kvh, L, c0, c1, st, bad);
 
         const bool starts_before = c0 > 0;    // the segment began before this range
         const bool ends_after = c1 < nb;      // it continues past this range
@@ -803,16 +803,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     if (threadIdx.x == 0) reinterpret_cast<int4*>(a.ws_meta)[w] = meta;
 }
 
-template <typename Tag, int BS, typename Kv>
-hipError_t launch_kv(const DecodeArgs& a, hipStream_t s) {
+template <typename Tag, int BS, typename Kv, int kRows>
+hipError_t launch_rows(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
-        hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv>), dim3(a.num_wg),
+        hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv, kRows>), dim3(a.num_wg),
                            dim3(kDecodeThreads), 0, s, a);
     } else {
         dim3 grid(a.num_kv_heads, a.num_seqs, a.num_parts);
-        hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS, Kv>), grid, dim3(kDecodeThreads), 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS, Kv, kRows>), grid, dim3(kDecodeThreads),
+                           0, s, a);
     }
     return hipGetLastError();
+}
+
+// Decode rows with a row map (verify mode) run their own instantiation.
+template <typename Tag, int BS, typename Kv>
+hipError_t launch_kv(const DecodeArgs& a, hipStream_t s) {
+    return a.table_rows != nullptr ? launch_rows<Tag, BS, Kv, 1>(a, s)
+                                   : launch_rows<Tag, BS, Kv, 0>(a, s);
 }
 
 template <typename Tag, int BS>

@@ -131,10 +131,13 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const Pieces& 
 // be one sequence's in verify mode).
 // b is the same in every lane of the wavefront (read through the constant
 // address space, so the read is a scalar load and the row stays uniform).
+// kRows = 1: the launch carries a row map (verify mode); 0: it does not;
+// -1: test a.table_rows at run time.
+template <int kRows = -1>
 __device__ __forceinline__ uint64_t table_row_offset(const DecodeArgs& a, int b) {
     typedef __attribute__((address_space(4))) const int32_t ConstRow;
     int r = b;
-    if (a.table_rows != nullptr)
+    if (kRows == 1 || (kRows < 0 && a.table_rows != nullptr))
         r = __builtin_amdgcn_readfirstlane(((const ConstRow*)a.table_rows)[b]);
     return (uint64_t)r * a.max_blocks_per_seq;
 }
