@@ -118,7 +118,46 @@ def cpu_baseline(inp, budget_s):
         "seconds": elapsed,
         "cpu_model": _cpu_model(),
         "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "all_cores": cpu_baseline_threads(inp, budget_s, (q, kc, vc, bt, cl)),
     }
+
+
+def cpu_baseline_threads(inp, budget_s, arrays, max_workers=16):
+    """The same oracle on a thread pool over sequences, one BLAS thread per
+    worker, for about budget_s of wall time (NumPy releases the interpreter
+    lock inside its array operations; the speed-up measured is what this
+    host gives)."""
+    import concurrent.futures as cf
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
+    import oracle
+
+    q, kc, vc, bt, cl = arrays
+    S, H = q.shape[0], q.shape[1]
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+
+    def one(b):
+        oracle.decode_contiguous(q, kc, vc, bt, cl, inp.cfg.scale,
+                                 pairs=[(b, h) for h in range(H)])
+        return 1
+
+    done = 0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < budget_s:
+                batch = [(done + i) % S for i in range(S)]       # one pass
+                done += sum(ex.map(one, batch))
+            elapsed = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": workers,
+            "sample": "%d sequence-steps on %d threads in %.1f s" % (done, workers, elapsed)}
 
 
 def fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
@@ -465,6 +504,15 @@ def main():
         # decode call duration: K back-to-back decode calls, HIP events around them
         dec_ms = np.array([timed_replay(g_dec)[1] / args.steps * 1e3 for _ in range(3)])
 
+    # distribution of single decode calls: HIP events around each of 100
+    # calls launched one by one (launch gaps excluded, each call timed alone)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(100)]
+    for k in range(100):
+        step(k, ev[k], decode_only=True)
+    torch.cuda.synchronize()
+    one_us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+
     # practical streaming-read ceiling of this GPU (hand-written kernel)
     rd = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
     sink = torch.empty(16 * 65536, dtype=torch.uint8, device=dev)
@@ -533,6 +581,7 @@ def main():
             "decode_us_mean": float(dec_ms.mean()) * 1e3,
             "decode_us_min": float(dec_ms.min()) * 1e3,
             "decode_us_max": float(dec_ms.max()) * 1e3,
+            "single_call_us_p10_p50_p90": [float(np.percentile(one_us, p)) for p in (10, 50, 90)],
         },
         "decode_tokens_per_s": S / dec_s,
         "hbm_read_ceiling_gbps": ceiling_gbps,
