@@ -96,6 +96,9 @@ def cpu_baseline(inp, budget_s):
     bt = inp.block_tables.numpy().astype(np.int64)
     cl = inp.context_lens.numpy().astype(np.int64)
     S, H = q.shape[0], q.shape[1]
+    # float64 K and V bytes of one history token (all KV heads): the gathered
+    # rows the oracle reduces
+    kv_row_bytes = 2 * kc.shape[1] * kc.shape[3] * 8
     done, tokens, elapsed = 0, 0, 0.0
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     try:
@@ -116,6 +119,7 @@ def cpu_baseline(inp, budget_s):
                   "(%.2f passes over the %d sequences, all %d heads, %d history tokens), "
                   "%.1f s, 1 BLAS thread" % (done, done / S, S, H, tokens, elapsed),
         "seconds": elapsed,
+        "fp64_gbps": tokens * kv_row_bytes / elapsed / 1e9,
         "cpu_model": _cpu_model(),
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
@@ -144,20 +148,23 @@ def cpu_baseline_threads(inp, budget_s, arrays, max_workers=16):
                                  pairs=[(b, h) for h in range(H)])
         return 1
 
-    done = 0
+    done, tokens = 0, 0
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     try:
         with cf.ThreadPoolExecutor(max_workers=workers) as ex:
             t0 = time.perf_counter()
             while time.perf_counter() - t0 < budget_s:
-                batch = [(done + i) % S for i in range(S)]       # one pass
-                done += sum(ex.map(one, batch))
+                done += sum(ex.map(one, range(S)))               # one pass
+                tokens += int(cl.sum())
             elapsed = time.perf_counter() - t0
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
+    kv_row_bytes = 2 * kc.shape[1] * kc.shape[3] * 8
     return {"value": done / elapsed, "unit": "tokens/s", "cores": workers,
-            "sample": "%d sequence-steps on %d threads in %.1f s" % (done, workers, elapsed)}
+            "fp64_gbps": tokens * kv_row_bytes / elapsed / 1e9,
+            "sample": "%d sequence-steps (whole passes over the batch) on %d threads in %.1f s"
+                      % (done, workers, elapsed)}
 
 
 def fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
@@ -503,6 +510,12 @@ def main():
         wall, _ = timed_replay(g_step)
         # decode call duration: K back-to-back decode calls, HIP events around them
         dec_ms = np.array([timed_replay(g_dec)[1] / args.steps * 1e3 for _ in range(3)])
+    # hot-cache figure, labelled as such: every call reads the same pool
+    # replica, so whatever of it the 256 MB last-level cache keeps is reused
+    g_hot = capture(lambda: [step(k * R, decode_only=True) for k in range(args.steps)])
+    g_hot.replay()
+    hot_us = timed_replay(g_hot)[1] / args.steps * 1e6
+    del g_hot
 
     # distribution of single decode calls: HIP events around each of 100
     # calls launched one by one (launch gaps excluded, each call timed alone)
@@ -582,6 +595,7 @@ def main():
             "decode_us_min": float(dec_ms.min()) * 1e3,
             "decode_us_max": float(dec_ms.max()) * 1e3,
             "single_call_us_p10_p50_p90": [float(np.percentile(one_us, p)) for p in (10, 50, 90)],
+            "hot_cache_decode_us": hot_us,
         },
         "decode_tokens_per_s": S / dec_s,
         "hbm_read_ceiling_gbps": ceiling_gbps,
