@@ -217,18 +217,20 @@ def fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, cap
 def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
                 timed_replay, q_len=4):
     """Verify step (pa_paged_attention_verify) on the same workload: q_len new
-    query tokens per sequence, K calls replayed from a HIP graph.  Each query
-    token is reduced as its own decode row, so the KV bytes read are q_len
-    times the algorithmic ones."""
+    query tokens per sequence, K calls replayed from a HIP graph.  The
+    matrix-core kernel serves 16 // G query tokens of a sequence per pass over
+    its K/V (their (token, head) pairs are its 16 columns), so a call reads
+    the histories ceil(q_len / (16 // G)) times."""
+    import math
     import numpy as np
     import torch
     from paged_kv_decode_attention_amd import ops
 
     S, H, D = q.shape
+    N, H_kv, BS, _ = kcs[0].shape
     qv = q.repeat_interleave(q_len, dim=0).contiguous()
     qs = torch.arange(0, S * q_len + 1, q_len, dtype=torch.int32, device=dev)
     out = torch.empty_like(qv)
-    N, H_kv, BS, _ = kcs[0].shape
     ws = torch.zeros(max(ops.load_library().pa_verify_workspace_size(
         S * q_len, H, H_kv, D, BS, max_ctx, 0, ops.dtype_code(q.dtype)), 256),
         dtype=torch.uint8, device=dev)
@@ -243,12 +245,16 @@ def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture
     g = capture(lambda: [call(k) for k in range(args.steps)])
     g.replay()
     us = np.array([timed_replay(g)[1] / args.steps * 1e6 for _ in range(3)])
+    del g
     t = float(us.mean()) * 1e-6
-    read = alg_bytes * q_len        # histories re-read per query token (to first order)
+    per_pass = max(1, 16 // (H // H_kv))
+    passes = math.ceil(q_len / per_pass)
+    read = alg_bytes * passes       # histories read once per pass (to first order)
     return {"query_tokens_per_seq": q_len, "call_us_mean": t * 1e6,
             "verified_tokens_per_s": S * q_len / t, "alg_bytes_per_launch": alg_bytes,
-            "kv_bytes_read_approx": read, "read_gbps": read / t / 1e9,
-            "note": "each query token reduced as its own decode row"}
+            "kv_passes": passes, "kv_bytes_read_approx": read, "read_gbps": read / t / 1e9,
+            "note": "%d query tokens of a sequence share a pass over its K/V "
+                    "(%d (token, head) columns of 16)" % (per_pass, per_pass * (H // H_kv))}
 
 
 def shape_sweep(args, dev):
@@ -547,6 +553,8 @@ def main():
         copy = copy_blocks_rate(kcs, vcs, dev)
         verify = verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
                              timed_replay)
+        verify["q_len_2"] = verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
+                                        capture, timed_replay, q_len=2)
         if cfg.dtype in ("bf16", "f16"):
             fp8_kv = fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
                                      capture, timed_replay)

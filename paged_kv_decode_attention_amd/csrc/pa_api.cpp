@@ -1,5 +1,6 @@
 // Host side of libpagedattn.so: argument validation, partition sizing,
 // workspace layout and kernel dispatch behind the C ABI of pagedattn.h.
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cmath>
@@ -197,7 +198,8 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                        int max_context_len, float scale, pa_dtype dtype, int partition_size,
                        void* workspace, size_t workspace_bytes, void* hip_stream,
                        int kv_format = pa::kKvSame, float k_scale = 1.0f, float v_scale = 1.0f,
-                       const int32_t* table_rows = nullptr) {
+                       const int32_t* table_rows = nullptr, const int32_t* row_tokens = nullptr,
+                       int kernel_kind = -1) {
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
     const bool e4m3 = kv_format == pa::kKvE4M3;
     if (e4m3 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
@@ -240,7 +242,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
         return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a positive multiple of 32 "
                     "and of block_size, at most 64*block_size", partition_size);
 
-    const int kind = g_kernel_kind.load();
+    const int kind = kernel_kind >= 0 ? kernel_kind : g_kernel_kind.load();
     const bool mfma_ok = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size);
     const bool use_mfma = mfma_ok && kind != pa::kGeneric;
     if (kind == pa::kMfma && !mfma_ok)
@@ -272,6 +274,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.table_rows = table_rows;
+    a.row_tokens = row_tokens;
     a.ws_lse = needs_ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off)
                         : nullptr;
     a.ws_out = needs_ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_off)
@@ -416,7 +419,7 @@ size_t pa_verify_workspace_size(int total_queries, int num_heads, int num_kv_hea
                                                 block_size, max_context_len, partition_size,
                                                 dtype);
     if (dec == (size_t)-1) return dec;
-    return align256(dec) + 2 * align256((size_t)total_queries * sizeof(int32_t));
+    return align256(dec) + 3 * align256((size_t)total_queries * sizeof(int32_t));
 }
 
 int pa_paged_attention_verify(void* out, const void* query, const void* key_cache,
@@ -442,21 +445,31 @@ int pa_paged_attention_verify(void* out, const void* query, const void* key_cach
                     workspace ? workspace_bytes : (size_t)0);
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(PA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-    const size_t dec = need - 2 * align256((size_t)total_queries * sizeof(int32_t));
+    const size_t arr = align256((size_t)total_queries * sizeof(int32_t));
+    const size_t dec = need - 3 * arr;
     char* base = static_cast<char*>(workspace);
     int32_t* rows = reinterpret_cast<int32_t*>(base + dec);
-    int32_t* lens = reinterpret_cast<int32_t*>(base + dec +
-                                               align256((size_t)total_queries * sizeof(int32_t)));
+    int32_t* lens = reinterpret_cast<int32_t*>(base + dec + arr);
+    int32_t* toks = reinterpret_cast<int32_t*>(base + dec + 2 * arr);
     if (!context_lens) return fail(PA_ERR_INVALID_ARG, "null context_lens");
+    if (gqa_group_size < 1) return fail(PA_ERR_INVALID_ARG, "gqa_group_size must be positive");
+    // The matrix-core kernel serves up to 16 / G query rows of a sequence in
+    // one pass over its K/V (their (row, head) pairs fill its 16 columns);
+    // the vector-ALU kernel takes one row per pass.  The kernel family is
+    // chosen once here, so the grouping and the decode launch agree.
+    const int kind = g_kernel_kind.load();
+    const bool mfma = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size) &&
+                      kind != pa::kGeneric;
+    const int u = mfma ? std::max(1, pa::kMaxGroup / gqa_group_size) : 1;
     hipError_t e = pa::launch_verify_rows(query_start, context_lens, num_seqs, total_queries,
-                                          max_query_len, max_context_len, rows, lens,
+                                          max_query_len, max_context_len, u, rows, lens, toks,
                                           static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "verify row kernel launch");
     return decode_impl(out, query, nullptr, nullptr, key_cache, value_cache, block_tables, lens,
                        total_queries, num_heads, num_kv_heads, gqa_group_size, head_dim,
                        block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
                        partition_size, dec > 0 ? workspace : nullptr, dec, hip_stream,
-                       pa::kKvSame, 1.0f, 1.0f, rows);
+                       pa::kKvSame, 1.0f, 1.0f, rows, toks, kind);
 }
 
 int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,

@@ -90,14 +90,18 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
 // Verify mode: query row r belongs to the sequence b with query_start[b] <=
 // r < query_start[b+1]; it is that sequence's token i = r - query_start[b]
 // of q_b, at history position L_b - q_b + i, and attends the L_b - q_b + i + 1
-// positions up to it.  Every row is written on every call: rows whose
-// sequence cannot be found, whose q_b exceeds max_query_len or L_b, or whose
-// L_b is invalid get length -1 (the decode kernels give them NaN rows) and
+// positions up to it.  The sequence's rows are grouped u at a time (u =
+// tokens_per_row): the decode row starting at the group's first row i
+// carries n = min(u, q_b - i) rows, and its length is that of its last row,
+// L_b - q_b + i + n; the group's other rows carry none (length 0).  Every
+// row is written on every call: rows whose sequence cannot be found, whose
+// q_b exceeds max_query_len or L_b, or whose L_b is invalid each carry
+// themselves with length -1 (the decode kernels give them NaN rows) and
 // table row 0.
 __global__ __launch_bounds__(kCopyThreads) void verify_rows_kernel(
     const int32_t* __restrict__ query_start, const int32_t* __restrict__ context_lens,
-    int num_seqs, int total_queries, int max_query_len, int max_context_len,
-    int32_t* table_rows, int32_t* lens) {
+    int num_seqs, int total_queries, int max_query_len, int max_context_len, int u,
+    int32_t* table_rows, int32_t* lens, int32_t* row_tokens) {
     const int r = blockIdx.x * kCopyThreads + threadIdx.x;
     if (r >= total_queries) return;
     int lo = 0, hi = num_seqs - 1;   // largest b with query_start[b] <= r
@@ -111,8 +115,11 @@ __global__ __launch_bounds__(kCopyThreads) void verify_rows_kernel(
     const int L = context_lens[b];
     const int qb = q1 - q0;
     const bool ok = q0 <= r && r < q1 && qb <= max_query_len && L >= qb && L <= max_context_len;
+    const int i = r - q0;
+    const int n = !ok ? 1 : i % u == 0 ? min(u, qb - i) : 0;
     table_rows[r] = ok ? b : 0;
-    lens[r] = ok ? L - qb + (r - q0) + 1 : -1;
+    lens[r] = !ok ? -1 : n > 0 ? L - qb + i + n : 0;
+    row_tokens[r] = n;
 }
 
 // Sequence b's newest token (history position L_b - 1): key[b, h, c] ->
@@ -238,13 +245,14 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
 
 hipError_t launch_verify_rows(const int32_t* query_start, const int32_t* context_lens,
                               int num_seqs, int total_queries, int max_query_len,
-                              int max_context_len, int32_t* table_rows, int32_t* lens,
-                              hipStream_t s) {
+                              int max_context_len, int tokens_per_row, int32_t* table_rows,
+                              int32_t* lens, int32_t* row_tokens, hipStream_t s) {
     if (total_queries == 0) return hipSuccess;
+    if (tokens_per_row < 1) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((total_queries + kCopyThreads - 1) / kCopyThreads);
     hipLaunchKernelGGL(verify_rows_kernel, dim3(grid), dim3(kCopyThreads), 0, s, query_start,
                        context_lens, num_seqs, total_queries, max_query_len, max_context_len,
-                       table_rows, lens);
+                       tokens_per_row, table_rows, lens, row_tokens);
     return hipGetLastError();
 }
 

@@ -39,16 +39,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
     const int b = blockIdx.y;
     const int part = blockIdx.z;     // slowest: full partitions dispatch first
     const int g0 = hg * GT;
-    const int nh = min(GT, a.group - g0);
+    // This kernel serves decode rows of at most one query row (a verify row
+    // map built for it groups none), so its columns are the group's heads.
+    const int ncols = min(row_tokens(a, b), 1) * a.group;
+    const int nh = min(GT, ncols - g0);
+    if (nh <= 0) return;
     const int head0 = kvh * a.group + g0;
     const int L = a.context_lens[b];
 
     if (L < 0 || L > a.max_context_len) {
-        if (part == 0) fill_rows<Tag>(a, b, head0, nh, __builtin_nanf(""));
+        if (part == 0) fill_cols<Tag>(a, b, kvh, g0, nh, __builtin_nanf(""));
         return;
     }
     if (L == 0) {
-        if (part == 0) fill_rows<Tag>(a, b, head0, nh, 0.0f);
+        if (part == 0) fill_cols<Tag>(a, b, kvh, g0, nh, 0.0f);
         return;
     }
     const int t_begin = part * a.part_len;
@@ -154,14 +158,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
         }
     }
     __syncthreads();
-    if (nparts_b == 1) {
-        finalize_state<Tag>(a, sm_m, sm_l, sm_o, NW, GT * D, D, head0, nh, b, bad, nullptr, 0,
-                            nullptr, 0);
-    } else {
-        const uint64_t row = ((uint64_t)b * a.num_heads + head0) * a.num_parts + part;
-        finalize_state<Tag>(a, sm_m, sm_l, sm_o, NW, GT * D, D, head0, nh, b, bad,
-                            a.ws_lse + row, a.num_parts, a.ws_out + row * D, a.num_parts * D);
-    }
+    finalize_state<Tag>(a, sm_m, sm_l, sm_o, NW, GT * D, D, b, kvh, g0, nh, bad,
+                        nparts_b == 1 ? -1 : part);
 }
 
 template <typename Tag, int D, int BS, int GT>

@@ -228,16 +228,23 @@ __device__ __forceinline__ uint32_t lane_voff(int n, int q) {
     return Kv::kE4M3 ? (uint32_t)(4 * q * 128 + 8 * n) : (uint32_t)(4 * q * 128 + 8 * n) * 2;
 }
 
-// Query operand: Q[head n][d] for the d each MFMA step contracts (see the
-// K layouts above); zero for padding heads n >= G.
-template <typename Kv>
+// [S, H] row of column n of decode row b (KV head kvh): query head kvh G + n
+// of row b, or with verify columns (kCols) the (query row, head) pair the
+// column stands for.
+template <bool kCols>
+__device__ __forceinline__ uint64_t column_row(const DecodeArgs& a, int b, int kvh, int n) {
+    return kCols ? col_row(a, b, kvh, n) : (uint64_t)b * a.num_heads + kvh * a.group + n;
+}
+
+// Query operand: Q[column n][d] for the d each MFMA step contracts (see the
+// K layouts above); zero for padding columns n >= ncols.
+template <typename Kv, bool kCols>
 __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, int n, int q,
-                                           u32x4* qop) {
+                                           int ncols, u32x4* qop) {
     constexpr int D = 128;
-    const int G = a.group;
-    if (n < G) {
+    if (n < ncols) {
         const char* qp = reinterpret_cast<const char*>(a.query) +
-                         ((uint64_t)b * a.num_heads + kvh * G + n) * D * 2;
+                         column_row<kCols>(a, b, kvh, n) * D * 2;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             qop[kk] = load16(qp + (Kv::kE4M3 ? 32 * q + 8 * kk : 32 * kk + 8 * q) * 2);
@@ -294,9 +301,15 @@ struct WaveState {
 // 16-bit weights hold that range with no loss of relative precision).
 constexpr float kLazy = 8.0f;
 
-template <typename Tag>
+// Tokens at or past t_end (the end of the history, or of the piece) are
+// excluded.  With verify columns (kCols) column n's causal end t_col (this
+// lane's column) may lie before t_end; t_lo is the smallest column end of the
+// wavefront.  A column that has seen no token yet has m_ref = -inf: its
+// weights are then 2^(-inf) = 0 and its rescale factor 0.
+template <typename Tag, bool kCols>
 __device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const u32x4* qop,
-                                              float sl2, int tc, int t_end, int q) {
+                                              float sl2, int tc, int t_end, int t_col, int t_lo,
+                                              int q) {
     // Scores: S^T[token][head] for the two 16-token tiles.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -309,20 +322,19 @@ __device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const
         s[i] = s0[i] * sl2;
         s[4 + i] = s1[i] * sl2;
     }
-    if (tc + kChunk > t_end) {
+    if (tc + kChunk > (kCols ? t_lo : t_end)) {
         // Tokens at or past the end of the history are excluded (the last
         // block is masked past the context length): score -inf, and the V
         // row zeroed so stale slot contents cannot reach the accumulator.
+        // A verify column's tokens past its causal end only get score -inf
+        // (their V rows hold data other columns use).
+        const int t_s = kCols ? t_col : t_end;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (tc + 4 * q + i >= t_end) {
-                s[i] = -INFINITY;
-                r.v[i] = (u32x4){0u, 0u, 0u, 0u};
-            }
-            if (tc + 16 + 4 * q + i >= t_end) {
-                s[4 + i] = -INFINITY;
-                r.v[4 + i] = (u32x4){0u, 0u, 0u, 0u};
-            }
+            if (tc + 4 * q + i >= t_s) s[i] = -INFINITY;
+            if (tc + 4 * q + i >= t_end) r.v[i] = (u32x4){0u, 0u, 0u, 0u};
+            if (tc + 16 + 4 * q + i >= t_s) s[4 + i] = -INFINITY;
+            if (tc + 16 + 4 * q + i >= t_end) r.v[4 + i] = (u32x4){0u, 0u, 0u, 0u};
         }
     }
     float cmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
@@ -333,16 +345,17 @@ __device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const
     // accumulators deferred until the running max has grown by 2^kLazy.
     if (__any(cmax > st.m_ref + kLazy)) {
         const float m_new = fmaxf(st.m_ref, cmax);
-        const float alpha = fast_exp2(st.m_ref - m_new);
+        const float alpha = kCols ? rescale_weight(st.m_ref, m_new) : fast_exp2(st.m_ref - m_new);
 #pragma unroll
         for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
         st.acc_l *= alpha;
         st.m_ref = m_new;
     }
+    const float m_ref = (kCols && st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
     u32x4 pop;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-        pop[u] = pack2(Tag(), fast_exp2(s[2 * u] - st.m_ref), fast_exp2(s[2 * u + 1] - st.m_ref));
+        pop[u] = pack2(Tag(), fast_exp2(s[2 * u] - m_ref), fast_exp2(s[2 * u + 1] - m_ref));
     const u32x4 ones = {kOnePair<Tag>(), kOnePair<Tag>(), kOnePair<Tag>(), kOnePair<Tag>()};
     st.acc_l = mfma16x16x32(Tag(), ones, pop, st.acc_l);
 #pragma unroll
@@ -358,14 +371,15 @@ __device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const
 }
 
 // One chunk's math on either storage format.
-template <typename Tag, typename Kv>
+template <typename Tag, typename Kv, bool kCols>
 __device__ __forceinline__ void compute(WaveState& st, KvRegs<Kv>& r, const u32x4* qop,
-                                        float sl2, int tc, int t_end, int q) {
+                                        float sl2, int tc, int t_end, int t_col, int t_lo,
+                                        int q) {
     if constexpr (Kv::kE4M3) {
         ChunkRegs ops = expand<Tag>(r);
-        compute_chunk<Tag>(st, ops, qop, sl2, tc, t_end, q);
+        compute_chunk<Tag, kCols>(st, ops, qop, sl2, tc, t_end, t_col, t_lo, q);
     } else {
-        compute_chunk<Tag>(st, r, qop, sl2, tc, t_end, q);
+        compute_chunk<Tag, kCols>(st, r, qop, sl2, tc, t_end, t_col, t_lo, q);
     }
 }
 
@@ -378,18 +392,15 @@ struct SegmentLds {
     __attribute__((aligned(16))) float o[kNW * 16 * kOS];
 };
 
-// All wavefronts of the workgroup attend chunks [c0, c1) of (sequence b,
+// All wavefronts of the workgroup attend chunks [c0, c1) of (decode row b,
 // KV head kvh) -- chunk c covers history tokens [32 c, 32 c + 32) -- with
 // the chunks dealt round-robin to the wavefronts, then merge their states
 // and write the result: the final output rows when the segment is the whole
-// history, else a partial state at (plse, po) with head strides
-// (plse_hs, po_hs).
+// history (part < 0), else partition state `part`.
 template <typename Tag, int BS, typename Kv, int kRows>
 __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& sm, int b, int kvh,
-                                               int L, int c0, int c1, float* plse, int plse_hs,
-                                               float* po, int po_hs) {
-    constexpr int D = 128;
-    constexpr int E = 2;
+                                               int L, int c0, int c1, int part) {
+    constexpr bool kCols = kRows == 1;
     // The segment is the same for every lane; say so, so that block numbers
     // are fetched with scalar loads (which do not share the vector loads'
     // in-order counter) and addresses are computed once per wavefront.
@@ -399,15 +410,18 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
     c0 = __builtin_amdgcn_readfirstlane(c0);
     c1 = __builtin_amdgcn_readfirstlane(c1);
     const int G = a.group;
-    const int head0 = kvh * G;
+    const int ntok = kCols ? row_tokens<kRows>(a, b) : 1;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;
     const int q = lane >> 4;
     const int t_end = min(c1 * kChunk, L);
+    // verify columns: column n attends the L - (ntok - 1 - n / G) oldest tokens
+    const int t_lo = kCols ? min(t_end, L - (ntok - 1)) : t_end;
+    const int t_col = kCols ? min(t_end, L - (ntok - 1 - n / G)) : t_end;
 
     u32x4 qop[4];
-    load_query<Kv>(a, b, kvh, n, q, qop);
+    load_query<Kv, kCols>(a, b, kvh, n, q, ntok * G, qop);
 
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
@@ -461,14 +475,16 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
                            kvh, a.num_kv_heads, koff, voff);
             idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
-            compute<Tag, Kv>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+            compute<Tag, Kv, kCols>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo,
+                                    q);
             if (++k >= K) break;
             __builtin_amdgcn_sched_barrier(0);
             load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1),
                            kvh, a.num_kv_heads, koff, voff);
             idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
-            compute<Tag, Kv>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+            compute<Tag, Kv, kCols>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo,
+                                    q);
             if (++k >= K) break;
         }
     }
@@ -486,8 +502,8 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
             (f32x4){st.acc[4][i], st.acc[5][i], st.acc[6][i], st.acc[7][i]};
     }
     const bool any_bad = __syncthreads_or(bad);
-    finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, 16 * kOS, kOS, head0, G, b, any_bad, plse,
-                        plse_hs, po, po_hs);
+    finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, 16 * kOS, kOS, b, kvh, 0, ntok * G, any_bad,
+                        part);
     __syncthreads();   // LDS is reused by the next segment
 }
 
@@ -500,14 +516,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
     const int kvh = blockIdx.x;
     const int b = blockIdx.y;
     const int part = blockIdx.z;
-    const int G = a.group;
+    const int ncols = row_tokens<kRows>(a, b) * a.group;
     const int L = a.context_lens[b];
     if (L < 0 || L > a.max_context_len) {
-        if (part == 0) fill_rows<Tag>(a, b, kvh * G, G, __builtin_nanf(""));
+        if (part == 0) fill_cols<Tag>(a, b, kvh, 0, ncols, __builtin_nanf(""));
         return;
     }
     if (L == 0) {
-        if (part == 0) fill_rows<Tag>(a, b, kvh * G, G, 0.0f);
+        if (part == 0) fill_cols<Tag>(a, b, kvh, 0, ncols, 0.0f);
         return;
     }
     const int t_begin = part * a.part_len;
@@ -516,13 +532,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
     const int c0 = t_begin / kChunk;
     const int c1 = min(L, t_begin + a.part_len);
     const int c1c = (c1 + kChunk - 1) / kChunk;
-    if (nparts_b == 1) {
-        attend_segment<Tag, BS, Kv, kRows>(a, sm, b, kvh, L, c0, c1c, nullptr, 0, nullptr, 0);
-    } else {
-        const uint64_t row = ((uint64_t)b * a.num_heads + kvh * G) * a.num_parts + part;
-        attend_segment<Tag, BS, Kv, kRows>(a, sm, b, kvh, L, c0, c1c, a.ws_lse + row, a.num_parts,
-                                a.ws_out + row * 128, a.num_parts * 128);
-    }
+    attend_segment<Tag, BS, Kv, kRows>(a, sm, b, kvh, L, c0, c1c, nparts_b == 1 ? -1 : part);
 }
 
 // ---- balanced schedule ----------------------------------------------------
@@ -551,23 +561,25 @@ struct EdgeLds {
     int bad[2 * kNW];
 };
 
-// Wavefront state over chunks [cs, ce) of (sequence b, KV head kvh) with a
-// history of L tokens: the two-buffer pipeline of attend_segment with the
-// chunks taken in order.  Includes the append step when the newest history
-// position lies in [cs, ce): this wavefront alone reads that chunk.
+// Wavefront state over chunks [cs, ce) of (decode row b, KV head kvh) with
+// a history of L tokens (ntok query rows carried: verify columns): the
+// two-buffer pipeline of attend_segment with the chunks taken in order.
+// Includes the append step when the newest history position lies in
+// [cs, ce): this wavefront alone reads that chunk.
 template <typename Tag, int BS, typename Kv, int kRows>
-__device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh, int L, int cs,
-                                             int ce, WaveState& st, int& bad) {
-    constexpr int D = 128;
-    constexpr int E = 2;
+__device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh, int L, int ntok,
+                                             int cs, int ce, WaveState& st, int& bad) {
+    constexpr bool kCols = kRows == 1;
     const int G = a.group;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int q = lane >> 4;
     const int t_end = min(ce * kChunk, L);
+    const int t_lo = kCols ? min(t_end, L - (ntok - 1)) : t_end;
+    const int t_col = kCols ? min(t_end, L - (ntok - 1 - n / G)) : t_end;
 
     u32x4 qop[4];
-    load_query<Kv>(a, b, kvh, n, q, qop);
+    load_query<Kv, kCols>(a, b, kvh, n, q, ntok * G, qop);
 
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
@@ -597,33 +609,34 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
                        a.num_kv_heads, koff, voff);
         idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
         __builtin_amdgcn_sched_barrier(0);
-        compute<Tag, Kv>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+        compute<Tag, Kv, kCols>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo, q);
         if (++k >= K) break;
         __builtin_amdgcn_sched_barrier(0);
         load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
                        a.num_kv_heads, koff, voff);
         idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
         __builtin_amdgcn_sched_barrier(0);
-        compute<Tag, Kv>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, q);
+        compute<Tag, Kv, kCols>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo, q);
         if (++k >= K) break;
     }
 }
 
 // Output rows of a whole history held by one wavefront: o = õ / l for the
-// G heads of the group (lane 16 q + n holds head n, d = 32 q + 8 i + j in
-// acc[j][i]), rounded once to the storage type; NaN when a table entry was
-// out of the pool.
-template <typename Tag>
-__device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh,
+// ncols columns (the G heads of the group; verify: its (query row, head)
+// pairs) -- lane 16 q + n holds column n, d = 32 q + 8 i + j in acc[j][i] --
+// rounded once to the storage type; NaN when a table entry was out of the
+// pool.
+template <typename Tag, bool kCols>
+__device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, int ncols,
                                            const WaveState& st, bool bad) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int q = lane >> 4;
-    if (n >= a.group) return;
+    if (n >= ncols) return;
     const float l = st.acc_l[0];
     const float vs = a.out_scale;
     char* orow = reinterpret_cast<char*>(a.out) +
-                 (((uint64_t)b * a.num_heads + kvh * a.group + n) * 128 + 32 * q) * 2;
+                 (column_row<kCols>(a, b, kvh, n) * 128 + 32 * q) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float o[8];
@@ -637,17 +650,18 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh,
 
 // Merge of the edge pieces in `mask` (bit p: piece p) of one segment (the
 // update of [MiniPaged-Qwen] §5.2 applied to whole states, in piece order)
-// and its write: output rows when plse == nullptr, else the partial state
-// (o~/l, m + log2 l) at (plse, po).  Called by every thread of the
-// workgroup; a thread takes 4 consecutive d of one head.  The pieces are
-// listed by position (absent slots repeat the last piece with weight 0) so
-// that all of a thread's LDS reads are issued together.
-template <typename Tag>
+// and its write for its ncols columns: output rows when plse == nullptr,
+// else the partial state (o~/l, m + log2 l) at (plse, po) -- the empty state
+// (o 0, lse -inf) for a verify column none of whose tokens lie in the
+// pieces.  Called by every thread of the workgroup; a thread takes 4
+// consecutive d of one column.  The pieces are listed by position (absent
+// slots repeat the last piece with weight 0) so that all of a thread's LDS
+// reads are issued together.
+template <typename Tag, bool kCols>
 __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLds& e,
-                                               unsigned mask, int b, int kvh, bool bad,
+                                               unsigned mask, int b, int kvh, int ncols, bool bad,
                                                float* plse, float* po) {
     constexpr int NP = 2 * kNW;
-    const int G = a.group;
     int idx[NP];
     bool on[NP];
     unsigned mm = mask;
@@ -659,7 +673,7 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
         last = idx[k];
         mm &= mm - 1;
     }
-    for (int it = threadIdx.x; it < G * 32; it += blockDim.x) {
+    for (int it = threadIdx.x; it < ncols * 32; it += blockDim.x) {
         const int g = it >> 5;
         const int d = (it & 31) * 4;
         float mv[NP], lv[NP];
@@ -681,7 +695,7 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
             den += w * lv[k];
             num += w * ov[k];
         }
-        f32x4 o = num / den;
+        f32x4 o = den == 0.0f ? (f32x4){0.f, 0.f, 0.f, 0.f} : num / den;
         if (bad) o = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                              __builtin_nanf("")};
         if (plse == nullptr) {
@@ -689,7 +703,7 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
             const uint32_t lo = pack2(Tag(), os[0], os[1]);
             const uint32_t hi = pack2(Tag(), os[2], os[3]);
             char* dst = reinterpret_cast<char*>(a.out) +
-                        (((uint64_t)b * a.num_heads + kvh * G + g) * 128 + d) * 2;
+                        (column_row<kCols>(a, b, kvh, g) * 128 + d) * 2;
             *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
         } else {
             *reinterpret_cast<f32x4*>(po + g * 128 + d) = o;
@@ -700,6 +714,7 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
 
 template <typename Tag, int BS, typename Kv, int kRows>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
+    constexpr bool kCols = kRows == 1;
     __shared__ EdgeLds edge;
     __shared__ int pref[kMaxBalancedSeqs + 1];
     __shared__ int wsum[kNW];
@@ -732,6 +747,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         const int c0 = __builtin_amdgcn_readfirstlane((int)(off - (int64_t)kvh * nb));
         const int c1 = __builtin_amdgcn_readfirstlane((int)min((int64_t)nb, c0 + (we - x)));
         const int L = __builtin_amdgcn_readfirstlane(a.context_lens[b]);
+        const int ntok = row_tokens<kRows>(a, b);
 
         WaveState st;
         st.m_ref = -INFINITY;
@@ -739,12 +755,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         for (int j = 0; j < 8; ++j) st.acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
         st.acc_l = (f32x4){0.f, 0.f, 0.f, 0.f};
         int bad = 0;
-        attend_piece<Tag, BS, Kv, kRows>(a, b, kvh, L, c0, c1, st, bad);
+        attend_piece<Tag, BS, Kv, kRows>(a, b, kvh, L, ntok, c0, c1, st, bad);
 
         const bool starts_before = c0 > 0;    // the segment began before this range
         const bool ends_after = c1 < nb;      // it continues past this range
         if (!starts_before && !ends_after) {
-            write_rows<Tag>(a, b, kvh, st, bad != 0);
+            write_rows<Tag, kCols>(a, b, kvh, ntok * a.group, st, bad != 0);
         } else {
             const int p = 2 * wave + (starts_before ? 0 : 1);
             if (q == 0) {
@@ -790,12 +806,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         const int64_t xs = (int64_t)H_kv * pref[b] + (int64_t)kvh * nb;
         const bool head = xs < xb;            // continues from the previous range
         const bool tail = xs + nb > xe;       // continues into the next range
+        const int ncols = row_tokens<kRows>(a, b) * a.group;
         if (!head && !tail) {
-            finalize_edges<Tag>(a, edge, mask, b, kvh, bad != 0, nullptr, nullptr);
+            finalize_edges<Tag, kCols>(a, edge, mask, b, kvh, ncols, bad != 0, nullptr, nullptr);
         } else {
             const uint64_t slot = (uint64_t)w * 2 + (head ? 0 : 1);
-            finalize_edges<Tag>(a, edge, mask, b, kvh, bad != 0, a.ws_lse + slot * kMaxGroup,
-                                a.ws_out + slot * kMaxGroup * 128);
+            finalize_edges<Tag, kCols>(a, edge, mask, b, kvh, ncols, bad != 0,
+                                       a.ws_lse + slot * kMaxGroup,
+                                       a.ws_out + slot * kMaxGroup * 128);
             if (!head) meta.x = k, meta.y = range_owner(xs + nb - 1, T, a.num_wg);
         }
         p = p1;

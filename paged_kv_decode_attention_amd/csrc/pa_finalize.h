@@ -10,32 +10,54 @@
 
 namespace pa {
 
-// Rows of sequence b, heads head0 .. head0+nheads-1, set to one value
+// Query rows carried by decode row b: 1 without a row map; in verify mode
+// the count the row map gives (0: the rows are carried by an earlier decode
+// row).  kRows = 1: the launch carries a row map; 0: it does not; -1: test
+// a.row_tokens at run time.
+// b is the same in every lane of the wavefront (a scalar load).
+template <int kRows = -1>
+__device__ __forceinline__ int row_tokens(const DecodeArgs& a, int b) {
+    typedef __attribute__((address_space(4))) const int32_t ConstRow;
+    if (kRows == 0 || (kRows < 0 && a.row_tokens == nullptr)) return 1;
+    return __builtin_amdgcn_readfirstlane(((const ConstRow*)a.row_tokens)[b]);
+}
+
+// [S, H] row index (of out, query and the fixed schedule's partition states)
+// of column n of decode row b, KV head kvh: query row b + n / G, head
+// kvh G + n % G.  Without a row map n < G, so this is b H + kvh G + n.
+__device__ __forceinline__ uint64_t col_row(const DecodeArgs& a, int b, int kvh, int n) {
+    const int t = n / a.group;
+    return (uint64_t)(b + t) * a.num_heads + kvh * a.group + (n - t * a.group);
+}
+
+// Columns n0 .. n0 + ncols - 1 of decode row b, KV head kvh, set to one value
 // (0 for an empty history, NaN for an invalid context length).
 template <typename Tag>
-__device__ __forceinline__ void fill_rows(const DecodeArgs& a, int b, int head0,
-                                          int nheads, float v) {
+__device__ __forceinline__ void fill_cols(const DecodeArgs& a, int b, int kvh, int n0,
+                                          int ncols, float v) {
     const int D = a.head_dim;
-    for (int idx = threadIdx.x; idx < nheads * D; idx += blockDim.x) {
-        const int g = idx / D;
-        store_elem(Tag(), a.out, ((uint64_t)b * a.num_heads + head0 + g) * D + (idx - g * D), v);
+    for (int idx = threadIdx.x; idx < ncols * D; idx += blockDim.x) {
+        const int n = idx / D;
+        store_elem(Tag(), a.out, col_row(a, b, kvh, n0 + n) * D + (idx - n * D), v);
     }
 }
 
 // sm_m/sm_l: [nw][16] reference max (log2 units) and denominator per
-// wavefront and head slot; sm_o: un-normalised accumulators, element
+// wavefront and column slot; sm_o: un-normalised accumulators, element
 // (w, g, d) at w * wave_stride + g * head_stride + d.  Merges the nw states
-// of each head g < nheads (the update of [MiniPaged-Qwen] §5.2 applied to
-// whole states) and writes, for heads head0 + g of sequence b:
-//   plse == nullptr : out row = o~ / l (rounded once to the output type);
-//   otherwise       : po[g * po_hs + d] = o~ / l, plse[g * plse_hs] = m + log2 l.
+// of each column n0 + g, g < ncols (the update of [MiniPaged-Qwen] §5.2
+// applied to whole states) and writes, for decode row b, KV head kvh:
+//   part < 0 : the output row, o~ / l rounded once to the output type;
+//   else     : partition state `part` of the fixed schedule: o~ / l and
+//              m + log2 l at row col_row * num_parts + part.
+// A column with no token in the partition (a verify column whose causal end
+// lies before it) leaves the empty state: lse -inf, o 0.
 template <typename Tag>
 __device__ __forceinline__ void finalize_state(
     const DecodeArgs& a, const float* sm_m, const float* sm_l, const float* sm_o, int nw,
-    int wave_stride, int head_stride, int head0, int nheads, int b, bool bad, float* plse,
-    int plse_hs, float* po, int po_hs) {
+    int wave_stride, int head_stride, int b, int kvh, int n0, int ncols, bool bad, int part) {
     const int D = a.head_dim;
-    for (int idx = threadIdx.x; idx < nheads * D; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < ncols * D; idx += blockDim.x) {
         const int g = idx / D;
         const int d = idx - g * D;
         float M = -INFINITY;
@@ -46,50 +68,39 @@ __device__ __forceinline__ void finalize_state(
             den += e * sm_l[w * 16 + g];
             num += e * sm_o[w * wave_stride + g * head_stride + d];
         }
-        float o = num / den;
+        float o = den == 0.0f ? 0.0f : num / den;
         if (bad) o = __builtin_nanf("");
-        if (plse == nullptr) {
-            store_elem(Tag(), a.out, ((uint64_t)b * a.num_heads + head0 + g) * D + d,
-                       a.out_scale * o);
+        const uint64_t r = col_row(a, b, kvh, n0 + g);
+        if (part < 0) {
+            store_elem(Tag(), a.out, r * D + d, a.out_scale * o);
         } else {
-            po[(uint64_t)g * po_hs + d] = o;
-            if (d == 0) plse[(uint64_t)g * plse_hs] = bad ? __builtin_nanf("") : M + __log2f(den);
+            const uint64_t row = r * a.num_parts + part;
+            a.ws_out[row * D + d] = o;
+            if (d == 0) a.ws_lse[row] = bad ? __builtin_nanf("") : M + __log2f(den);
         }
     }
 }
 
-// Partial states of the fixed schedule: partition p of head head0 + g.
-struct FixedPieces {
-    const float* lse;    // a.ws_lse
-    const float* o;      // a.ws_out
-    uint64_t row0;       // (b * H + head0) * num_parts
-    int num_parts;
-    int D;
-    __device__ __forceinline__ float lse_at(int p, int g) const {
-        return lse[row0 + (uint64_t)g * num_parts + p];
-    }
-    __device__ __forceinline__ const f32x4* o_at(int p, int g) const {
-        return reinterpret_cast<const f32x4*>(o + (row0 + (uint64_t)g * num_parts + p) * D);
-    }
-};
-
-// Log-sum-exp merge of npieces partial states of heads head0 .. head0 +
-// nheads - 1 of sequence b ("reduce locally, then merge globally",
+// Log-sum-exp merge of the npieces partition states of columns 0 .. ncols-1
+// of decode row b, KV head kvh ("reduce locally, then merge globally",
 // [MiniPaged-Qwen] §10.2 (2)):
 //   o = sum_p 2^(lse_p - M) o_p / sum_p 2^(lse_p - M),  M = max_p lse_p,
 // the online update of §5.2 applied to whole pieces: batches of kBatch
 // pieces are loaded together (one memory round trip per batch) and folded
 // into a running (max, denominator, numerator).  Always in piece (token)
 // order, so the result is deterministic.
-template <typename Tag, typename Pieces>
-__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const Pieces& pc, int b,
-                                             int head0, int nheads, int npieces) {
+template <typename Tag>
+__device__ __forceinline__ void merge_pieces(const DecodeArgs& a, int b, int kvh, int ncols,
+                                             int npieces) {
     constexpr int kBatch = 8;
     const int D = a.head_dim;
     const int D4 = D / 4;
-    for (int it = threadIdx.x; it < nheads * D4; it += blockDim.x) {
+    for (int it = threadIdx.x; it < ncols * D4; it += blockDim.x) {
         const int g = it / D4;
         const int d4 = it - g * D4;
+        const uint64_t r = col_row(a, b, kvh, g);
+        const float* lse_r = a.ws_lse + r * a.num_parts;
+        const f32x4* o_r = reinterpret_cast<const f32x4*>(a.ws_out + r * a.num_parts * D) + d4;
         float M = -INFINITY, den = 0.0f;
         f32x4 num = {0.f, 0.f, 0.f, 0.f};
         int has_nan = 0;
@@ -99,8 +110,8 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const Pieces& 
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {
                 const int p = min(p0 + k, npieces - 1);
-                o[k] = pc.o_at(p, g)[d4];
-                lse[k] = p0 + k < npieces ? pc.lse_at(p, g) : -INFINITY;
+                o[k] = o_r[(uint64_t)p * D4];
+                lse[k] = p0 + k < npieces ? lse_r[p] : -INFINITY;
             }
             float mb = M;
 #pragma unroll
@@ -119,7 +130,7 @@ __device__ __forceinline__ void merge_pieces(const DecodeArgs& a, const Pieces& 
             }
             M = mb;
         }
-        const uint64_t out0 = ((uint64_t)b * a.num_heads + head0 + g) * D + 4 * d4;
+        const uint64_t out0 = r * D + 4 * d4;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             store_elem(Tag(), a.out, out0 + e,

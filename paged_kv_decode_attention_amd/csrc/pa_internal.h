@@ -20,6 +20,13 @@ struct DecodeArgs {
     const int32_t* block_tables;   // [S, W]
     const int32_t* context_lens;   // [S]
     const int32_t* table_rows;     // [S]: block-table row of decode row b, or null (row b)
+    // [S]: query rows carried by decode row b, or null (1 each).  Decode row
+    // b with n_b > 0 query rows serves rows b .. b + n_b - 1 of one sequence
+    // as n_b * group "columns": column n is query row b + n / group, head
+    // kvh * group + n % group, and attends the context_lens[b] - (n_b - 1 -
+    // n / group) oldest positions.  n_b = 0: the rows are carried by an
+    // earlier decode row (its context_lens entry is 0 and nothing is written).
+    const int32_t* row_tokens;
     const void* new_key;       // [S, H_kv, D] appended token per sequence, or null
     const void* new_value;     // [S, H_kv, D]
     float* ws_lse;             // [S, H, num_parts] float32 (log2 units)
@@ -93,12 +100,15 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                                         int num_blocks, pa_dtype src_dtype, float k_inv_scale,
                                         float v_inv_scale, hipStream_t s);
 
-// Verify mode: for every query row r < total_q, the block-table row of its
-// sequence and its effective history length (-1 for an invalid row).
+// Verify mode: for every query row r < total_q, the decode row that starts
+// at r -- the block-table row of its sequence, the effective history length
+// of its last query row (-1 for an invalid row) and the number of query rows
+// it carries (up to tokens_per_row consecutive rows of one sequence, 0 for a
+// row carried by an earlier one; an invalid row carries itself alone).
 hipError_t launch_verify_rows(const int32_t* query_start, const int32_t* context_lens,
                               int num_seqs, int total_queries, int max_query_len,
-                              int max_context_len, int32_t* table_rows, int32_t* lens,
-                              hipStream_t s);
+                              int max_context_len, int tokens_per_row, int32_t* table_rows,
+                              int32_t* lens, int32_t* row_tokens, hipStream_t s);
 
 // Copy whole blocks of both caches: pair i = (src, dst) in device memory.
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs,

@@ -1,7 +1,8 @@
 // Log-sum-exp merge of partial decode states: the "merge globally" half of
 // the partitioned reduction ([MiniPaged-Qwen] §10.2 (2)).  The float32
-// states (lse, o) the decode workgroups left for the G query heads of a
-// (sequence, KV head) are combined in token order.
+// states (lse, o) the decode workgroups left for the columns of a (decode
+// row, KV head) -- its G query heads, or in verify mode the (query row, head)
+// pairs it carries -- are combined in token order.
 #include "pa_finalize.h"
 
 namespace pa {
@@ -18,11 +19,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
     const int L = a.context_lens[b];
     if (L <= a.part_len || L > a.max_context_len) return;
     const int nparts = (L + a.part_len - 1) / a.part_len;
-    const int head0 = kvh * a.group;
-    const FixedPieces pc{a.ws_lse, a.ws_out,
-                         ((uint64_t)b * a.num_heads + head0) * a.num_parts, a.num_parts,
-                         a.head_dim};
-    merge_pieces<Tag>(a, pc, b, head0, a.group, nparts);
+    merge_pieces<Tag>(a, b, kvh, row_tokens(a, b) * a.group, nparts);
 }
 
 // Balanced schedule.  Workgroup w < num_wg merges the segment whose first
@@ -31,9 +28,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
 // token order.  The record and the first kSpec candidate pieces are loaded
 // together (one memory round trip for the common case of a segment spread
 // over at most kSpec ranges).  Workgroup num_wg + b writes the rows of
-// sequence b when the decode kernel has none to write: zeros for an empty
+// decode row b when the decode kernel has none to write: zeros for an empty
 // history, NaN for an invalid context length.  A thread takes 4
-// consecutive d of one head (head_dim 128, at most kMaxGroup heads).
+// consecutive d of one column (head_dim 128, at most kMaxGroup columns).
 constexpr int kMergeBalancedThreads = kMaxGroup * 32;
 
 template <typename Tag>
@@ -42,12 +39,17 @@ __global__ __launch_bounds__(kMergeBalancedThreads) void merge_balanced(DecodeAr
     constexpr int D = 128;
     const int w = blockIdx.x;
     if (w >= a.num_wg) {
+        // the query rows decode row b carries (b .. b + n_b - 1), every
+        // head: contiguous in out
         const int b = w - a.num_wg;
         const int L = a.context_lens[b];
-        if (L < 0 || L > a.max_context_len)
-            fill_rows<Tag>(a, b, 0, a.num_heads, __builtin_nanf(""));
-        else if (L == 0)
-            fill_rows<Tag>(a, b, 0, a.num_heads, 0.0f);
+        const bool invalid = L < 0 || L > a.max_context_len;
+        if (!invalid && L != 0) return;
+        const float v = invalid ? __builtin_nanf("") : 0.0f;
+        const int64_t count = (int64_t)row_tokens(a, b) * a.num_heads * a.head_dim;
+        const uint64_t base = (uint64_t)b * a.num_heads * a.head_dim;
+        for (int64_t i = threadIdx.x; i < count; i += blockDim.x)
+            store_elem(Tag(), a.out, base + i, v);
         return;
     }
     const int g = threadIdx.x >> 5;
@@ -66,12 +68,11 @@ __global__ __launch_bounds__(kMergeBalancedThreads) void merge_balanced(DecodeAr
     const int key = meta.x;
     const int w1 = meta.y;
     // (a record outside these bounds cannot come from the decode kernel)
-    if (key < 0 || key >= a.num_seqs * a.num_kv_heads || w1 <= w || w1 >= nwg ||
-        g >= a.group)
-        return;
+    if (key < 0 || key >= a.num_seqs * a.num_kv_heads || w1 <= w || w1 >= nwg) return;
     const int64_t T = (int64_t)(uint32_t)meta.z | ((int64_t)meta.w << 32);
     const int b = key / a.num_kv_heads;
     const int kvh = key - b * a.num_kv_heads;
+    if (g >= row_tokens(a, b) * a.group) return;     // g: column of the decode row
     // every range is non-empty when T >= num_wg: pieces are then [w][1],
     // [w+1][0], ..., [w1][0]
     const int npieces = w1 - w + 1;
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kMergeBalancedThreads) void merge_balanced(DecodeAr
                  *reinterpret_cast<const f32x4*>(a.ws_out + slot_row(slot) * D + d));
         }
     }
-    const uint64_t out0 = ((uint64_t)b * a.num_heads + kvh * a.group + g) * D + d;
+    const uint64_t out0 = col_row(a, b, kvh, g) * D + d;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
         store_elem(Tag(), a.out, out0 + e,

@@ -63,6 +63,48 @@ def test_verify_parity(case, partition_size):
     compare(out[2:], ref[2:], dtype, what="verify %s P=%d" % (case, partition_size))
 
 
+# Matrix-core verify groups up to 16 // G query rows of a sequence into one
+# pass (their (row, head) pairs are the MFMA's 16 columns, each with its own
+# causal end).  Lengths put a column's end on a 32-token chunk boundary
+# (L_b - q_b + i + 1 = 32 k), so that some chunk (a piece of its own when the
+# work list is short, or a partition at P = 32) holds no token of that column
+# and leaves an empty state for the merge.
+# The sequence of length 3 has q = 5 > L: its rows are NaN.
+COL_LENS = (33, 34, 65, 66, 97, 40, 2, 513, 8, 3, 129)
+COL_QLENS = (2, 3, 2, 3, 2, 8, 2, 5, 8, 5, 17)
+COL_CASES = [("bf16", 2, 7, 16), ("f16", 2, 4, 32), ("bf16", 4, 1, 16), ("bf16", 1, 16, 64),
+             ("bf16", 2, 3, 16), ("f16", 1, 8, 16), ("bf16", 2, 5, 32)]
+
+
+@pytest.mark.parametrize("partition_size", [0, 64])
+@pytest.mark.parametrize("case", COL_CASES, ids=lambda c: "%s-hkv%d-g%d-bs%d" % c)
+def test_verify_columns_parity(case, partition_size):
+    dtype, H_kv, G, BS = case
+    cfg = small_config(dtype, H_kv, G, 128, BS, COL_LENS)
+    inp, q, qs = verify_inputs(cfg, list(COL_QLENS), seed=11)
+    out = run_verify(inp, q, qs, 17, ops.KERNEL_MFMA, partition_size)
+    ref = oracle_verify(inp, q, qs)
+    bad = np.isnan(ref).any(axis=(1, 2))          # the rows of the L < q sequence
+    assert bad.sum() == 5
+    assert torch.isnan(out[torch.from_numpy(bad)].float()).all()
+    compare(out[torch.from_numpy(~bad)], ref[~bad], dtype,
+            what="verify columns %s P=%d" % (case, partition_size))
+
+
+@pytest.mark.parametrize("G,BS", [(7, 16), (1, 16)])
+def test_verify_columns_fixed_partition_boundary(G, BS):
+    """P = 32: every 32-token partition is its own state; columns whose causal
+    end is a multiple of 32 have an empty trailing partition."""
+    cfg = small_config("bf16", 2, G, 128, BS, COL_LENS)
+    inp, q, qs = verify_inputs(cfg, list(COL_QLENS), seed=12)
+    out = run_verify(inp, q, qs, 17, ops.KERNEL_MFMA, 32)
+    ref = oracle_verify(inp, q, qs)
+    bad = np.isnan(ref).any(axis=(1, 2))
+    assert bad.sum() == 5
+    assert torch.isnan(out[torch.from_numpy(bad)].float()).all()
+    compare(out[torch.from_numpy(~bad)], ref[~bad], "bf16", what="verify columns P=32 G=%d" % G)
+
+
 def test_verify_single_query_equals_decode():
     cfg = small_config("bf16", 2, 7, 128, 16, RAGGED)
     inp, _, _ = verify_inputs(cfg, [1] * len(RAGGED))
