@@ -328,7 +328,7 @@ def shape_sweep(args, dev):
                 us.append(e0.elapsed_time(e1) * 1e3 / K)
             t = float(np.mean(us)) * 1e-6
             alg = int(lens.sum()) * H_kv * D * 2 * 2
-            mfma = D == 128 and BS in (16, 32, 64) and G <= 16
+            mfma = ops.decode_kernel(D, BS, G, q.dtype) == ops.KERNEL_MFMA
             row = {"head_dim": D, "block_size": BS,
                    "kernel": "matrix-core, balanced" if mfma else "vector-ALU, partitions",
                    "decode_us": t * 1e6, "alg_bytes": alg, "achieved_gbps": alg / t / 1e9,

@@ -130,9 +130,12 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  *   workspace      device buffer of at least pa_decode_workspace_size() bytes,
  *                  256-byte aligned (may be NULL when that size is 0)
  *
- * Supported: dtype f32, f16, bf16; head_dim 64 or 128; block_size 16 or 32;
- * any gqa_group_size >= 1.  Pointers to query/out/caches must be 16-byte
- * aligned.
+ * Supported: dtype f32, f16, bf16; head_dim 64, 128 or 256; block_size 8,
+ * 16, 32 or 64; any gqa_group_size >= 1 (other head_dim / block_size values
+ * return PA_ERR_UNSUPPORTED).  bf16/f16 with head_dim 64 or 128, block_size
+ * 16, 32 or 64 and gqa_group_size <= 16 run on the matrix-core kernel, the
+ * rest on the vector-ALU kernel.  Pointers to query/out/caches must be
+ * 16-byte aligned.
  *
  * Device-data preconditions and what happens when they are broken:
  *   0 <= L_b <= max_context_len      otherwise out[b] is all NaN
@@ -278,9 +281,9 @@ int pa_paged_attention_verify(void* out, const void* query, const void* key_cach
  * pa_paged_attention_decode_fp8 -- pa_paged_attention_decode over E4M3
  *   caches: the attention of each query over the dequantised history.  Same
  *   arguments, plus k_scale and v_scale (finite, > 0); dtype is that of query
- *   and out (bf16 or f16).  Supported: head_dim 128, block_size 16 or 32,
- *   gqa_group_size <= 16 (the matrix-core kernel); other shapes return
- *   PA_ERR_UNSUPPORTED.  The workspace is sized by pa_decode_workspace_size
+ *   and out (bf16 or f16).  Supported: head_dim 64 or 128, block_size 16,
+ *   32 or 64, gqa_group_size <= 16 (the matrix-core kernel); other shapes
+ *   return PA_ERR_UNSUPPORTED.  The workspace is sized by pa_decode_workspace_size
  *   with the query dtype.
  * pa_decode_append_fp8 -- pa_decode_append over E4M3 caches: each newest
  *   token's key/value (query dtype) is quantised as it is stored.
@@ -437,6 +440,15 @@ int pa_debug_gather_kv(void* k_out, void* v_out,
  * calls running on other threads.
  */
 int pa_debug_select_kernel(int kind);
+
+/*
+ * pa_decode_kernel -- the decode kernel family a decode call of this shape
+ * runs under the current pa_debug_select_kernel setting: 1 = vector-ALU
+ * kernel, 2 = matrix-core kernel.  PA_ERR_UNSUPPORTED when no kernel serves
+ * the shape (or the matrix-core kernel is forced and does not),
+ * PA_ERR_INVALID_ARG for an unknown dtype or gqa_group_size < 1.  Host only.
+ */
+int pa_decode_kernel(int head_dim, int block_size, int gqa_group_size, pa_dtype dtype);
 
 /*
  * Measurement helpers (not part of the decode path).

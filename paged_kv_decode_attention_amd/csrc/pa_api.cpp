@@ -106,20 +106,25 @@ Layout balanced_layout(int head_dim) {
     return l;
 }
 
-// Workgroups of the balanced schedule: two per compute unit of the current
-// device (the matrix-core kernel's occupancy), so all are resident at once.
-int balanced_workgroups() {
+// Workgroups of the balanced schedule: as many per compute unit of the
+// current device as the matrix-core kernel keeps resident at this head_dim,
+// so all are resident at once.
+int balanced_workgroups(int head_dim) {
     static int cached[64] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-    if (cached[dev] == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-        cached[dev] = cus * 2 > pa::kMaxBalancedWg ? pa::kMaxBalancedWg : cus * 2;
+    int cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        if (cached[dev] == 0) {
+            int n = 0;
+            if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                    hipSuccess || n <= 0)
+                n = 256;
+            cached[dev] = n;
+        }
+        cus = cached[dev];
     }
-    return cached[dev];
+    const int wgs = cus * pa::mfma_workgroups_per_cu(head_dim);
+    return wgs > pa::kMaxBalancedWg ? pa::kMaxBalancedWg : wgs;
 }
 
 // The balanced schedule serves the matrix-core kernel when no partition
@@ -159,6 +164,20 @@ int pa_debug_select_kernel(int kind) {
     if (kind != pa::kAuto && kind != pa::kGeneric && kind != pa::kMfma)
         return fail(PA_ERR_INVALID_ARG, "kernel kind %d not in {0,1,2}", kind);
     return g_kernel_kind.exchange(kind);
+}
+
+int pa_decode_kernel(int head_dim, int block_size, int gqa_group_size, pa_dtype dtype) {
+    if (elem_bytes(dtype) == 0 || gqa_group_size < 1)
+        return fail(PA_ERR_INVALID_ARG, "unknown dtype %d or gqa_group_size %d < 1", (int)dtype,
+                    gqa_group_size);
+    if (!supported_shape(head_dim, block_size))
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d with block_size %d not built", head_dim,
+                    block_size);
+    const int kind = g_kernel_kind.load();
+    const bool mfma_ok = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size);
+    if (kind == pa::kMfma && !mfma_ok)
+        return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
+    return mfma_ok && kind != pa::kGeneric ? pa::kMfma : pa::kGeneric;
 }
 
 int pa_decode_partition_size(int num_seqs, int num_kv_heads, int gqa_group_size, int head_dim,
@@ -249,7 +268,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
         return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
     if (e4m3 && !use_mfma)
         return fail(PA_ERR_UNSUPPORTED, "FP8 caches are served by the matrix-core kernel only "
-                    "(bf16/f16 queries, head_dim 128, block_size 16/32, group <= 16)");
+                    "(bf16/f16 queries, head_dim 64/128, block_size 16/32/64, group <= 16)");
     const bool balanced = use_balanced(use_mfma, partition_size, num_seqs, max_context_len);
 
     const int P = partition_size ? partition_size
@@ -294,7 +313,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     a.part_len = P;
     a.num_parts = balanced ? 1 : lay.num_parts;
     a.schedule = balanced ? pa::kBalanced : pa::kFixed;
-    a.num_wg = balanced ? balanced_workgroups() : 0;
+    a.num_wg = balanced ? balanced_workgroups(head_dim) : 0;
     // scale * log2(e), and the key scale of an FP8 cache folded into it
     a.scale_log2 = (float)((double)scale * 1.4426950408889634 * (e4m3 ? (double)k_scale : 1.0));
     a.kv_format = e4m3 ? pa::kKvE4M3 : pa::kKvSame;

@@ -1,16 +1,18 @@
-// Decode paged attention on the gfx950 matrix cores, bf16/fp16 caches,
-// head_dim 128, GQA groups of up to 16 query heads.
+// Decode paged attention on the gfx950 matrix cores, bf16/fp16 queries,
+// 16-bit or FP8 E4M3 caches, head_dim 64 or 128, GQA groups of up to 16
+// query heads.
 //
 // Work decomposition: one workgroup of 4 wavefronts per (sequence b, KV head,
-// context partition); the partition's tokens are split into 32-token chunks
-// dealt round-robin to the wavefronts.  Every query head of the GQA group is
-// served from the same K/V bytes, so each KV byte is fetched once.
+// context partition), or per equal-work range of the whole batch (balanced
+// schedule, below); tokens are taken in 32-token chunks.  Every query head of
+// the GQA group is served from the same K/V bytes, so each KV byte is fetched
+// once.
 //
 // Per chunk a wavefront computes (the per-block online softmax of
 // [MiniPaged-Qwen] §5.2, one 32-token chunk at a time):
-//   S^T = K Q^T      (tokens x heads)   4 MFMA 16x16x32 per 16-token tile
+//   S^T = K Q^T      (tokens x heads)   D/32 MFMA 16x16x32 per 16-token tile
 //   m'  = max(m, max_t s),  p = 2^(s - m'),  l' = l 2^(m-m') + sum p
-//   O^T = 2^(m-m') O^T + V^T P^T   (d x heads)  8 MFMA 16x16x32
+//   O^T = 2^(m-m') O^T + V^T P^T   (d x heads)  D/16 MFMA 16x16x32
 // with scores in log2 units (scale * log2 e folded in), so exp is a single
 // v_exp_f32.  The reference max m is only moved (and O, l rescaled) when a
 // chunk's max exceeds it by more than 2^8; in between, weights 2^(s - m) are
@@ -20,18 +22,19 @@
 // buffers).  Histories longer than one partition leave float32 partition
 // states that the merge kernel (pa_merge.hip) combines.
 //
-// Lane layout (lane = 16 q + n): in every MFMA the column index (lane % 16)
-// is the query head n of the group, so the running max / denominator of head
-// n and the rescale of its accumulators stay inside the lanes that own them.
+// Lane layout (lane = 16 q + n; VW = D / 16): in every MFMA the column index
+// (lane % 16) is the query head n of the group, so the running max /
+// denominator of head n and the rescale of its accumulators stay inside the
+// lanes that own them.
 //   K operand: lane holds K[token n][d = 32 kk + 8 q .. +8], a 16-byte load;
 //   Q operand: lane holds Q[head n][same d];
 //   S^T tile : lane holds s[token 4 q + i][head n], i = 0..3;
 //   P operand: lane holds p[head n][its own 8 tokens] -- no data movement;
-//   V operand: lane loads V[token][d = 8 n .. 8 n + 8] for its 8 tokens
-//              (four whole 256-byte rows per load instruction, fully
-//              coalesced) and transposes them in registers so that MFMA j
-//              consumes d = 8 m + j for row m = lane % 16;
-//   O^T acc  : lane holds O[head n][d = 32 q + 8 i + j] for MFMA j, reg i.
+//   V operand: lane loads V[token][d = VW n .. VW n + VW] for its 8 tokens
+//              (whole rows per load instruction, fully coalesced) and
+//              transposes them in registers so that MFMA j consumes
+//              d = VW m + j for row m = lane % 16;
+//   O^T acc  : lane holds O[head n][d = VW (4 q + i) + j] for MFMA j, reg i.
 // The address of every row is kv_row(): block_tables[b, t / BS] gives the
 // physical block, t % BS the slot ([MiniPaged-Qwen] §6.2).
 #include <type_traits>
@@ -58,10 +61,24 @@ constexpr uint32_t kOnePair<BF16>() { return 0x3f803f80u; }
 template <>
 constexpr uint32_t kOnePair<F16>() { return 0x3c003c00u; }
 
+// Tile geometry of one head dimension.
+template <int D>
+struct Dim {
+    static_assert(D == 64 || D == 128, "matrix-core kernel: head_dim 64 or 128");
+    static constexpr int KD = D / 32;   // K / Q MFMA steps per 16-token tile
+    static constexpr int VW = D / 16;   // d values a lane holds per V row = PV MFMAs
+    static constexpr int RB = D * 2;    // bytes per 16-bit token row
+    static constexpr int OS = D + 4;    // padded LDS row of one column (floats)
+    // 32-bit dwords of this lane's slice of a V row: 16-bit / E4M3 storage
+    using VRow = typename std::conditional<D == 64, u32x2, u32x4>::type;
+    using VRow8 = typename std::conditional<D == 64, uint32_t, u32x2>::type;
+};
+
 // One 32-token chunk's K and V operands, as loaded (two 16-token tiles).
+template <int D>
 struct ChunkRegs {
-    u32x4 k0[4], k1[4];   // K tile 0 / tile 1: row n, d = 32 kk + 8 q .. +8
-    u32x4 v[8];           // V rows of this lane's 8 tokens, d = 8 n .. +8
+    u32x4 k0[Dim<D>::KD], k1[Dim<D>::KD];   // K tile 0 / 1: row n, d = 32 kk + 8 q .. +8
+    typename Dim<D>::VRow v[8];              // V rows of this lane's 8 tokens, d = VW n ..
 };
 
 // Physical blocks of chunk c's two 16-token tiles, read from the sequence's
@@ -93,54 +110,65 @@ __device__ __forceinline__ int2 chunk_blocks(const ConstI32* row, int c, int L, 
     return make_int2(pb0, pb1);
 }
 
-// Buffer descriptor of one 16-token tile (4 KB of 16-bit values, 2 KB of
-// 8-bit codes): base address, size.  A size of 0 makes every load from it
-// return zero without touching memory.
-template <int kTileBytes = 16 * 128 * 2>
+// Buffer descriptor of one 16-token tile (kTileBytes: 16 rows of K or V):
+// base address, size.  A size of 0 makes every load from it return zero
+// without touching memory.
+template <int kTileBytes>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, bool live) {
     constexpr int kRawBufferFlags = 0x00020000;   // 32-bit data format: raw loads return data
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, live ? kTileBytes : 0,
                                              kRawBufferFlags);
 }
 
-// Issue the 16 loads of one chunk: always 16, so the in-order load counter
-// the compiler waits on is the same on every path and the next chunk's loads
-// stay in flight while this one is computed.  KV is streamed once: loads are
-// nontemporal.  A tile that is not live (past the end of the history, or a
-// prefetch past the wave's last chunk) is read through an empty descriptor:
-// the loads return zeros and move no bytes.
+// Issue the loads of one chunk: always the same number, so the in-order load
+// counter the compiler waits on is the same on every path and the next
+// chunk's loads stay in flight while this one is computed.  KV is streamed
+// once: loads are nontemporal.  A tile that is not live (past the end of the
+// history, or a prefetch past the wave's last chunk) is read through an
+// empty descriptor: the loads return zeros and move no bytes.
 constexpr int kNonTemporal = 2;   // buffer cache-policy bit: nt
 
-template <int BS>
-__device__ __forceinline__ void load_chunk(ChunkRegs& r, const char* kbase, const char* vbase,
+// V row slices: 8 bytes (head_dim 64) or 16 bytes (head_dim 128) of 16-bit
+// values; 4 or 8 bytes of E4M3 codes.
+__device__ __forceinline__ void load_row(u32x4& x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ void load_row(u32x2& x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNonTemporal);
+}
+__device__ __forceinline__ void load_row(uint32_t& x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
+}
+
+template <int BS, int D>
+__device__ __forceinline__ void load_chunk(ChunkRegs<D>& r, const char* kbase, const char* vbase,
                                            int2 pb, int r0, bool live0, bool live1, int kvh,
                                            int num_kv_heads, uint32_t koff, uint32_t voff) {
-    constexpr int RB = 128 * 2;   // bytes per token row
+    constexpr int RB = Dim<D>::RB;   // bytes per token row
+    constexpr int KD = Dim<D>::KD;
     const uint64_t row0 = kv_row(pb.x, kvh, r0, num_kv_heads, BS) * RB;
     const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : r0 + 16, num_kv_heads, BS) * RB;
-    const __amdgpu_buffer_rsrc_t k0 = tile_rsrc(kbase + row0, live0);
-    const __amdgpu_buffer_rsrc_t k1 = tile_rsrc(kbase + row1, live1);
-    const __amdgpu_buffer_rsrc_t v0 = tile_rsrc(vbase + row0, live0);
-    const __amdgpu_buffer_rsrc_t v1 = tile_rsrc(vbase + row1, live1);
+    const __amdgpu_buffer_rsrc_t k0 = tile_rsrc<16 * RB>(kbase + row0, live0);
+    const __amdgpu_buffer_rsrc_t k1 = tile_rsrc<16 * RB>(kbase + row1, live1);
+    const __amdgpu_buffer_rsrc_t v0 = tile_rsrc<16 * RB>(vbase + row0, live0);
+    const __amdgpu_buffer_rsrc_t v1 = tile_rsrc<16 * RB>(vbase + row1, live1);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < KD; ++kk)
         r.k0[kk] = __builtin_amdgcn_raw_buffer_load_b128(k0, koff + kk * 64, 0, kNonTemporal);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < KD; ++kk)
         r.k1[kk] = __builtin_amdgcn_raw_buffer_load_b128(k1, koff + kk * 64, 0, kNonTemporal);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r.v[i] = __builtin_amdgcn_raw_buffer_load_b128(v0, voff + i * RB, 0, kNonTemporal);
+    for (int i = 0; i < 4; ++i) load_row(r.v[i], v0, voff + i * RB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r.v[4 + i] = __builtin_amdgcn_raw_buffer_load_b128(v1, voff + i * RB, 0, kNonTemporal);
+    for (int i = 0; i < 4; ++i) load_row(r.v[4 + i], v1, voff + i * RB);
 }
 
 // ---- KV storage formats -----------------------------------------------------
 // KvSame: the caches hold the query's 16-bit type.  KvE4M3: they hold OCP FP8
 // E4M3 codes (one scale per cache; the value of a code is decode(code) *
-// scale).  For E4M3 a lane takes a contiguous 32-element slice of d for K:
-// in MFMA step kk it supplies K[token n][d = 32 q + 8 kk .. +8] and Q uses
+// scale).  For E4M3 a lane takes a contiguous D/4-element slice of d for K:
+// in MFMA step kk it supplies K[token n][d = (D/4) q + 8 kk .. +8] and Q uses
 // the same d, so the contraction over d is the same sum in another order.
 struct KvSame {
     static constexpr bool kE4M3 = false;
@@ -150,18 +178,19 @@ struct KvE4M3 {
 };
 
 // One 32-token chunk of E4M3 codes, as loaded.
+template <int D>
 struct ChunkRegs8 {
-    u32x4 k0[2], k1[2];   // K tile 0 / 1: row n, d = 32 q .. 32 q + 32
-    u32x2 v[8];           // V rows of this lane's 8 tokens, d = 8 n .. +8
+    u32x4 k0[D / 64], k1[D / 64];            // K tile 0 / 1: row n, d = (D/4) q ..
+    typename Dim<D>::VRow8 v[8];             // V rows of this lane's 8 tokens, d = VW n ..
 };
 
-// The 12 loads of one E4M3 chunk (same rules as load_chunk: always issued,
-// dead tiles through an empty descriptor, nontemporal).
-template <int BS>
-__device__ __forceinline__ void load_chunk(ChunkRegs8& r, const char* kbase, const char* vbase,
+// The loads of one E4M3 chunk (same rules as load_chunk: always issued, dead
+// tiles through an empty descriptor, nontemporal).
+template <int BS, int D>
+__device__ __forceinline__ void load_chunk(ChunkRegs8<D>& r, const char* kbase, const char* vbase,
                                            int2 pb, int r0, bool live0, bool live1, int kvh,
                                            int num_kv_heads, uint32_t koff, uint32_t voff) {
-    constexpr int RB = 128;       // bytes per token row
+    constexpr int RB = D;         // bytes per token row
     constexpr int kTile = 16 * RB;
     const uint64_t row0 = kv_row(pb.x, kvh, r0, num_kv_heads, BS) * RB;
     const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : r0 + 16, num_kv_heads, BS) * RB;
@@ -170,17 +199,15 @@ __device__ __forceinline__ void load_chunk(ChunkRegs8& r, const char* kbase, con
     const __amdgpu_buffer_rsrc_t v0 = tile_rsrc<kTile>(vbase + row0, live0);
     const __amdgpu_buffer_rsrc_t v1 = tile_rsrc<kTile>(vbase + row1, live1);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < D / 64; ++h)
         r.k0[h] = __builtin_amdgcn_raw_buffer_load_b128(k0, koff + h * 16, 0, kNonTemporal);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < D / 64; ++h)
         r.k1[h] = __builtin_amdgcn_raw_buffer_load_b128(k1, koff + h * 16, 0, kNonTemporal);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r.v[i] = __builtin_amdgcn_raw_buffer_load_b64(v0, voff + i * RB, 0, kNonTemporal);
+    for (int i = 0; i < 4; ++i) load_row(r.v[i], v0, voff + i * RB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        r.v[4 + i] = __builtin_amdgcn_raw_buffer_load_b64(v1, voff + i * RB, 0, kNonTemporal);
+    for (int i = 0; i < 4; ++i) load_row(r.v[4 + i], v1, voff + i * RB);
 }
 
 // Two E4M3 codes (the low or the high half of w) -> two 16-bit values,
@@ -198,34 +225,44 @@ __device__ __forceinline__ u32x4 e4m3_eight(uint32_t w0, uint32_t w1) {
     return (u32x4){e4m3_pair<false>(Tag(), w0), e4m3_pair<true>(Tag(), w0),
                    e4m3_pair<false>(Tag(), w1), e4m3_pair<true>(Tag(), w1)};
 }
+// One V row slice of E4M3 codes -> the 16-bit slice.
+template <typename Tag>
+__device__ __forceinline__ u32x4 e4m3_row(u32x2 w) { return e4m3_eight<Tag>(w[0], w[1]); }
+template <typename Tag>
+__device__ __forceinline__ u32x2 e4m3_row(uint32_t w) {
+    return (u32x2){e4m3_pair<false>(Tag(), w), e4m3_pair<true>(Tag(), w)};
+}
 
 // E4M3 chunk -> the 16-bit operands compute_chunk takes (K step kk holds
-// d = 32 q + 8 kk .. +8; V rows as for the 16-bit format).
-template <typename Tag>
-__device__ __forceinline__ ChunkRegs expand(const ChunkRegs8& r8) {
-    ChunkRegs r;
+// d = (D/4) q + 8 kk .. +8: dwords 2 kk, 2 kk + 1 of the lane's slice; V
+// rows as for the 16-bit format).
+template <typename Tag, int D>
+__device__ __forceinline__ ChunkRegs<D> expand(const ChunkRegs8<D>& r8) {
+    ChunkRegs<D> r;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const u32x4 a = r8.k0[kk >> 1], b = r8.k1[kk >> 1];
-        r.k0[kk] = e4m3_eight<Tag>(a[2 * (kk & 1)], a[2 * (kk & 1) + 1]);
-        r.k1[kk] = e4m3_eight<Tag>(b[2 * (kk & 1)], b[2 * (kk & 1) + 1]);
+    for (int kk = 0; kk < Dim<D>::KD; ++kk) {
+        const int w = 2 * kk;
+        const u32x4 a = r8.k0[w >> 2], b = r8.k1[w >> 2];
+        r.k0[kk] = e4m3_eight<Tag>(a[w & 3], a[(w & 3) + 1]);
+        r.k1[kk] = e4m3_eight<Tag>(b[w & 3], b[(w & 3) + 1]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.v[i] = e4m3_eight<Tag>(r8.v[i][0], r8.v[i][1]);
+    for (int i = 0; i < 8; ++i) r.v[i] = e4m3_row<Tag>(r8.v[i]);
     return r;
 }
 
-template <typename Kv>
-using KvRegs = typename std::conditional<Kv::kE4M3, ChunkRegs8, ChunkRegs>::type;
+template <typename Kv, int D>
+using KvRegs = typename std::conditional<Kv::kE4M3, ChunkRegs8<D>, ChunkRegs<D>>::type;
 
 // Byte offsets of this lane's K and V data inside a tile.
-template <typename Kv>
+template <typename Kv, int D>
 __device__ __forceinline__ uint32_t lane_koff(int n, int q) {
-    return Kv::kE4M3 ? (uint32_t)(n * 128 + 32 * q) : (uint32_t)(n * 128 + 8 * q) * 2;
+    return Kv::kE4M3 ? (uint32_t)(n * D + (D / 4) * q) : (uint32_t)(n * D + 8 * q) * 2;
 }
-template <typename Kv>
+template <typename Kv, int D>
 __device__ __forceinline__ uint32_t lane_voff(int n, int q) {
-    return Kv::kE4M3 ? (uint32_t)(4 * q * 128 + 8 * n) : (uint32_t)(4 * q * 128 + 8 * n) * 2;
+    constexpr int VW = Dim<D>::VW;
+    return Kv::kE4M3 ? (uint32_t)(4 * q * D + VW * n) : (uint32_t)(4 * q * D + VW * n) * 2;
 }
 
 // [S, H] row of column n of decode row b (KV head kvh): query head kvh G + n
@@ -238,51 +275,53 @@ __device__ __forceinline__ uint64_t column_row(const DecodeArgs& a, int b, int k
 
 // Query operand: Q[column n][d] for the d each MFMA step contracts (see the
 // K layouts above); zero for padding columns n >= ncols.
-template <typename Kv, bool kCols>
+template <typename Kv, bool kCols, int D>
 __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, int n, int q,
                                            int ncols, u32x4* qop) {
-    constexpr int D = 128;
+    constexpr int KD = Dim<D>::KD;
     if (n < ncols) {
         const char* qp = reinterpret_cast<const char*>(a.query) +
                          column_row<kCols>(a, b, kvh, n) * D * 2;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            qop[kk] = load16(qp + (Kv::kE4M3 ? 32 * q + 8 * kk : 32 * kk + 8 * q) * 2);
+        for (int kk = 0; kk < KD; ++kk)
+            qop[kk] = load16(qp + (Kv::kE4M3 ? (D / 4) * q + 8 * kk : 32 * kk + 8 * q) * 2);
     } else {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) qop[kk] = (u32x4){0u, 0u, 0u, 0u};
+        for (int kk = 0; kk < KD; ++kk) qop[kk] = (u32x4){0u, 0u, 0u, 0u};
     }
 }
 
-// Append step: lanes 0-15 store the newest token's K row, lanes 16-31 its V
-// row, into slot pos of the sequence's tail block (row: its table row).  For
-// E4M3 each value is quantised: E4M3(fp32(x) * fp32(1 / scale)), nearest,
-// ties to even, saturating at +-448.
-template <typename Tag, typename Kv, int BS>
+// Append step: lanes 0 .. D/8-1 store the newest token's K row, the next D/8
+// lanes its V row (8 values each), into slot pos of the sequence's tail
+// block (row: its table row).  For E4M3 each value is quantised:
+// E4M3(fp32(x) * fp32(1 / scale)), nearest, ties to even, saturating at
+// +-448.
+template <typename Tag, typename Kv, int BS, int D>
 __device__ __forceinline__ void append_token(const DecodeArgs& a, const ConstI32* row, int b,
                                              int kvh, int pos, int lane) {
-    constexpr int D = 128;
+    constexpr int LP = D / 8;     // lanes per row
     const int pb = row[pos / BS];
-    if ((unsigned)pb >= (unsigned)a.num_blocks || lane >= 32) return;
-    const bool is_k = lane < 16;
+    if ((unsigned)pb >= (unsigned)a.num_blocks || lane >= 2 * LP) return;
+    const bool is_k = lane < LP;
+    const int c = lane % LP;
     const char* from = reinterpret_cast<const char*>(is_k ? a.new_key : a.new_value) +
-                       (((uint64_t)b * a.num_kv_heads + kvh) * D + (lane & 15) * 8) * 2;
+                       (((uint64_t)b * a.num_kv_heads + kvh) * D + c * 8) * 2;
     char* to = reinterpret_cast<char*>(const_cast<void*>(is_k ? a.key_cache : a.value_cache));
     const uint64_t r = kv_row(pb, kvh, pos % BS, a.num_kv_heads, BS);
     const u32x4 x = load16(from);
     if constexpr (Kv::kE4M3) {
         const float inv = is_k ? a.k_inv_scale : a.v_inv_scale;
-        uint32_t c[8];
+        uint32_t cd[8];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            c[2 * u] = e4m3_encode(unpack_lo(Tag(), x[u]) * inv);
-            c[2 * u + 1] = e4m3_encode(unpack_hi(Tag(), x[u]) * inv);
+            cd[2 * u] = e4m3_encode(unpack_lo(Tag(), x[u]) * inv);
+            cd[2 * u + 1] = e4m3_encode(unpack_hi(Tag(), x[u]) * inv);
         }
-        const u32x2 w = {c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
-                         c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24};
-        *reinterpret_cast<u32x2*>(to + r * D + (lane & 15) * 8) = w;
+        const u32x2 w = {cd[0] | cd[1] << 8 | cd[2] << 16 | cd[3] << 24,
+                         cd[4] | cd[5] << 8 | cd[6] << 16 | cd[7] << 24};
+        *reinterpret_cast<u32x2*>(to + r * D + c * 8) = w;
     } else {
-        *reinterpret_cast<u32x4*>(to + r * D * 2 + (lane & 15) * 16) = x;
+        *reinterpret_cast<u32x4*>(to + r * D * 2 + c * 16) = x;
     }
 }
 
@@ -290,11 +329,20 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, const ConstI32
 // m_ref (log2 units), the accumulators O^T and the denominator l (computed
 // on the matrix core as P times a ones operand, so it sums exactly the
 // rounded weights the PV product uses).
+template <int D>
 struct WaveState {
     float m_ref;
-    f32x4 acc[8];
+    f32x4 acc[Dim<D>::VW];
     f32x4 acc_l;
 };
+
+template <int D>
+__device__ __forceinline__ void init_state(WaveState<D>& st) {
+    st.m_ref = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < Dim<D>::VW; ++j) st.acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    st.acc_l = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
 
 // Scores may exceed the reference max by up to 2^kLazy before the
 // accumulators are rescaled (weights stay <= 2^8; float32 accumulators and
@@ -306,16 +354,18 @@ constexpr float kLazy = 8.0f;
 // lane's column) may lie before t_end; t_lo is the smallest column end of the
 // wavefront.  A column that has seen no token yet has m_ref = -inf: its
 // weights are then 2^(-inf) = 0 and its rescale factor 0.
-template <typename Tag, bool kCols>
-__device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const u32x4* qop,
+template <typename Tag, bool kCols, int D>
+__device__ __forceinline__ void compute_chunk(WaveState<D>& st, ChunkRegs<D>& r, const u32x4* qop,
                                               float sl2, int tc, int t_end, int t_col, int t_lo,
                                               int q) {
+    constexpr int KD = Dim<D>::KD;
+    constexpr int VW = Dim<D>::VW;
     // Scores: S^T[token][head] for the two 16-token tiles.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) s0 = mfma16x16x32(Tag(), r.k0[kk], qop[kk], s0);
+    for (int kk = 0; kk < KD; ++kk) s0 = mfma16x16x32(Tag(), r.k0[kk], qop[kk], s0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) s1 = mfma16x16x32(Tag(), r.k1[kk], qop[kk], s1);
+    for (int kk = 0; kk < KD; ++kk) s1 = mfma16x16x32(Tag(), r.k1[kk], qop[kk], s1);
     float s[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -329,12 +379,14 @@ __device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const
         // A verify column's tokens past its causal end only get score -inf
         // (their V rows hold data other columns use).
         const int t_s = kCols ? t_col : t_end;
+        using VRow = typename Dim<D>::VRow;
+        const VRow zero = {};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (tc + 4 * q + i >= t_s) s[i] = -INFINITY;
-            if (tc + 4 * q + i >= t_end) r.v[i] = (u32x4){0u, 0u, 0u, 0u};
+            if (tc + 4 * q + i >= t_end) r.v[i] = zero;
             if (tc + 16 + 4 * q + i >= t_s) s[4 + i] = -INFINITY;
-            if (tc + 16 + 4 * q + i >= t_end) r.v[4 + i] = (u32x4){0u, 0u, 0u, 0u};
+            if (tc + 16 + 4 * q + i >= t_end) r.v[4 + i] = zero;
         }
     }
     float cmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
@@ -347,7 +399,7 @@ __device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const
         const float m_new = fmaxf(st.m_ref, cmax);
         const float alpha = kCols ? rescale_weight(st.m_ref, m_new) : fast_exp2(st.m_ref - m_new);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
+        for (int j = 0; j < VW; ++j) st.acc[j] *= alpha;
         st.acc_l *= alpha;
         st.m_ref = m_new;
     }
@@ -359,8 +411,8 @@ __device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const
     const u32x4 ones = {kOnePair<Tag>(), kOnePair<Tag>(), kOnePair<Tag>(), kOnePair<Tag>()};
     st.acc_l = mfma16x16x32(Tag(), ones, pop, st.acc_l);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        // V^T operand for d = 8 n + j: 16-bit element j of each of the 8 rows.
+    for (int j = 0; j < VW; ++j) {
+        // V^T operand for d = VW n + j: 16-bit element j of each of the 8 rows.
         const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
         u32x4 w;
 #pragma unroll
@@ -371,25 +423,39 @@ __device__ __forceinline__ void compute_chunk(WaveState& st, ChunkRegs& r, const
 }
 
 // One chunk's math on either storage format.
-template <typename Tag, typename Kv, bool kCols>
-__device__ __forceinline__ void compute(WaveState& st, KvRegs<Kv>& r, const u32x4* qop,
+template <typename Tag, typename Kv, bool kCols, int D>
+__device__ __forceinline__ void compute(WaveState<D>& st, KvRegs<Kv, D>& r, const u32x4* qop,
                                         float sl2, int tc, int t_end, int t_col, int t_lo,
                                         int q) {
     if constexpr (Kv::kE4M3) {
-        ChunkRegs ops = expand<Tag>(r);
-        compute_chunk<Tag, kCols>(st, ops, qop, sl2, tc, t_end, t_col, t_lo, q);
+        ChunkRegs<D> ops = expand<Tag, D>(r);
+        compute_chunk<Tag, kCols, D>(st, ops, qop, sl2, tc, t_end, t_col, t_lo, q);
     } else {
-        compute_chunk<Tag, kCols>(st, r, qop, sl2, tc, t_end, t_col, t_lo, q);
+        compute_chunk<Tag, kCols, D>(st, r, qop, sl2, tc, t_end, t_col, t_lo, q);
     }
 }
 
-constexpr int kNW = kDecodeThreads / 64;   // wavefronts per workgroup
-constexpr int kOS = 128 + 4;               // padded LDS row of one head (floats)
+// This lane's accumulators (column n = lane % 16, d = VW (4 q + i) + j in
+// acc[j][i]) -> an LDS row of the column (float offsets 4 q VW + VW i + j).
+template <int D>
+__device__ __forceinline__ void stage_acc(float* col_row_lds, int q, const WaveState<D>& st) {
+    constexpr int VW = Dim<D>::VW;
+    float* ow = col_row_lds + 4 * q * VW;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j0 = 0; j0 < VW; j0 += 4)
+            *reinterpret_cast<f32x4*>(ow + VW * i + j0) =
+                (f32x4){st.acc[j0][i], st.acc[j0 + 1][i], st.acc[j0 + 2][i], st.acc[j0 + 3][i]};
+}
 
+constexpr int kNW = kDecodeThreads / 64;   // wavefronts per workgroup
+
+template <int D>
 struct SegmentLds {
     float m[kNW * 16];
     float l[kNW * 16];
-    __attribute__((aligned(16))) float o[kNW * 16 * kOS];
+    __attribute__((aligned(16))) float o[kNW * 16 * Dim<D>::OS];
 };
 
 // All wavefronts of the workgroup attend chunks [c0, c1) of (decode row b,
@@ -397,10 +463,11 @@ struct SegmentLds {
 // the chunks dealt round-robin to the wavefronts, then merge their states
 // and write the result: the final output rows when the segment is the whole
 // history (part < 0), else partition state `part`.
-template <typename Tag, int BS, typename Kv, int kRows>
-__device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& sm, int b, int kvh,
-                                               int L, int c0, int c1, int part) {
+template <typename Tag, int BS, typename Kv, int kRows, int D>
+__device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D>& sm, int b,
+                                               int kvh, int L, int c0, int c1, int part) {
     constexpr bool kCols = kRows == 1;
+    constexpr int OS = Dim<D>::OS;
     // The segment is the same for every lane; say so, so that block numbers
     // are fetched with scalar loads (which do not share the vector loads'
     // in-order counter) and addresses are computed once per wavefront.
@@ -420,15 +487,15 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
     const int t_lo = kCols ? min(t_end, L - (ntok - 1)) : t_end;
     const int t_col = kCols ? min(t_end, L - (ntok - 1 - n / G)) : t_end;
 
-    u32x4 qop[4];
-    load_query<Kv, kCols>(a, b, kvh, n, q, ntok * G, qop);
+    u32x4 qop[Dim<D>::KD];
+    load_query<Kv, kCols, D>(a, b, kvh, n, q, ntok * G, qop);
 
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
         (const ConstI32*)(a.block_tables) + table_row_offset<kRows>(a, b);
-    const uint32_t koff = lane_koff<Kv>(n, q);
-    const uint32_t voff = lane_voff<Kv>(n, q);
+    const uint32_t koff = lane_koff<Kv, D>(n, q);
+    const uint32_t voff = lane_voff<Kv, D>(n, q);
     const float sl2 = a.scale_log2;
 
     // Append step: the wave that will read the chunk holding the newest
@@ -439,14 +506,11 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
     if (a.new_key != nullptr) {
         const int c_last = (L - 1) / kChunk;
         if (c_last >= c0 && c_last < c1 && (c_last - c0) % kNW == wave)
-            append_token<Tag, Kv, BS>(a, row, b, kvh, L - 1, lane);
+            append_token<Tag, Kv, BS, D>(a, row, b, kvh, L - 1, lane);
     }
 
-    WaveState st;
-    st.m_ref = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    st.acc_l = (f32x4){0.f, 0.f, 0.f, 0.f};
+    WaveState<D> st;
+    init_state(st);
     int bad = 0;
 
     // This wave's chunks are c0 + wave + kNW k, k < K.  Two register buffers:
@@ -458,33 +522,34 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
         auto chunk_of = [&](int k) { return first + kNW * min(k, K - 1); };
         // tile 1 of chunk c is live when it holds history tokens
         auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
-        KvRegs<Kv> bufA, bufB;
+        KvRegs<Kv, D> bufA, bufB;
         int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
         int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
-        load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true, tile1_live(0), kvh, a.num_kv_heads, koff,
-                       voff);
+        load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true,
+                          tile1_live(0), kvh, a.num_kv_heads, koff, voff);
         int k = 0;
         // The scheduling barriers keep each phase's loads after the previous
         // chunk's math and before this chunk's: the load counter is in
         // order, so a load hoisted above the math would make it wait for
         // the prefetch too.  A prefetch past the wave's last chunk is issued
-        // dead (no bytes move) so that every path has 16 loads in flight.
+        // dead (no bytes move) so that every path has the same loads in
+        // flight.
         for (;;) {
             __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1),
-                           kvh, a.num_kv_heads, koff, voff);
+            load_chunk<BS, D>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
+                              k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
             idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
-            compute<Tag, Kv, kCols>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo,
-                                    q);
+            compute<Tag, Kv, kCols, D>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
+                                       t_lo, q);
             if (++k >= K) break;
             __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1),
-                           kvh, a.num_kv_heads, koff, voff);
+            load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
+                              k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
             idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
-            compute<Tag, Kv, kCols>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo,
-                                    q);
+            compute<Tag, Kv, kCols, D>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
+                                       t_lo, q);
             if (++k >= K) break;
         }
     }
@@ -493,16 +558,9 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
         sm.m[wave * 16 + n] = st.m_ref;
         sm.l[wave * 16 + n] = st.acc_l[0];
     }
-    float* ow = sm.o + (wave * 16 + n) * kOS + 32 * q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<f32x4*>(ow + 8 * i) =
-            (f32x4){st.acc[0][i], st.acc[1][i], st.acc[2][i], st.acc[3][i]};
-        *reinterpret_cast<f32x4*>(ow + 8 * i + 4) =
-            (f32x4){st.acc[4][i], st.acc[5][i], st.acc[6][i], st.acc[7][i]};
-    }
+    stage_acc<D>(sm.o + (wave * 16 + n) * OS, q, st);
     const bool any_bad = __syncthreads_or(bad);
-    finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, 16 * kOS, kOS, b, kvh, 0, ntok * G, any_bad,
+    finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, 16 * OS, OS, b, kvh, 0, ntok * G, any_bad,
                         part);
     __syncthreads();   // LDS is reused by the next segment
 }
@@ -510,9 +568,10 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds& 
 // Fixed schedule: workgroup (kvh, b, part) takes tokens [part P, part P + P).
 // The partition index varies slowest, so every sequence's first (full)
 // partition is dispatched before any shorter trailing one.
-template <typename Tag, int BS, typename Kv, int kRows>
-__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a) {
-    __shared__ SegmentLds sm;
+template <typename Tag, int BS, typename Kv, int kRows, int D>
+__global__ __launch_bounds__(kDecodeThreads)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void decode_mfma_fixed(DecodeArgs a) {
+    __shared__ SegmentLds<D> sm;
     const int kvh = blockIdx.x;
     const int b = blockIdx.y;
     const int part = blockIdx.z;
@@ -532,7 +591,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
     const int c0 = t_begin / kChunk;
     const int c1 = min(L, t_begin + a.part_len);
     const int c1c = (c1 + kChunk - 1) / kChunk;
-    attend_segment<Tag, BS, Kv, kRows>(a, sm, b, kvh, L, c0, c1c, nparts_b == 1 ? -1 : part);
+    attend_segment<Tag, BS, Kv, kRows, D>(a, sm, b, kvh, L, c0, c1c, nparts_b == 1 ? -1 : part);
 }
 
 // ---- balanced schedule ----------------------------------------------------
@@ -553,10 +612,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
 // 2 v + 0 is the segment wavefront v starts inside (or its only piece),
 // 2 v + 1 the one it ends inside.  key: sequence * num_kv_heads + KV head of
 // the piece's segment, -1 when the piece is absent.
+template <int D>
 struct EdgeLds {
     float m[2 * kNW][16];
     float l[2 * kNW][16];
-    __attribute__((aligned(16))) float o[2 * kNW][16 * kOS];
+    __attribute__((aligned(16))) float o[2 * kNW][16 * Dim<D>::OS];
     int key[2 * kNW];
     int bad[2 * kNW];
 };
@@ -566,9 +626,9 @@ struct EdgeLds {
 // two-buffer pipeline of attend_segment with the chunks taken in order.
 // Includes the append step when the newest history position lies in
 // [cs, ce): this wavefront alone reads that chunk.
-template <typename Tag, int BS, typename Kv, int kRows>
+template <typename Tag, int BS, typename Kv, int kRows, int D>
 __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh, int L, int ntok,
-                                             int cs, int ce, WaveState& st, int& bad) {
+                                             int cs, int ce, WaveState<D>& st, int& bad) {
     constexpr bool kCols = kRows == 1;
     const int G = a.group;
     const int lane = threadIdx.x & 63;
@@ -578,57 +638,61 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
     const int t_lo = kCols ? min(t_end, L - (ntok - 1)) : t_end;
     const int t_col = kCols ? min(t_end, L - (ntok - 1 - n / G)) : t_end;
 
-    u32x4 qop[4];
-    load_query<Kv, kCols>(a, b, kvh, n, q, ntok * G, qop);
+    u32x4 qop[Dim<D>::KD];
+    load_query<Kv, kCols, D>(a, b, kvh, n, q, ntok * G, qop);
 
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
         (const ConstI32*)(a.block_tables) + table_row_offset<kRows>(a, b);
-    const uint32_t koff = lane_koff<Kv>(n, q);
-    const uint32_t voff = lane_voff<Kv>(n, q);
+    const uint32_t koff = lane_koff<Kv, D>(n, q);
+    const uint32_t voff = lane_voff<Kv, D>(n, q);
     const float sl2 = a.scale_log2;
 
     if (a.new_key != nullptr) {
         const int c_last = (L - 1) / kChunk;
-        if (c_last >= cs && c_last < ce) append_token<Tag, Kv, BS>(a, row, b, kvh, L - 1, lane);
+        if (c_last >= cs && c_last < ce)
+            append_token<Tag, Kv, BS, D>(a, row, b, kvh, L - 1, lane);
     }
 
     const int K = ce - cs;
     auto chunk_of = [&](int k) { return cs + min(k, K - 1); };
     auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
-    KvRegs<Kv> bufA, bufB;
+    KvRegs<Kv, D> bufA, bufB;
     int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
     int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
-    load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true, tile1_live(0), kvh, a.num_kv_heads, koff,
-                   voff);
+    load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true, tile1_live(0),
+                      kvh, a.num_kv_heads, koff, voff);
     int k = 0;
     for (;;) {
         __builtin_amdgcn_sched_barrier(0);
-        load_chunk<BS>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
-                       a.num_kv_heads, koff, voff);
+        load_chunk<BS, D>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
+                          k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
         idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
         __builtin_amdgcn_sched_barrier(0);
-        compute<Tag, Kv, kCols>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo, q);
+        compute<Tag, Kv, kCols, D>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo,
+                                   q);
         if (++k >= K) break;
         __builtin_amdgcn_sched_barrier(0);
-        load_chunk<BS>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K, k + 1 < K && tile1_live(k + 1), kvh,
-                       a.num_kv_heads, koff, voff);
+        load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
+                          k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
         idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
         __builtin_amdgcn_sched_barrier(0);
-        compute<Tag, Kv, kCols>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo, q);
+        compute<Tag, Kv, kCols, D>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo,
+                                   q);
         if (++k >= K) break;
     }
 }
 
 // Output rows of a whole history held by one wavefront: o = õ / l for the
 // ncols columns (the G heads of the group; verify: its (query row, head)
-// pairs) -- lane 16 q + n holds column n, d = 32 q + 8 i + j in acc[j][i] --
-// rounded once to the storage type; NaN when a table entry was out of the
+// pairs) -- lane 16 q + n holds column n, d = VW (4 q + i) + j in acc[j][i]
+// -- rounded once to the storage type; NaN when a table entry was out of the
 // pool.
-template <typename Tag, bool kCols>
+template <typename Tag, bool kCols, int D>
 __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, int ncols,
-                                           const WaveState& st, bool bad) {
+                                           const WaveState<D>& st, bool bad) {
+    constexpr int VW = Dim<D>::VW;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int q = lane >> 4;
@@ -636,15 +700,20 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, 
     const float l = st.acc_l[0];
     const float vs = a.out_scale;
     char* orow = reinterpret_cast<char*>(a.out) +
-                 (column_row<kCols>(a, b, kvh, n) * 128 + 32 * q) * 2;
+                 (column_row<kCols>(a, b, kvh, n) * D + 4 * q * VW) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float o[8];
+        float o[VW];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = bad ? __builtin_nanf("") : vs * (st.acc[j][i] / l);
-        const u32x4 v = {pack2(Tag(), o[0], o[1]), pack2(Tag(), o[2], o[3]),
-                         pack2(Tag(), o[4], o[5]), pack2(Tag(), o[6], o[7])};
-        *reinterpret_cast<u32x4*>(orow + 16 * i) = v;
+        for (int j = 0; j < VW; ++j) o[j] = bad ? __builtin_nanf("") : vs * (st.acc[j][i] / l);
+        if constexpr (VW == 8) {
+            const u32x4 v = {pack2(Tag(), o[0], o[1]), pack2(Tag(), o[2], o[3]),
+                             pack2(Tag(), o[4], o[5]), pack2(Tag(), o[6], o[7])};
+            *reinterpret_cast<u32x4*>(orow + 2 * VW * i) = v;
+        } else {
+            const u32x2 v = {pack2(Tag(), o[0], o[1]), pack2(Tag(), o[2], o[3])};
+            *reinterpret_cast<u32x2*>(orow + 2 * VW * i) = v;
+        }
     }
 }
 
@@ -657,11 +726,13 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, 
 // consecutive d of one column.  The pieces are listed by position (absent
 // slots repeat the last piece with weight 0) so that all of a thread's LDS
 // reads are issued together.
-template <typename Tag, bool kCols>
-__device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLds& e,
+template <typename Tag, bool kCols, int D>
+__device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLds<D>& e,
                                                unsigned mask, int b, int kvh, int ncols, bool bad,
                                                float* plse, float* po) {
     constexpr int NP = 2 * kNW;
+    constexpr int OS = Dim<D>::OS;
+    constexpr int D4 = D / 4;
     int idx[NP];
     bool on[NP];
     unsigned mm = mask;
@@ -673,16 +744,16 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
         last = idx[k];
         mm &= mm - 1;
     }
-    for (int it = threadIdx.x; it < ncols * 32; it += blockDim.x) {
-        const int g = it >> 5;
-        const int d = (it & 31) * 4;
+    for (int it = threadIdx.x; it < ncols * D4; it += blockDim.x) {
+        const int g = it / D4;
+        const int d = (it % D4) * 4;
         float mv[NP], lv[NP];
         f32x4 ov[NP];
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
             mv[k] = e.m[idx[k]][g];
             lv[k] = e.l[idx[k]][g];
-            ov[k] = *reinterpret_cast<const f32x4*>(&e.o[idx[k]][g * kOS + d]);
+            ov[k] = *reinterpret_cast<const f32x4*>(&e.o[idx[k]][g * OS + d]);
         }
         float M = -INFINITY;
 #pragma unroll
@@ -703,21 +774,27 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
             const uint32_t lo = pack2(Tag(), os[0], os[1]);
             const uint32_t hi = pack2(Tag(), os[2], os[3]);
             char* dst = reinterpret_cast<char*>(a.out) +
-                        (column_row<kCols>(a, b, kvh, g) * 128 + d) * 2;
+                        (column_row<kCols>(a, b, kvh, g) * D + d) * 2;
             *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
         } else {
-            *reinterpret_cast<f32x4*>(po + g * 128 + d) = o;
+            *reinterpret_cast<f32x4*>(po + g * D + d) = o;
             if (d == 0) plse[g] = bad ? __builtin_nanf("") : M + __log2f(den);
         }
     }
 }
 
-template <typename Tag, int BS, typename Kv, int kRows>
-__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
+// The prefix table of the balanced schedule (num_seqs + 1 ints) is dynamic
+// LDS, sized at launch.
+extern __shared__ int balanced_pref[];
+
+template <typename Tag, int BS, typename Kv, int kRows, int D>
+__global__ __launch_bounds__(kDecodeThreads)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void decode_mfma_balanced(DecodeArgs a) {
     constexpr bool kCols = kRows == 1;
-    __shared__ EdgeLds edge;
-    __shared__ int pref[kMaxBalancedSeqs + 1];
+    constexpr int OS = Dim<D>::OS;
+    __shared__ EdgeLds<D> edge;
     __shared__ int wsum[kNW];
+    int* pref = balanced_pref;
     chunk_prefix(a, pref, wsum);
     const int H_kv = a.num_kv_heads;
     const int64_t T = (int64_t)H_kv * pref[a.num_seqs];
@@ -749,32 +826,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         const int L = __builtin_amdgcn_readfirstlane(a.context_lens[b]);
         const int ntok = row_tokens<kRows>(a, b);
 
-        WaveState st;
-        st.m_ref = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st.acc[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        st.acc_l = (f32x4){0.f, 0.f, 0.f, 0.f};
+        WaveState<D> st;
+        init_state(st);
         int bad = 0;
-        attend_piece<Tag, BS, Kv, kRows>(a, b, kvh, L, ntok, c0, c1, st, bad);
+        attend_piece<Tag, BS, Kv, kRows, D>(a, b, kvh, L, ntok, c0, c1, st, bad);
 
         const bool starts_before = c0 > 0;    // the segment began before this range
         const bool ends_after = c1 < nb;      // it continues past this range
         if (!starts_before && !ends_after) {
-            write_rows<Tag, kCols>(a, b, kvh, ntok * a.group, st, bad != 0);
+            write_rows<Tag, kCols, D>(a, b, kvh, ntok * a.group, st, bad != 0);
         } else {
             const int p = 2 * wave + (starts_before ? 0 : 1);
             if (q == 0) {
                 edge.m[p][n] = st.m_ref;
                 edge.l[p][n] = st.acc_l[0];
             }
-            float* ow = &edge.o[p][n * kOS + 32 * q];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                *reinterpret_cast<f32x4*>(ow + 8 * i) =
-                    (f32x4){st.acc[0][i], st.acc[1][i], st.acc[2][i], st.acc[3][i]};
-                *reinterpret_cast<f32x4*>(ow + 8 * i + 4) =
-                    (f32x4){st.acc[4][i], st.acc[5][i], st.acc[6][i], st.acc[7][i]};
-            }
+            stage_acc<D>(&edge.o[p][n * OS], q, st);
             if (lane == 0) {
                 edge.key[p] = b * H_kv + kvh;
                 edge.bad[p] = bad;
@@ -808,12 +875,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         const bool tail = xs + nb > xe;       // continues into the next range
         const int ncols = row_tokens<kRows>(a, b) * a.group;
         if (!head && !tail) {
-            finalize_edges<Tag, kCols>(a, edge, mask, b, kvh, ncols, bad != 0, nullptr, nullptr);
+            finalize_edges<Tag, kCols, D>(a, edge, mask, b, kvh, ncols, bad != 0, nullptr,
+                                          nullptr);
         } else {
             const uint64_t slot = (uint64_t)w * 2 + (head ? 0 : 1);
-            finalize_edges<Tag, kCols>(a, edge, mask, b, kvh, ncols, bad != 0,
-                                       a.ws_lse + slot * kMaxGroup,
-                                       a.ws_out + slot * kMaxGroup * 128);
+            finalize_edges<Tag, kCols, D>(a, edge, mask, b, kvh, ncols, bad != 0,
+                                          a.ws_lse + slot * kMaxGroup,
+                                          a.ws_out + slot * kMaxGroup * D);
             if (!head) meta.x = k, meta.y = range_owner(xs + nb - 1, T, a.num_wg);
         }
         p = p1;
@@ -821,51 +889,62 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     if (threadIdx.x == 0) reinterpret_cast<int4*>(a.ws_meta)[w] = meta;
 }
 
-template <typename Tag, int BS, typename Kv, int kRows>
+template <typename Tag, int BS, typename Kv, int kRows, int D>
 hipError_t launch_rows(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
-        hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv, kRows>), dim3(a.num_wg),
-                           dim3(kDecodeThreads), 0, s, a);
+        const size_t pref_bytes = (size_t)(a.num_seqs + 1) * sizeof(int);
+        hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv, kRows, D>), dim3(a.num_wg),
+                           dim3(kDecodeThreads), pref_bytes, s, a);
     } else {
         dim3 grid(a.num_kv_heads, a.num_seqs, a.num_parts);
-        hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS, Kv, kRows>), grid, dim3(kDecodeThreads),
-                           0, s, a);
+        hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS, Kv, kRows, D>), grid,
+                           dim3(kDecodeThreads), 0, s, a);
     }
     return hipGetLastError();
 }
 
 // Decode rows with a row map (verify mode) run their own instantiation.
-template <typename Tag, int BS, typename Kv>
+template <typename Tag, int BS, typename Kv, int D>
 hipError_t launch_kv(const DecodeArgs& a, hipStream_t s) {
-    return a.table_rows != nullptr ? launch_rows<Tag, BS, Kv, 1>(a, s)
-                                   : launch_rows<Tag, BS, Kv, 0>(a, s);
+    return a.table_rows != nullptr ? launch_rows<Tag, BS, Kv, 1, D>(a, s)
+                                   : launch_rows<Tag, BS, Kv, 0, D>(a, s);
 }
 
-template <typename Tag, int BS>
+template <typename Tag, int BS, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
-    return a.kv_format == kKvE4M3 ? launch_kv<Tag, BS, KvE4M3>(a, s)
-                                  : launch_kv<Tag, BS, KvSame>(a, s);
+    return a.kv_format == kKvE4M3 ? launch_kv<Tag, BS, KvE4M3, D>(a, s)
+                                  : launch_kv<Tag, BS, KvSame, D>(a, s);
+}
+
+template <typename Tag, int D>
+hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
+    switch (a.block_size) {
+        case 16: return launch_typed<Tag, 16, D>(a, s);
+        case 32: return launch_typed<Tag, 32, D>(a, s);
+        default: return launch_typed<Tag, 64, D>(a, s);
+    }
+}
+
+template <typename Tag>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
+    return a.head_dim == 64 ? launch_bs<Tag, 64>(a, s) : launch_bs<Tag, 128>(a, s);
 }
 
 }  // namespace
 
 bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group) {
-    return (dt == PA_BF16 || dt == PA_F16) && head_dim == 128 &&
+    return (dt == PA_BF16 || dt == PA_F16) && (head_dim == 64 || head_dim == 128) &&
            (block_size == 16 || block_size == 32 || block_size == 64) && group >= 1 &&
            group <= 16;
 }
 
-template <typename Tag>
-hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
-    switch (a.block_size) {
-        case 16: return launch_typed<Tag, 16>(a, s);
-        case 32: return launch_typed<Tag, 32>(a, s);
-        default: return launch_typed<Tag, 64>(a, s);
-    }
-}
+// Workgroups of the matrix-core kernel one compute unit holds at once: two at
+// head_dim 128, four at head_dim 64 (half the registers and LDS each), so
+// the bytes in flight per compute unit are the same.
+int mfma_workgroups_per_cu(int head_dim) { return head_dim == 64 ? 4 : 2; }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s) {
-    return dt == PA_BF16 ? launch_bs<BF16>(a, s) : launch_bs<F16>(a, s);
+    return dt == PA_BF16 ? launch_d<BF16>(a, s) : launch_d<F16>(a, s);
 }
 
 }  // namespace pa

@@ -64,7 +64,7 @@ enum KvFormat { kKvSame = 0, kKvE4M3 = 1 };
 enum Schedule { kFixed = 0, kBalanced = 1 };
 constexpr int kMaxGroup = 16;          // heads per slot (matrix-core kernel)
 constexpr int kMaxBalancedWg = 1024;   // workspace is sized for this many
-constexpr int kMaxBalancedSeqs = 2048; // LDS prefix table of the balanced schedule
+constexpr int kMaxBalancedSeqs = 2048; // prefix table of the balanced schedule (dynamic LDS)
 
 constexpr int kDecodeThreads = 256;   // 4 wavefronts per workgroup
 constexpr int kChunk = 32;            // tokens a wavefront handles per step
@@ -73,6 +73,8 @@ constexpr int kChunk = 32;            // tokens a wavefront handles per step
 enum KernelKind { kAuto = 0, kGeneric = 1, kMfma = 2 };
 
 bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group);
+// Workgroups of the matrix-core kernel resident per compute unit.
+int mfma_workgroups_per_cu(int head_dim);
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_lse_merge(const DecodeArgs& a, pa_dtype dt, hipStream_t s);

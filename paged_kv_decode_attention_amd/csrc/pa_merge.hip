@@ -30,13 +30,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
 // over at most kSpec ranges).  Workgroup num_wg + b writes the rows of
 // decode row b when the decode kernel has none to write: zeros for an empty
 // history, NaN for an invalid context length.  A thread takes 4
-// consecutive d of one column (head_dim 128, at most kMaxGroup columns).
-constexpr int kMergeBalancedThreads = kMaxGroup * 32;
-
-template <typename Tag>
-__global__ __launch_bounds__(kMergeBalancedThreads) void merge_balanced(DecodeArgs a) {
+// consecutive d of one column (at most kMaxGroup columns): kMaxGroup * D / 4
+// threads.
+template <typename Tag, int D>
+__global__ __launch_bounds__(kMaxGroup * D / 4) void merge_balanced(DecodeArgs a) {
     constexpr int kSpec = 4;
-    constexpr int D = 128;
     const int w = blockIdx.x;
     if (w >= a.num_wg) {
         // the query rows decode row b carries (b .. b + n_b - 1), every
@@ -52,8 +50,8 @@ __global__ __launch_bounds__(kMergeBalancedThreads) void merge_balanced(DecodeAr
             store_elem(Tag(), a.out, base + i, v);
         return;
     }
-    const int g = threadIdx.x >> 5;
-    const int d = (threadIdx.x & 31) * 4;
+    const int g = threadIdx.x / (D / 4);
+    const int d = (threadIdx.x % (D / 4)) * 4;
     const int nwg = a.num_wg;
     auto slot_row = [&](int slot) { return (uint64_t)slot * kMaxGroup + g; };
     const int4 meta = reinterpret_cast<const int4*>(a.ws_meta)[w];
@@ -140,8 +138,12 @@ __global__ __launch_bounds__(kMergeBalancedThreads) void merge_balanced(DecodeAr
 template <typename Tag>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
-        hipLaunchKernelGGL((merge_balanced<Tag>), dim3(a.num_wg + a.num_seqs),
-                           dim3(kMergeBalancedThreads), 0, s, a);
+        if (a.head_dim == 64)
+            hipLaunchKernelGGL((merge_balanced<Tag, 64>), dim3(a.num_wg + a.num_seqs),
+                               dim3(kMaxGroup * 64 / 4), 0, s, a);
+        else
+            hipLaunchKernelGGL((merge_balanced<Tag, 128>), dim3(a.num_wg + a.num_seqs),
+                               dim3(kMaxGroup * 128 / 4), 0, s, a);
     } else {
         hipLaunchKernelGGL((merge_fixed<Tag>), dim3(a.num_kv_heads, a.num_seqs),
                            dim3(kMergeThreads), 0, s, a);

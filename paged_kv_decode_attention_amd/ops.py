@@ -29,6 +29,7 @@ _SIGNATURES = {
     "pa_status_string": (ctypes.c_char_p, [_I]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_debug_select_kernel": (_I, [_I]),
+    "pa_decode_kernel": (_I, [_I, _I, _I, _I]),
     "pa_decode_partition_size": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "pa_decode_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I, _I]),
     "pa_paged_attention_decode": (
@@ -129,6 +130,16 @@ def select_kernel(kind):
     if prev < 0:
         _check(prev, "select_kernel")
     return prev
+
+
+def decode_kernel(head_dim, block_size, gqa_group_size, dtype):
+    """The kernel family a decode call of this shape runs now: KERNEL_GENERIC
+    (vector ALU) or KERNEL_MFMA (matrix cores)."""
+    k = load_library().pa_decode_kernel(int(head_dim), int(block_size), int(gqa_group_size),
+                                        dtype_code(dtype))
+    if k < 0:
+        _check(k, "decode_kernel")
+    return k
 
 
 def decode_partition_size(num_seqs, num_kv_heads, gqa_group_size, head_dim, block_size,

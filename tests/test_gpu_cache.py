@@ -120,6 +120,29 @@ def test_decode_append_equals_write_then_decode(name, kernel, partition_size):
     assert torch.equal(d1["value_cache"], d2["value_cache"])
 
 
+@pytest.mark.parametrize("partition_size", [0, 256])
+def test_decode_append_head_dim_64_equals_write_then_decode(partition_size):
+    """The matrix-core kernel's own append step at head_dim 64 (8 lanes per
+    row) against reshape_and_cache followed by decode, bit for bit."""
+    cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_seqs=12, num_blocks=4000,
+                           head_dim=64)
+    inp = I.generate(cfg, new_tokens_at="last")
+    d1 = upload(inp)
+    ops.reshape_and_cache(d1["new_key"], d1["new_value"], d1["key_cache"], d1["value_cache"],
+                          d1["slot_mapping"])
+    o1 = ops.paged_attention_decode(d1["query"], d1["key_cache"], d1["value_cache"],
+                                    d1["block_tables"], d1["context_lens"],
+                                    partition_size=partition_size)
+    d2 = upload(inp)
+    o2 = ops.decode_append(d2["query"], d2["new_key"], d2["new_value"], d2["key_cache"],
+                           d2["value_cache"], d2["block_tables"], d2["context_lens"],
+                           partition_size=partition_size)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(d1["key_cache"], d2["key_cache"])
+    assert torch.equal(d1["value_cache"], d2["value_cache"])
+
+
 def test_decode_append_against_oracle():
     cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_seqs=6, num_blocks=400,
                            max_blocks_per_seq=64, lens_kind="list",

@@ -48,8 +48,12 @@ SMALL_CASES = [
     ("bf16", 1, 16, 128, 16, ops.KERNEL_MFMA),
     ("bf16", 2, 8, 128, 32, ops.KERNEL_MFMA),
     ("bf16", 2, 20, 128, 16, ops.KERNEL_AUTO),      # G > 16: vector-ALU kernel
-    ("f16", 2, 3, 64, 16, ops.KERNEL_AUTO),         # head_dim 64: vector-ALU kernel
+    ("f16", 2, 3, 64, 16, ops.KERNEL_AUTO),         # head_dim 64: matrix-core kernel
     ("bf16", 2, 5, 64, 32, ops.KERNEL_GENERIC),
+    ("bf16", 2, 7, 64, 16, ops.KERNEL_MFMA),
+    ("bf16", 3, 1, 64, 32, ops.KERNEL_MFMA),
+    ("f16", 1, 16, 64, 64, ops.KERNEL_MFMA),
+    ("bf16", 2, 8, 64, 16, ops.KERNEL_MFMA),
     ("f32", 2, 1, 64, 16, ops.KERNEL_AUTO),
     ("f32", 2, 4, 128, 32, ops.KERNEL_GENERIC),
     ("f32", 1, 12, 128, 16, ops.KERNEL_GENERIC),
@@ -84,7 +88,8 @@ def test_kernels_agree():
 
 def test_single_token_history_is_v0_exactly():
     for dtype, D, kernel in (("bf16", 128, ops.KERNEL_MFMA), ("f16", 128, ops.KERNEL_MFMA),
-                             ("f32", 64, ops.KERNEL_GENERIC), ("bf16", 128, ops.KERNEL_GENERIC)):
+                             ("bf16", 64, ops.KERNEL_MFMA), ("f32", 64, ops.KERNEL_GENERIC),
+                             ("bf16", 128, ops.KERNEL_GENERIC)):
         inp = I.generate(small_config(dtype, 2, 4, D, 16, (1, 1, 1)))
         out = run_decode(upload(inp), kernel).cpu()
         for b in range(3):
@@ -127,10 +132,11 @@ def test_permutation_and_block_size_invariance_bitwise():
         assert torch.equal(out, base), "layout (bs=%d, seed=%d) changed the result" % (bs, seed)
 
 
-def test_balanced_schedule_layout_invariance_bitwise():
+@pytest.mark.parametrize("D", [128, 64])
+def test_balanced_schedule_layout_invariance_bitwise(D):
     """The balanced schedule's work split depends on lengths only, so moving
     the history to other physical blocks, or to blocks of 32, changes no bit."""
-    inp = I.generate(small_config("bf16", 2, 7, 128, 16, RAGGED + (2000, 3000), seed=12))
+    inp = I.generate(small_config("bf16", 2, 7, D, 16, RAGGED + (2000, 3000), seed=12))
     base = run_decode(upload(inp), ops.KERNEL_MFMA, 0).cpu()
     for bs, seed in ((16, 4), (32, 5)):
         kc, vc, bt = same_history_other_layout(inp, bs, seed)

@@ -80,17 +80,18 @@ def test_fp8_cache_write_bit_exact(src, scales):
     assert np.array_equal(dv.cpu().numpy(), rv)
 
 
-CASES = [("bf16", 2, 7, 16), ("bf16", 2, 4, 32), ("f16", 2, 4, 16), ("bf16", 1, 16, 16),
-         ("f16", 3, 1, 32), ("bf16", 2, 7, 64)]
+CASES = [("bf16", 2, 7, 128, 16), ("bf16", 2, 4, 128, 32), ("f16", 2, 4, 128, 16),
+         ("bf16", 1, 16, 128, 16), ("f16", 3, 1, 128, 32), ("bf16", 2, 7, 128, 64),
+         ("bf16", 2, 7, 64, 16), ("f16", 2, 4, 64, 32), ("bf16", 1, 16, 64, 64)]
 
 
 @pytest.mark.parametrize("partition_size", [0, 64, 256])
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-hkv%d-g%d-bs%d" % c)
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-hkv%d-g%d-d%d-bs%d" % c)
 def test_fp8_decode_parity(case, partition_size):
-    dtype, H_kv, G, BS = case
+    dtype, H_kv, G, D, BS = case
     if partition_size % BS:
         pytest.skip("partition not a multiple of the block size")
-    inp = I.poison_unread(I.generate(small_config(dtype, H_kv, G, 128, BS, RAGGED)))
+    inp = I.poison_unread(I.generate(small_config(dtype, H_kv, G, D, BS, RAGGED)))
     kq, vq, kdq, vdq = fp8_inputs(inp)
     out = run_fp8(inp, kq, vq, partition_size)
     compare(out, oracle_fp8(inp, kdq, vdq), dtype, what="fp8 %s P=%d" % (case, partition_size))
@@ -117,9 +118,11 @@ def test_fp8_float8_tensor_type_and_errors():
         ops.select_kernel(prev)
 
 
+@pytest.mark.parametrize("head_dim", [128, 64])
 @pytest.mark.parametrize("partition_size", [0, 256])
-def test_fp8_decode_append_equals_write_then_decode(partition_size):
-    cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_seqs=12, num_blocks=4000)
+def test_fp8_decode_append_equals_write_then_decode(partition_size, head_dim):
+    cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_seqs=12, num_blocks=4000,
+                           head_dim=head_dim)
     inp = I.generate(cfg, new_tokens_at="last")
     kq, vq, _, _ = fp8_inputs(inp)
     q = inp.query.to(DEV)

@@ -72,15 +72,16 @@ def test_verify_parity(case, partition_size):
 # The sequence of length 3 has q = 5 > L: its rows are NaN.
 COL_LENS = (33, 34, 65, 66, 97, 40, 2, 513, 8, 3, 129)
 COL_QLENS = (2, 3, 2, 3, 2, 8, 2, 5, 8, 5, 17)
-COL_CASES = [("bf16", 2, 7, 16), ("f16", 2, 4, 32), ("bf16", 4, 1, 16), ("bf16", 1, 16, 64),
-             ("bf16", 2, 3, 16), ("f16", 1, 8, 16), ("bf16", 2, 5, 32)]
+COL_CASES = [("bf16", 2, 7, 128, 16), ("f16", 2, 4, 128, 32), ("bf16", 4, 1, 128, 16),
+             ("bf16", 1, 16, 128, 64), ("bf16", 2, 3, 128, 16), ("f16", 1, 8, 128, 16),
+             ("bf16", 2, 5, 128, 32), ("bf16", 2, 7, 64, 16), ("f16", 2, 2, 64, 32)]
 
 
 @pytest.mark.parametrize("partition_size", [0, 64])
-@pytest.mark.parametrize("case", COL_CASES, ids=lambda c: "%s-hkv%d-g%d-bs%d" % c)
+@pytest.mark.parametrize("case", COL_CASES, ids=lambda c: "%s-hkv%d-g%d-d%d-bs%d" % c)
 def test_verify_columns_parity(case, partition_size):
-    dtype, H_kv, G, BS = case
-    cfg = small_config(dtype, H_kv, G, 128, BS, COL_LENS)
+    dtype, H_kv, G, D, BS = case
+    cfg = small_config(dtype, H_kv, G, D, BS, COL_LENS)
     inp, q, qs = verify_inputs(cfg, list(COL_QLENS), seed=11)
     out = run_verify(inp, q, qs, 17, ops.KERNEL_MFMA, partition_size)
     ref = oracle_verify(inp, q, qs)
