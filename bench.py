@@ -59,6 +59,10 @@ def parse():
                     help="only run the block-size x head-dim sweep (one JSON line per shape)")
     ap.add_argument("--sweep-out", default=None,
                     help="with --sweep: also write the table as markdown to this file")
+    ap.add_argument("--sweep-head-dims", default="64,128,256",
+                    help="with --sweep: comma-separated head dims")
+    ap.add_argument("--sweep-block-sizes", default="8,16,32,64",
+                    help="with --sweep: comma-separated block sizes")
     return ap.parse_args()
 
 
@@ -274,8 +278,8 @@ def shape_sweep(args, dev):
     G = H // H_kv
     K = min(args.steps, 100)
     rows = []
-    for D in (64, 128, 256):
-        for BS in (8, 16, 32, 64):
+    for D in [int(x) for x in args.sweep_head_dims.split(",")]:
+        for BS in [int(x) for x in args.sweep_block_sizes.split(",")]:
             rng = np.random.default_rng(7)
             nblk = -(-lens // BS)
             N = int(nblk.sum()) + 64
@@ -287,7 +291,9 @@ def shape_sweep(args, dev):
                 bt[b, :nblk[b]] = perm[k:k + nblk[b]]
                 k += nblk[b]
             pool = N * H_kv * BS * D * 2
-            R = max(2, int(np.ceil(600e6 / (2 * pool))))
+            # replicas cycled through: 1.2 GB or more of K/V between two
+            # reads of the same bytes, well beyond the 256 MB last-level cache
+            R = max(2, int(np.ceil(1.2e9 / (2 * pool))))
             g = torch.Generator(device=dev).manual_seed(11)
             kcs = [torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(torch.bfloat16)
                    for _ in range(R)]

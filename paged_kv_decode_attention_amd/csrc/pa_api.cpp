@@ -106,9 +106,8 @@ Layout balanced_layout(int head_dim) {
     return l;
 }
 
-// Workgroups of the balanced schedule: as many per compute unit of the
-// current device as the matrix-core kernel keeps resident at this head_dim,
-// so all are resident at once.
+// Workgroups of the balanced schedule: pa::mfma_workgroups_per_cu per compute
+// unit of the current device, all resident at once.
 int balanced_workgroups(int head_dim) {
     static int cached[64] = {0};
     int dev = 0;
@@ -268,7 +267,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
         return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
     if (e4m3 && !use_mfma)
         return fail(PA_ERR_UNSUPPORTED, "FP8 caches are served by the matrix-core kernel only "
-                    "(bf16/f16 queries, head_dim 64/128, block_size 16/32/64, group <= 16)");
+                    "(bf16/f16 queries, head_dim 64/128/256, block_size 16/32/64, group <= 16)");
     const bool balanced = use_balanced(use_mfma, partition_size, num_seqs, max_context_len);
 
     const int P = partition_size ? partition_size

@@ -1,5 +1,5 @@
 // Decode paged attention on the gfx950 matrix cores, bf16/fp16 queries,
-// 16-bit or FP8 E4M3 caches, head_dim 64 or 128, GQA groups of up to 16
+// 16-bit or FP8 E4M3 caches, head_dim 64, 128 or 256, GQA groups of up to 16
 // query heads.
 //
 // Work decomposition: one workgroup of 4 wavefronts per (sequence b, KV head,
@@ -64,14 +64,16 @@ constexpr uint32_t kOnePair<F16>() { return 0x3c003c00u; }
 // Tile geometry of one head dimension.
 template <int D>
 struct Dim {
-    static_assert(D == 64 || D == 128, "matrix-core kernel: head_dim 64 or 128");
+    static_assert(D == 64 || D == 128 || D == 256, "matrix-core kernel: head_dim 64/128/256");
     static constexpr int KD = D / 32;   // K / Q MFMA steps per 16-token tile
     static constexpr int VW = D / 16;   // d values a lane holds per V row = PV MFMAs
     static constexpr int RB = D * 2;    // bytes per 16-bit token row
     static constexpr int OS = D + 4;    // padded LDS row of one column (floats)
     // 32-bit dwords of this lane's slice of a V row: 16-bit / E4M3 storage
-    using VRow = typename std::conditional<D == 64, u32x2, u32x4>::type;
-    using VRow8 = typename std::conditional<D == 64, uint32_t, u32x2>::type;
+    using VRow = typename std::conditional<
+        D == 64, u32x2, typename std::conditional<D == 128, u32x4, u32x8>::type>::type;
+    using VRow8 = typename std::conditional<
+        D == 64, uint32_t, typename std::conditional<D == 128, u32x2, u32x4>::type>::type;
 };
 
 // One 32-token chunk's K and V operands, as loaded (two 16-token tiles).
@@ -96,18 +98,34 @@ __device__ __forceinline__ int tile_row(int c) {
     return BS == 64 ? (c & 1) * 32 : 0;
 }
 
+// Blocks of 8 tokens: a chunk spans four blocks (two per 16-token tile).
 template <int BS>
-__device__ __forceinline__ int2 chunk_blocks(const ConstI32* row, int c, int L, int num_blocks,
-                                             int& bad) {
+using BlockIds = typename std::conditional<BS == 8, int4, int2>::type;
+
+__device__ __forceinline__ int checked_block(int pb, int num_blocks, int& bad) {
+    if ((unsigned)pb >= (unsigned)num_blocks) { bad = 1; return 0; }
+    return pb;
+}
+
+template <int BS>
+__device__ __forceinline__ BlockIds<BS> chunk_blocks(const ConstI32* row, int c, int L,
+                                                     int num_blocks, int& bad) {
     const int j0 = c * kChunk / BS;
-    int pb0 = row[j0];
-    int pb1 = pb0;
-    if constexpr (BS == 16) {
-        if (c * kChunk + 16 < L) pb1 = row[j0 + 1];
+    const int pb0 = checked_block(row[j0], num_blocks, bad);
+    if constexpr (BS == 8) {
+        // a block past the end of the history reuses the first block
+        const int t0 = c * kChunk;
+        const int pb1 = t0 + 8 < L ? checked_block(row[j0 + 1], num_blocks, bad) : pb0;
+        const int pb2 = t0 + 16 < L ? checked_block(row[j0 + 2], num_blocks, bad) : pb0;
+        const int pb3 = t0 + 24 < L ? checked_block(row[j0 + 3], num_blocks, bad) : pb0;
+        return make_int4(pb0, pb1, pb2, pb3);
+    } else {
+        int pb1 = pb0;
+        if constexpr (BS == 16) {
+            if (c * kChunk + 16 < L) pb1 = checked_block(row[j0 + 1], num_blocks, bad);
+        }
+        return make_int2(pb0, pb1);
     }
-    if ((unsigned)pb0 >= (unsigned)num_blocks) { bad = 1; pb0 = 0; }
-    if ((unsigned)pb1 >= (unsigned)num_blocks) { bad = 1; pb1 = 0; }
-    return make_int2(pb0, pb1);
 }
 
 // Buffer descriptor of one 16-token tile (kTileBytes: 16 rows of K or V):
@@ -128,8 +146,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, bo
 // empty descriptor: the loads return zeros and move no bytes.
 constexpr int kNonTemporal = 2;   // buffer cache-policy bit: nt
 
-// V row slices: 8 bytes (head_dim 64) or 16 bytes (head_dim 128) of 16-bit
-// values; 4 or 8 bytes of E4M3 codes.
+// V row slices: 8, 16 or 32 bytes (head_dim 64, 128, 256) of 16-bit values;
+// 4, 8 or 16 bytes of E4M3 codes.
+__device__ __forceinline__ void load_row(u32x8& x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
+    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kNonTemporal);
+    x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 __device__ __forceinline__ void load_row(u32x4& x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
 }
@@ -140,12 +163,92 @@ __device__ __forceinline__ void load_row(uint32_t& x, __amdgpu_buffer_rsrc_t r, 
     x = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kNonTemporal);
 }
 
+// Loads through per-lane 64-bit addresses instead of a tile descriptor.
+// Blocks of 8 tokens need them: each 16-token tile spans two blocks, so one
+// instruction's lanes read rows of two blocks (the K operand row of lane
+// (q, n) is token n of the tile, block n / 8; its V rows are tokens
+// 4 q .. 4 q + 3, block q / 2).  Larger blocks keep the descriptor path
+// (measured equal or up to 1 % faster with the last-level cache defeated).
+// A tile that is not live points every lane at the first bytes of the pool
+// (one cache line per instruction, never out of bounds); such tiles are
+// masked or never computed.  Loads are nontemporal.  kin / vin: this lane's
+// byte offsets inside a K row / V row.
+template <int BS, int D>
+constexpr bool lane_addressed() { return BS == 8; }
+typedef __attribute__((address_space(1))) const u32x4 GlobalU32x4;
+typedef __attribute__((address_space(1))) const u32x2 GlobalU32x2;
+typedef __attribute__((address_space(1))) const uint32_t GlobalU32;
+
+__device__ __forceinline__ void load_row_at(u32x8& x, const char* p) {
+    const u32x4 lo = __builtin_nontemporal_load((GlobalU32x4*)p);
+    const u32x4 hi = __builtin_nontemporal_load((GlobalU32x4*)(p + 16));
+    x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void load_row_at(u32x4& x, const char* p) {
+    x = __builtin_nontemporal_load((GlobalU32x4*)p);
+}
+__device__ __forceinline__ void load_row_at(u32x2& x, const char* p) {
+    x = __builtin_nontemporal_load((GlobalU32x2*)p);
+}
+__device__ __forceinline__ void load_row_at(uint32_t& x, const char* p) {
+    x = __builtin_nontemporal_load((GlobalU32*)p);
+}
+
+// kRB: bytes per token row; kKLoads 16-byte K loads per tile, kKStep bytes
+// apart; Regs: ChunkRegs or ChunkRegs8.  Blocks of 16 or more tokens: tile
+// t lies in block pb[t] from row r0 (tile 0) or the row after tile 0's
+// (tile 1), as in load_chunk.
+template <int BS, int kRB, int kKLoads, int kKStep, typename Regs>
+__device__ __forceinline__ void load_chunk_lanes(Regs& r, const char* kbase, const char* vbase,
+                                                 BlockIds<BS> pb, int r0, bool live0, bool live1,
+                                                 int kvh, int num_kv_heads, uint32_t kin,
+                                                 uint32_t vin) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int q = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const bool live = t == 0 ? live0 : live1;
+        int kblk, kslot, vblk, vslot;
+        if constexpr (BS == 8) {
+            const int blk_a = t == 0 ? pb.x : pb.z;
+            const int blk_b = t == 0 ? pb.y : pb.w;
+            kblk = n < 8 ? blk_a : blk_b;
+            kslot = n & 7;
+            vblk = q < 2 ? blk_a : blk_b;
+            vslot = 4 * (q & 1);
+        } else {
+            const int row_t = t == 0 ? r0 : (BS == 16 ? 0 : r0 + 16);
+            kblk = vblk = t == 0 ? pb.x : pb.y;
+            kslot = row_t + n;
+            vslot = row_t + 4 * q;
+        }
+        const uint64_t krow = live ? kv_row(kblk, kvh, kslot, num_kv_heads, BS) : 0;
+        const uint64_t vrow = live ? kv_row(vblk, kvh, vslot, num_kv_heads, BS) : 0;
+        const char* kp = kbase + krow * kRB + kin;
+        const char* vp = vbase + vrow * kRB + vin;
+#pragma unroll
+        for (int kk = 0; kk < kKLoads; ++kk)
+            load_row_at(t == 0 ? r.k0[kk] : r.k1[kk], kp + kk * kKStep);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_row_at(r.v[4 * t + i], vp + i * kRB);
+    }
+}
+
 template <int BS, int D>
 __device__ __forceinline__ void load_chunk(ChunkRegs<D>& r, const char* kbase, const char* vbase,
-                                           int2 pb, int r0, bool live0, bool live1, int kvh,
-                                           int num_kv_heads, uint32_t koff, uint32_t voff) {
+                                           BlockIds<BS> pb, int r0, bool live0, bool live1,
+                                           int kvh, int num_kv_heads, uint32_t koff,
+                                           uint32_t voff) {
     constexpr int RB = Dim<D>::RB;   // bytes per token row
     constexpr int KD = Dim<D>::KD;
+    if constexpr (lane_addressed<BS, D>()) {
+        // koff = n RB + kin, voff = 4 q RB + vin
+        const int lane = threadIdx.x & 63;
+        load_chunk_lanes<BS, RB, KD, 64>(r, kbase, vbase, pb, r0, live0, live1, kvh,
+                                         num_kv_heads, koff - (lane & 15) * RB,
+                                         voff - 4 * (lane >> 4) * RB);
+    } else {
     const uint64_t row0 = kv_row(pb.x, kvh, r0, num_kv_heads, BS) * RB;
     const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : r0 + 16, num_kv_heads, BS) * RB;
     const __amdgpu_buffer_rsrc_t k0 = tile_rsrc<16 * RB>(kbase + row0, live0);
@@ -162,6 +265,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D>& r, const char* kbase, c
     for (int i = 0; i < 4; ++i) load_row(r.v[i], v0, voff + i * RB);
 #pragma unroll
     for (int i = 0; i < 4; ++i) load_row(r.v[4 + i], v1, voff + i * RB);
+    }
 }
 
 // ---- KV storage formats -----------------------------------------------------
@@ -188,10 +292,17 @@ struct ChunkRegs8 {
 // tiles through an empty descriptor, nontemporal).
 template <int BS, int D>
 __device__ __forceinline__ void load_chunk(ChunkRegs8<D>& r, const char* kbase, const char* vbase,
-                                           int2 pb, int r0, bool live0, bool live1, int kvh,
-                                           int num_kv_heads, uint32_t koff, uint32_t voff) {
+                                           BlockIds<BS> pb, int r0, bool live0, bool live1,
+                                           int kvh, int num_kv_heads, uint32_t koff,
+                                           uint32_t voff) {
     constexpr int RB = D;         // bytes per token row
     constexpr int kTile = 16 * RB;
+    if constexpr (lane_addressed<BS, D>()) {
+        const int lane = threadIdx.x & 63;
+        load_chunk_lanes<BS, RB, D / 64, 16>(r, kbase, vbase, pb, r0, live0, live1, kvh,
+                                             num_kv_heads, koff - (lane & 15) * RB,
+                                             voff - 4 * (lane >> 4) * RB);
+    } else {
     const uint64_t row0 = kv_row(pb.x, kvh, r0, num_kv_heads, BS) * RB;
     const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : r0 + 16, num_kv_heads, BS) * RB;
     const __amdgpu_buffer_rsrc_t k0 = tile_rsrc<kTile>(kbase + row0, live0);
@@ -208,6 +319,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs8<D>& r, const char* kbase, 
     for (int i = 0; i < 4; ++i) load_row(r.v[i], v0, voff + i * RB);
 #pragma unroll
     for (int i = 0; i < 4; ++i) load_row(r.v[4 + i], v1, voff + i * RB);
+    }
 }
 
 // Two E4M3 codes (the low or the high half of w) -> two 16-bit values,
@@ -226,6 +338,11 @@ __device__ __forceinline__ u32x4 e4m3_eight(uint32_t w0, uint32_t w1) {
                    e4m3_pair<false>(Tag(), w1), e4m3_pair<true>(Tag(), w1)};
 }
 // One V row slice of E4M3 codes -> the 16-bit slice.
+template <typename Tag>
+__device__ __forceinline__ u32x8 e4m3_row(u32x4 w) {
+    return __builtin_shufflevector(e4m3_eight<Tag>(w[0], w[1]), e4m3_eight<Tag>(w[2], w[3]), 0,
+                                   1, 2, 3, 4, 5, 6, 7);
+}
 template <typename Tag>
 __device__ __forceinline__ u32x4 e4m3_row(u32x2 w) { return e4m3_eight<Tag>(w[0], w[1]); }
 template <typename Tag>
@@ -435,6 +552,68 @@ __device__ __forceinline__ void compute(WaveState<D>& st, KvRegs<Kv, D>& r, cons
     }
 }
 
+// The wavefront's chunks chunk_of(0 .. K-1) (K >= 1) of one (decode row,
+// KV head): loads and math.  Two register buffers (head_dim 64 and 128):
+// while chunk k is computed, chunk k+1's loads are in flight and chunk
+// k+2's block numbers are being fetched (scalar loads of the table).  At
+// head_dim 256 a chunk's operands take 128 registers, so there is one
+// buffer; only the next chunk's block numbers are fetched ahead, and the
+// other wavefronts of the compute unit keep its loads in flight.
+template <typename Tag, int BS, typename Kv, bool kCols, int D, typename ChunkOf>
+__device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>& st, int K,
+                                              ChunkOf chunk_of, const ConstI32* row, int L,
+                                              int kvh, uint32_t koff, uint32_t voff,
+                                              const u32x4* qop, int t_end, int t_col, int t_lo,
+                                              int q, int& bad) {
+    const char* kbase = reinterpret_cast<const char*>(a.key_cache);
+    const char* vbase = reinterpret_cast<const char*>(a.value_cache);
+    const float sl2 = a.scale_log2;
+    // tile 1 of chunk c is live when it holds history tokens
+    auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
+    if constexpr (D == 256) {
+        BlockIds<BS> ids = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
+        for (int k = 0; k < K; ++k) {
+            KvRegs<Kv, D> buf;
+            load_chunk<BS, D>(buf, kbase, vbase, ids, tile_row<BS>(chunk_of(k)), true,
+                              tile1_live(k), kvh, a.num_kv_heads, koff, voff);
+            ids = chunk_blocks<BS>(row, chunk_of(k + 1), L, a.num_blocks, bad);
+            compute<Tag, Kv, kCols, D>(st, buf, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
+                                       t_lo, q);
+        }
+    } else {
+        KvRegs<Kv, D> bufA, bufB;
+        BlockIds<BS> idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
+        BlockIds<BS> idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
+        load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true,
+                          tile1_live(0), kvh, a.num_kv_heads, koff, voff);
+        int k = 0;
+        // The scheduling barriers keep each phase's loads after the previous
+        // chunk's math and before this chunk's: the load counter is in
+        // order, so a load hoisted above the math would make it wait for
+        // the prefetch too.  A prefetch past the wave's last chunk is issued
+        // dead (no bytes move) so that every path has the same loads in
+        // flight.
+        for (;;) {
+            __builtin_amdgcn_sched_barrier(0);
+            load_chunk<BS, D>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
+                              k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
+            idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
+            __builtin_amdgcn_sched_barrier(0);
+            compute<Tag, Kv, kCols, D>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
+                                       t_lo, q);
+            if (++k >= K) break;
+            __builtin_amdgcn_sched_barrier(0);
+            load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
+                              k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
+            idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
+            __builtin_amdgcn_sched_barrier(0);
+            compute<Tag, Kv, kCols, D>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
+                                       t_lo, q);
+            if (++k >= K) break;
+        }
+    }
+}
+
 // This lane's accumulators (column n = lane % 16, d = VW (4 q + i) + j in
 // acc[j][i]) -> an LDS row of the column (float offsets 4 q VW + VW i + j).
 template <int D>
@@ -490,13 +669,10 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
     u32x4 qop[Dim<D>::KD];
     load_query<Kv, kCols, D>(a, b, kvh, n, q, ntok * G, qop);
 
-    const char* kbase = reinterpret_cast<const char*>(a.key_cache);
-    const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
         (const ConstI32*)(a.block_tables) + table_row_offset<kRows>(a, b);
     const uint32_t koff = lane_koff<Kv, D>(n, q);
     const uint32_t voff = lane_voff<Kv, D>(n, q);
-    const float sl2 = a.scale_log2;
 
     // Append step: the wave that will read the chunk holding the newest
     // history position (L - 1) first stores that token's K/V row there.  Its
@@ -513,45 +689,13 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
     init_state(st);
     int bad = 0;
 
-    // This wave's chunks are c0 + wave + kNW k, k < K.  Two register buffers:
-    // while chunk k is computed, chunk k+1's loads are in flight and chunk
-    // k+2's block numbers are being fetched (scalar loads of the table).
+    // This wave's chunks are c0 + wave + kNW k, k < K.
     const int first = c0 + wave;
     const int K = first < c1 ? (c1 - first + kNW - 1) / kNW : 0;
     if (K > 0) {
-        auto chunk_of = [&](int k) { return first + kNW * min(k, K - 1); };
-        // tile 1 of chunk c is live when it holds history tokens
-        auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
-        KvRegs<Kv, D> bufA, bufB;
-        int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
-        int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
-        load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true,
-                          tile1_live(0), kvh, a.num_kv_heads, koff, voff);
-        int k = 0;
-        // The scheduling barriers keep each phase's loads after the previous
-        // chunk's math and before this chunk's: the load counter is in
-        // order, so a load hoisted above the math would make it wait for
-        // the prefetch too.  A prefetch past the wave's last chunk is issued
-        // dead (no bytes move) so that every path has the same loads in
-        // flight.
-        for (;;) {
-            __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS, D>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
-                              k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
-            idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
-            __builtin_amdgcn_sched_barrier(0);
-            compute<Tag, Kv, kCols, D>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
-                                       t_lo, q);
-            if (++k >= K) break;
-            __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
-                              k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
-            idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
-            __builtin_amdgcn_sched_barrier(0);
-            compute<Tag, Kv, kCols, D>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
-                                       t_lo, q);
-            if (++k >= K) break;
-        }
+        auto chunk_of = [=](int k) { return first + kNW * min(k, K - 1); };
+        stream_chunks<Tag, BS, Kv, kCols, D>(a, st, K, chunk_of, row, L, kvh, koff, voff, qop,
+                                             t_end, t_col, t_lo, q, bad);
     }
 
     if (q == 0) {
@@ -569,8 +713,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
 // The partition index varies slowest, so every sequence's first (full)
 // partition is dispatched before any shorter trailing one.
 template <typename Tag, int BS, typename Kv, int kRows, int D>
-__global__ __launch_bounds__(kDecodeThreads)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void decode_mfma_fixed(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a) {
     __shared__ SegmentLds<D> sm;
     const int kvh = blockIdx.x;
     const int b = blockIdx.y;
@@ -641,13 +784,10 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
     u32x4 qop[Dim<D>::KD];
     load_query<Kv, kCols, D>(a, b, kvh, n, q, ntok * G, qop);
 
-    const char* kbase = reinterpret_cast<const char*>(a.key_cache);
-    const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const ConstI32* row =
         (const ConstI32*)(a.block_tables) + table_row_offset<kRows>(a, b);
     const uint32_t koff = lane_koff<Kv, D>(n, q);
     const uint32_t voff = lane_voff<Kv, D>(n, q);
-    const float sl2 = a.scale_log2;
 
     if (a.new_key != nullptr) {
         const int c_last = (L - 1) / kChunk;
@@ -656,32 +796,9 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
     }
 
     const int K = ce - cs;
-    auto chunk_of = [&](int k) { return cs + min(k, K - 1); };
-    auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
-    KvRegs<Kv, D> bufA, bufB;
-    int2 idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
-    int2 idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
-    load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true, tile1_live(0),
-                      kvh, a.num_kv_heads, koff, voff);
-    int k = 0;
-    for (;;) {
-        __builtin_amdgcn_sched_barrier(0);
-        load_chunk<BS, D>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
-                          k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
-        idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
-        __builtin_amdgcn_sched_barrier(0);
-        compute<Tag, Kv, kCols, D>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo,
-                                   q);
-        if (++k >= K) break;
-        __builtin_amdgcn_sched_barrier(0);
-        load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
-                          k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
-        idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
-        __builtin_amdgcn_sched_barrier(0);
-        compute<Tag, Kv, kCols, D>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col, t_lo,
-                                   q);
-        if (++k >= K) break;
-    }
+    auto chunk_of = [=](int k) { return cs + min(k, K - 1); };
+    stream_chunks<Tag, BS, Kv, kCols, D>(a, st, K, chunk_of, row, L, kvh, koff, voff, qop, t_end,
+                                         t_col, t_lo, q, bad);
 }
 
 // Output rows of a whole history held by one wavefront: o = õ / l for the
@@ -706,10 +823,14 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, 
         float o[VW];
 #pragma unroll
         for (int j = 0; j < VW; ++j) o[j] = bad ? __builtin_nanf("") : vs * (st.acc[j][i] / l);
-        if constexpr (VW == 8) {
-            const u32x4 v = {pack2(Tag(), o[0], o[1]), pack2(Tag(), o[2], o[3]),
-                             pack2(Tag(), o[4], o[5]), pack2(Tag(), o[6], o[7])};
-            *reinterpret_cast<u32x4*>(orow + 2 * VW * i) = v;
+        if constexpr (VW >= 8) {
+#pragma unroll
+            for (int j0 = 0; j0 < VW; j0 += 8) {
+                const u32x4 v = {pack2(Tag(), o[j0], o[j0 + 1]), pack2(Tag(), o[j0 + 2], o[j0 + 3]),
+                                 pack2(Tag(), o[j0 + 4], o[j0 + 5]),
+                                 pack2(Tag(), o[j0 + 6], o[j0 + 7])};
+                *reinterpret_cast<u32x4*>(orow + 2 * VW * i + 2 * j0) = v;
+            }
         } else {
             const u32x2 v = {pack2(Tag(), o[0], o[1]), pack2(Tag(), o[2], o[3])};
             *reinterpret_cast<u32x2*>(orow + 2 * VW * i) = v;
@@ -788,8 +909,7 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
 extern __shared__ int balanced_pref[];
 
 template <typename Tag, int BS, typename Kv, int kRows, int D>
-__global__ __launch_bounds__(kDecodeThreads)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 1))) void decode_mfma_balanced(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
     constexpr bool kCols = kRows == 1;
     constexpr int OS = Dim<D>::OS;
     __shared__ EdgeLds<D> edge;
@@ -919,6 +1039,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
 template <typename Tag, int D>
 hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
     switch (a.block_size) {
+        case 8: return launch_typed<Tag, 8, D>(a, s);
         case 16: return launch_typed<Tag, 16, D>(a, s);
         case 32: return launch_typed<Tag, 32, D>(a, s);
         default: return launch_typed<Tag, 64, D>(a, s);
@@ -927,21 +1048,29 @@ hipError_t launch_bs(const DecodeArgs& a, hipStream_t s) {
 
 template <typename Tag>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
-    return a.head_dim == 64 ? launch_bs<Tag, 64>(a, s) : launch_bs<Tag, 128>(a, s);
+    switch (a.head_dim) {
+        case 64: return launch_bs<Tag, 64>(a, s);
+        case 128: return launch_bs<Tag, 128>(a, s);
+        default: return launch_bs<Tag, 256>(a, s);
+    }
 }
 
 }  // namespace
 
 bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group) {
-    return (dt == PA_BF16 || dt == PA_F16) && (head_dim == 64 || head_dim == 128) &&
-           (block_size == 16 || block_size == 32 || block_size == 64) && group >= 1 &&
+    return (dt == PA_BF16 || dt == PA_F16) &&
+           (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
+           (block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64) &&
+           group >= 1 &&
            group <= 16;
 }
 
-// Workgroups of the matrix-core kernel one compute unit holds at once: two at
-// head_dim 128, four at head_dim 64 (half the registers and LDS each), so
-// the bytes in flight per compute unit are the same.
-int mfma_workgroups_per_cu(int head_dim) { return head_dim == 64 ? 4 : 2; }
+// Workgroups of the balanced schedule per compute unit: one (4 wavefronts,
+// one per SIMD).  One wavefront's two chunk buffers per SIMD already keep the
+// compute unit at its share of the HBM bandwidth; more, smaller ranges only
+// add split segments, partial states and merge work (measured: two per
+// compute unit is 2.5 % slower at head_dim 128, four 4 % slower at 64).
+int mfma_workgroups_per_cu(int) { return 1; }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s) {
     return dt == PA_BF16 ? launch_d<BF16>(a, s) : launch_d<F16>(a, s);

@@ -138,12 +138,15 @@ __global__ __launch_bounds__(kMaxGroup * D / 4) void merge_balanced(DecodeArgs a
 template <typename Tag>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
+        const dim3 grid(a.num_wg + a.num_seqs);
         if (a.head_dim == 64)
-            hipLaunchKernelGGL((merge_balanced<Tag, 64>), dim3(a.num_wg + a.num_seqs),
-                               dim3(kMaxGroup * 64 / 4), 0, s, a);
+            hipLaunchKernelGGL((merge_balanced<Tag, 64>), grid, dim3(kMaxGroup * 64 / 4), 0, s, a);
+        else if (a.head_dim == 128)
+            hipLaunchKernelGGL((merge_balanced<Tag, 128>), grid, dim3(kMaxGroup * 128 / 4), 0, s,
+                               a);
         else
-            hipLaunchKernelGGL((merge_balanced<Tag, 128>), dim3(a.num_wg + a.num_seqs),
-                               dim3(kMaxGroup * 128 / 4), 0, s, a);
+            hipLaunchKernelGGL((merge_balanced<Tag, 256>), grid, dim3(kMaxGroup * 256 / 4), 0, s,
+                               a);
     } else {
         hipLaunchKernelGGL((merge_fixed<Tag>), dim3(a.num_kv_heads, a.num_seqs),
                            dim3(kMergeThreads), 0, s, a);

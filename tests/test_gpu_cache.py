@@ -120,12 +120,14 @@ def test_decode_append_equals_write_then_decode(name, kernel, partition_size):
     assert torch.equal(d1["value_cache"], d2["value_cache"])
 
 
+@pytest.mark.parametrize("head_dim", [64, 256])
 @pytest.mark.parametrize("partition_size", [0, 256])
-def test_decode_append_head_dim_64_equals_write_then_decode(partition_size):
-    """The matrix-core kernel's own append step at head_dim 64 (8 lanes per
-    row) against reshape_and_cache followed by decode, bit for bit."""
+def test_decode_append_other_head_dims_equals_write_then_decode(partition_size, head_dim):
+    """The matrix-core kernel's own append step at head_dim 64 and 256 (8 and
+    32 lanes per row) against reshape_and_cache followed by decode, bit for
+    bit."""
     cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_seqs=12, num_blocks=4000,
-                           head_dim=64)
+                           head_dim=head_dim)
     inp = I.generate(cfg, new_tokens_at="last")
     d1 = upload(inp)
     ops.reshape_and_cache(d1["new_key"], d1["new_value"], d1["key_cache"], d1["value_cache"],

@@ -59,8 +59,16 @@ SMALL_CASES = [
     ("f32", 1, 12, 128, 16, ops.KERNEL_GENERIC),
     # block sizes 8 and 64, head_dim 256
     ("bf16", 2, 7, 128, 64, ops.KERNEL_MFMA),
-    ("f16", 2, 4, 128, 8, ops.KERNEL_AUTO),         # block size 8: vector-ALU kernel
-    ("bf16", 2, 4, 256, 16, ops.KERNEL_AUTO),       # head_dim 256: vector-ALU kernel
+    ("f16", 2, 4, 128, 8, ops.KERNEL_AUTO),         # block size 8: matrix-core kernel
+    ("bf16", 2, 7, 128, 8, ops.KERNEL_MFMA),
+    ("bf16", 1, 8, 64, 8, ops.KERNEL_MFMA),
+    ("f16", 2, 4, 256, 8, ops.KERNEL_MFMA),
+    ("bf16", 2, 7, 128, 8, ops.KERNEL_GENERIC),
+    ("bf16", 2, 4, 256, 16, ops.KERNEL_AUTO),       # head_dim 256: matrix-core kernel
+    ("f16", 2, 7, 256, 32, ops.KERNEL_MFMA),
+    ("bf16", 1, 16, 256, 64, ops.KERNEL_MFMA),
+    ("bf16", 3, 1, 256, 16, ops.KERNEL_MFMA),
+    ("bf16", 2, 4, 256, 16, ops.KERNEL_GENERIC),
     ("f32", 2, 2, 256, 64, ops.KERNEL_GENERIC),
     ("bf16", 1, 8, 64, 8, ops.KERNEL_GENERIC),
     ("f16", 2, 3, 64, 64, ops.KERNEL_GENERIC),
@@ -88,7 +96,8 @@ def test_kernels_agree():
 
 def test_single_token_history_is_v0_exactly():
     for dtype, D, kernel in (("bf16", 128, ops.KERNEL_MFMA), ("f16", 128, ops.KERNEL_MFMA),
-                             ("bf16", 64, ops.KERNEL_MFMA), ("f32", 64, ops.KERNEL_GENERIC),
+                             ("bf16", 64, ops.KERNEL_MFMA), ("bf16", 256, ops.KERNEL_MFMA),
+                             ("f32", 64, ops.KERNEL_GENERIC),
                              ("bf16", 128, ops.KERNEL_GENERIC)):
         inp = I.generate(small_config(dtype, 2, 4, D, 16, (1, 1, 1)))
         out = run_decode(upload(inp), kernel).cpu()
@@ -109,9 +118,10 @@ def test_empty_history_gives_zeros():
         compare(out, ref, "bf16", what="with empty row")
 
 
-def test_invalid_device_data_gives_nan_rows():
+@pytest.mark.parametrize("BS", [16, 8])
+def test_invalid_device_data_gives_nan_rows(BS):
     for kernel in (ops.KERNEL_MFMA, ops.KERNEL_GENERIC):
-        inp = I.generate(small_config("bf16", 2, 7, 128, 16, (40, 40, 40, 40)))
+        inp = I.generate(small_config("bf16", 2, 7, 128, BS, (40, 40, 40, 40)))
         inp.context_lens[1] = 10_000          # > max_context_len
         inp.context_lens[2] = -3
         inp.block_tables[3, 1] = 10_000_000   # outside the pool
@@ -132,13 +142,14 @@ def test_permutation_and_block_size_invariance_bitwise():
         assert torch.equal(out, base), "layout (bs=%d, seed=%d) changed the result" % (bs, seed)
 
 
-@pytest.mark.parametrize("D", [128, 64])
+@pytest.mark.parametrize("D", [128, 64, 256])
 def test_balanced_schedule_layout_invariance_bitwise(D):
     """The balanced schedule's work split depends on lengths only, so moving
-    the history to other physical blocks, or to blocks of 32, changes no bit."""
+    the history to other physical blocks, or to blocks of 8, 32 or 64, changes
+    no bit."""
     inp = I.generate(small_config("bf16", 2, 7, D, 16, RAGGED + (2000, 3000), seed=12))
     base = run_decode(upload(inp), ops.KERNEL_MFMA, 0).cpu()
-    for bs, seed in ((16, 4), (32, 5)):
+    for bs, seed in ((16, 4), (32, 5), (8, 6), (64, 7)):
         kc, vc, bt = same_history_other_layout(inp, bs, seed)
         d = dict(query=inp.query.to(DEV), key_cache=kc.to(DEV), value_cache=vc.to(DEV),
                  block_tables=bt.to(DEV), context_lens=inp.context_lens.to(DEV))

@@ -82,7 +82,9 @@ def test_fp8_cache_write_bit_exact(src, scales):
 
 CASES = [("bf16", 2, 7, 128, 16), ("bf16", 2, 4, 128, 32), ("f16", 2, 4, 128, 16),
          ("bf16", 1, 16, 128, 16), ("f16", 3, 1, 128, 32), ("bf16", 2, 7, 128, 64),
-         ("bf16", 2, 7, 64, 16), ("f16", 2, 4, 64, 32), ("bf16", 1, 16, 64, 64)]
+         ("bf16", 2, 7, 64, 16), ("f16", 2, 4, 64, 32), ("bf16", 1, 16, 64, 64),
+         ("bf16", 2, 7, 256, 16), ("f16", 1, 8, 256, 32), ("bf16", 2, 7, 128, 8),
+         ("f16", 2, 4, 64, 8)]
 
 
 @pytest.mark.parametrize("partition_size", [0, 64, 256])
@@ -118,7 +120,7 @@ def test_fp8_float8_tensor_type_and_errors():
         ops.select_kernel(prev)
 
 
-@pytest.mark.parametrize("head_dim", [128, 64])
+@pytest.mark.parametrize("head_dim", [128, 64, 256])
 @pytest.mark.parametrize("partition_size", [0, 256])
 def test_fp8_decode_append_equals_write_then_decode(partition_size, head_dim):
     cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_seqs=12, num_blocks=4000,
