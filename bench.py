@@ -223,8 +223,9 @@ def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture
     """Verify step (pa_paged_attention_verify) on the same workload: q_len new
     query tokens per sequence, K calls replayed from a HIP graph.  The
     matrix-core kernel serves 16 // G query tokens of a sequence per pass over
-    its K/V (their (token, head) pairs are its 16 columns), so a call reads
-    the histories ceil(q_len / (16 // G)) times."""
+    its K/V (their (token, head) pairs are its 16 columns), or 32 // G with
+    two column tiles when q_len * G > 16 (head_dim 64 and 128), so a call
+    reads the histories ceil(q_len / tokens per pass) times."""
     import math
     import numpy as np
     import torch
@@ -251,14 +252,16 @@ def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture
     us = np.array([timed_replay(g)[1] / args.steps * 1e6 for _ in range(3)])
     del g
     t = float(us.mean()) * 1e-6
-    per_pass = max(1, 16 // (H // H_kv))
+    G = H // H_kv
+    cols = 32 if q_len * G > 16 and D <= 128 else 16
+    per_pass = max(1, cols // G)
     passes = math.ceil(q_len / per_pass)
     read = alg_bytes * passes       # histories read once per pass (to first order)
     return {"query_tokens_per_seq": q_len, "call_us_mean": t * 1e6,
             "verified_tokens_per_s": S * q_len / t, "alg_bytes_per_launch": alg_bytes,
             "kv_passes": passes, "kv_bytes_read_approx": read, "read_gbps": read / t / 1e9,
             "note": "%d query tokens of a sequence share a pass over its K/V "
-                    "(%d (token, head) columns of 16)" % (per_pass, per_pass * (H // H_kv))}
+                    "(%d (token, head) columns of %d)" % (per_pass, per_pass * G, cols)}
 
 
 def shape_sweep(args, dev):

@@ -245,11 +245,12 @@ int pa_reshape_and_cache(const void* key, const void* value,
  *
  * Rows of a sequence with q_b > max_query_len, q_b > L_b or an invalid L_b,
  * and rows outside every sequence's range, are NaN.  On the matrix-core
- * kernel up to 16 / G query rows of a sequence share one pass over its K/V
- * (their (row, head) pairs are the 16 columns of its tiles, each column
- * masked at its own causal end), so the K/V of a sequence is read
- * ceil(q_b / (16 / G)) times; the vector-ALU kernel reduces each query row
- * on its own.
+ * kernel up to u = 16 / G query rows of a sequence share one pass over its
+ * K/V (their (row, head) pairs are the 16 columns of its tiles, each column
+ * masked at its own causal end), or u = 32 / G with two column tiles when
+ * max_query_len * G > 16 and head_dim is 64 or 128; the K/V of a sequence
+ * is read ceil(q_b / u) times.  The vector-ALU kernel reduces each query
+ * row on its own.
  */
 size_t pa_verify_workspace_size(int total_queries, int num_heads, int num_kv_heads,
                                 int head_dim, int block_size, int max_context_len,

@@ -94,11 +94,12 @@ Layout fixed_layout(int num_seqs, int num_heads, int head_dim, int max_context_l
     return l;
 }
 
-// Balanced schedule: two slots per workgroup of kMaxGroup heads each, and
-// one 16-byte record per workgroup.
-Layout balanced_layout(int head_dim) {
+// Balanced schedule: two slots per workgroup of `cols` columns each (16, or
+// 32 for verify rows with two column tiles), and one 16-byte record per
+// workgroup.
+Layout balanced_layout(int head_dim, int cols = pa::kMaxGroup) {
     Layout l;
-    const size_t rows = (size_t)pa::kMaxBalancedWg * 2 * pa::kMaxGroup;
+    const size_t rows = (size_t)pa::kMaxBalancedWg * 2 * cols;
     l.lse_off = 0;
     l.out_off = align256(rows * sizeof(float));
     l.meta_off = l.out_off + align256(rows * head_dim * sizeof(float));
@@ -217,7 +218,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                        void* workspace, size_t workspace_bytes, void* hip_stream,
                        int kv_format = pa::kKvSame, float k_scale = 1.0f, float v_scale = 1.0f,
                        const int32_t* table_rows = nullptr, const int32_t* row_tokens = nullptr,
-                       int kernel_kind = -1) {
+                       int kernel_kind = -1, int col_tiles = 1) {
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
     const bool e4m3 = kv_format == pa::kKvE4M3;
     if (e4m3 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
@@ -273,7 +274,9 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     const int P = partition_size ? partition_size
                                  : heuristic_partition(num_seqs, num_kv_heads, block_size,
                                                        max_context_len);
-    const Layout lay = balanced ? balanced_layout(head_dim)
+    if (col_tiles != 1 && !(col_tiles == 2 && use_mfma && head_dim <= 128 && table_rows))
+        return fail(PA_ERR_INVALID_ARG, "two column tiles serve matrix-core verify rows only");
+    const Layout lay = balanced ? balanced_layout(head_dim, pa::kMaxGroup * col_tiles)
                                 : fixed_layout(num_seqs, num_heads, head_dim, max_context_len, P);
     const bool needs_ws = lay.bytes > 0;
     if (needs_ws) {
@@ -313,6 +316,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     a.num_parts = balanced ? 1 : lay.num_parts;
     a.schedule = balanced ? pa::kBalanced : pa::kFixed;
     a.num_wg = balanced ? balanced_workgroups(head_dim) : 0;
+    a.col_tiles = col_tiles;
     // scale * log2(e), and the key scale of an FP8 cache folded into it
     a.scale_log2 = (float)((double)scale * 1.4426950408889634 * (e4m3 ? (double)k_scale : 1.0));
     a.kv_format = e4m3 ? pa::kKvE4M3 : pa::kKvSame;
@@ -437,7 +441,11 @@ size_t pa_verify_workspace_size(int total_queries, int num_heads, int num_kv_hea
                                                 block_size, max_context_len, partition_size,
                                                 dtype);
     if (dec == (size_t)-1) return dec;
-    return align256(dec) + 3 * align256((size_t)total_queries * sizeof(int32_t));
+    // room for the 32-column slots of two column tiles (head_dim <= 128)
+    const size_t bal = head_dim <= 128 && partition_size == 0 && max_context_len > 0
+                           ? balanced_layout(head_dim, 2 * pa::kMaxGroup).bytes
+                           : 0;
+    return align256(std::max(dec, bal)) + 3 * align256((size_t)total_queries * sizeof(int32_t));
 }
 
 int pa_paged_attention_verify(void* out, const void* query, const void* key_cache,
@@ -472,13 +480,19 @@ int pa_paged_attention_verify(void* out, const void* query, const void* key_cach
     if (!context_lens) return fail(PA_ERR_INVALID_ARG, "null context_lens");
     if (gqa_group_size < 1) return fail(PA_ERR_INVALID_ARG, "gqa_group_size must be positive");
     // The matrix-core kernel serves up to 16 / G query rows of a sequence in
-    // one pass over its K/V (their (row, head) pairs fill its 16 columns);
-    // the vector-ALU kernel takes one row per pass.  The kernel family is
-    // chosen once here, so the grouping and the decode launch agree.
+    // one pass over its K/V (their (row, head) pairs fill its 16 columns), or
+    // 32 / G with two column tiles when a sequence may hold more (head_dim
+    // 64 and 128); the vector-ALU kernel takes one row per pass.  The kernel
+    // family is chosen once here, so the grouping and the decode launch
+    // agree.
     const int kind = g_kernel_kind.load();
     const bool mfma = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size) &&
                       kind != pa::kGeneric;
-    const int u = mfma ? std::max(1, pa::kMaxGroup / gqa_group_size) : 1;
+    const int nt = mfma && head_dim <= 128 &&
+                           (int64_t)max_query_len * gqa_group_size > pa::kMaxGroup
+                       ? 2
+                       : 1;
+    const int u = mfma ? std::max(1, pa::kMaxGroup * nt / gqa_group_size) : 1;
     hipError_t e = pa::launch_verify_rows(query_start, context_lens, num_seqs, total_queries,
                                           max_query_len, max_context_len, u, rows, lens, toks,
                                           static_cast<hipStream_t>(hip_stream));
@@ -487,7 +501,7 @@ int pa_paged_attention_verify(void* out, const void* query, const void* key_cach
                        total_queries, num_heads, num_kv_heads, gqa_group_size, head_dim,
                        block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
                        partition_size, dec > 0 ? workspace : nullptr, dec, hip_stream,
-                       pa::kKvSame, 1.0f, 1.0f, rows, toks, kind);
+                       pa::kKvSame, 1.0f, 1.0f, rows, toks, kind, nt);
 }
 
 int pa_reshape_and_cache(const void* key, const void* value, void* key_cache, void* value_cache,

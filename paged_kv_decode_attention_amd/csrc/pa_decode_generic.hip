@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
         }
     }
     __syncthreads();
-    finalize_state<Tag>(a, sm_m, sm_l, sm_o, NW, GT * D, D, b, kvh, g0, nh, bad,
+    finalize_state<Tag>(a, sm_m, sm_l, sm_o, NW, 16, GT * D, D, b, kvh, g0, nh, bad,
                         nparts_b == 1 ? -1 : part);
 }
 

@@ -468,26 +468,31 @@ constexpr float kLazy = 8.0f;
 
 // Tokens at or past t_end (the end of the history, or of the piece) are
 // excluded.  With verify columns (kCols) column n's causal end t_col (this
-// lane's column) may lie before t_end; t_lo is the smallest column end of the
-// wavefront.  A column that has seen no token yet has m_ref = -inf: its
-// weights are then 2^(-inf) = 0 and its rescale factor 0.
-template <typename Tag, bool kCols, int D>
-__device__ __forceinline__ void compute_chunk(WaveState<D>& st, ChunkRegs<D>& r, const u32x4* qop,
-                                              float sl2, int tc, int t_end, int t_col, int t_lo,
-                                              int q) {
+// lane's column in tile t) may lie before t_end; t_lo is the smallest column
+// end of the wavefront.  A column that has seen no token yet has m_ref =
+// -inf: its weights are then 2^(-inf) = 0 and its rescale factor 0.  NT
+// column tiles (16 columns each) share the chunk's K and V operands: st,
+// qop (KD per tile) and t_col hold one entry per tile.
+template <typename Tag, bool kCols, int D, int NT>
+__device__ __forceinline__ void compute_chunk(WaveState<D>* st, ChunkRegs<D>& r, const u32x4* qop,
+                                              float sl2, int tc, int t_end, const int* t_col,
+                                              int t_lo, int q) {
     constexpr int KD = Dim<D>::KD;
     constexpr int VW = Dim<D>::VW;
-    // Scores: S^T[token][head] for the two 16-token tiles.
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    // Scores: S^T[token][column] for the two 16-token tiles.
+    float s[NT][8];
 #pragma unroll
-    for (int kk = 0; kk < KD; ++kk) s0 = mfma16x16x32(Tag(), r.k0[kk], qop[kk], s0);
+    for (int t = 0; t < NT; ++t) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < KD; ++kk) s1 = mfma16x16x32(Tag(), r.k1[kk], qop[kk], s1);
-    float s[8];
+        for (int kk = 0; kk < KD; ++kk) s0 = mfma16x16x32(Tag(), r.k0[kk], qop[t * KD + kk], s0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        s[i] = s0[i] * sl2;
-        s[4 + i] = s1[i] * sl2;
+        for (int kk = 0; kk < KD; ++kk) s1 = mfma16x16x32(Tag(), r.k1[kk], qop[t * KD + kk], s1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[t][i] = s0[i] * sl2;
+            s[t][4 + i] = s1[i] * sl2;
+        }
     }
     if (tc + kChunk > (kCols ? t_lo : t_end)) {
         // Tokens at or past the end of the history are excluded (the last
@@ -495,38 +500,46 @@ __device__ __forceinline__ void compute_chunk(WaveState<D>& st, ChunkRegs<D>& r,
         // row zeroed so stale slot contents cannot reach the accumulator.
         // A verify column's tokens past its causal end only get score -inf
         // (their V rows hold data other columns use).
-        const int t_s = kCols ? t_col : t_end;
         using VRow = typename Dim<D>::VRow;
         const VRow zero = {};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (tc + 4 * q + i >= t_s) s[i] = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int t_s = kCols ? t_col[t] : t_end;
+                if (tc + 4 * q + i >= t_s) s[t][i] = -INFINITY;
+                if (tc + 16 + 4 * q + i >= t_s) s[t][4 + i] = -INFINITY;
+            }
             if (tc + 4 * q + i >= t_end) r.v[i] = zero;
-            if (tc + 16 + 4 * q + i >= t_s) s[4 + i] = -INFINITY;
             if (tc + 16 + 4 * q + i >= t_end) r.v[4 + i] = zero;
         }
     }
-    float cmax = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
-                       fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    // Online softmax update ([MiniPaged-Qwen] §5.2), with the rescale of the
-    // accumulators deferred until the running max has grown by 2^kLazy.
-    if (__any(cmax > st.m_ref + kLazy)) {
-        const float m_new = fmaxf(st.m_ref, cmax);
-        const float alpha = kCols ? rescale_weight(st.m_ref, m_new) : fast_exp2(st.m_ref - m_new);
-#pragma unroll
-        for (int j = 0; j < VW; ++j) st.acc[j] *= alpha;
-        st.acc_l *= alpha;
-        st.m_ref = m_new;
-    }
-    const float m_ref = (kCols && st.m_ref == -INFINITY) ? 0.0f : st.m_ref;
-    u32x4 pop;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-        pop[u] = pack2(Tag(), fast_exp2(s[2 * u] - m_ref), fast_exp2(s[2 * u + 1] - m_ref));
     const u32x4 ones = {kOnePair<Tag>(), kOnePair<Tag>(), kOnePair<Tag>(), kOnePair<Tag>()};
-    st.acc_l = mfma16x16x32(Tag(), ones, pop, st.acc_l);
+    u32x4 pop[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float cmax = fmaxf(fmaxf(fmaxf(s[t][0], s[t][1]), fmaxf(s[t][2], s[t][3])),
+                           fmaxf(fmaxf(s[t][4], s[t][5]), fmaxf(s[t][6], s[t][7])));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        // Online softmax update ([MiniPaged-Qwen] §5.2), with the rescale of
+        // the accumulators deferred until the running max has grown by 2^kLazy.
+        WaveState<D>& w = st[t];
+        if (__any(cmax > w.m_ref + kLazy)) {
+            const float m_new = fmaxf(w.m_ref, cmax);
+            const float alpha = kCols ? rescale_weight(w.m_ref, m_new) : fast_exp2(w.m_ref - m_new);
+#pragma unroll
+            for (int j = 0; j < VW; ++j) w.acc[j] *= alpha;
+            w.acc_l *= alpha;
+            w.m_ref = m_new;
+        }
+        const float m_ref = (kCols && w.m_ref == -INFINITY) ? 0.0f : w.m_ref;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            pop[t][u] = pack2(Tag(), fast_exp2(s[t][2 * u] - m_ref),
+                              fast_exp2(s[t][2 * u + 1] - m_ref));
+        w.acc_l = mfma16x16x32(Tag(), ones, pop[t], w.acc_l);
+    }
 #pragma unroll
     for (int j = 0; j < VW; ++j) {
         // V^T operand for d = VW n + j: 16-bit element j of each of the 8 rows.
@@ -535,20 +548,21 @@ __device__ __forceinline__ void compute_chunk(WaveState<D>& st, ChunkRegs<D>& r,
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             w[u] = __builtin_amdgcn_perm(r.v[2 * u + 1][j >> 1], r.v[2 * u][j >> 1], sel);
-        st.acc[j] = mfma16x16x32(Tag(), w, pop, st.acc[j]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) st[t].acc[j] = mfma16x16x32(Tag(), w, pop[t], st[t].acc[j]);
     }
 }
 
 // One chunk's math on either storage format.
-template <typename Tag, typename Kv, bool kCols, int D>
-__device__ __forceinline__ void compute(WaveState<D>& st, KvRegs<Kv, D>& r, const u32x4* qop,
-                                        float sl2, int tc, int t_end, int t_col, int t_lo,
+template <typename Tag, typename Kv, bool kCols, int D, int NT>
+__device__ __forceinline__ void compute(WaveState<D>* st, KvRegs<Kv, D>& r, const u32x4* qop,
+                                        float sl2, int tc, int t_end, const int* t_col, int t_lo,
                                         int q) {
     if constexpr (Kv::kE4M3) {
         ChunkRegs<D> ops = expand<Tag, D>(r);
-        compute_chunk<Tag, kCols, D>(st, ops, qop, sl2, tc, t_end, t_col, t_lo, q);
+        compute_chunk<Tag, kCols, D, NT>(st, ops, qop, sl2, tc, t_end, t_col, t_lo, q);
     } else {
-        compute_chunk<Tag, kCols, D>(st, r, qop, sl2, tc, t_end, t_col, t_lo, q);
+        compute_chunk<Tag, kCols, D, NT>(st, r, qop, sl2, tc, t_end, t_col, t_lo, q);
     }
 }
 
@@ -559,12 +573,12 @@ __device__ __forceinline__ void compute(WaveState<D>& st, KvRegs<Kv, D>& r, cons
 // head_dim 256 a chunk's operands take 128 registers, so there is one
 // buffer; only the next chunk's block numbers are fetched ahead, and the
 // other wavefronts of the compute unit keep its loads in flight.
-template <typename Tag, int BS, typename Kv, bool kCols, int D, typename ChunkOf>
-__device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>& st, int K,
+template <typename Tag, int BS, typename Kv, bool kCols, int D, int NT, typename ChunkOf>
+__device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>* st, int K,
                                               ChunkOf chunk_of, const ConstI32* row, int L,
                                               int kvh, uint32_t koff, uint32_t voff,
-                                              const u32x4* qop, int t_end, int t_col, int t_lo,
-                                              int q, int& bad) {
+                                              const u32x4* qop, int t_end, const int* t_col,
+                                              int t_lo, int q, int& bad) {
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const float sl2 = a.scale_log2;
@@ -577,7 +591,7 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>&
             load_chunk<BS, D>(buf, kbase, vbase, ids, tile_row<BS>(chunk_of(k)), true,
                               tile1_live(k), kvh, a.num_kv_heads, koff, voff);
             ids = chunk_blocks<BS>(row, chunk_of(k + 1), L, a.num_blocks, bad);
-            compute<Tag, Kv, kCols, D>(st, buf, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
+            compute<Tag, Kv, kCols, D, NT>(st, buf, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
                                        t_lo, q);
         }
     } else {
@@ -599,7 +613,7 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>&
                               k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
             idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
-            compute<Tag, Kv, kCols, D>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
+            compute<Tag, Kv, kCols, D, NT>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
                                        t_lo, q);
             if (++k >= K) break;
             __builtin_amdgcn_sched_barrier(0);
@@ -607,7 +621,7 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>&
                               k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
             idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
-            compute<Tag, Kv, kCols, D>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
+            compute<Tag, Kv, kCols, D, NT>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
                                        t_lo, q);
             if (++k >= K) break;
         }
@@ -630,20 +644,37 @@ __device__ __forceinline__ void stage_acc(float* col_row_lds, int q, const WaveS
 
 constexpr int kNW = kDecodeThreads / 64;   // wavefronts per workgroup
 
-template <int D>
+template <int D, int NT>
 struct SegmentLds {
-    float m[kNW * 16];
-    float l[kNW * 16];
-    __attribute__((aligned(16))) float o[kNW * 16 * Dim<D>::OS];
+    float m[kNW * 16 * NT];
+    float l[kNW * 16 * NT];
+    __attribute__((aligned(16))) float o[kNW * 16 * NT * Dim<D>::OS];
 };
+
+// Query operands and causal ends of the NT column tiles of this lane
+// (column t 16 + n of tile t): see load_query and compute_chunk.
+template <typename Kv, bool kCols, int D, int NT>
+__device__ __forceinline__ void tile_columns(const DecodeArgs& a, int b, int kvh, int n, int q,
+                                             int ntok, int L, int t_end, u32x4* qop,
+                                             int* t_col) {
+    const int G = a.group;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int col = t * 16 + n;
+        load_query<Kv, kCols, D>(a, b, kvh, col, q, ntok * G, qop + t * Dim<D>::KD);
+        // verify columns: column col attends the L - (ntok - 1 - col / G)
+        // oldest tokens
+        t_col[t] = kCols ? min(t_end, L - (ntok - 1 - col / G)) : t_end;
+    }
+}
 
 // All wavefronts of the workgroup attend chunks [c0, c1) of (decode row b,
 // KV head kvh) -- chunk c covers history tokens [32 c, 32 c + 32) -- with
 // the chunks dealt round-robin to the wavefronts, then merge their states
 // and write the result: the final output rows when the segment is the whole
 // history (part < 0), else partition state `part`.
-template <typename Tag, int BS, typename Kv, int kRows, int D>
-__device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D>& sm, int b,
+template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
+__device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D, NT>& sm, int b,
                                                int kvh, int L, int c0, int c1, int part) {
     constexpr bool kCols = kRows == 1;
     constexpr int OS = Dim<D>::OS;
@@ -662,12 +693,10 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
     const int n = lane & 15;
     const int q = lane >> 4;
     const int t_end = min(c1 * kChunk, L);
-    // verify columns: column n attends the L - (ntok - 1 - n / G) oldest tokens
     const int t_lo = kCols ? min(t_end, L - (ntok - 1)) : t_end;
-    const int t_col = kCols ? min(t_end, L - (ntok - 1 - n / G)) : t_end;
-
-    u32x4 qop[Dim<D>::KD];
-    load_query<Kv, kCols, D>(a, b, kvh, n, q, ntok * G, qop);
+    u32x4 qop[NT * Dim<D>::KD];
+    int t_col[NT];
+    tile_columns<Kv, kCols, D, NT>(a, b, kvh, n, q, ntok, L, t_end, qop, t_col);
 
     const ConstI32* row =
         (const ConstI32*)(a.block_tables) + table_row_offset<kRows>(a, b);
@@ -685,8 +714,9 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
             append_token<Tag, Kv, BS, D>(a, row, b, kvh, L - 1, lane);
     }
 
-    WaveState<D> st;
-    init_state(st);
+    WaveState<D> st[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) init_state(st[t]);
     int bad = 0;
 
     // This wave's chunks are c0 + wave + kNW k, k < K.
@@ -694,17 +724,22 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
     const int K = first < c1 ? (c1 - first + kNW - 1) / kNW : 0;
     if (K > 0) {
         auto chunk_of = [=](int k) { return first + kNW * min(k, K - 1); };
-        stream_chunks<Tag, BS, Kv, kCols, D>(a, st, K, chunk_of, row, L, kvh, koff, voff, qop,
-                                             t_end, t_col, t_lo, q, bad);
+        stream_chunks<Tag, BS, Kv, kCols, D, NT>(a, st, K, chunk_of, row, L, kvh, koff, voff,
+                                                 qop, t_end, t_col, t_lo, q, bad);
     }
 
-    if (q == 0) {
-        sm.m[wave * 16 + n] = st.m_ref;
-        sm.l[wave * 16 + n] = st.acc_l[0];
+    constexpr int NC = 16 * NT;   // columns per wavefront state
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int col = wave * NC + t * 16 + n;
+        if (q == 0) {
+            sm.m[col] = st[t].m_ref;
+            sm.l[col] = st[t].acc_l[0];
+        }
+        stage_acc<D>(sm.o + col * OS, q, st[t]);
     }
-    stage_acc<D>(sm.o + (wave * 16 + n) * OS, q, st);
     const bool any_bad = __syncthreads_or(bad);
-    finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, 16 * OS, OS, b, kvh, 0, ntok * G, any_bad,
+    finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, NC, NC * OS, OS, b, kvh, 0, ntok * G, any_bad,
                         part);
     __syncthreads();   // LDS is reused by the next segment
 }
@@ -712,9 +747,9 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
 // Fixed schedule: workgroup (kvh, b, part) takes tokens [part P, part P + P).
 // The partition index varies slowest, so every sequence's first (full)
 // partition is dispatched before any shorter trailing one.
-template <typename Tag, int BS, typename Kv, int kRows, int D>
+template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a) {
-    __shared__ SegmentLds<D> sm;
+    __shared__ SegmentLds<D, NT> sm;
     const int kvh = blockIdx.x;
     const int b = blockIdx.y;
     const int part = blockIdx.z;
@@ -734,7 +769,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
     const int c0 = t_begin / kChunk;
     const int c1 = min(L, t_begin + a.part_len);
     const int c1c = (c1 + kChunk - 1) / kChunk;
-    attend_segment<Tag, BS, Kv, kRows, D>(a, sm, b, kvh, L, c0, c1c, nparts_b == 1 ? -1 : part);
+    attend_segment<Tag, BS, Kv, kRows, D, NT>(a, sm, b, kvh, L, c0, c1c,
+                                              nparts_b == 1 ? -1 : part);
 }
 
 // ---- balanced schedule ----------------------------------------------------
@@ -755,11 +791,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
 // 2 v + 0 is the segment wavefront v starts inside (or its only piece),
 // 2 v + 1 the one it ends inside.  key: sequence * num_kv_heads + KV head of
 // the piece's segment, -1 when the piece is absent.
-template <int D>
+template <int D, int NT>
 struct EdgeLds {
-    float m[2 * kNW][16];
-    float l[2 * kNW][16];
-    __attribute__((aligned(16))) float o[2 * kNW][16 * Dim<D>::OS];
+    float m[2 * kNW][16 * NT];
+    float l[2 * kNW][16 * NT];
+    __attribute__((aligned(16))) float o[2 * kNW][16 * NT * Dim<D>::OS];
     int key[2 * kNW];
     int bad[2 * kNW];
 };
@@ -769,20 +805,18 @@ struct EdgeLds {
 // two-buffer pipeline of attend_segment with the chunks taken in order.
 // Includes the append step when the newest history position lies in
 // [cs, ce): this wavefront alone reads that chunk.
-template <typename Tag, int BS, typename Kv, int kRows, int D>
+template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
 __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh, int L, int ntok,
-                                             int cs, int ce, WaveState<D>& st, int& bad) {
+                                             int cs, int ce, WaveState<D>* st, int& bad) {
     constexpr bool kCols = kRows == 1;
-    const int G = a.group;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
     const int q = lane >> 4;
     const int t_end = min(ce * kChunk, L);
     const int t_lo = kCols ? min(t_end, L - (ntok - 1)) : t_end;
-    const int t_col = kCols ? min(t_end, L - (ntok - 1 - n / G)) : t_end;
-
-    u32x4 qop[Dim<D>::KD];
-    load_query<Kv, kCols, D>(a, b, kvh, n, q, ntok * G, qop);
+    u32x4 qop[NT * Dim<D>::KD];
+    int t_col[NT];
+    tile_columns<Kv, kCols, D, NT>(a, b, kvh, n, q, ntok, L, t_end, qop, t_col);
 
     const ConstI32* row =
         (const ConstI32*)(a.block_tables) + table_row_offset<kRows>(a, b);
@@ -797,8 +831,8 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
 
     const int K = ce - cs;
     auto chunk_of = [=](int k) { return cs + min(k, K - 1); };
-    stream_chunks<Tag, BS, Kv, kCols, D>(a, st, K, chunk_of, row, L, kvh, koff, voff, qop, t_end,
-                                         t_col, t_lo, q, bad);
+    stream_chunks<Tag, BS, Kv, kCols, D, NT>(a, st, K, chunk_of, row, L, kvh, koff, voff, qop,
+                                             t_end, t_col, t_lo, q, bad);
 }
 
 // Output rows of a whole history held by one wavefront: o = õ / l for the
@@ -808,10 +842,10 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
 // pool.
 template <typename Tag, bool kCols, int D>
 __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, int ncols,
-                                           const WaveState<D>& st, bool bad) {
+                                           int col0, const WaveState<D>& st, bool bad) {
     constexpr int VW = Dim<D>::VW;
     const int lane = threadIdx.x & 63;
-    const int n = lane & 15;
+    const int n = col0 + (lane & 15);
     const int q = lane >> 4;
     if (n >= ncols) return;
     const float l = st.acc_l[0];
@@ -847,8 +881,8 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, 
 // consecutive d of one column.  The pieces are listed by position (absent
 // slots repeat the last piece with weight 0) so that all of a thread's LDS
 // reads are issued together.
-template <typename Tag, bool kCols, int D>
-__device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLds<D>& e,
+template <typename Tag, bool kCols, int D, int NT>
+__device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLds<D, NT>& e,
                                                unsigned mask, int b, int kvh, int ncols, bool bad,
                                                float* plse, float* po) {
     constexpr int NP = 2 * kNW;
@@ -908,11 +942,12 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
 // LDS, sized at launch.
 extern __shared__ int balanced_pref[];
 
-template <typename Tag, int BS, typename Kv, int kRows, int D>
+template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
     constexpr bool kCols = kRows == 1;
     constexpr int OS = Dim<D>::OS;
-    __shared__ EdgeLds<D> edge;
+    constexpr int NC = 16 * NT;   // columns per slot
+    __shared__ EdgeLds<D, NT> edge;
     __shared__ int wsum[kNW];
     int* pref = balanced_pref;
     chunk_prefix(a, pref, wsum);
@@ -946,22 +981,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         const int L = __builtin_amdgcn_readfirstlane(a.context_lens[b]);
         const int ntok = row_tokens<kRows>(a, b);
 
-        WaveState<D> st;
-        init_state(st);
+        WaveState<D> st[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) init_state(st[t]);
         int bad = 0;
-        attend_piece<Tag, BS, Kv, kRows, D>(a, b, kvh, L, ntok, c0, c1, st, bad);
+        attend_piece<Tag, BS, Kv, kRows, D, NT>(a, b, kvh, L, ntok, c0, c1, st, bad);
 
         const bool starts_before = c0 > 0;    // the segment began before this range
         const bool ends_after = c1 < nb;      // it continues past this range
         if (!starts_before && !ends_after) {
-            write_rows<Tag, kCols, D>(a, b, kvh, ntok * a.group, st, bad != 0);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                write_rows<Tag, kCols, D>(a, b, kvh, ntok * a.group, t * 16, st[t], bad != 0);
         } else {
             const int p = 2 * wave + (starts_before ? 0 : 1);
-            if (q == 0) {
-                edge.m[p][n] = st.m_ref;
-                edge.l[p][n] = st.acc_l[0];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const int col = t * 16 + n;
+                if (q == 0) {
+                    edge.m[p][col] = st[t].m_ref;
+                    edge.l[p][col] = st[t].acc_l[0];
+                }
+                stage_acc<D>(&edge.o[p][col * OS], q, st[t]);
             }
-            stage_acc<D>(&edge.o[p][n * OS], q, st);
             if (lane == 0) {
                 edge.key[p] = b * H_kv + kvh;
                 edge.bad[p] = bad;
@@ -995,13 +1037,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         const bool tail = xs + nb > xe;       // continues into the next range
         const int ncols = row_tokens<kRows>(a, b) * a.group;
         if (!head && !tail) {
-            finalize_edges<Tag, kCols, D>(a, edge, mask, b, kvh, ncols, bad != 0, nullptr,
-                                          nullptr);
+            finalize_edges<Tag, kCols, D, NT>(a, edge, mask, b, kvh, ncols, bad != 0, nullptr,
+                                              nullptr);
         } else {
             const uint64_t slot = (uint64_t)w * 2 + (head ? 0 : 1);
-            finalize_edges<Tag, kCols, D>(a, edge, mask, b, kvh, ncols, bad != 0,
-                                          a.ws_lse + slot * kMaxGroup,
-                                          a.ws_out + slot * kMaxGroup * D);
+            finalize_edges<Tag, kCols, D, NT>(a, edge, mask, b, kvh, ncols, bad != 0,
+                                              a.ws_lse + slot * NC, a.ws_out + slot * NC * D);
             if (!head) meta.x = k, meta.y = range_owner(xs + nb - 1, T, a.num_wg);
         }
         p = p1;
@@ -1009,31 +1050,31 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     if (threadIdx.x == 0) reinterpret_cast<int4*>(a.ws_meta)[w] = meta;
 }
 
-template <typename Tag, int BS, typename Kv, int kRows, int D>
+template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
 hipError_t launch_rows(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
         const size_t pref_bytes = (size_t)(a.num_seqs + 1) * sizeof(int);
-        hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv, kRows, D>), dim3(a.num_wg),
+        hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv, kRows, D, NT>), dim3(a.num_wg),
                            dim3(kDecodeThreads), pref_bytes, s, a);
     } else {
         dim3 grid(a.num_kv_heads, a.num_seqs, a.num_parts);
-        hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS, Kv, kRows, D>), grid,
+        hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS, Kv, kRows, D, NT>), grid,
                            dim3(kDecodeThreads), 0, s, a);
     }
     return hipGetLastError();
 }
 
-// Decode rows with a row map (verify mode) run their own instantiation.
-template <typename Tag, int BS, typename Kv, int D>
-hipError_t launch_kv(const DecodeArgs& a, hipStream_t s) {
-    return a.table_rows != nullptr ? launch_rows<Tag, BS, Kv, 1, D>(a, s)
-                                   : launch_rows<Tag, BS, Kv, 0, D>(a, s);
-}
-
+// Decode rows with a row map (verify mode, 16-bit caches only) run their own
+// instantiations: one column tile, or two (up to 32 columns; head_dim 64 and
+// 128, whose edge LDS then still fits a compute unit).
 template <typename Tag, int BS, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
-    return a.kv_format == kKvE4M3 ? launch_kv<Tag, BS, KvE4M3, D>(a, s)
-                                  : launch_kv<Tag, BS, KvSame, D>(a, s);
+    if (a.kv_format == kKvE4M3) return launch_rows<Tag, BS, KvE4M3, 0, D, 1>(a, s);
+    if (a.table_rows == nullptr) return launch_rows<Tag, BS, KvSame, 0, D, 1>(a, s);
+    if constexpr (D <= 128) {
+        if (a.col_tiles == 2) return launch_rows<Tag, BS, KvSame, 1, D, 2>(a, s);
+    }
+    return launch_rows<Tag, BS, KvSame, 1, D, 1>(a, s);
 }
 
 template <typename Tag, int D>

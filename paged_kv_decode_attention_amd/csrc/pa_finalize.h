@@ -42,7 +42,7 @@ __device__ __forceinline__ void fill_cols(const DecodeArgs& a, int b, int kvh, i
     }
 }
 
-// sm_m/sm_l: [nw][16] reference max (log2 units) and denominator per
+// sm_m/sm_l: [nw][m_stride] reference max (log2 units) and denominator per
 // wavefront and column slot; sm_o: un-normalised accumulators, element
 // (w, g, d) at w * wave_stride + g * head_stride + d.  Merges the nw states
 // of each column n0 + g, g < ncols (the update of [MiniPaged-Qwen] §5.2
@@ -55,17 +55,18 @@ __device__ __forceinline__ void fill_cols(const DecodeArgs& a, int b, int kvh, i
 template <typename Tag>
 __device__ __forceinline__ void finalize_state(
     const DecodeArgs& a, const float* sm_m, const float* sm_l, const float* sm_o, int nw,
-    int wave_stride, int head_stride, int b, int kvh, int n0, int ncols, bool bad, int part) {
+    int m_stride, int wave_stride, int head_stride, int b, int kvh, int n0, int ncols, bool bad,
+    int part) {
     const int D = a.head_dim;
     for (int idx = threadIdx.x; idx < ncols * D; idx += blockDim.x) {
         const int g = idx / D;
         const int d = idx - g * D;
         float M = -INFINITY;
-        for (int w = 0; w < nw; ++w) M = fmaxf(M, sm_m[w * 16 + g]);
+        for (int w = 0; w < nw; ++w) M = fmaxf(M, sm_m[w * m_stride + g]);
         float den = 0.0f, num = 0.0f;
         for (int w = 0; w < nw; ++w) {
-            const float e = rescale_weight(sm_m[w * 16 + g], M);
-            den += e * sm_l[w * 16 + g];
+            const float e = rescale_weight(sm_m[w * m_stride + g], M);
+            den += e * sm_l[w * m_stride + g];
             num += e * sm_o[w * wave_stride + g * head_stride + d];
         }
         float o = den == 0.0f ? 0.0f : num / den;

@@ -38,6 +38,8 @@ struct DecodeArgs {
     int num_parts;             // ceil(max_context_len / part_len)
     int schedule;              // kFixed or kBalanced
     int num_wg;                // workgroups of the balanced schedule
+    int col_tiles;             // 16-column tiles per decode row (2 only for verify rows
+                               //   of the matrix-core kernel); slots hold 16 * col_tiles
     float scale_log2;          // scale * log2(e) (* k_scale): scores in log2 units
     int kv_format;             // kKvSame or kKvE4M3
     float out_scale;           // v_scale for E4M3 caches, else 1: output = out_scale * o
@@ -62,7 +64,8 @@ enum KvFormat { kKvSame = 0, kKvE4M3 = 1 };
 //     head, -1 if none), the last range w1 holding it, and the work-list
 //     size T; the decode kernel writes every record on every launch.
 enum Schedule { kFixed = 0, kBalanced = 1 };
-constexpr int kMaxGroup = 16;          // heads per slot (matrix-core kernel)
+constexpr int kMaxGroup = 16;          // heads per column tile (matrix-core kernel)
+constexpr int kMaxColTiles = 2;        // column tiles per decode row (verify)
 constexpr int kMaxBalancedWg = 1024;   // workspace is sized for this many
 constexpr int kMaxBalancedSeqs = 2048; // prefix table of the balanced schedule (dynamic LDS)
 

@@ -30,10 +30,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
 // over at most kSpec ranges).  Workgroup num_wg + b writes the rows of
 // decode row b when the decode kernel has none to write: zeros for an empty
 // history, NaN for an invalid context length.  A thread takes 4
-// consecutive d of one column (at most kMaxGroup columns): kMaxGroup * D / 4
+// consecutive d of one column (NC columns per slot, 16 or 32): NC * D / 4
 // threads.
-template <typename Tag, int D>
-__global__ __launch_bounds__(kMaxGroup * D / 4) void merge_balanced(DecodeArgs a) {
+template <typename Tag, int D, int NC>
+__global__ __launch_bounds__(NC * D / 4) void merge_balanced(DecodeArgs a) {
     constexpr int kSpec = 4;
     const int w = blockIdx.x;
     if (w >= a.num_wg) {
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kMaxGroup * D / 4) void merge_balanced(DecodeArgs a
     const int g = threadIdx.x / (D / 4);
     const int d = (threadIdx.x % (D / 4)) * 4;
     const int nwg = a.num_wg;
-    auto slot_row = [&](int slot) { return (uint64_t)slot * kMaxGroup + g; };
+    auto slot_row = [&](int slot) { return (uint64_t)slot * NC + g; };
     const int4 meta = reinterpret_cast<const int4*>(a.ws_meta)[w];
     f32x4 o[kSpec];
     float lse[kSpec];
@@ -139,14 +139,17 @@ template <typename Tag>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
         const dim3 grid(a.num_wg + a.num_seqs);
-        if (a.head_dim == 64)
-            hipLaunchKernelGGL((merge_balanced<Tag, 64>), grid, dim3(kMaxGroup * 64 / 4), 0, s, a);
+        const bool two = a.col_tiles == 2;
+        if (a.head_dim == 64 && two)
+            hipLaunchKernelGGL((merge_balanced<Tag, 64, 32>), grid, dim3(32 * 64 / 4), 0, s, a);
+        else if (a.head_dim == 64)
+            hipLaunchKernelGGL((merge_balanced<Tag, 64, 16>), grid, dim3(16 * 64 / 4), 0, s, a);
+        else if (a.head_dim == 128 && two)
+            hipLaunchKernelGGL((merge_balanced<Tag, 128, 32>), grid, dim3(32 * 128 / 4), 0, s, a);
         else if (a.head_dim == 128)
-            hipLaunchKernelGGL((merge_balanced<Tag, 128>), grid, dim3(kMaxGroup * 128 / 4), 0, s,
-                               a);
+            hipLaunchKernelGGL((merge_balanced<Tag, 128, 16>), grid, dim3(16 * 128 / 4), 0, s, a);
         else
-            hipLaunchKernelGGL((merge_balanced<Tag, 256>), grid, dim3(kMaxGroup * 256 / 4), 0, s,
-                               a);
+            hipLaunchKernelGGL((merge_balanced<Tag, 256, 16>), grid, dim3(16 * 256 / 4), 0, s, a);
     } else {
         hipLaunchKernelGGL((merge_fixed<Tag>), dim3(a.num_kv_heads, a.num_seqs),
                            dim3(kMergeThreads), 0, s, a);

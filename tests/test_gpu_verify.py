@@ -65,7 +65,8 @@ def test_verify_parity(case, partition_size):
 
 # Matrix-core verify groups up to 16 // G query rows of a sequence into one
 # pass (their (row, head) pairs are the MFMA's 16 columns, each with its own
-# causal end).  Lengths put a column's end on a 32-token chunk boundary
+# causal end), or 32 // G with two column tiles when max_query_len * G > 16
+# (head_dim 64 and 128; the cases below pass max_query_len 17).  Lengths put a column's end on a 32-token chunk boundary
 # (L_b - q_b + i + 1 = 32 k), so that some chunk (a piece of its own when the
 # work list is short, or a partition at P = 32) holds no token of that column
 # and leaves an empty state for the merge.
@@ -91,6 +92,21 @@ def test_verify_columns_parity(case, partition_size):
     assert torch.isnan(out[torch.from_numpy(bad)].float()).all()
     compare(out[torch.from_numpy(~bad)], ref[~bad], dtype,
             what="verify columns %s P=%d" % (case, partition_size))
+
+
+@pytest.mark.parametrize("partition_size", [0, 32])
+@pytest.mark.parametrize("G", [1, 2, 4, 5])
+def test_verify_one_column_tile(G, partition_size):
+    """max_query_len * G <= 16: one column tile, 16 // G rows per group
+    (with max_query_len = 16 // G, every sequence is one group)."""
+    u = 16 // G
+    lens = (33, 34, 65, 66, 97, 40, 513, 129, 16)
+    qlens = [min(u, x) for x in (2, 3, 1, 16, 2, 8, 5, 16, 7)]
+    cfg = small_config("bf16", 2, G, 128, 16, lens)
+    inp, q, qs = verify_inputs(cfg, qlens, seed=13)
+    out = run_verify(inp, q, qs, u, ops.KERNEL_MFMA, partition_size)
+    compare(out, oracle_verify(inp, q, qs), "bf16",
+            what="verify one tile G=%d P=%d" % (G, partition_size))
 
 
 @pytest.mark.parametrize("G,BS", [(7, 16), (1, 16)])
