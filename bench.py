@@ -265,11 +265,13 @@ def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture
 
 
 def shape_sweep(args, dev):
-    """Decode-call rate over block sizes 8/16/32/64 and head dims 64/128/256:
-    the bench batch (64 sequences, 28 query / 4 KV heads, the same seeded
-    context lengths), bf16, shuffled tables, random pools on the GPU, pool
-    replicas rotated so the last-level cache cannot hold the working set;
-    K calls replayed from a HIP graph, HIP events around each replay."""
+    """Decode-call rate over block sizes 8/16/32/64 and head dims 64/128/256,
+    on 16-bit caches and on FP8 E4M3 caches: the bench batch (64 sequences,
+    28 query / 4 KV heads, the same seeded context lengths), bf16 queries,
+    shuffled tables, random pools on the GPU (the FP8 ones quantised by the
+    library's cache write), pool replicas rotated so the last-level cache
+    cannot hold the working set; K calls replayed from a HIP graph, HIP
+    events around each replay."""
     import numpy as np
     import torch
     from paged_kv_decode_attention_amd import inputs as I
@@ -280,7 +282,34 @@ def shape_sweep(args, dev):
     S, H, H_kv = base.num_seqs, base.num_heads, base.num_kv_heads
     G = H // H_kv
     K = min(args.steps, 100)
+    k_scale = v_scale = 1.0 / 64
     rows = []
+
+    def timed(call):
+        for j in range(5):
+            call(j)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(gr, stream=st):
+                for j in range(K):
+                    call(j)
+        torch.cuda.current_stream().wait_stream(st)
+        gr.replay()
+        torch.cuda.synchronize()
+        us = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3 / K)
+        del gr
+        return float(np.mean(us)) * 1e-6
+
     for D in [int(x) for x in args.sweep_head_dims.split(",")]:
         for BS in [int(x) for x in args.sweep_block_sizes.split(",")]:
             rng = np.random.default_rng(7)
@@ -293,15 +322,7 @@ def shape_sweep(args, dev):
             for b in range(S):
                 bt[b, :nblk[b]] = perm[k:k + nblk[b]]
                 k += nblk[b]
-            pool = N * H_kv * BS * D * 2
-            # replicas cycled through: 1.2 GB or more of K/V between two
-            # reads of the same bytes, well beyond the 256 MB last-level cache
-            R = max(2, int(np.ceil(1.2e9 / (2 * pool))))
             g = torch.Generator(device=dev).manual_seed(11)
-            kcs = [torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(torch.bfloat16)
-                   for _ in range(R)]
-            vcs = [torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(torch.bfloat16)
-                   for _ in range(R)]
             q = torch.randn(S, H, D, generator=g, device=dev).to(torch.bfloat16)
             btd = torch.from_numpy(bt).to(dev)
             cld = torch.from_numpy(lens.astype(np.int32)).to(dev)
@@ -310,55 +331,65 @@ def shape_sweep(args, dev):
             ws = torch.zeros(max(ops.decode_workspace_size(S, H, H_kv, D, BS, max_ctx, 0,
                                                            q.dtype), 256),
                              dtype=torch.uint8, device=dev)
-
-            def call(j):
-                ops.paged_attention_decode(q, kcs[j % R], vcs[j % R], btd, cld,
-                                           max_context_len=max_ctx, out=out, workspace=ws)
-            for j in range(5):
-                call(j)
-            torch.cuda.synchronize()
-            gr = torch.cuda.CUDAGraph()
-            st = torch.cuda.Stream()
-            st.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(st):
-                with torch.cuda.graph(gr, stream=st):
-                    for j in range(K):
-                        call(j)
-            torch.cuda.current_stream().wait_stream(st)
-            gr.replay()
-            torch.cuda.synchronize()
-            us = []
-            for _ in range(3):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                gr.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                us.append(e0.elapsed_time(e1) * 1e3 / K)
-            t = float(np.mean(us)) * 1e-6
-            alg = int(lens.sum()) * H_kv * D * 2 * 2
             mfma = ops.decode_kernel(D, BS, G, q.dtype) == ops.KERNEL_MFMA
-            row = {"head_dim": D, "block_size": BS,
-                   "kernel": "matrix-core, balanced" if mfma else "vector-ALU, partitions",
-                   "decode_us": t * 1e6, "alg_bytes": alg, "achieved_gbps": alg / t / 1e9,
-                   "frac": alg / t / 1e9 / HBM_PEAK_GBPS, "decode_tokens_per_s": S / t,
-                   "pool_replicas": R}
-            rows.append(row)
-            print(json.dumps(row), flush=True)
-            del kcs, vcs, gr
-            torch.cuda.empty_cache()
+            for kv in ("bf16", "fp8"):
+                if kv == "fp8" and not mfma:
+                    continue
+                e = 2 if kv == "bf16" else 1
+                pool = N * H_kv * BS * D * e
+                # replicas cycled through: 1.2 GB or more of K/V between two
+                # reads of the same bytes, well beyond the 256 MB last-level
+                # cache
+                R = max(2, int(np.ceil(1.2e9 / (2 * pool))))
+                kcs, vcs = [], []
+                for _ in range(2 * R):
+                    x = torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(torch.bfloat16)
+                    if kv == "fp8":
+                        # pool rows as tokens: slot pb * BS + off holds row (pb, :, off)
+                        c = torch.empty(N, H_kv, BS, D, dtype=torch.uint8, device=dev)
+                        rows_ = x.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous()
+                        slots = torch.arange(N * BS, dtype=torch.int64, device=dev)
+                        ops.reshape_and_cache_fp8(rows_, rows_, c, torch.empty_like(c), slots,
+                                                  k_scale, v_scale)
+                        x = c
+                    (kcs if len(kcs) < R else vcs).append(x)
+                torch.cuda.synchronize()
+
+                if kv == "bf16":
+                    def call(j):
+                        ops.paged_attention_decode(q, kcs[j % R], vcs[j % R], btd, cld,
+                                                   max_context_len=max_ctx, out=out,
+                                                   workspace=ws)
+                else:
+                    def call(j):
+                        ops.paged_attention_decode_fp8(q, kcs[j % R], vcs[j % R], btd, cld,
+                                                       k_scale, v_scale, max_context_len=max_ctx,
+                                                       out=out, workspace=ws)
+                t = timed(call)
+                alg = int(lens.sum()) * H_kv * D * e * 2
+                row = {"head_dim": D, "block_size": BS,
+                       "kv": "bf16" if kv == "bf16" else "fp8 e4m3",
+                       "kernel": "matrix-core, balanced" if mfma else "vector-ALU, partitions",
+                       "decode_us": t * 1e6, "alg_bytes": alg, "achieved_gbps": alg / t / 1e9,
+                       "frac": alg / t / 1e9 / HBM_PEAK_GBPS, "decode_tokens_per_s": S / t,
+                       "pool_replicas": R}
+                rows.append(row)
+                print(json.dumps(row), flush=True)
+                del kcs, vcs
+                torch.cuda.empty_cache()
     if args.sweep_out:
-        L = ["# Decode shape sweep: block size x head dim (bf16, 64 sequences, 28/4 heads, "
-             "L~U[512,4096] seed 2)", "",
+        L = ["# Decode shape sweep: block size x head dim x KV format (bf16 queries, "
+             "64 sequences, 28/4 heads, L~U[512,4096] seed 2)", "",
              "Command (repository root, one MI355X):", "",
              "    python bench.py --sweep --sweep-out <file>", "",
-             "| head_dim | block_size | kernel | decode call us | KV TB/s | % of 8 TB/s | "
-             "decode tokens/s |", "|---|---|---|---|---|---|---|"]
+             "| head_dim | block_size | KV | kernel | decode call us | KV TB/s | % of 8 TB/s | "
+             "decode tokens/s |", "|---|---|---|---|---|---|---|---|"]
         for r in rows:
-            L.append("| %d | %d | %s | %.1f | %.2f | %.1f | %.0f |" % (
-                r["head_dim"], r["block_size"], r["kernel"], r["decode_us"],
+            L.append("| %d | %d | %s | %s | %.1f | %.2f | %.1f | %.0f |" % (
+                r["head_dim"], r["block_size"], r["kv"], r["kernel"], r["decode_us"],
                 r["achieved_gbps"] / 1e3, 100 * r["frac"], r["decode_tokens_per_s"]))
-        L += ["", "Algorithmic bytes: sum_b L_b x 4 KV heads x head_dim x 2 B x 2 (K and V).  "
+        L += ["", "Algorithmic bytes: sum_b L_b x 4 KV heads x head_dim x element bytes (2 for "
+              "bf16, 1 for FP8 E4M3) x 2 (K and V).  "
               "Timing: K decode calls replayed from a HIP graph, HIP events around each "
               "replay, mean of 3."]
         with open(args.sweep_out, "w") as fh:
