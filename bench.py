@@ -637,6 +637,8 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
+            # counter HBM bytes (the traffic figure) over the same duration
+            "counter_gbps": traffic / dec_s / 1e9 if traffic else None,
             "kernel": "paged_attention_decode call (partition kernel + lse merge kernel)",
             "alg_bytes_per_launch": alg_bytes,
             "decode_us_mean": float(dec_ms.mean()) * 1e3,

@@ -5,6 +5,8 @@
         --copy-bytes N --config NAME --out FILE.json [--command CMD ...]
     python -m paged_kv_decode_attention_amd.counters trace \\
         --db FILE.db --out FILE.md --title TEXT --command CMD [--note TEXT ...]
+    python -m paged_kv_decode_attention_amd.counters compute \\
+        --run DIR --out FILE.md --title TEXT --command CMD [--note TEXT ...]
 
 traffic: HBM bytes of one decode call, from counter runs.
 
@@ -88,6 +90,47 @@ def trace_table(db):
             for r in rows]
 
 
+# Instruction and utilisation counters of one --pmc run (8 SQ counters and
+# one derived metric fit one pass).
+COMPUTE_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU",
+                    "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD", "SQ_LDS_BANK_CONFLICT", "MfmaUtil")
+
+
+def compute_main(a):
+    """Per-dispatch means of the compute counters for every decode kernel,
+    with instructions per wavefront derived from them."""
+    data = {c: per_dispatch(read_counter(a.run, c), DECODE_KERNELS) for c in COMPUTE_COUNTERS}
+    kernels = sorted(data["SQ_WAVES"], key=lambda k: -data["SQ_INSTS_VALU"].get(k, (0, 0))[0])
+    lines = ["# " + a.title, "", "Command (repository root, one MI355X):", "",
+             "    " + a.command, "",
+             "Per dispatch (mean over dispatches):", "",
+             "| kernel | dispatches | waves | VALU insts | MFMA insts | SALU insts | LDS insts "
+             "| VMEM read insts | LDS bank conflict cycles | MFMA busy % |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for k in kernels:
+        v = {c: data[c].get(k, (float("nan"), 0))[0] for c in COMPUTE_COUNTERS}
+        lines.append("| %s | %d | %.0f | %.0f | %.0f | %.0f | %.0f | %.0f | %.0f | %.2f |" % (
+            k, data["SQ_WAVES"][k][1], v["SQ_WAVES"], v["SQ_INSTS_VALU"], v["SQ_INSTS_MFMA"],
+            v["SQ_INSTS_SALU"], v["SQ_INSTS_LDS"], v["SQ_INSTS_VMEM_RD"],
+            v["SQ_LDS_BANK_CONFLICT"], v["MfmaUtil"]))
+    lines += ["", "Per wavefront:", "",
+              "| kernel | VALU | MFMA | SALU | LDS | VMEM read |", "|---|---|---|---|---|---|"]
+    for k in kernels:
+        w = data["SQ_WAVES"][k][0] or float("nan")
+        lines.append("| %s | %.0f | %.0f | %.0f | %.0f | %.0f |" % (
+            k, data["SQ_INSTS_VALU"].get(k, (0, 0))[0] / w,
+            data["SQ_INSTS_MFMA"].get(k, (0, 0))[0] / w,
+            data["SQ_INSTS_SALU"].get(k, (0, 0))[0] / w,
+            data["SQ_INSTS_LDS"].get(k, (0, 0))[0] / w,
+            data["SQ_INSTS_VMEM_RD"].get(k, (0, 0))[0] / w))
+    if a.note:
+        lines += [""] + ["- " + t for t in a.note]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def trace_main(a):
     lines = ["# " + a.title, "", "Command (repository root, one MI355X):", "",
              "    " + a.command, "",
@@ -112,6 +155,12 @@ def main(argv=None):
     tr.add_argument("--title", required=True)
     tr.add_argument("--command", required=True)
     tr.add_argument("--note", action="append", default=[])
+    cp = sub.add_parser("compute", help="instruction counters of the decode kernels")
+    cp.add_argument("--run", required=True)
+    cp.add_argument("--out", required=True)
+    cp.add_argument("--title", required=True)
+    cp.add_argument("--command", required=True)
+    cp.add_argument("--note", action="append", default=[])
     ap = sub.add_parser("traffic", help="HBM bytes per decode call from counter runs")
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
@@ -125,6 +174,8 @@ def main(argv=None):
     a = top.parse_args(argv)
     if a.cmd == "trace":
         return trace_main(a)
+    if a.cmd == "compute":
+        return compute_main(a)
 
     from . import inputs as I
     from .build import decode_source_hash

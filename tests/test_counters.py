@@ -76,3 +76,33 @@ def test_trace_table(tmp_path):
     k, calls, avg, lo, hi, share = table[0]
     assert (calls, avg, lo, hi) == (2, 55.0, 50.0, 60.0)
     assert share == pytest.approx(100.0 * 110 / 115)
+
+
+def test_compute_counter_summary(tmp_path):
+    """Per-dispatch means of the instruction counters and the per-wavefront
+    figures derived from them, for the decode kernels only."""
+    d = tmp_path / "c"
+    os.makedirs(d)
+    vals = {"SQ_WAVES": (1024, 576), "SQ_INSTS_VALU": (2048000, 57600),
+            "SQ_INSTS_MFMA": (409600, 0), "SQ_INSTS_SALU": (102400, 5760),
+            "SQ_INSTS_LDS": (20480, 576), "SQ_INSTS_VMEM_RD": (163840, 2304),
+            "SQ_LDS_BANK_CONFLICT": (100, 0), "MfmaUtil": (12.5, 0.0)}
+    with open(d / "x_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        i = 0
+        for c, (vd, vm) in vals.items():
+            for name, v in ((DEC, vd), (DEC, vd), (MRG, vm), ("other", 7.0)):
+                w.writerow({"Correlation_Id": i, "Dispatch_Id": i, "Kernel_Name": name,
+                            "Counter_Name": c, "Counter_Value": v})
+                i += 1
+    out = tmp_path / "c.md"
+    counters.main(["compute", "--run", str(d), "--out", str(out), "--title", "t",
+                   "--command", "cmd"])
+    text = out.read_text()
+    assert "other" not in text
+    dec_rows = [l for l in text.splitlines() if l.startswith("| decode_mfma_balanced")]
+    assert dec_rows[0].split("|")[2].strip() == "2"             # dispatches
+    assert dec_rows[0].split("|")[-2].strip() == "12.50"        # MFMA busy %
+    # per wavefront: 2048000 / 1024 VALU, 409600 / 1024 MFMA, 160 VMEM reads
+    assert [c.strip() for c in dec_rows[1].split("|")[2:7]] == ["2000", "400", "100", "20", "160"]

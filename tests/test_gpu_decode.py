@@ -246,3 +246,21 @@ def test_long_context_ragged_tails():
     for P in (0, 512, 2048):
         out = run_decode(d, partition_size=P)
         compare(out, ref, "bf16", pairs=pairs, what="long ragged P=%d" % P)
+
+
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("S", [2048, 2049])
+def test_many_sequences_balanced_limit(S, D):
+    """The balanced schedule's prefix table (dynamic LDS, S + 1 ints) at its
+    largest, next to 134 KB of edge LDS at head_dim 256; one sequence more
+    takes the fixed schedule.  Short ragged histories, some empty."""
+    rng = np.random.default_rng(S + D)
+    lens = rng.integers(0, 48, S)
+    lens[::97] = 0
+    cfg = small_config("bf16", 1, 4, D, 16, tuple(int(x) for x in lens), extra_blocks=4)
+    inp = I.poison_unread(I.generate(cfg))
+    out = run_decode(upload(inp), ops.KERNEL_MFMA)
+    rows = rng.choice(S, 64, replace=False)
+    pairs = [(int(b), h) for b in rows for h in range(4)]
+    compare(out, oracle_ref(inp, pairs), "bf16", pairs=pairs, what="S=%d D=%d" % (S, D))
+    assert torch.all(out[torch.from_numpy(lens == 0)] == 0)
