@@ -19,8 +19,11 @@
 // at most 2^8, and the final o = O / l does not depend on the choice of m.
 // l is summed on the matrix core (P times a ones operand).  While one
 // chunk is computed, the next chunk's loads are in flight (two register
-// buffers).  Histories longer than one partition leave float32 partition
-// states that the merge kernel (pa_merge.hip) combines.
+// buffers; one at head_dim 256).  Histories longer than one partition leave
+// float32 partition states that the merge kernel (pa_merge.hip) combines.
+// In verify mode the 16 columns (or 32, in two column tiles) are (query
+// row, head) pairs of several query rows of one sequence, each column
+// masked at its own causal end.
 //
 // Lane layout (lane = 16 q + n; VW = D / 16): in every MFMA the column index
 // (lane % 16) is the query head n of the group, so the running max /
