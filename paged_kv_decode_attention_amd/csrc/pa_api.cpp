@@ -110,18 +110,20 @@ Layout balanced_layout(int head_dim, int cols = pa::kMaxGroup) {
 // Workgroups of the balanced schedule: pa::mfma_workgroups_per_cu per compute
 // unit of the current device, all resident at once.
 int balanced_workgroups(int head_dim) {
-    static int cached[64] = {0};
+    // compute units per device, queried once (calls may come from any thread)
+    static std::atomic<int> cached[64];
     int dev = 0;
     int cus = 256;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
-        if (cached[dev] == 0) {
+        cus = cached[dev].load(std::memory_order_relaxed);
+        if (cus == 0) {
             int n = 0;
             if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
                     hipSuccess || n <= 0)
                 n = 256;
-            cached[dev] = n;
+            cached[dev].store(n, std::memory_order_relaxed);
+            cus = n;
         }
-        cus = cached[dev];
     }
     const int wgs = cus * pa::mfma_workgroups_per_cu(head_dim);
     return wgs > pa::kMaxBalancedWg ? pa::kMaxBalancedWg : wgs;

@@ -98,12 +98,17 @@ int pa_pool_add_sequence(pa_block_pool* pool) {
 int pa_pool_fork(pa_block_pool* pool, int seq) {
     if (!pool) return pa::report_error(PA_ERR_INVALID_ARG, "null pool");
     if (!pool->valid(seq)) return invalid("unknown sequence %lld", seq);
+    std::vector<int32_t> table;
+    try {
+        table = pool->seqs[seq].table;
+    } catch (const std::bad_alloc&) {
+        return pa::report_error(PA_ERR_INVALID_ARG, "out of host memory");
+    }
     const int id = new_sequence(pool);
     if (id < 0) return id;
     pa_block_pool::Sequence& child = pool->seqs[id];
-    const pa_block_pool::Sequence& parent = pool->seqs[seq];   // after the emplace
-    child.table = parent.table;
-    child.length = parent.length;
+    child.table.swap(table);
+    child.length = pool->seqs[seq].length;   // seqs may have moved: index again
     for (int32_t b : child.table) ++pool->refs[b];
     return id;
 }
@@ -120,47 +125,50 @@ int pa_pool_append(pa_block_pool* pool, const int* seqs, int n, int64_t* slots,
 
     // Validate ids and count the blocks the appends take, applying the same
     // rules to a scratch copy of the reference counts they change (a shared
-    // tail loses the reference of each sequence that copies it).
-    std::unordered_map<int, int> seen;
-    std::unordered_map<int32_t, int32_t> tail_refs;
+    // tail loses the reference of each sequence that copies it).  Tables that
+    // grow get their room here, so that nothing below can fail half-way:
+    // the batch is applied whole or not at all.
     int64_t need = 0;
-    for (int i = 0; i < n; ++i) {
-        const int s = seqs[i];
-        if (!pool->valid(s)) return invalid("unknown sequence %lld", s);
-        if (!seen.emplace(s, i).second) return invalid("sequence %lld listed twice", s);
-        const std::vector<int32_t>& t = pool->seqs[s].table;
-        if (t.empty() || pool->fill[t.back()] == BS) {
-            ++need;
-            continue;
+    try {
+        std::unordered_map<int, int> seen;
+        std::unordered_map<int32_t, int32_t> tail_refs;
+        for (int i = 0; i < n; ++i) {
+            const int s = seqs[i];
+            if (!pool->valid(s)) return invalid("unknown sequence %lld", s);
+            if (!seen.emplace(s, i).second) return invalid("sequence %lld listed twice", s);
+            std::vector<int32_t>& t = pool->seqs[s].table;
+            if (t.empty() || pool->fill[t.back()] == BS) {
+                t.reserve(t.size() + 1);
+                ++need;
+                continue;
+            }
+            auto it = tail_refs.find(t.back());
+            int32_t& r = it != tail_refs.end()
+                             ? it->second
+                             : tail_refs.emplace(t.back(), pool->refs[t.back()]).first->second;
+            if (r > 1) {
+                --r;
+                ++need;
+            }
         }
-        auto it = tail_refs.find(t.back());
-        int32_t& r = it != tail_refs.end() ? it->second
-                                           : tail_refs.emplace(t.back(), pool->refs[t.back()])
-                                                 .first->second;
-        if (r > 1) {
-            --r;
-            ++need;
-        }
+    } catch (const std::bad_alloc&) {
+        return pa::report_error(PA_ERR_INVALID_ARG, "out of host memory");
     }
     if (need > (int64_t)pool->free_list.size())
         return pa::report_error(PA_ERR_POOL_EXHAUSTED, "KV pool exhausted");
     for (int i = 0; i < n; ++i) {
         pa_block_pool::Sequence& q = pool->seqs[seqs[i]];
-        try {
-            if (q.table.empty() || pool->fill[q.table.back()] == BS) {
-                q.table.push_back(pool->take());
-            } else if (pool->refs[q.table.back()] > 1) {
-                const int32_t src = q.table.back();
-                const int32_t dst = pool->take();
-                pool->fill[dst] = pool->fill[src];
-                --pool->refs[src];        // other sequences still hold it
-                q.table.back() = dst;
-                copy_pairs[2 * *num_copies] = src;
-                copy_pairs[2 * *num_copies + 1] = dst;
-                ++*num_copies;
-            }
-        } catch (const std::bad_alloc&) {
-            return pa::report_error(PA_ERR_INVALID_ARG, "out of host memory");
+        if (q.table.empty() || pool->fill[q.table.back()] == BS) {
+            q.table.push_back(pool->take());      // capacity reserved above
+        } else if (pool->refs[q.table.back()] > 1) {
+            const int32_t src = q.table.back();
+            const int32_t dst = pool->take();
+            pool->fill[dst] = pool->fill[src];
+            --pool->refs[src];        // other sequences still hold it
+            q.table.back() = dst;
+            copy_pairs[2 * *num_copies] = src;
+            copy_pairs[2 * *num_copies + 1] = dst;
+            ++*num_copies;
         }
         const int32_t last = q.table.back();
         slots[i] = (int64_t)last * BS + pool->fill[last];
