@@ -24,6 +24,9 @@ ARCH = "gfx950"
 
 SOURCES = [
     "pa_api.cpp",
+    "pa_decode_mfma_d128.hip",
+    "pa_decode_mfma_d256.hip",
+    "pa_decode_mfma_d64.hip",
     "pa_decode_mfma.hip",
     "pa_decode_generic.hip",
     "pa_merge.hip",
@@ -41,8 +44,9 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
 
 # Sources whose change changes what the decode call's kernels do; hashed to
 # tell whether stored counter readings still describe the built kernels.
-DECODE_SOURCES = ["pa_decode_mfma.hip", "pa_decode_generic.hip", "pa_merge.hip",
-                  "pa_finalize.h", "pa_device.h", "pa_api.cpp"]
+DECODE_SOURCES = ["pa_decode_mfma.h", "pa_decode_mfma.hip", "pa_decode_mfma_d64.hip",
+                  "pa_decode_mfma_d128.hip", "pa_decode_mfma_d256.hip", "pa_decode_generic.hip",
+                  "pa_merge.hip", "pa_finalize.h", "pa_device.h", "pa_api.cpp"]
 
 
 def decode_source_hash():
@@ -78,7 +82,7 @@ def _compile(src, save_temps=False):
 
 def build(jobs=None, save_temps=False, verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(8, len(SOURCES))
+    jobs = jobs or min(os.cpu_count() or 8, len(SOURCES))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(lambda s: _compile(s, save_temps), SOURCES))
     objs = []

@@ -201,9 +201,13 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
     if (!valid_partition(P, block_size)) return (size_t)-1;
     size_t bytes = fixed_layout(num_seqs, num_heads, head_dim, max_context_len, P).bytes;
     // enough for either kernel family (pa_debug_select_kernel may force one)
-    const bool mfma = pa::mfma_supported(dtype, head_dim, block_size, num_heads / num_kv_heads);
+    const int group = num_heads / num_kv_heads;
+    const bool mfma = pa::mfma_supported(dtype, head_dim, block_size, group);
     if (use_balanced(mfma, partition_size, num_seqs, max_context_len)) {
-        const size_t bal = balanced_layout(head_dim).bytes;
+        // groups of more than 16 heads take two 16-column tiles per slot
+        const size_t bal =
+            balanced_layout(head_dim, group > pa::kMaxGroup ? 2 * pa::kMaxGroup : pa::kMaxGroup)
+                .bytes;
         if (bal > bytes) bytes = bal;
     }
     return bytes;
@@ -270,14 +274,18 @@ static int decode_impl(void* out, const void* query, const void* new_key,
         return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
     if (e4m3 && !use_mfma)
         return fail(PA_ERR_UNSUPPORTED, "FP8 caches are served by the matrix-core kernel only "
-                    "(bf16/f16 queries, head_dim 64/128/256, block_size 16/32/64, group <= 16)");
+                    "(bf16/f16 queries, head_dim 64/128/256, block_size 8/16/32/64, group <= 16, "
+                    "or <= 32 at head_dim 64/128)");
     const bool balanced = use_balanced(use_mfma, partition_size, num_seqs, max_context_len);
 
     const int P = partition_size ? partition_size
                                  : heuristic_partition(num_seqs, num_kv_heads, block_size,
                                                        max_context_len);
-    if (col_tiles != 1 && !(col_tiles == 2 && use_mfma && head_dim <= 128 && table_rows))
-        return fail(PA_ERR_INVALID_ARG, "two column tiles serve matrix-core verify rows only");
+    // groups of more than 16 heads always take two column tiles
+    if (use_mfma && gqa_group_size > pa::kMaxGroup) col_tiles = 2;
+    if (col_tiles != 1 && !(col_tiles == 2 && use_mfma && head_dim <= 128))
+        return fail(PA_ERR_INVALID_ARG, "two column tiles serve the matrix-core kernel at "
+                    "head_dim 64/128 only");
     const Layout lay = balanced ? balanced_layout(head_dim, pa::kMaxGroup * col_tiles)
                                 : fixed_layout(num_seqs, num_heads, head_dim, max_context_len, P);
     const bool needs_ws = lay.bytes > 0;

@@ -79,6 +79,9 @@ bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group);
 // Workgroups of the matrix-core kernel resident per compute unit.
 int mfma_workgroups_per_cu(int head_dim);
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_decode_mfma_d64(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_decode_mfma_d128(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
+hipError_t launch_decode_mfma_d256(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 hipError_t launch_lse_merge(const DecodeArgs& a, pa_dtype dt, hipStream_t s);
 

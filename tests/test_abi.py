@@ -155,7 +155,7 @@ def test_fp8_entry_points_reject_on_host(lib):
                  f32(a["ks"]), f32(a["vs"]), 0, vp(FAKE), ctypes.c_size_t(1 << 30), vp(0))
     assert call(ks=-1.0) == INVALID
     assert call(vs=float("nan")) == INVALID
-    assert call(G=17, H=68) == UNSUPPORTED                     # matrix-core kernel: group <= 16
+    assert call(G=33, H=132) == UNSUPPORTED                    # matrix-core kernel: group <= 32
     assert call(dtype=ops.PA_F32) == UNSUPPORTED               # f32 queries: vector-ALU only
     assert call(S=0) == OK
 
@@ -168,7 +168,10 @@ def test_decode_kernel_choice(lib):
     assert f(64, 64, 16, ops.PA_F16) == MFMA
     assert f(128, 8, 7, ops.PA_BF16) == MFMA
     assert f(256, 16, 7, ops.PA_BF16) == MFMA
-    assert f(128, 16, 17, ops.PA_BF16) == GEN        # group > 16
+    assert f(128, 16, 17, ops.PA_BF16) == MFMA       # groups of 17..32: two column tiles
+    assert f(64, 8, 32, ops.PA_F16) == MFMA
+    assert f(128, 16, 33, ops.PA_BF16) == GEN        # group > 32
+    assert f(256, 16, 17, ops.PA_BF16) == GEN        # group > 16 at head_dim 256
     assert f(128, 16, 7, ops.PA_F32) == GEN
     assert f(96, 16, 7, ops.PA_BF16) == UNSUPPORTED
     assert f(128, 16, 0, ops.PA_BF16) == INVALID
@@ -178,7 +181,7 @@ def test_decode_kernel_choice(lib):
         assert f(128, 16, 7, ops.PA_BF16) == GEN
         lib.pa_debug_select_kernel(2)
         assert f(128, 16, 7, ops.PA_BF16) == MFMA
-        assert f(128, 8, 17, ops.PA_BF16) == UNSUPPORTED
+        assert f(128, 8, 33, ops.PA_BF16) == UNSUPPORTED
     finally:
         lib.pa_debug_select_kernel(prev)
 

@@ -47,7 +47,12 @@ SMALL_CASES = [
     ("bf16", 3, 1, 128, 32, ops.KERNEL_MFMA),
     ("bf16", 1, 16, 128, 16, ops.KERNEL_MFMA),
     ("bf16", 2, 8, 128, 32, ops.KERNEL_MFMA),
-    ("bf16", 2, 20, 128, 16, ops.KERNEL_AUTO),      # G > 16: vector-ALU kernel
+    ("bf16", 2, 20, 128, 16, ops.KERNEL_AUTO),      # G 17..32: two column tiles
+    ("bf16", 1, 32, 128, 32, ops.KERNEL_MFMA),
+    ("f16", 2, 17, 64, 16, ops.KERNEL_MFMA),
+    ("bf16", 1, 24, 128, 8, ops.KERNEL_MFMA),
+    ("bf16", 1, 40, 128, 16, ops.KERNEL_AUTO),      # G > 32: vector-ALU kernel
+    ("bf16", 1, 20, 256, 16, ops.KERNEL_AUTO),      # G > 16 at head_dim 256: vector ALU
     ("f16", 2, 3, 64, 16, ops.KERNEL_AUTO),         # head_dim 64: matrix-core kernel
     ("bf16", 2, 5, 64, 32, ops.KERNEL_GENERIC),
     ("bf16", 2, 7, 64, 16, ops.KERNEL_MFMA),

@@ -76,7 +76,8 @@ COL_QLENS = (2, 3, 2, 3, 2, 8, 2, 5, 8, 5, 17)
 COL_CASES = [("bf16", 2, 7, 128, 16), ("f16", 2, 4, 128, 32), ("bf16", 4, 1, 128, 16),
              ("bf16", 1, 16, 128, 64), ("bf16", 2, 3, 128, 16), ("f16", 1, 8, 128, 16),
              ("bf16", 2, 5, 128, 32), ("bf16", 2, 7, 64, 16), ("f16", 2, 2, 64, 32),
-             ("bf16", 2, 7, 256, 16), ("bf16", 1, 4, 256, 64), ("bf16", 2, 7, 128, 8)]
+             ("bf16", 2, 7, 256, 16), ("bf16", 1, 4, 256, 64), ("bf16", 2, 7, 128, 8),
+             ("bf16", 1, 20, 128, 16), ("f16", 1, 32, 64, 16)]
 
 
 @pytest.mark.parametrize("partition_size", [0, 64])
