@@ -886,14 +886,13 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, 
 // else the partial state (o~/l, m + log2 l) at (plse, po) -- the empty state
 // (o 0, lse -inf) for a verify column none of whose tokens lie in the
 // pieces.  Called by every thread of the workgroup; a thread takes 4
-// consecutive d of one column.  The pieces are listed by position (absent
-// slots repeat the last piece with weight 0) so that all of a thread's LDS
-// reads are issued together.
-template <typename Tag, bool kCols, int D, int NT>
-__device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLds<D, NT>& e,
-                                               unsigned mask, int b, int kvh, int ncols, bool bad,
-                                               float* plse, float* po) {
-    constexpr int NP = 2 * kNW;
+// consecutive d of one column.  The pieces are listed by position in NP
+// slots, NP >= the number of pieces (absent slots repeat the last piece with
+// weight 0), so that all of a thread's LDS reads are issued together.
+template <typename Tag, bool kCols, int D, int NT, int NP>
+__device__ __forceinline__ void finalize_edges_n(const DecodeArgs& a, const EdgeLds<D, NT>& e,
+                                                 unsigned mask, int b, int kvh, int ncols,
+                                                 bool bad, float* plse, float* po) {
     constexpr int OS = Dim<D>::OS;
     constexpr int D4 = D / 4;
     int idx[NP];
@@ -929,7 +928,7 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
             den += w * lv[k];
             num += w * ov[k];
         }
-        f32x4 o = den == 0.0f ? (f32x4){0.f, 0.f, 0.f, 0.f} : num / den;
+        f32x4 o = num * (den == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(den));
         if (bad) o = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                              __builtin_nanf("")};
         if (plse == nullptr) {
@@ -944,6 +943,24 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
             if (d == 0) plse[g] = bad ? __builtin_nanf("") : M + __log2f(den);
         }
     }
+}
+
+// The merge above with as few slots as the segment has pieces (1, 2, 4 or
+// all 2 kNW): at one wavefront per SIMD this loop runs on the critical path
+// at the end of the workgroup, and its length is set by its instruction count.
+template <typename Tag, bool kCols, int D, int NT>
+__device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLds<D, NT>& e,
+                                               unsigned mask, int b, int kvh, int ncols, bool bad,
+                                               float* plse, float* po) {
+    const int np = __builtin_popcount(mask);
+    if (np == 1)
+        finalize_edges_n<Tag, kCols, D, NT, 1>(a, e, mask, b, kvh, ncols, bad, plse, po);
+    else if (np == 2)
+        finalize_edges_n<Tag, kCols, D, NT, 2>(a, e, mask, b, kvh, ncols, bad, plse, po);
+    else if (np <= 4)
+        finalize_edges_n<Tag, kCols, D, NT, 4>(a, e, mask, b, kvh, ncols, bad, plse, po);
+    else
+        finalize_edges_n<Tag, kCols, D, NT, 2 * kNW>(a, e, mask, b, kvh, ncols, bad, plse, po);
 }
 
 // The prefix table of the balanced schedule (num_seqs + 1 ints) is dynamic
