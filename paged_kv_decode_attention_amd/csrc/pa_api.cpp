@@ -130,11 +130,14 @@ int balanced_workgroups(int head_dim) {
 }
 
 // The balanced schedule serves the matrix-core kernel when no partition
-// size is forced, the prefix table of context lengths fits in LDS and there
-// can be history to read.
+// size is forced, the prefix table of context lengths fits in LDS, its
+// work-unit sums fit in 32 bits and there can be history to read.
 bool use_balanced(bool mfma, int partition_size, int num_seqs, int max_context_len) {
+    const int64_t units = (int64_t)num_seqs *
+                          (pa::kMaxStartUnits + (int64_t)pa::kChunkUnits *
+                                               (((int64_t)max_context_len + pa::kChunk - 1) / pa::kChunk));
     return mfma && partition_size == 0 && num_seqs <= pa::kMaxBalancedSeqs &&
-           max_context_len > 0;
+           max_context_len > 0 && units <= INT32_MAX;
 }
 
 bool supported_shape(int head_dim, int block_size) {

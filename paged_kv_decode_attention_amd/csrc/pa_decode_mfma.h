@@ -974,8 +974,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     constexpr int NC = 16 * NT;   // columns per slot
     __shared__ EdgeLds<D, NT> edge;
     __shared__ int wsum[kNW];
+    constexpr int kSU = Kv::kE4M3 ? kStartUnitsE4M3 : kStartUnits16;
     int* pref = balanced_pref;
-    chunk_prefix(a, pref, wsum);
+    unit_prefix(a, kSU, pref, wsum);
     const int H_kv = a.num_kv_heads;
     const int64_t T = (int64_t)H_kv * pref[a.num_seqs];
     const int w = blockIdx.x;
@@ -998,11 +999,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
 
     for (int64_t x = ws; x < we;) {
         const int b = __builtin_amdgcn_readfirstlane(find_seq(pref, a.num_seqs, H_kv, x));
-        const int nb = __builtin_amdgcn_readfirstlane(pref[b + 1] - pref[b]);
+        const int nu = __builtin_amdgcn_readfirstlane(pref[b + 1] - pref[b]);
+        const int nb = (nu - kSU) / kChunkUnits;
         const int64_t off = x - (int64_t)H_kv * pref[b];
-        const int kvh = __builtin_amdgcn_readfirstlane((int)(off / nb));
-        const int c0 = __builtin_amdgcn_readfirstlane((int)(off - (int64_t)kvh * nb));
-        const int c1 = __builtin_amdgcn_readfirstlane((int)min((int64_t)nb, c0 + (we - x)));
+        const int kvh = __builtin_amdgcn_readfirstlane((int)(off / nu));
+        const int u0 = __builtin_amdgcn_readfirstlane((int)(off - (int64_t)kvh * nu));
+        const int u1 = __builtin_amdgcn_readfirstlane((int)min((int64_t)nu, u0 + (we - x)));
+        const int c0 = chunks_before_unit(u0, nb, kSU);
+        const int c1 = chunks_before_unit(u1, nb, kSU);
+        x += u1 - u0;
+        // no chunk starts here: nothing to do before the history's first
+        // chunk or after its last; inside it, an empty piece keeps the
+        // pieces of every range the history crosses in place
+        if (c0 == c1 && (c0 == 0 || c0 == nb)) continue;
         const int L = __builtin_amdgcn_readfirstlane(a.context_lens[b]);
         const int ntok = row_tokens<kRows>(a, b);
 
@@ -1010,7 +1019,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
 #pragma unroll
         for (int t = 0; t < NT; ++t) init_state(st[t]);
         int bad = 0;
-        attend_piece<Tag, BS, Kv, kRows, D, NT>(a, b, kvh, L, ntok, c0, c1, st, bad);
+        if (c0 < c1) attend_piece<Tag, BS, Kv, kRows, D, NT>(a, b, kvh, L, ntok, c0, c1, st, bad);
 
         const bool starts_before = c0 > 0;    // the segment began before this range
         const bool ends_after = c1 < nb;      // it continues past this range
@@ -1034,7 +1043,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
                 edge.bad[p] = bad;
             }
         }
-        x += c1 - c0;
     }
     __syncthreads();
 
@@ -1056,10 +1064,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         const int p1 = 32 - __builtin_clz(mask);
         const int b = k / H_kv;
         const int kvh = k - b * H_kv;
-        const int nb = pref[b + 1] - pref[b];
-        const int64_t xs = (int64_t)H_kv * pref[b] + (int64_t)kvh * nb;
-        const bool head = xs < xb;            // continues from the previous range
-        const bool tail = xs + nb > xe;       // continues into the next range
+        const int nu = pref[b + 1] - pref[b];
+        const int nb = (nu - kSU) / kChunkUnits;
+        // units where the history's first and last chunks start
+        const int64_t xf = (int64_t)H_kv * pref[b] + (int64_t)kvh * nu + kSU;
+        const int64_t xl = xf + (int64_t)kChunkUnits * (nb - 1);
+        const bool head = xf < xb;            // continues from the previous range
+        const bool tail = xl >= xe;           // continues into the next range
         const int ncols = row_tokens<kRows>(a, b) * a.group;
         if (!head && !tail) {
             finalize_edges<Tag, kCols, D, NT>(a, edge, mask, b, kvh, ncols, bad != 0, nullptr,
@@ -1068,7 +1079,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
             const uint64_t slot = (uint64_t)w * 2 + (head ? 0 : 1);
             finalize_edges<Tag, kCols, D, NT>(a, edge, mask, b, kvh, ncols, bad != 0,
                                               a.ws_lse + slot * NC, a.ws_out + slot * NC * D);
-            if (!head) meta.x = k, meta.y = range_owner(xs + nb - 1, T, a.num_wg);
+            if (!head) meta.x = k, meta.y = range_owner(xl, T, a.num_wg);
         }
         p = p1;
     }

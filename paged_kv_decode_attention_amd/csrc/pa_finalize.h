@@ -161,6 +161,19 @@ __device__ __forceinline__ int seq_chunks(int L, int max_context_len) {
     return (L <= 0 || L > max_context_len) ? 0 : (L + kChunk - 1) / kChunk;
 }
 
+// Work units of a history of L tokens whose start counts su units (the
+// balanced schedule's cost model, kChunkUnits per chunk).
+__device__ __forceinline__ int seq_units(int L, int max_context_len, int su) {
+    const int nb = seq_chunks(L, max_context_len);
+    return nb == 0 ? 0 : su + kChunkUnits * nb;
+}
+
+// Chunks of a history of nb chunks (start: su units) that start before unit
+// u (0 <= u <= its units): the first chunk a range beginning at u holds.
+__device__ __forceinline__ int chunks_before_unit(int u, int nb, int su) {
+    return u <= su ? 0 : min(nb, (u - su + kChunkUnits - 1) / kChunkUnits);
+}
+
 // First work item of workgroup w when T items are cut into nwg equal ranges,
 // and the workgroup whose range holds item x (T > 0).
 __device__ __forceinline__ int64_t range_start(int w, int64_t T, int nwg) {
@@ -170,17 +183,17 @@ __device__ __forceinline__ int range_owner(int64_t x, int64_t T, int nwg) {
     return (int)(((x + 1) * nwg + T - 1) / T - 1);
 }
 
-// Inclusive prefix sums of seq_chunks over the sequences into LDS:
-// pref[0] = 0, pref[1 + i] = chunks of sequences 0..i.  wsum: LDS scratch of
+// Inclusive prefix sums of seq_units (start: su units) over the sequences
+// into LDS: pref[0] = 0, pref[1 + i] = units of sequences 0..i (per KV head).  wsum: LDS scratch of
 // one int per wavefront.  Called by every thread of the workgroup.
-__device__ __forceinline__ void chunk_prefix(const DecodeArgs& a, int* pref, int* wsum) {
+__device__ __forceinline__ void unit_prefix(const DecodeArgs& a, int su, int* pref, int* wsum) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
     if (threadIdx.x == 0) pref[0] = 0;
     for (int base = 0; base < a.num_seqs; base += blockDim.x) {
         const int i = base + threadIdx.x;
-        int x = i < a.num_seqs ? seq_chunks(a.context_lens[i], a.max_context_len) : 0;
+        int x = i < a.num_seqs ? seq_units(a.context_lens[i], a.max_context_len, su) : 0;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int y = __shfl_up(x, off);
@@ -195,7 +208,7 @@ __device__ __forceinline__ void chunk_prefix(const DecodeArgs& a, int* pref, int
     }
 }
 
-// Sequence whose chunks (counted per kv head) contain flattened work item x:
+// Sequence whose units (counted per kv head) contain flattened work item x:
 // the largest b with num_kv_heads * pref[b] <= x and a non-empty history.
 __device__ __forceinline__ int find_seq(const int* pref, int num_seqs, int num_kv_heads,
                                         int64_t x) {

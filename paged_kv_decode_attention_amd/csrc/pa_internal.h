@@ -71,6 +71,18 @@ constexpr int kMaxBalancedSeqs = 2048; // prefix table of the balanced schedule 
 
 constexpr int kDecodeThreads = 256;   // 4 wavefronts per workgroup
 constexpr int kChunk = 32;            // tokens a wavefront handles per step
+// Work units of the balanced schedule.  A (decode row, KV head) history of
+// nb chunks counts s + kChunkUnits nb units: its chunk c starts at unit
+// s + kChunkUnits c, and the s units before its first chunk stand for the
+// fixed cost of starting a history (loading its table row and first chunk
+// with nothing else in flight, and writing its state).  s depends on the
+// cache format (an E4M3 chunk streams in half the time of a 16-bit one);
+// the values are tuned by measurement.  A range of units holds the chunks
+// that start inside it.
+constexpr int kChunkUnits = 2;
+constexpr int kStartUnits16 = 1;
+constexpr int kStartUnitsE4M3 = 3;
+constexpr int kMaxStartUnits = 3;
 
 // Kernel families.
 enum KernelKind { kAuto = 0, kGeneric = 1, kMfma = 2 };
