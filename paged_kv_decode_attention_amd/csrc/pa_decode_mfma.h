@@ -963,8 +963,8 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
         finalize_edges_n<Tag, kCols, D, NT, 2 * kNW>(a, e, mask, b, kvh, ncols, bad, plse, po);
 }
 
-// The prefix table of the balanced schedule (num_seqs + 1 ints) is dynamic
-// LDS, sized at launch.
+// The prefix table of the balanced schedule (num_seqs + 1 ints) and the
+// context lengths (num_seqs ints) are dynamic LDS, sized at launch.
 extern __shared__ int balanced_pref[];
 
 template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
@@ -976,7 +976,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     __shared__ int wsum[kNW];
     constexpr int kSU = Kv::kE4M3 ? kStartUnitsE4M3 : kStartUnits16;
     int* pref = balanced_pref;
-    unit_prefix(a, kSU, pref, wsum);
+    int* lens = balanced_pref + a.num_seqs + 1;
+    unit_prefix(a, kSU, pref, lens, wsum);
     const int H_kv = a.num_kv_heads;
     const int64_t T = (int64_t)H_kv * pref[a.num_seqs];
     const int w = blockIdx.x;
@@ -998,11 +999,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     if (lane < 2) edge.key[2 * wave + lane] = -1;
 
     for (int64_t x = ws; x < we;) {
-        const int b = __builtin_amdgcn_readfirstlane(find_seq(pref, a.num_seqs, H_kv, x));
+        const int b = find_seq(pref, a.num_seqs, H_kv, x);
         const int nu = __builtin_amdgcn_readfirstlane(pref[b + 1] - pref[b]);
         const int nb = (nu - kSU) / kChunkUnits;
         const int64_t off = x - (int64_t)H_kv * pref[b];
-        const int kvh = __builtin_amdgcn_readfirstlane((int)(off / nu));
+        const int kvh = __builtin_amdgcn_readfirstlane(
+            (off >> 31) == 0 ? (int)((uint32_t)off / (uint32_t)nu) : (int)(off / nu));
         const int u0 = __builtin_amdgcn_readfirstlane((int)(off - (int64_t)kvh * nu));
         const int u1 = __builtin_amdgcn_readfirstlane((int)min((int64_t)nu, u0 + (we - x)));
         const int c0 = chunks_before_unit(u0, nb, kSU);
@@ -1012,7 +1014,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         // chunk or after its last; inside it, an empty piece keeps the
         // pieces of every range the history crosses in place
         if (c0 == c1 && (c0 == 0 || c0 == nb)) continue;
-        const int L = __builtin_amdgcn_readfirstlane(a.context_lens[b]);
+        const int L = __builtin_amdgcn_readfirstlane(lens[b]);
         const int ntok = row_tokens<kRows>(a, b);
 
         WaveState<D> st[NT];
@@ -1089,7 +1091,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
 template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
 hipError_t launch_rows(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
-        const size_t pref_bytes = (size_t)(a.num_seqs + 1) * sizeof(int);
+        const size_t pref_bytes = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
         hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv, kRows, D, NT>), dim3(a.num_wg),
                            dim3(kDecodeThreads), pref_bytes, s, a);
     } else {

@@ -176,24 +176,34 @@ __device__ __forceinline__ int chunks_before_unit(int u, int nb, int su) {
 
 // First work item of workgroup w when T items are cut into nwg equal ranges,
 // and the workgroup whose range holds item x (T > 0).
+// (32-bit division when the operands allow: the 64-bit one is a long
+// scalar routine, and these sit on the path to a workgroup's first load.)
 __device__ __forceinline__ int64_t range_start(int w, int64_t T, int nwg) {
+    if ((T >> 21) == 0) return (uint32_t)w * (uint32_t)T / (uint32_t)nwg;   // w <= nwg <= 2^11
     return (int64_t)w * T / nwg;
 }
 __device__ __forceinline__ int range_owner(int64_t x, int64_t T, int nwg) {
-    return (int)(((x + 1) * nwg + T - 1) / T - 1);
+    const int64_t num = (x + 1) * nwg + T - 1;
+    if ((num >> 32) == 0) return (int)((uint32_t)num / (uint32_t)T) - 1;
+    return (int)(num / T - 1);
 }
 
 // Inclusive prefix sums of seq_units (start: su units) over the sequences
-// into LDS: pref[0] = 0, pref[1 + i] = units of sequences 0..i (per KV head).  wsum: LDS scratch of
-// one int per wavefront.  Called by every thread of the workgroup.
-__device__ __forceinline__ void unit_prefix(const DecodeArgs& a, int su, int* pref, int* wsum) {
+// into LDS, pref[0] = 0, pref[1 + i] = units of sequences 0..i (per KV
+// head), and the context lengths into lens[0 .. num_seqs).  wsum: LDS
+// scratch of one int per wavefront.  Called by every thread of the
+// workgroup.
+__device__ __forceinline__ void unit_prefix(const DecodeArgs& a, int su, int* pref, int* lens,
+                                            int* wsum) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
     if (threadIdx.x == 0) pref[0] = 0;
     for (int base = 0; base < a.num_seqs; base += blockDim.x) {
         const int i = base + threadIdx.x;
-        int x = i < a.num_seqs ? seq_units(a.context_lens[i], a.max_context_len, su) : 0;
+        const int L = i < a.num_seqs ? a.context_lens[i] : 0;
+        if (i < a.num_seqs) lens[i] = L;
+        int x = i < a.num_seqs ? seq_units(L, a.max_context_len, su) : 0;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const int y = __shfl_up(x, off);
@@ -210,14 +220,24 @@ __device__ __forceinline__ void unit_prefix(const DecodeArgs& a, int su, int* pr
 
 // Sequence whose units (counted per kv head) contain flattened work item x:
 // the largest b with num_kv_heads * pref[b] <= x and a non-empty history.
+// Wavefront-parallel: each round tests 64 evenly spaced candidates with one
+// LDS read per lane and keeps the span after the last that passes (one
+// round up to 64 sequences, two up to 4096).  Called with the whole
+// wavefront active; the result is the same in every lane.
 __device__ __forceinline__ int find_seq(const int* pref, int num_seqs, int num_kv_heads,
                                         int64_t x) {
-    int lo = 0, hi = num_seqs - 1;     // answer in [lo, hi]
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)num_kv_heads * pref[mid] <= x) lo = mid; else hi = mid - 1;
+    const int lane = threadIdx.x & 63;
+    int lo = 0, n = num_seqs;      // answer in [lo, lo + n)
+    while (n > 1) {
+        const int stride = (n + 63) >> 6;
+        const int i = lo + lane * stride;
+        const bool ok = lane * stride < n && (int64_t)num_kv_heads * pref[i] <= x;
+        const uint64_t m = __ballot(ok);        // lanes 0 .. j pass (pref is nondecreasing)
+        const int j = 63 - __builtin_clzll(m);  // lane 0 passes: pref[lo] <= x
+        lo += j * stride;
+        n = min(stride, n - j * stride);
     }
-    return lo;
+    return __builtin_amdgcn_readfirstlane(lo);
 }
 
 }  // namespace pa
