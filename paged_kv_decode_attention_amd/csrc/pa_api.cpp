@@ -218,6 +218,13 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
 
 }  // extern "C"
 
+// Verify rows whose row map the balanced decode kernel computes itself.
+struct VerifyFold {
+    const int32_t* query_start;
+    const int32_t* src_lens;
+    int num_src_seqs, max_query_len, u;
+};
+
 static int decode_impl(void* out, const void* query, const void* new_key,
                        const void* new_value, const void* key_cache, const void* value_cache,
                        const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
@@ -227,7 +234,8 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                        void* workspace, size_t workspace_bytes, void* hip_stream,
                        int kv_format = pa::kKvSame, float k_scale = 1.0f, float v_scale = 1.0f,
                        const int32_t* table_rows = nullptr, const int32_t* row_tokens = nullptr,
-                       int kernel_kind = -1, int col_tiles = 1) {
+                       int kernel_kind = -1, int col_tiles = 1,
+                       const VerifyFold* fold = nullptr) {
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
     const bool e4m3 = kv_format == pa::kKvE4M3;
     if (e4m3 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
@@ -279,7 +287,11 @@ static int decode_impl(void* out, const void* query, const void* new_key,
         return fail(PA_ERR_UNSUPPORTED, "FP8 caches are served by the matrix-core kernel only "
                     "(bf16/f16 queries, head_dim 64/128/256, block_size 8/16/32/64, group <= 16, "
                     "or <= 32 at head_dim 64/128)");
-    const bool balanced = use_balanced(use_mfma, partition_size, num_seqs, max_context_len);
+    // a row map held in memory is read by the fixed schedule's kernels only
+    const bool balanced = table_rows == nullptr &&
+                          use_balanced(use_mfma, partition_size, num_seqs, max_context_len);
+    if (fold && !balanced)
+        return fail(PA_ERR_INVALID_ARG, "internal: verify row map folded off the balanced path");
 
     const int P = partition_size ? partition_size
                                  : heuristic_partition(num_seqs, num_kv_heads, block_size,
@@ -309,6 +321,13 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     a.context_lens = context_lens;
     a.table_rows = table_rows;
     a.row_tokens = row_tokens;
+    if (fold) {
+        a.query_start = fold->query_start;
+        a.src_lens = fold->src_lens;
+        a.num_src_seqs = fold->num_src_seqs;
+        a.max_query_len = fold->max_query_len;
+        a.row_group = fold->u;
+    }
     a.ws_lse = needs_ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_off)
                         : nullptr;
     a.ws_out = needs_ws ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.out_off)
@@ -506,6 +525,19 @@ int pa_paged_attention_verify(void* out, const void* query, const void* key_cach
                        ? 2
                        : 1;
     const int u = mfma ? std::max(1, pa::kMaxGroup * nt / gqa_group_size) : 1;
+    // On the balanced schedule the decode kernel computes the row map in its
+    // prologue (one launch fewer); otherwise a kernel writes it to the
+    // workspace for the fixed schedule's kernels.
+    if (mfma && use_balanced(true, partition_size, total_queries, max_context_len) &&
+        num_seqs <= pa::kMaxVerifyFoldSeqs) {
+        const VerifyFold fold{query_start, context_lens, num_seqs, max_query_len, u};
+        return decode_impl(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                           context_lens, total_queries, num_heads, num_kv_heads, gqa_group_size,
+                           head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                           scale, dtype, partition_size, dec > 0 ? workspace : nullptr, dec,
+                           hip_stream, pa::kKvSame, 1.0f, 1.0f, nullptr, nullptr, kind, nt,
+                           &fold);
+    }
     hipError_t e = pa::launch_verify_rows(query_start, context_lens, num_seqs, total_queries,
                                           max_query_len, max_context_len, u, rows, lens, toks,
                                           static_cast<hipStream_t>(hip_stream));

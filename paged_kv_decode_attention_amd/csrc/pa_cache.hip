@@ -87,39 +87,22 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
                 cv[4] | cv[5] << 8 | cv[6] << 16 | cv[7] << 24};
 }
 
-// Verify mode: query row r belongs to the sequence b with query_start[b] <=
-// r < query_start[b+1]; it is that sequence's token i = r - query_start[b]
-// of q_b, at history position L_b - q_b + i, and attends the L_b - q_b + i + 1
-// positions up to it.  The sequence's rows are grouped u at a time (u =
-// tokens_per_row): the decode row starting at the group's first row i
-// carries n = min(u, q_b - i) rows, and its length is that of its last row,
-// L_b - q_b + i + n; the group's other rows carry none (length 0).  Every
-// row is written on every call: rows whose sequence cannot be found, whose
-// q_b exceeds max_query_len or L_b, or whose L_b is invalid each carry
-// themselves with length -1 (the decode kernels give them NaN rows) and
-// table row 0.
+// Verify mode's row map (verify_row) of every query row, for the kernels
+// that read it from memory (the fixed schedule and the vector-ALU kernel;
+// the balanced schedule computes it in its own prologue).  Every row is
+// written on every call.
 __global__ __launch_bounds__(kCopyThreads) void verify_rows_kernel(
     const int32_t* __restrict__ query_start, const int32_t* __restrict__ context_lens,
     int num_seqs, int total_queries, int max_query_len, int max_context_len, int u,
     int32_t* table_rows, int32_t* lens, int32_t* row_tokens) {
     const int r = blockIdx.x * kCopyThreads + threadIdx.x;
     if (r >= total_queries) return;
-    int lo = 0, hi = num_seqs - 1;   // largest b with query_start[b] <= r
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (query_start[mid] <= r) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const int q0 = query_start[b];
-    const int q1 = query_start[b + 1];
-    const int L = context_lens[b];
-    const int qb = q1 - q0;
-    const bool ok = q0 <= r && r < q1 && qb <= max_query_len && L >= qb && L <= max_context_len;
-    const int i = r - q0;
-    const int n = !ok ? 1 : i % u == 0 ? min(u, qb - i) : 0;
-    table_rows[r] = ok ? b : 0;
-    lens[r] = !ok ? -1 : n > 0 ? L - qb + i + n : 0;
-    row_tokens[r] = n;
+    const VerifyRow v = verify_row([=](int i) { return query_start[i]; },
+                                   [=](int i) { return context_lens[i]; }, num_seqs,
+                                   max_query_len, max_context_len, u, r);
+    table_rows[r] = v.table_row;
+    lens[r] = v.len;
+    row_tokens[r] = v.ntok;
 }
 
 // Sequence b's newest token (history position L_b - 1): key[b, h, c] ->

@@ -435,7 +435,14 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, const ConstI32
     const uint64_t r = kv_row(pb, kvh, pos % BS, a.num_kv_heads, BS);
     const u32x4 x = load16(from);
     if constexpr (Kv::kE4M3) {
-        const float inv = is_k ? a.k_inv_scale : a.v_inv_scale;
+        // both scales as register values first: a per-lane choice between
+        // two kernel-argument fields would otherwise become a per-lane load
+        // from a private copy of the arguments
+        const float ki = __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.k_inv_scale)));
+        const float vi = __builtin_bit_cast(
+            float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, a.v_inv_scale)));
+        const float inv = is_k ? ki : vi;
         uint32_t cd[8];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -809,13 +816,14 @@ struct EdgeLds {
 };
 
 // Wavefront state over chunks [cs, ce) of (decode row b, KV head kvh) with
-// a history of L tokens (ntok query rows carried: verify columns): the
-// two-buffer pipeline of attend_segment with the chunks taken in order.
-// Includes the append step when the newest history position lies in
-// [cs, ce): this wavefront alone reads that chunk.
+// a history of L tokens in block-table row trow (ntok query rows carried:
+// verify columns): the two-buffer pipeline of attend_segment with the chunks
+// taken in order.  Includes the append step when the newest history position
+// lies in [cs, ce): this wavefront alone reads that chunk.
 template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
-__device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh, int L, int ntok,
-                                             int cs, int ce, WaveState<D>* st, int& bad) {
+__device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int trow, int kvh, int L,
+                                             int ntok, int cs, int ce, WaveState<D>* st,
+                                             int& bad) {
     constexpr bool kCols = kRows == 1;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;
@@ -827,7 +835,7 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int kvh
     tile_columns<Kv, kCols, D, NT>(a, b, kvh, n, q, ntok, L, t_end, qop, t_col);
 
     const ConstI32* row =
-        (const ConstI32*)(a.block_tables) + table_row_offset<kRows>(a, b);
+        (const ConstI32*)(a.block_tables) + (uint64_t)trow * a.max_blocks_per_seq;
     const uint32_t koff = lane_koff<Kv, D>(n, q);
     const uint32_t voff = lane_voff<Kv, D>(n, q);
 
@@ -963,9 +971,16 @@ __device__ __forceinline__ void finalize_edges(const DecodeArgs& a, const EdgeLd
         finalize_edges_n<Tag, kCols, D, NT, 2 * kNW>(a, e, mask, b, kvh, ncols, bad, plse, po);
 }
 
-// The prefix table of the balanced schedule (num_seqs + 1 ints) and the
-// context lengths (num_seqs ints) are dynamic LDS, sized at launch.
+// The prefix table of the balanced schedule (num_seqs + 1 ints), the decode
+// rows' context lengths (num_seqs ints) and, for verify rows, their row map
+// (num_seqs ints: block-table row * 64 + query rows carried) are dynamic
+// LDS, sized at launch.
 extern __shared__ int balanced_pref[];
+
+template <int kRows>
+constexpr int balanced_lds_ints(int num_seqs) {
+    return (kRows == 1 ? 3 : 2) * num_seqs + 1;
+}
 
 template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
@@ -976,11 +991,54 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
     __shared__ int wsum[kNW];
     constexpr int kSU = Kv::kE4M3 ? kStartUnitsE4M3 : kStartUnits16;
     int* pref = balanced_pref;
-    int* lens = balanced_pref + a.num_seqs + 1;
-    unit_prefix(a, kSU, pref, lens, wsum);
+    int* lens = pref + a.num_seqs + 1;
+    int* rmap = lens + a.num_seqs;     // verify rows only
+    if constexpr (kRows == 1) {
+        // Verify rows: the row map of every decode row, from the sequences'
+        // query starts and lengths staged in the edge LDS (untouched until
+        // the first piece ends; unit_prefix's barriers come first).
+        static_assert(sizeof(edge.o) >= (2 * kMaxVerifyFoldSeqs + 1) * sizeof(int),
+                      "edge LDS too small to stage the sequences");
+        int* qs = reinterpret_cast<int*>(&edge.o);
+        int* sl = qs + a.num_src_seqs + 1;
+        for (int i = threadIdx.x; i <= a.num_src_seqs; i += blockDim.x) {
+            qs[i] = a.query_start[i];
+            if (i < a.num_src_seqs) sl[i] = a.src_lens[i];
+        }
+        __syncthreads();
+        unit_prefix(a, kSU, [&](int r) {
+            const VerifyRow v = verify_row([=](int i) { return qs[i]; },
+                                           [=](int i) { return sl[i]; }, a.num_src_seqs,
+                                           a.max_query_len, a.max_context_len, a.row_group, r);
+            rmap[r] = v.table_row * 64 + v.ntok;
+            return v.len;
+        }, pref, lens, wsum);
+    } else {
+        unit_prefix(a, kSU, [&](int r) { return a.context_lens[r]; }, pref, lens, wsum);
+    }
+    // query rows decode row b carries, and its block-table row (b is uniform)
+    auto ntok_of = [&](int b) {
+        return kRows == 1 ? __builtin_amdgcn_readfirstlane(rmap[b] & 63) : 1;
+    };
+    auto trow_of = [&](int b) {
+        return kRows == 1 ? __builtin_amdgcn_readfirstlane(rmap[b] >> 6) : b;
+    };
     const int H_kv = a.num_kv_heads;
     const int64_t T = (int64_t)H_kv * pref[a.num_seqs];
     const int w = blockIdx.x;
+
+    // Output rows of decode rows with no history to attend: zeros for an
+    // empty one, NaN for an invalid length (rows w, w + num_wg, ...).
+    for (int r = w; r < a.num_seqs; r += a.num_wg) {
+        const int L = lens[r];
+        if (L > 0 && L <= a.max_context_len) continue;
+        const float v = L == 0 ? 0.0f : __builtin_nanf("");
+        const int64_t count = (int64_t)ntok_of(r) * a.num_heads * D;
+        const uint64_t base = (uint64_t)r * a.num_heads * D;
+        for (int64_t i = threadIdx.x; i < count; i += blockDim.x)
+            store_elem(Tag(), a.out, base + i, v);
+    }
+
     // record of the segment whose first piece this range leaves in [w][1]
     int4 meta = make_int4(-1, 0, (int)(uint32_t)T, (int)(T >> 32));
     const int64_t xb = T > 0 ? range_start(w, T, a.num_wg) : 0;
@@ -1015,13 +1073,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         // pieces of every range the history crosses in place
         if (c0 == c1 && (c0 == 0 || c0 == nb)) continue;
         const int L = __builtin_amdgcn_readfirstlane(lens[b]);
-        const int ntok = row_tokens<kRows>(a, b);
+        const int ntok = ntok_of(b);
 
         WaveState<D> st[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) init_state(st[t]);
         int bad = 0;
-        if (c0 < c1) attend_piece<Tag, BS, Kv, kRows, D, NT>(a, b, kvh, L, ntok, c0, c1, st, bad);
+        if (c0 < c1)
+            attend_piece<Tag, BS, Kv, kRows, D, NT>(a, b, trow_of(b), kvh, L, ntok, c0, c1, st,
+                                                    bad);
 
         const bool starts_before = c0 > 0;    // the segment began before this range
         const bool ends_after = c1 < nb;      // it continues past this range
@@ -1073,7 +1133,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         const int64_t xl = xf + (int64_t)kChunkUnits * (nb - 1);
         const bool head = xf < xb;            // continues from the previous range
         const bool tail = xl >= xe;           // continues into the next range
-        const int ncols = row_tokens<kRows>(a, b) * a.group;
+        const int ntok = ntok_of(b);
+        const int ncols = ntok * a.group;
         if (!head && !tail) {
             finalize_edges<Tag, kCols, D, NT>(a, edge, mask, b, kvh, ncols, bad != 0, nullptr,
                                               nullptr);
@@ -1081,7 +1142,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
             const uint64_t slot = (uint64_t)w * 2 + (head ? 0 : 1);
             finalize_edges<Tag, kCols, D, NT>(a, edge, mask, b, kvh, ncols, bad != 0,
                                               a.ws_lse + slot * NC, a.ws_out + slot * NC * D);
-            if (!head) meta.x = k, meta.y = range_owner(xl, T, a.num_wg);
+            if (!head) meta.x = k, meta.y = range_owner(xl, T, a.num_wg) | ntok << 16;
         }
         p = p1;
     }
@@ -1091,7 +1152,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
 template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
 hipError_t launch_rows(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
-        const size_t pref_bytes = (size_t)(2 * a.num_seqs + 1) * sizeof(int);
+        const size_t pref_bytes = (size_t)balanced_lds_ints<kRows>(a.num_seqs) * sizeof(int);
         hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv, kRows, D, NT>), dim3(a.num_wg),
                            dim3(kDecodeThreads), pref_bytes, s, a);
     } else {
@@ -1117,7 +1178,8 @@ hipError_t launch_tiles(const DecodeArgs& a, hipStream_t s) {
 template <typename Tag, int BS, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
     if (a.kv_format == kKvE4M3) return launch_tiles<Tag, BS, KvE4M3, 0, D>(a, s);
-    if (a.table_rows == nullptr) return launch_tiles<Tag, BS, KvSame, 0, D>(a, s);
+    if (a.table_rows == nullptr && a.query_start == nullptr)
+        return launch_tiles<Tag, BS, KvSame, 0, D>(a, s);
     return launch_tiles<Tag, BS, KvSame, 1, D>(a, s);
 }
 

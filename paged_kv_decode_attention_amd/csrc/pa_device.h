@@ -132,4 +132,38 @@ __device__ __forceinline__ float rescale_weight(float m, float M) {
     return m == -INFINITY ? 0.0f : fast_exp2(m - M);
 }
 
+// Verify mode's row map, for query row r: the sequence b with qs[b] <= r <
+// qs[b + 1] (qs: query_start, nsrc + 1 entries, in LDS or global memory) is
+// found by binary search; its token i = r - qs[b] of q_b sits at history
+// position L_b - q_b + i (L_b = lens(b)).  Rows are grouped u at a time: the
+// row at a group's start carries n = min(u, q_b - i) query rows and the
+// length of its last one, L_b - q_b + i + n; the group's other rows carry
+// none (length 0).  A row whose sequence cannot be found, whose q_b exceeds
+// max_query_len or L_b, or whose L_b is invalid carries itself with length
+// -1 (a NaN row) and table row 0.
+struct VerifyRow {
+    int table_row;   // block-table row
+    int len;         // history length the decode row attends (its last row's)
+    int ntok;        // query rows it carries
+};
+
+template <typename QS, typename Lens>
+__device__ __forceinline__ VerifyRow verify_row(QS qs, Lens lens, int nsrc, int max_query_len,
+                                                int max_context_len, int u, int r) {
+    int lo = 0, hi = nsrc - 1;   // largest b with qs[b] <= r
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (qs(mid) <= r) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int q0 = qs(b);
+    const int q1 = qs(b + 1);
+    const int L = lens(b);
+    const int qb = q1 - q0;
+    const bool ok = q0 <= r && r < q1 && qb <= max_query_len && L >= qb && L <= max_context_len;
+    const int i = r - q0;
+    const int n = !ok ? 1 : i % u == 0 ? min(u, qb - i) : 0;
+    return VerifyRow{ok ? b : 0, !ok ? -1 : n > 0 ? L - qb + i + n : 0, n};
+}
+
 }  // namespace pa

@@ -188,20 +188,21 @@ __device__ __forceinline__ int range_owner(int64_t x, int64_t T, int nwg) {
     return (int)(num / T - 1);
 }
 
-// Inclusive prefix sums of seq_units (start: su units) over the sequences
-// into LDS, pref[0] = 0, pref[1 + i] = units of sequences 0..i (per KV
-// head), and the context lengths into lens[0 .. num_seqs).  wsum: LDS
-// scratch of one int per wavefront.  Called by every thread of the
+// Inclusive prefix sums of seq_units (start: su units) over the decode rows
+// into LDS, pref[0] = 0, pref[1 + i] = units of rows 0..i (per KV head),
+// and the rows' context lengths len_of(i) into lens[0 .. num_seqs).  wsum:
+// LDS scratch of one int per wavefront.  Called by every thread of the
 // workgroup.
-__device__ __forceinline__ void unit_prefix(const DecodeArgs& a, int su, int* pref, int* lens,
-                                            int* wsum) {
+template <typename LenOf>
+__device__ __forceinline__ void unit_prefix(const DecodeArgs& a, int su, LenOf len_of, int* pref,
+                                            int* lens, int* wsum) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
     if (threadIdx.x == 0) pref[0] = 0;
     for (int base = 0; base < a.num_seqs; base += blockDim.x) {
         const int i = base + threadIdx.x;
-        const int L = i < a.num_seqs ? a.context_lens[i] : 0;
+        const int L = i < a.num_seqs ? len_of(i) : 0;
         if (i < a.num_seqs) lens[i] = L;
         int x = i < a.num_seqs ? seq_units(L, a.max_context_len, su) : 0;
 #pragma unroll

@@ -27,6 +27,14 @@ struct DecodeArgs {
     // n / group) oldest positions.  n_b = 0: the rows are carried by an
     // earlier decode row (its context_lens entry is 0 and nothing is written).
     const int32_t* row_tokens;
+    // Verify rows on the balanced schedule: the kernels compute the row map
+    // (verify_row) themselves from query_start [num_src_seqs + 1] and
+    // src_lens [num_src_seqs] (the sequences' context lengths), with
+    // table_rows, row_tokens and context_lens unused; null otherwise.
+    const int32_t* query_start;
+    const int32_t* src_lens;
+    int num_src_seqs, max_query_len;
+    int row_group;             // u: query rows a decode row carries at most
     const void* new_key;       // [S, H_kv, D] appended token per sequence, or null
     const void* new_value;     // [S, H_kv, D]
     float* ws_lse;             // [S, H, num_parts] float32 (log2 units)
@@ -54,20 +62,27 @@ enum KvFormat { kKvSame = 0, kKvE4M3 = 1 };
 // Work schedules of the decode kernels.
 //   kFixed: workgroup (kv head, sequence, p) takes tokens [p P, (p+1) P);
 //     partition states are indexed [S, H, num_parts].
-//   kBalanced: the (sequence, kv head, 32-token chunk) work list, in that
-//     order, is cut into num_wg equal contiguous ranges, one per workgroup;
+//   kBalanced: the (sequence, kv head, work unit) list (kChunkUnits per
+//     32-token chunk plus a start cost per history), in that order, is cut
+//     into num_wg equal contiguous ranges, one per workgroup;
 //     a (sequence, kv head) cut by a range boundary leaves one state per
 //     piece in slot [w][0] (the piece that continues from workgroup w-1) or
 //     [w][1] (the piece that continues into w+1), each slot holding up to
-//     kMaxGroup heads.  Record ws_meta[w] = {key, w1, T lo, T hi} names the
-//     segment whose first piece is slot [w][1] (key = sequence * H_kv + KV
-//     head, -1 if none), the last range w1 holding it, and the work-list
-//     size T; the decode kernel writes every record on every launch.
+//     kMaxGroup heads.  Record ws_meta[w] = {key, w1 + 65536 n, T lo, T hi}
+//     names the segment whose first piece is slot [w][1] (key = sequence *
+//     H_kv + KV head, -1 if none), the last range w1 holding it, the query
+//     rows n its decode row carries, and the work-list size T; the decode
+//     kernel writes every record on every launch, and also the output rows
+//     of decode rows with an empty (zeros) or invalid (NaN) history.
 enum Schedule { kFixed = 0, kBalanced = 1 };
 constexpr int kMaxGroup = 16;          // heads per column tile (matrix-core kernel)
 constexpr int kMaxColTiles = 2;        // column tiles per decode row (verify)
 constexpr int kMaxBalancedWg = 1024;   // workspace is sized for this many
 constexpr int kMaxBalancedSeqs = 2048; // prefix table of the balanced schedule (dynamic LDS)
+// Verify rows on the balanced schedule compute their row map in the decode
+// kernel's prologue from the sequences' query starts and lengths, staged in
+// its edge LDS (at least 8704 floats): up to this many sequences.
+constexpr int kMaxVerifyFoldSeqs = 4096;
 
 constexpr int kDecodeThreads = 256;   // 4 wavefronts per workgroup
 constexpr int kChunk = 32;            // tokens a wavefront handles per step

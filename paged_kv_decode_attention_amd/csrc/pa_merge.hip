@@ -22,34 +22,19 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
     merge_pieces<Tag>(a, b, kvh, row_tokens(a, b) * a.group, nparts);
 }
 
-// Balanced schedule.  Workgroup w < num_wg merges the segment whose first
-// piece range w left in slot [w][1], as named by record ws_meta[w]: the
-// pieces are [w][1] and [w'][0] for every non-empty range w' in (w, w1], in
-// token order.  The record and the first kSpec candidate pieces are loaded
+// Balanced schedule.  Workgroup w merges the segment whose first piece
+// range w left in slot [w][1], as named by record ws_meta[w]: the pieces
+// are [w][1] and [w'][0] for every non-empty range w' in (w, w1], in token
+// order, for the n G columns of its decode row (n query rows carried, from
+// the record).  The record and the first kSpec candidate pieces are loaded
 // together (one memory round trip for the common case of a segment spread
-// over at most kSpec ranges).  Workgroup num_wg + b writes the rows of
-// decode row b when the decode kernel has none to write: zeros for an empty
-// history, NaN for an invalid context length.  A thread takes 4
-// consecutive d of one column (NC columns per slot, 16 or 32): NC * D / 4
-// threads.
+// over at most kSpec ranges).  (The rows of decode rows with no history are
+// written by the decode kernel.)  A thread takes 4 consecutive d of one
+// column (NC columns per slot, 16 or 32): NC * D / 4 threads.
 template <typename Tag, int D, int NC>
 __global__ __launch_bounds__(NC * D / 4) void merge_balanced(DecodeArgs a) {
     constexpr int kSpec = 4;
     const int w = blockIdx.x;
-    if (w >= a.num_wg) {
-        // the query rows decode row b carries (b .. b + n_b - 1), every
-        // head: contiguous in out
-        const int b = w - a.num_wg;
-        const int L = a.context_lens[b];
-        const bool invalid = L < 0 || L > a.max_context_len;
-        if (!invalid && L != 0) return;
-        const float v = invalid ? __builtin_nanf("") : 0.0f;
-        const int64_t count = (int64_t)row_tokens(a, b) * a.num_heads * a.head_dim;
-        const uint64_t base = (uint64_t)b * a.num_heads * a.head_dim;
-        for (int64_t i = threadIdx.x; i < count; i += blockDim.x)
-            store_elem(Tag(), a.out, base + i, v);
-        return;
-    }
     const int g = threadIdx.x / (D / 4);
     const int d = (threadIdx.x % (D / 4)) * 4;
     const int nwg = a.num_wg;
@@ -64,13 +49,14 @@ __global__ __launch_bounds__(NC * D / 4) void merge_balanced(DecodeArgs a) {
         lse[k] = a.ws_lse[slot_row(slot)];
     }
     const int key = meta.x;
-    const int w1 = meta.y;
+    const int w1 = meta.y & 0xffff;
+    const int ntok = meta.y >> 16;
     // (a record outside these bounds cannot come from the decode kernel)
     if (key < 0 || key >= a.num_seqs * a.num_kv_heads || w1 <= w || w1 >= nwg) return;
     const int64_t T = (int64_t)(uint32_t)meta.z | ((int64_t)meta.w << 32);
     const int b = key / a.num_kv_heads;
     const int kvh = key - b * a.num_kv_heads;
-    if (g >= row_tokens(a, b) * a.group) return;     // g: column of the decode row
+    if (g >= ntok * a.group) return;     // g: column of the decode row
     // every range is non-empty when T >= num_wg: pieces are then [w][1],
     // [w+1][0], ..., [w1][0]
     const int npieces = w1 - w + 1;
@@ -138,7 +124,7 @@ __global__ __launch_bounds__(NC * D / 4) void merge_balanced(DecodeArgs a) {
 template <typename Tag>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
-        const dim3 grid(a.num_wg + a.num_seqs);
+        const dim3 grid(a.num_wg);
         const bool two = a.col_tiles == 2;
         if (a.head_dim == 64 && two)
             hipLaunchKernelGGL((merge_balanced<Tag, 64, 32>), grid, dim3(32 * 64 / 4), 0, s, a);

@@ -162,3 +162,35 @@ def test_verify_bench_workload_q4_sampled():
                                    np.array([0, 4]), cfg.scale)
         ref[r] = sel[r - 4 * b]
     compare(out[rows], ref[rows], "bf16", what="verify bench workload q=4")
+
+
+@pytest.mark.parametrize("G,D", [(7, 128), (4, 256)])
+def test_verify_balanced_row_limit(G, D):
+    """2048 query rows on the balanced schedule, the most it takes: the
+    decode kernel's prologue then holds the prefix table, the rows' lengths
+    and their row map in LDS beside the edge pieces (two column tiles at
+    head_dim 128, the largest edge LDS)."""
+    nseq = 512
+    lens = tuple(33 + (7 * i) % 90 for i in range(nseq))
+    cfg = small_config("bf16", 2, G, D, 16, lens)
+    inp, q, qs = verify_inputs(cfg, [4] * nseq, seed=21)
+    out = run_verify(inp, q, qs, 4, ops.KERNEL_MFMA)
+    compare(out, oracle_verify(inp, q, qs), "bf16", what="verify 2048 rows G=%d D=%d" % (G, D))
+
+
+@pytest.mark.parametrize("nsrc", [4096, 4097])
+def test_verify_many_sequences_few_queries(nsrc):
+    """Sequences without query rows.  The balanced decode kernel stages every
+    sequence's query start and length in LDS to compute the row map (up to
+    4096 sequences); with more, the row map is written to memory first and
+    the fixed schedule reads it."""
+    lens = tuple(5 + (i * 13) % 60 for i in range(nsrc))
+    rng = np.random.default_rng(nsrc)
+    qlens = [0] * nsrc
+    for b in rng.choice(nsrc, 40, replace=False):
+        qlens[int(b)] = int(min(lens[int(b)], rng.integers(1, 5)))
+    qlens[nsrc - 1] = 2                       # the last sequence has rows too
+    cfg = small_config("bf16", 1, 4, 64, 16, lens)
+    inp, q, qs = verify_inputs(cfg, qlens, seed=22)
+    out = run_verify(inp, q, qs, 4, ops.KERNEL_MFMA)
+    compare(out, oracle_verify(inp, q, qs), "bf16", what="verify %d sequences" % nsrc)
