@@ -33,10 +33,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
 // column (NC columns per slot, 16 or 32): NC * D / 4 threads.
 template <typename Tag, int D, int NC>
 __global__ __launch_bounds__(NC * D / 4) void merge_balanced(DecodeArgs a) {
-    constexpr int kSpec = 4;
+    constexpr int kSpec = 3;
     const int w = blockIdx.x;
     const int g = threadIdx.x / (D / 4);
     const int d = (threadIdx.x % (D / 4)) * 4;
+    // columns a decode row can have (G, or u G for verify rows): the others
+    // load nothing
+    if (g >= max(a.row_group, 1) * a.group) return;
     const int nwg = a.num_wg;
     auto slot_row = [&](int slot) { return (uint64_t)slot * NC + g; };
     const int4 meta = reinterpret_cast<const int4*>(a.ws_meta)[w];
