@@ -37,9 +37,13 @@ SOURCES = [
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-# -amdgpu-mfma-vgpr-form: keep matrix-core results in VGPRs (no AGPR copies)
+# -amdgpu-mfma-vgpr-form: keep matrix-core results in VGPRs (no AGPR copies).
+# -amdgpu-kernarg-preload-count: the first kernel arguments arrive in scalar
+# registers (the balanced decode and merge kernels put there what their
+# first loads need).
 DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=true"]
+          "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=true",
+          "-mllvm", "-amdgpu-kernarg-preload-count=6"]
 
 
 # Sources whose change changes what the decode call's kernels do; hashed to

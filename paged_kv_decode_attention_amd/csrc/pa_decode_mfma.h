@@ -982,13 +982,24 @@ constexpr int balanced_lds_ints(int num_seqs) {
     return (kRows == 1 ? 3 : 2) * num_seqs + 1;
 }
 
+// The first arguments (p0, p1, n0) are the arrays the prologue reads first:
+// the context lengths (p1 unused, n0 = num_seqs), or for verify rows the
+// query starts and the sequences' lengths (n0 = num_src_seqs).  They come
+// first so that the compiler preloads them into scalar registers
+// (-amdgpu-kernarg-preload-count): the first loads then leave at once,
+// without a round trip for the kernel arguments before them.
 template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
-__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
+    const int32_t* __restrict__ p0, const int32_t* __restrict__ p1, int n0, DecodeArgs a) {
     constexpr bool kCols = kRows == 1;
     constexpr int OS = Dim<D>::OS;
     constexpr int NC = 16 * NT;   // columns per slot
     __shared__ EdgeLds<D, NT> edge;
     __shared__ int wsum[kNW];
+    // this thread's first entries, loaded before anything waits
+    const int t0 = threadIdx.x;
+    const int v0 = t0 < n0 + (kRows == 1 ? 1 : 0) ? p0[t0] : 0;
+    const int v1 = kRows == 1 && t0 < n0 ? p1[t0] : 0;
     constexpr int kSU = Kv::kE4M3 ? kStartUnitsE4M3 : kStartUnits16;
     int* pref = balanced_pref;
     int* lens = pref + a.num_seqs + 1;
@@ -1000,21 +1011,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(DecodeArg
         static_assert(sizeof(edge.o) >= (2 * kMaxVerifyFoldSeqs + 1) * sizeof(int),
                       "edge LDS too small to stage the sequences");
         int* qs = reinterpret_cast<int*>(&edge.o);
-        int* sl = qs + a.num_src_seqs + 1;
-        for (int i = threadIdx.x; i <= a.num_src_seqs; i += blockDim.x) {
-            qs[i] = a.query_start[i];
-            if (i < a.num_src_seqs) sl[i] = a.src_lens[i];
+        int* sl = qs + n0 + 1;
+        for (int i = t0; i <= n0; i += blockDim.x) {
+            qs[i] = i == t0 ? v0 : p0[i];
+            if (i < n0) sl[i] = i == t0 ? v1 : p1[i];
         }
         __syncthreads();
         unit_prefix(a, kSU, [&](int r) {
             const VerifyRow v = verify_row([=](int i) { return qs[i]; },
-                                           [=](int i) { return sl[i]; }, a.num_src_seqs,
+                                           [=](int i) { return sl[i]; }, n0,
                                            a.max_query_len, a.max_context_len, a.row_group, r);
             rmap[r] = v.table_row * 64 + v.ntok;
             return v.len;
         }, pref, lens, wsum);
     } else {
-        unit_prefix(a, kSU, [&](int r) { return a.context_lens[r]; }, pref, lens, wsum);
+        unit_prefix(a, kSU, [&](int r) { return r == t0 ? v0 : p0[r]; }, pref, lens, wsum);
     }
     // query rows decode row b carries, and its block-table row (b is uniform)
     auto ntok_of = [&](int b) {
@@ -1153,8 +1164,12 @@ template <typename Tag, int BS, typename Kv, int kRows, int D, int NT>
 hipError_t launch_rows(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
         const size_t pref_bytes = (size_t)balanced_lds_ints<kRows>(a.num_seqs) * sizeof(int);
+        const bool rows = kRows == 1;
         hipLaunchKernelGGL((decode_mfma_balanced<Tag, BS, Kv, kRows, D, NT>), dim3(a.num_wg),
-                           dim3(kDecodeThreads), pref_bytes, s, a);
+                           dim3(kDecodeThreads), pref_bytes, s,
+                           rows ? a.query_start : a.context_lens,
+                           rows ? a.src_lens : (const int32_t*)nullptr,
+                           rows ? a.num_src_seqs : a.num_seqs, a);
     } else {
         dim3 grid(a.num_kv_heads, a.num_seqs, a.num_parts);
         hipLaunchKernelGGL((decode_mfma_fixed<Tag, BS, Kv, kRows, D, NT>), grid,

@@ -76,6 +76,17 @@ __device__ __forceinline__ void store_elem(F16, void* base, uint64_t i, float v)
     reinterpret_cast<_Float16*>(base)[i] = (_Float16)v;
 }
 
+// Store four float32 as elements i .. i + 3 of the storage type in one
+// instruction (i a multiple of 4; base 16-byte aligned).
+__device__ __forceinline__ void store4(F32, void* base, uint64_t i, f32x4 v) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + i) = v;
+}
+template <typename Tag>
+__device__ __forceinline__ void store4(Tag t, void* base, uint64_t i, f32x4 v) {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(base) + i) =
+        (u32x2){pack2(t, v[0], v[1]), pack2(t, v[2], v[3])};
+}
+
 // OCP FP8 E4M3 code of a float32 (sign, 4 exponent bits of bias 7, 3
 // mantissa bits; no infinities; 0x7F is NaN; largest finite 448): nearest
 // representable value, ties to the even code, saturating to +-448.

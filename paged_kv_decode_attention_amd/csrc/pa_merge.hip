@@ -31,35 +31,47 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
 // over at most kSpec ranges).  (The rows of decode rows with no history are
 // written by the decode kernel.)  A thread takes 4 consecutive d of one
 // column (NC columns per slot, 16 or 32): NC * D / 4 threads.
+// The first arguments repeat what the first loads need (records, slots, the
+// range count and the columns a decode row can have: G, or u G for verify
+// rows), so that the compiler preloads them into scalar registers and the
+// loads leave without a round trip for the kernel arguments.
 template <typename Tag, int D, int NC>
-__global__ __launch_bounds__(NC * D / 4) void merge_balanced(DecodeArgs a) {
+__global__ __launch_bounds__(NC * D / 4) void merge_balanced(
+    const int4* __restrict__ ws_meta, const float* __restrict__ ws_out,
+    const float* __restrict__ ws_lse, int nwg, int max_cols, DecodeArgs a) {
     constexpr int kSpec = 3;
     const int w = blockIdx.x;
     const int g = threadIdx.x / (D / 4);
     const int d = (threadIdx.x % (D / 4)) * 4;
-    // columns a decode row can have (G, or u G for verify rows): the others
-    // load nothing
-    if (g >= max(a.row_group, 1) * a.group) return;
-    const int nwg = a.num_wg;
+    if (g >= max_cols) return;            // a column no decode row has: load nothing
     auto slot_row = [&](int slot) { return (uint64_t)slot * NC + g; };
-    const int4 meta = reinterpret_cast<const int4*>(a.ws_meta)[w];
+    const int4 meta = ws_meta[w];
     f32x4 o[kSpec];
     float lse[kSpec];
 #pragma unroll
     for (int k = 0; k < kSpec; ++k) {
         const int slot = k == 0 ? 2 * w + 1 : 2 * min(w + k, nwg - 1);
-        o[k] = *reinterpret_cast<const f32x4*>(a.ws_out + slot_row(slot) * D + d);
-        lse[k] = a.ws_lse[slot_row(slot)];
+        o[k] = *reinterpret_cast<const f32x4*>(ws_out + slot_row(slot) * D + d);
+        lse[k] = ws_lse[slot_row(slot)];
     }
+    // The pieces' loads, and those of the kernel arguments used below, go
+    // out with the record's: without these uses the compiler sinks them
+    // below the record's checks, a second round trip.
+    const int H_kv = a.num_kv_heads;
+    const int nkeys = a.num_seqs * H_kv;
+    const int G = a.group;
+#pragma unroll
+    for (int k = 0; k < kSpec; ++k) asm volatile("" ::"v"(o[k]), "v"(lse[k]));
+    asm volatile("" ::"s"(nkeys), "s"(G), "s"(a.num_heads), "s"(a.out), "s"(a.out_scale));
     const int key = meta.x;
     const int w1 = meta.y & 0xffff;
     const int ntok = meta.y >> 16;
     // (a record outside these bounds cannot come from the decode kernel)
-    if (key < 0 || key >= a.num_seqs * a.num_kv_heads || w1 <= w || w1 >= nwg) return;
+    if (key < 0 || key >= nkeys || w1 <= w || w1 >= nwg) return;
     const int64_t T = (int64_t)(uint32_t)meta.z | ((int64_t)meta.w << 32);
-    const int b = key / a.num_kv_heads;
-    const int kvh = key - b * a.num_kv_heads;
-    if (g >= ntok * a.group) return;     // g: column of the decode row
+    const int b = key / H_kv;
+    const int kvh = key - b * H_kv;
+    if (g >= ntok * G) return;     // g: column of the decode row
     // every range is non-empty when T >= num_wg: pieces are then [w][1],
     // [w+1][0], ..., [w1][0]
     const int npieces = w1 - w + 1;
@@ -100,8 +112,8 @@ __global__ __launch_bounds__(NC * D / 4) void merge_balanced(DecodeArgs a) {
 #pragma unroll
             for (int k = 0; k < kBatch; ++k) {
                 const int slot = 2 * (w + min(k0 + k, npieces - 1));
-                ob[k] = *reinterpret_cast<const f32x4*>(a.ws_out + slot_row(slot) * D + d);
-                lb[k] = a.ws_lse[slot_row(slot)];
+                ob[k] = *reinterpret_cast<const f32x4*>(ws_out + slot_row(slot) * D + d);
+                lb[k] = ws_lse[slot_row(slot)];
             }
 #pragma unroll
             for (int k = 0; k < kBatch; ++k)
@@ -113,15 +125,16 @@ __global__ __launch_bounds__(NC * D / 4) void merge_balanced(DecodeArgs a) {
         for (int w2 = w + 1; w2 <= w1; ++w2) {
             if (range_start(w2, T, nwg) >= range_start(w2 + 1, T, nwg)) continue;
             const int slot = 2 * w2;
-            fold(a.ws_lse[slot_row(slot)],
-                 *reinterpret_cast<const f32x4*>(a.ws_out + slot_row(slot) * D + d));
+            fold(ws_lse[slot_row(slot)],
+                 *reinterpret_cast<const f32x4*>(ws_out + slot_row(slot) * D + d));
         }
     }
     const uint64_t out0 = col_row(a, b, kvh, g) * D + d;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        store_elem(Tag(), a.out, out0 + e,
-                   has_nan ? __builtin_nanf("") : a.out_scale * (num[e] / den));
+    const f32x4 r = a.out_scale * (num / den);
+    store4(Tag(), a.out, out0,
+           has_nan ? (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                             __builtin_nanf("")}
+                   : r);
 }
 
 template <typename Tag>
@@ -129,16 +142,22 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
     if (a.schedule == kBalanced) {
         const dim3 grid(a.num_wg);
         const bool two = a.col_tiles == 2;
+        const int max_cols = (a.row_group > 0 ? a.row_group : 1) * a.group;
+        const int4* meta = reinterpret_cast<const int4*>(a.ws_meta);
+#define PA_MERGE(D_, NC_)                                                                  \
+    hipLaunchKernelGGL((merge_balanced<Tag, D_, NC_>), grid, dim3(NC_ * D_ / 4), 0, s, meta, \
+                       a.ws_out, a.ws_lse, a.num_wg, max_cols, a)
         if (a.head_dim == 64 && two)
-            hipLaunchKernelGGL((merge_balanced<Tag, 64, 32>), grid, dim3(32 * 64 / 4), 0, s, a);
+            PA_MERGE(64, 32);
         else if (a.head_dim == 64)
-            hipLaunchKernelGGL((merge_balanced<Tag, 64, 16>), grid, dim3(16 * 64 / 4), 0, s, a);
+            PA_MERGE(64, 16);
         else if (a.head_dim == 128 && two)
-            hipLaunchKernelGGL((merge_balanced<Tag, 128, 32>), grid, dim3(32 * 128 / 4), 0, s, a);
+            PA_MERGE(128, 32);
         else if (a.head_dim == 128)
-            hipLaunchKernelGGL((merge_balanced<Tag, 128, 16>), grid, dim3(16 * 128 / 4), 0, s, a);
+            PA_MERGE(128, 16);
         else
-            hipLaunchKernelGGL((merge_balanced<Tag, 256, 16>), grid, dim3(16 * 256 / 4), 0, s, a);
+            PA_MERGE(256, 16);
+#undef PA_MERGE
     } else {
         hipLaunchKernelGGL((merge_fixed<Tag>), dim3(a.num_kv_heads, a.num_seqs),
                            dim3(kMergeThreads), 0, s, a);
