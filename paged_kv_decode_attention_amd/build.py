@@ -50,7 +50,7 @@ DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang",
 # tell whether stored counter readings still describe the built kernels.
 DECODE_SOURCES = ["pa_decode_mfma.h", "pa_decode_mfma.hip", "pa_decode_mfma_d64.hip",
                   "pa_decode_mfma_d128.hip", "pa_decode_mfma_d256.hip", "pa_decode_generic.hip",
-                  "pa_merge.hip", "pa_finalize.h", "pa_device.h", "pa_api.cpp"]
+                  "pa_merge.hip", "pa_finalize.h", "pa_device.h", "pa_internal.h", "pa_api.cpp"]
 
 
 def decode_source_hash():

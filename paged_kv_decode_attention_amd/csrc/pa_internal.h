@@ -90,12 +90,13 @@ constexpr int kChunk = 32;            // tokens a wavefront handles per step
 // nb chunks counts s + kChunkUnits nb units: its chunk c starts at unit
 // s + kChunkUnits c, and the s units before its first chunk stand for the
 // fixed cost of starting a history (loading its table row and first chunk
-// with nothing else in flight, and writing its state).  s depends on the
-// cache format (an E4M3 chunk streams in half the time of a 16-bit one);
-// the values are tuned by measurement.  A range of units holds the chunks
-// that start inside it.
+// with nothing else in flight, and writing its state).  s may depend on the
+// cache format; both values are tuned by measurement (1.5 chunks: timed
+// wavefronts show about 2.3 us per history start against 2.9 us per chunk
+// when a wavefront's range holds many short histories).  A range of units
+// holds the chunks that start inside it.
 constexpr int kChunkUnits = 2;
-constexpr int kStartUnits16 = 1;
+constexpr int kStartUnits16 = 3;
 constexpr int kStartUnitsE4M3 = 3;
 constexpr int kMaxStartUnits = 3;
 
