@@ -90,15 +90,16 @@ constexpr int kChunk = 32;            // tokens a wavefront handles per step
 // nb chunks counts s + kChunkUnits nb units: its chunk c starts at unit
 // s + kChunkUnits c, and the s units before its first chunk stand for the
 // fixed cost of starting a history (loading its table row and first chunk
-// with nothing else in flight, and writing its state).  s may depend on the
-// cache format; both values are tuned by measurement (1.5 chunks: timed
-// wavefronts show about 2.3 us per history start against 2.9 us per chunk
-// when a wavefront's range holds many short histories).  A range of units
-// holds the chunks that start inside it.
+// with nothing else in flight, and writing its state).  s depends on the
+// cache format, whose chunks take different times to stream; both values
+// are tuned by measurement (16-bit: 1.5 chunks, timed wavefronts show about
+// 2.3 us per history start against 2.9 us per chunk when a wavefront's
+// range holds many short histories; E4M3, half the bytes per chunk: 3
+// chunks).  A range of units holds the chunks that start inside it.
 constexpr int kChunkUnits = 2;
 constexpr int kStartUnits16 = 3;
-constexpr int kStartUnitsE4M3 = 3;
-constexpr int kMaxStartUnits = 3;
+constexpr int kStartUnitsE4M3 = 6;
+constexpr int kMaxStartUnits = 6;
 
 // Kernel families.
 enum KernelKind { kAuto = 0, kGeneric = 1, kMfma = 2 };
