@@ -374,7 +374,9 @@ def paged_attention_decode_fp8(query, key_cache, value_cache, block_tables, cont
                                partition_size=0, out=None, workspace=None):
     """paged_attention_decode over caches of OCP FP8 E4M3 codes (uint8 or
     float8_e4m3fn [N, H_kv, BS, D]); a code stands for decode(code) * k_scale
-    (keys) or * v_scale (values).  query/out bf16 or f16, head_dim 128."""
+    (keys) or * v_scale (values).  query/out bf16 or f16; the shapes of the
+    matrix-core kernel (head_dim 64/128/256, block size 8-64, GQA group up to
+    16, or 32 at head_dim 64/128)."""
     out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
                                     scale, max_context_len, partition_size, out, workspace,
                                     kv_fp8=True)

@@ -54,3 +54,78 @@ def test_graph_replays_match_eager(name, partition_size):
         step()                                    # eager step between replays
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
+
+
+def _replays_match(step, out, ws):
+    """Capture step() in a graph; each replay (after eager work that clobbers
+    out and the workspace) must equal the eager result bit for bit."""
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), "replay %d differs from the eager step" % rep
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+
+
+@pytest.mark.parametrize("partition_size", [0, 64])
+def test_graph_verify_replays_match_eager(partition_size):
+    """Verify calls in a graph: on the balanced schedule the row map is
+    computed inside the decode kernel, on the fixed one a kernel writes it to
+    the workspace first; both replay to the eager bits."""
+    cfg = I.CONFIGS["qwen7b_gqa_bf16"]
+    inp = I.generate(cfg)
+    d = upload(inp)
+    S, H, D = d["query"].shape
+    N, H_kv, BS, _ = d["key_cache"].shape
+    W = d["block_tables"].shape[1]
+    qs = torch.arange(0, 4 * S + 1, 4, dtype=torch.int32, device=DEV)
+    gen = torch.Generator().manual_seed(5)
+    q = torch.randn(4 * S, H, D, generator=gen).to(d["query"].dtype).to(DEV)
+    need = ops.load_library().pa_verify_workspace_size(4 * S, H, H_kv, D, BS, W * BS,
+                                                       partition_size, ops.dtype_code(q.dtype))
+    ws = torch.empty(max(256, need), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(q)
+
+    def step():
+        ops.paged_attention_verify(q, d["key_cache"], d["value_cache"], d["block_tables"],
+                                   d["context_lens"], qs, 4, partition_size=partition_size,
+                                   out=out, workspace=ws)
+
+    _replays_match(step, out, ws)
+
+
+def test_graph_decode_append_replays_match_eager():
+    """The fused step of the bench (newest token written inside the decode
+    kernel) in a graph."""
+    cfg = I.CONFIGS["qwen7b_gqa_bf16"]
+    inp = I.generate(cfg, new_tokens_at="last")
+    d = upload(inp)
+    S, H, D = d["query"].shape
+    N, H_kv, BS, _ = d["key_cache"].shape
+    W = d["block_tables"].shape[1]
+    ws = torch.empty(max(256, ops.decode_workspace_size(S, H, H_kv, D, BS, W * BS, 0,
+                                                        d["query"].dtype)),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(d["query"])
+
+    def step():
+        ops.decode_append(d["query"], d["new_key"], d["new_value"], d["key_cache"],
+                          d["value_cache"], d["block_tables"], d["context_lens"], out=out,
+                          workspace=ws)
+
+    _replays_match(step, out, ws)
