@@ -23,7 +23,10 @@ worked examples the pages print) or, for the block pool and the block copy
 copy-on-write example and invariants), or, for the FP8 KV cache
 (``fp8.py``), by ``tests/test_fp8_oracle.py`` (the E4M3 definition,
 PyTorch's float8_e4m3fn cast where it is defined, exhaustive round trips,
-ties and saturation); none is "parity unpinned".
+ties and saturation), or, for the INT8 KV cache (``int8.py``), by
+``tests/test_int8_oracle.py`` (two's complement codes, exhaustive round
+trips, torch.round's ties-to-even over every bf16 bit pattern, brute-force
+nearest integers, saturation); none is "parity unpinned".
 """
 
 from .paged_attention import (  # noqa: F401
