@@ -315,6 +315,50 @@ int pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache
                              pa_dtype dtype, float k_scale, float v_scale, void* hip_stream);
 
 /*
+ * INT8 KV cache.  The caches hold signed 8-bit integer codes (two's
+ * complement, -127 .. 127; the code -128 is never written and reads as
+ * -128), in the same [num_blocks, num_kv_heads, block_size, head_dim]
+ * layout, with ONE scale per cache: code c of the key cache stands for
+ * c * k_scale, of the value cache for c * v_scale (symmetric, no zero
+ * point).  Storing x gives the integer nearest fp32(x) * fp32(1 / scale),
+ * ties to even, clamped to [-127, 127]; NaN is stored as 0, the one code
+ * an integer cache has for it.  ([KV-principles] §3.3 "量化压缩 KV Cache":
+ * 16-bit K and V quantised to INT8 to halve their memory, with a small
+ * accuracy cost.  The pages fix neither the scale granularity nor the
+ * rounding; a per-cache symmetric scale and round-half-even are the
+ * readings taken here.)
+ *
+ * pa_paged_attention_decode_i8 -- pa_paged_attention_decode over INT8
+ *   caches: the attention of each query over the dequantised history.  Same
+ *   arguments, rules, supported shapes and workspace as
+ *   pa_paged_attention_decode_fp8.
+ * pa_decode_append_i8 -- pa_decode_append over INT8 caches: each newest
+ *   token's key/value (query dtype) is quantised as it is stored.
+ * pa_reshape_and_cache_i8 -- pa_reshape_and_cache into INT8 caches, with the
+ *   arguments and rules of pa_reshape_and_cache_fp8.
+ * Cache pointers must be 16-byte aligned.
+ */
+int pa_paged_attention_decode_i8(void* out, const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, int num_seqs, int num_heads,
+                                 int num_kv_heads, int gqa_group_size, int head_dim,
+                                 int block_size, int num_blocks, int max_blocks_per_seq,
+                                 int max_context_len, float scale, pa_dtype dtype, float k_scale,
+                                 float v_scale, int partition_size, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream);
+int pa_decode_append_i8(void* out, const void* query, const void* key, const void* value,
+                        void* key_cache, void* value_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, int num_seqs, int num_heads,
+                        int num_kv_heads, int gqa_group_size, int head_dim, int block_size,
+                        int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+                        pa_dtype dtype, float k_scale, float v_scale, int partition_size,
+                        void* workspace, size_t workspace_bytes, void* hip_stream);
+int pa_reshape_and_cache_i8(const void* key, const void* value, void* key_cache,
+                            void* value_cache, const int64_t* slot_mapping, int num_tokens,
+                            int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                            pa_dtype dtype, float k_scale, float v_scale, void* hip_stream);
+
+/*
  * pa_copy_blocks -- copy whole physical blocks of both caches:
  *     key_cache  [dst_i, :, :, :] = key_cache  [src_i, :, :, :]
  *     value_cache[dst_i, :, :, :] = value_cache[src_i, :, :, :]

@@ -237,8 +237,10 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                        int kernel_kind = -1, int col_tiles = 1,
                        const VerifyFold* fold = nullptr) {
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
-    const bool e4m3 = kv_format == pa::kKvE4M3;
-    if (e4m3 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
+    if (kv_format != pa::kKvSame && kv_format != pa::kKvE4M3 && kv_format != pa::kKvI8)
+        return fail(PA_ERR_INVALID_ARG, "internal: unknown cache format %d", kv_format);
+    const bool q8 = kv_format != pa::kKvSame;     // 8-bit codes with one scale per cache
+    if (q8 && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
                   v_scale > 0.0f))
         return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
     if (num_heads <= 0 || num_kv_heads <= 0)
@@ -283,8 +285,8 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     const bool use_mfma = mfma_ok && kind != pa::kGeneric;
     if (kind == pa::kMfma && !mfma_ok)
         return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
-    if (e4m3 && !use_mfma)
-        return fail(PA_ERR_UNSUPPORTED, "FP8 caches are served by the matrix-core kernel only "
+    if (q8 && !use_mfma)
+        return fail(PA_ERR_UNSUPPORTED, "8-bit caches are served by the matrix-core kernel only "
                     "(bf16/f16 queries, head_dim 64/128/256, block_size 8/16/32/64, group <= 16, "
                     "or <= 32 at head_dim 64/128)");
     // a row map held in memory is read by the fixed schedule's kernels only
@@ -350,11 +352,11 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     a.num_wg = balanced ? balanced_workgroups(head_dim) : 0;
     a.col_tiles = col_tiles;
     // scale * log2(e), and the key scale of an FP8 cache folded into it
-    a.scale_log2 = (float)((double)scale * 1.4426950408889634 * (e4m3 ? (double)k_scale : 1.0));
-    a.kv_format = e4m3 ? pa::kKvE4M3 : pa::kKvSame;
-    a.out_scale = e4m3 ? v_scale : 1.0f;
-    a.k_inv_scale = e4m3 ? (float)(1.0 / (double)k_scale) : 1.0f;
-    a.v_inv_scale = e4m3 ? (float)(1.0 / (double)v_scale) : 1.0f;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634 * (q8 ? (double)k_scale : 1.0));
+    a.kv_format = kv_format;
+    a.out_scale = q8 ? v_scale : 1.0f;
+    a.k_inv_scale = q8 ? (float)(1.0 / (double)k_scale) : 1.0f;
+    a.v_inv_scale = q8 ? (float)(1.0 / (double)v_scale) : 1.0f;
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = hipSuccess;
@@ -440,10 +442,13 @@ int pa_decode_append_fp8(void* out, const void* query, const void* key, const vo
                        k_scale, v_scale);
 }
 
-int pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
-                             void* value_cache, const int64_t* slot_mapping, int num_tokens,
-                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
-                             pa_dtype dtype, float k_scale, float v_scale, void* hip_stream) {
+}  // extern "C"
+
+static int reshape_and_cache_q8(const void* key, const void* value, void* key_cache,
+                                void* value_cache, const int64_t* slot_mapping, int num_tokens,
+                                int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                                pa_dtype dtype, float k_scale, float v_scale, bool int8,
+                                void* hip_stream) {
     const int e = elem_bytes(dtype);
     if (e == 0) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
     if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
@@ -457,12 +462,63 @@ int pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache
         return fail(PA_ERR_INVALID_ARG, "null tensor pointer");
     if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "key/value/cache pointers must be 16-byte aligned");
-    hipError_t err = pa::launch_reshape_and_cache_fp8(
+    hipError_t err = pa::launch_reshape_and_cache_q8(
         key, value, key_cache, value_cache, slot_mapping, num_tokens, num_kv_heads, head_dim,
-        block_size, num_blocks, dtype, (float)(1.0 / (double)k_scale),
+        block_size, num_blocks, dtype, int8, (float)(1.0 / (double)k_scale),
         (float)(1.0 / (double)v_scale), static_cast<hipStream_t>(hip_stream));
-    if (err != hipSuccess) return hip_fail(err, "fp8 cache write kernel launch");
+    if (err != hipSuccess)
+        return hip_fail(err, int8 ? "int8 cache write kernel launch" : "fp8 cache write kernel launch");
     return PA_OK;
+}
+
+extern "C" {
+
+int pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                             void* value_cache, const int64_t* slot_mapping, int num_tokens,
+                             int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                             pa_dtype dtype, float k_scale, float v_scale, void* hip_stream) {
+    return reshape_and_cache_q8(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                num_kv_heads, head_dim, block_size, num_blocks, dtype, k_scale,
+                                v_scale, false, hip_stream);
+}
+
+int pa_paged_attention_decode_i8(void* out, const void* query, const void* key_cache,
+                                 const void* value_cache, const int32_t* block_tables,
+                                 const int32_t* context_lens, int num_seqs, int num_heads,
+                                 int num_kv_heads, int gqa_group_size, int head_dim,
+                                 int block_size, int num_blocks, int max_blocks_per_seq,
+                                 int max_context_len, float scale, pa_dtype dtype, float k_scale,
+                                 float v_scale, int partition_size, void* workspace,
+                                 size_t workspace_bytes, void* hip_stream) {
+    return decode_impl(out, query, nullptr, nullptr, key_cache, value_cache, block_tables,
+                       context_lens, num_seqs, num_heads, num_kv_heads, gqa_group_size, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                       partition_size, workspace, workspace_bytes, hip_stream, pa::kKvI8,
+                       k_scale, v_scale);
+}
+
+int pa_decode_append_i8(void* out, const void* query, const void* key, const void* value,
+                        void* key_cache, void* value_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, int num_seqs, int num_heads,
+                        int num_kv_heads, int gqa_group_size, int head_dim, int block_size,
+                        int num_blocks, int max_blocks_per_seq, int max_context_len, float scale,
+                        pa_dtype dtype, float k_scale, float v_scale, int partition_size,
+                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!key || !value) return fail(PA_ERR_INVALID_ARG, "new key/value must be non-null");
+    return decode_impl(out, query, key, value, key_cache, value_cache, block_tables,
+                       context_lens, num_seqs, num_heads, num_kv_heads, gqa_group_size, head_dim,
+                       block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, dtype,
+                       partition_size, workspace, workspace_bytes, hip_stream, pa::kKvI8,
+                       k_scale, v_scale);
+}
+
+int pa_reshape_and_cache_i8(const void* key, const void* value, void* key_cache,
+                            void* value_cache, const int64_t* slot_mapping, int num_tokens,
+                            int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                            pa_dtype dtype, float k_scale, float v_scale, void* hip_stream) {
+    return reshape_and_cache_q8(key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                                num_kv_heads, head_dim, block_size, num_blocks, dtype, k_scale,
+                                v_scale, true, hip_stream);
 }
 
 size_t pa_verify_workspace_size(int total_queries, int num_heads, int num_kv_heads,

@@ -37,10 +37,11 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_kernel(
     *reinterpret_cast<u32x4*>(value_cache + dst) = vv;
 }
 
-// Cache write into OCP FP8 E4M3 caches: 8 consecutive values of token i,
-// KV head h (column group c) -> 8 codes at key_cache[pb, h, off, 8c .. +8],
-// each E4M3(fp32(x) * inv_scale) -- the quantised form of the cache write
-// above, with one scale per cache.
+// Cache write into 8-bit caches: 8 consecutive values of token i, KV head h
+// (column group c) -> 8 codes at key_cache[pb, h, off, 8c .. +8], each
+// Q(fp32(x) * inv_scale) with Q = OCP FP8 E4M3 (kI8 false) or INT8 (kI8
+// true) -- the quantised form of the cache write above, with one scale per
+// cache.
 template <typename Tag>
 __device__ __forceinline__ void load8_f32(const char* src, float* f) {
     if constexpr (Tag::kBytes == 4) {
@@ -51,8 +52,8 @@ __device__ __forceinline__ void load8_f32(const char* src, float* f) {
     }
 }
 
-template <typename Tag>
-__global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
+template <typename Tag, bool kI8>
+__global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_q8_kernel(
     const char* __restrict__ key, const char* __restrict__ value, uint8_t* key_cache,
     uint8_t* value_cache, const int64_t* __restrict__ slots, int num_tokens, int num_kv_heads,
     int head_dim, int block_size, int num_blocks, float k_inv, float v_inv) {
@@ -75,8 +76,8 @@ __global__ __launch_bounds__(kCopyThreads) void reshape_and_cache_fp8_kernel(
     uint32_t ck[8], cv[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        ck[e] = e4m3_encode(fk[e] * k_inv);
-        cv[e] = e4m3_encode(fv[e] * v_inv);
+        ck[e] = kI8 ? i8_encode(fk[e] * k_inv) : e4m3_encode(fk[e] * k_inv);
+        cv[e] = kI8 ? i8_encode(fv[e] * v_inv) : e4m3_encode(fv[e] * v_inv);
     }
     const uint64_t dst = kv_row(pb, h, off, num_kv_heads, block_size) * head_dim + 8 * c;
     *reinterpret_cast<u32x2*>(key_cache + dst) =
@@ -203,11 +204,11 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* ke
     return hipGetLastError();
 }
 
-hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
-                                        void* value_cache, const int64_t* slots, int num_tokens,
-                                        int num_kv_heads, int head_dim, int block_size,
-                                        int num_blocks, pa_dtype src_dtype, float k_inv_scale,
-                                        float v_inv_scale, hipStream_t s) {
+hipError_t launch_reshape_and_cache_q8(const void* key, const void* value, void* key_cache,
+                                       void* value_cache, const int64_t* slots, int num_tokens,
+                                       int num_kv_heads, int head_dim, int block_size,
+                                       int num_blocks, pa_dtype src_dtype, bool int8,
+                                       float k_inv_scale, float v_inv_scale, hipStream_t s) {
     const uint64_t total = (uint64_t)num_tokens * num_kv_heads * (head_dim / 8);
     if (total == 0) return hipSuccess;
     const unsigned grid = (unsigned)((total + kCopyThreads - 1) / kCopyThreads);
@@ -219,9 +220,18 @@ hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void
                            k_inv_scale, v_inv_scale);
     };
     switch (src_dtype) {
-        case PA_F32: go(reshape_and_cache_fp8_kernel<F32>); break;
-        case PA_F16: go(reshape_and_cache_fp8_kernel<F16>); break;
-        default: go(reshape_and_cache_fp8_kernel<BF16>); break;
+        case PA_F32:
+            int8 ? go(reshape_and_cache_q8_kernel<F32, true>)
+                 : go(reshape_and_cache_q8_kernel<F32, false>);
+            break;
+        case PA_F16:
+            int8 ? go(reshape_and_cache_q8_kernel<F16, true>)
+                 : go(reshape_and_cache_q8_kernel<F16, false>);
+            break;
+        default:
+            int8 ? go(reshape_and_cache_q8_kernel<BF16, true>)
+                 : go(reshape_and_cache_q8_kernel<BF16, false>);
+            break;
     }
     return hipGetLastError();
 }

@@ -1,5 +1,5 @@
 // Decode paged attention on the gfx950 matrix cores, bf16/fp16 queries,
-// 16-bit or FP8 E4M3 caches, head_dim 64, 128 or 256, GQA groups of up to 16
+// 16-bit, FP8 E4M3 or INT8 caches, head_dim 64, 128 or 256, GQA groups of up to 16
 // query heads (32 at head_dim 64 and 128).  The kernel templates; each head
 // dim is instantiated in a translation unit of its own
 // (pa_decode_mfma_d64.hip, _d128.hip, _d256.hip) so that they compile in
@@ -278,25 +278,32 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D>& r, const char* kbase, c
 
 // ---- KV storage formats -----------------------------------------------------
 // KvSame: the caches hold the query's 16-bit type.  KvE4M3: they hold OCP FP8
-// E4M3 codes (one scale per cache; the value of a code is decode(code) *
-// scale).  For E4M3 a lane takes a contiguous D/4-element slice of d for K:
-// in MFMA step kk it supplies K[token n][d = (D/4) q + 8 kk .. +8] and Q uses
-// the same d, so the contraction over d is the same sum in another order.
+// E4M3 codes; KvI8: signed 8-bit integer codes (one scale per cache; the
+// value of a code is decode(code) * scale).  For 8-bit codes a lane takes a
+// contiguous D/4-element slice of d for K: in MFMA step kk it supplies
+// K[token n][d = (D/4) q + 8 kk .. +8] and Q uses the same d, so the
+// contraction over d is the same sum in another order.
 struct KvSame {
-    static constexpr bool kE4M3 = false;
+    static constexpr bool k8 = false;    // 8-bit codes
+    static constexpr bool kI8 = false;   // integer codes
 };
 struct KvE4M3 {
-    static constexpr bool kE4M3 = true;
+    static constexpr bool k8 = true;
+    static constexpr bool kI8 = false;
+};
+struct KvI8 {
+    static constexpr bool k8 = true;
+    static constexpr bool kI8 = true;
 };
 
-// One 32-token chunk of E4M3 codes, as loaded.
+// One 32-token chunk of 8-bit codes, as loaded.
 template <int D>
 struct ChunkRegs8 {
     u32x4 k0[D / 64], k1[D / 64];            // K tile 0 / 1: row n, d = (D/4) q ..
     typename Dim<D>::VRow8 v[8];             // V rows of this lane's 8 tokens, d = VW n ..
 };
 
-// The loads of one E4M3 chunk (same rules as load_chunk: always issued, dead
+// The loads of one 8-bit chunk (same rules as load_chunk: always issued, dead
 // tiles through an empty descriptor, nontemporal).
 template <int BS, int D>
 __device__ __forceinline__ void load_chunk(ChunkRegs8<D>& r, const char* kbase, const char* vbase,
@@ -340,54 +347,73 @@ template <bool kHigh>
 __device__ __forceinline__ uint32_t e4m3_pair(F16, uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHigh));
 }
-template <typename Tag>
-__device__ __forceinline__ u32x4 e4m3_eight(uint32_t w0, uint32_t w1) {
-    return (u32x4){e4m3_pair<false>(Tag(), w0), e4m3_pair<true>(Tag(), w0),
-                   e4m3_pair<false>(Tag(), w1), e4m3_pair<true>(Tag(), w1)};
-}
-// One V row slice of E4M3 codes -> the 16-bit slice.
-template <typename Tag>
-__device__ __forceinline__ u32x8 e4m3_row(u32x4 w) {
-    return __builtin_shufflevector(e4m3_eight<Tag>(w[0], w[1]), e4m3_eight<Tag>(w[2], w[3]), 0,
-                                   1, 2, 3, 4, 5, 6, 7);
-}
-template <typename Tag>
-__device__ __forceinline__ u32x4 e4m3_row(u32x2 w) { return e4m3_eight<Tag>(w[0], w[1]); }
-template <typename Tag>
-__device__ __forceinline__ u32x2 e4m3_row(uint32_t w) {
-    return (u32x2){e4m3_pair<false>(Tag(), w), e4m3_pair<true>(Tag(), w)};
+// Two signed 8-bit codes (bytes 0, 1 or 2, 3 of w) -> two 16-bit values,
+// exactly (every integer in [-128, 127] is representable in bf16 and fp16).
+// The sign-extending field extract is typed unsigned: convert as int.
+template <bool kHigh, typename Tag>
+__device__ __forceinline__ uint32_t i8_pair(Tag t, uint32_t w) {
+    const int s = kHigh ? 16 : 0;
+    const float lo = (float)(int)__builtin_amdgcn_sbfe(w, s, 8);
+    const float hi = (float)(int)__builtin_amdgcn_sbfe(w, s + 8, 8);
+    return pack2(t, lo, hi);
 }
 
-// E4M3 chunk -> the 16-bit operands compute_chunk takes (K step kk holds
+// Two codes of format Kv (the low or the high half of w) -> two 16-bit values.
+template <typename Kv, bool kHigh, typename Tag>
+__device__ __forceinline__ uint32_t code_pair(Tag t, uint32_t w) {
+    if constexpr (Kv::kI8)
+        return i8_pair<kHigh>(t, w);
+    else
+        return e4m3_pair<kHigh>(t, w);
+}
+template <typename Tag, typename Kv>
+__device__ __forceinline__ u32x4 codes_eight(uint32_t w0, uint32_t w1) {
+    return (u32x4){code_pair<Kv, false>(Tag(), w0), code_pair<Kv, true>(Tag(), w0),
+                   code_pair<Kv, false>(Tag(), w1), code_pair<Kv, true>(Tag(), w1)};
+}
+// One V row slice of 8-bit codes -> the 16-bit slice.
+template <typename Tag, typename Kv>
+__device__ __forceinline__ u32x8 codes_row(u32x4 w) {
+    return __builtin_shufflevector(codes_eight<Tag, Kv>(w[0], w[1]),
+                                   codes_eight<Tag, Kv>(w[2], w[3]), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <typename Tag, typename Kv>
+__device__ __forceinline__ u32x4 codes_row(u32x2 w) { return codes_eight<Tag, Kv>(w[0], w[1]); }
+template <typename Tag, typename Kv>
+__device__ __forceinline__ u32x2 codes_row(uint32_t w) {
+    return (u32x2){code_pair<Kv, false>(Tag(), w), code_pair<Kv, true>(Tag(), w)};
+}
+
+// 8-bit chunk -> the 16-bit operands compute_chunk takes (K step kk holds
 // d = (D/4) q + 8 kk .. +8: dwords 2 kk, 2 kk + 1 of the lane's slice; V
 // rows as for the 16-bit format).
-template <typename Tag, int D>
+template <typename Tag, typename Kv, int D>
 __device__ __forceinline__ ChunkRegs<D> expand(const ChunkRegs8<D>& r8) {
     ChunkRegs<D> r;
 #pragma unroll
     for (int kk = 0; kk < Dim<D>::KD; ++kk) {
         const int w = 2 * kk;
         const u32x4 a = r8.k0[w >> 2], b = r8.k1[w >> 2];
-        r.k0[kk] = e4m3_eight<Tag>(a[w & 3], a[(w & 3) + 1]);
-        r.k1[kk] = e4m3_eight<Tag>(b[w & 3], b[(w & 3) + 1]);
+        r.k0[kk] = codes_eight<Tag, Kv>(a[w & 3], a[(w & 3) + 1]);
+        r.k1[kk] = codes_eight<Tag, Kv>(b[w & 3], b[(w & 3) + 1]);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r.v[i] = e4m3_row<Tag>(r8.v[i]);
+    for (int i = 0; i < 8; ++i) r.v[i] = codes_row<Tag, Kv>(r8.v[i]);
     return r;
 }
 
 template <typename Kv, int D>
-using KvRegs = typename std::conditional<Kv::kE4M3, ChunkRegs8<D>, ChunkRegs<D>>::type;
+using KvRegs = typename std::conditional<Kv::k8, ChunkRegs8<D>, ChunkRegs<D>>::type;
 
 // Byte offsets of this lane's K and V data inside a tile.
 template <typename Kv, int D>
 __device__ __forceinline__ uint32_t lane_koff(int n, int q) {
-    return Kv::kE4M3 ? (uint32_t)(n * D + (D / 4) * q) : (uint32_t)(n * D + 8 * q) * 2;
+    return Kv::k8 ? (uint32_t)(n * D + (D / 4) * q) : (uint32_t)(n * D + 8 * q) * 2;
 }
 template <typename Kv, int D>
 __device__ __forceinline__ uint32_t lane_voff(int n, int q) {
     constexpr int VW = Dim<D>::VW;
-    return Kv::kE4M3 ? (uint32_t)(4 * q * D + VW * n) : (uint32_t)(4 * q * D + VW * n) * 2;
+    return Kv::k8 ? (uint32_t)(4 * q * D + VW * n) : (uint32_t)(4 * q * D + VW * n) * 2;
 }
 
 // [S, H] row of column n of decode row b (KV head kvh): query head kvh G + n
@@ -409,7 +435,7 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, 
                          column_row<kCols>(a, b, kvh, n) * D * 2;
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk)
-            qop[kk] = load16(qp + (Kv::kE4M3 ? (D / 4) * q + 8 * kk : 32 * kk + 8 * q) * 2);
+            qop[kk] = load16(qp + (Kv::k8 ? (D / 4) * q + 8 * kk : 32 * kk + 8 * q) * 2);
     } else {
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk) qop[kk] = (u32x4){0u, 0u, 0u, 0u};
@@ -418,9 +444,9 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, 
 
 // Append step: lanes 0 .. D/8-1 store the newest token's K row, the next D/8
 // lanes its V row (8 values each), into slot pos of the sequence's tail
-// block (row: its table row).  For E4M3 each value is quantised:
-// E4M3(fp32(x) * fp32(1 / scale)), nearest, ties to even, saturating at
-// +-448.
+// block (row: its table row).  For 8-bit codes each value is quantised:
+// Q(fp32(x) * fp32(1 / scale)), Q = E4M3 (nearest, ties to even, saturating
+// at +-448) or INT8 (nearest integer, ties to even, saturating at +-127).
 template <typename Tag, typename Kv, int BS, int D>
 __device__ __forceinline__ void append_token(const DecodeArgs& a, const ConstI32* row, int b,
                                              int kvh, int pos, int lane) {
@@ -434,7 +460,7 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, const ConstI32
     char* to = reinterpret_cast<char*>(const_cast<void*>(is_k ? a.key_cache : a.value_cache));
     const uint64_t r = kv_row(pb, kvh, pos % BS, a.num_kv_heads, BS);
     const u32x4 x = load16(from);
-    if constexpr (Kv::kE4M3) {
+    if constexpr (Kv::k8) {
         // both scales as register values first: a per-lane choice between
         // two kernel-argument fields would otherwise become a per-lane load
         // from a private copy of the arguments
@@ -446,8 +472,9 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, const ConstI32
         uint32_t cd[8];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            cd[2 * u] = e4m3_encode(unpack_lo(Tag(), x[u]) * inv);
-            cd[2 * u + 1] = e4m3_encode(unpack_hi(Tag(), x[u]) * inv);
+            const float y0 = unpack_lo(Tag(), x[u]) * inv, y1 = unpack_hi(Tag(), x[u]) * inv;
+            cd[2 * u] = Kv::kI8 ? i8_encode(y0) : e4m3_encode(y0);
+            cd[2 * u + 1] = Kv::kI8 ? i8_encode(y1) : e4m3_encode(y1);
         }
         const u32x2 w = {cd[0] | cd[1] << 8 | cd[2] << 16 | cd[3] << 24,
                          cd[4] | cd[5] << 8 | cd[6] << 16 | cd[7] << 24};
@@ -573,8 +600,8 @@ template <typename Tag, typename Kv, bool kCols, int D, int NT>
 __device__ __forceinline__ void compute(WaveState<D>* st, KvRegs<Kv, D>& r, const u32x4* qop,
                                         float sl2, int tc, int t_end, const int* t_col, int t_lo,
                                         int q) {
-    if constexpr (Kv::kE4M3) {
-        ChunkRegs<D> ops = expand<Tag, D>(r);
+    if constexpr (Kv::k8) {
+        ChunkRegs<D> ops = expand<Tag, Kv, D>(r);
         compute_chunk<Tag, kCols, D, NT>(st, ops, qop, sl2, tc, t_end, t_col, t_lo, q);
     } else {
         compute_chunk<Tag, kCols, D, NT>(st, r, qop, sl2, tc, t_end, t_col, t_lo, q);
@@ -1000,7 +1027,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
     const int t0 = threadIdx.x;
     const int v0 = t0 < n0 + (kRows == 1 ? 1 : 0) ? p0[t0] : 0;
     const int v1 = kRows == 1 && t0 < n0 ? p1[t0] : 0;
-    constexpr int kSU = Kv::kE4M3 ? kStartUnitsE4M3 : kStartUnits16;
+    constexpr int kSU = Kv::k8 ? kStartUnits8 : kStartUnits16;
     int* pref = balanced_pref;
     int* lens = pref + a.num_seqs + 1;
     int* rmap = lens + a.num_seqs;     // verify rows only
@@ -1193,6 +1220,7 @@ hipError_t launch_tiles(const DecodeArgs& a, hipStream_t s) {
 template <typename Tag, int BS, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
     if (a.kv_format == kKvE4M3) return launch_tiles<Tag, BS, KvE4M3, 0, D>(a, s);
+    if (a.kv_format == kKvI8) return launch_tiles<Tag, BS, KvI8, 0, D>(a, s);
     if (a.table_rows == nullptr && a.query_start == nullptr)
         return launch_tiles<Tag, BS, KvSame, 0, D>(a, s);
     return launch_tiles<Tag, BS, KvSame, 1, D>(a, s);

@@ -110,6 +110,15 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
     return code | sign;
 }
 
+// Signed 8-bit code (two's complement byte) of a float32: the nearest
+// integer, ties to the even one, saturated to +-127; NaN, which no integer
+// code holds, is stored as 0.
+__device__ __forceinline__ uint32_t i8_encode(float y) {
+    if (y != y) return 0u;
+    const float r = __builtin_rintf(fminf(fmaxf(y, -127.0f), 127.0f));
+    return (uint32_t)(int)r & 0xFFu;
+}
+
 // 16 bytes -> float32 values (4 for F32, 8 for the 16-bit types).
 __device__ __forceinline__ void to_float(F32, u32x4 w, float* f) {
 #pragma unroll

@@ -49,15 +49,15 @@ struct DecodeArgs {
     int col_tiles;             // 16-column tiles per decode row (2 only for verify rows
                                //   of the matrix-core kernel); slots hold 16 * col_tiles
     float scale_log2;          // scale * log2(e) (* k_scale): scores in log2 units
-    int kv_format;             // kKvSame or kKvE4M3
-    float out_scale;           // v_scale for E4M3 caches, else 1: output = out_scale * o
+    int kv_format;             // KvFormat
+    float out_scale;           // v_scale for 8-bit caches, else 1: output = out_scale * o
     float k_inv_scale;         // fp32(1 / k_scale), fp32(1 / v_scale): the appended
-    float v_inv_scale;         //   token's quantisation (E4M3 caches)
+    float v_inv_scale;         //   token's quantisation (8-bit caches)
 };
 
-// Storage of the caches: the query's 16-bit type, or OCP FP8 E4M3 codes with
-// one scale per cache.
-enum KvFormat { kKvSame = 0, kKvE4M3 = 1 };
+// Storage of the caches: the query's 16-bit type, or OCP FP8 E4M3 or signed
+// INT8 codes with one scale per cache.
+enum KvFormat { kKvSame = 0, kKvE4M3 = 1, kKvI8 = 2 };
 
 // Work schedules of the decode kernels.
 //   kFixed: workgroup (kv head, sequence, p) takes tokens [p P, (p+1) P);
@@ -94,11 +94,11 @@ constexpr int kChunk = 32;            // tokens a wavefront handles per step
 // cache format, whose chunks take different times to stream; both values
 // are tuned by measurement (16-bit: 1.5 chunks, timed wavefronts show about
 // 2.3 us per history start against 2.9 us per chunk when a wavefront's
-// range holds many short histories; E4M3, half the bytes per chunk: 3
-// chunks).  A range of units holds the chunks that start inside it.
+// range holds many short histories; 8-bit codes, half the bytes per chunk:
+// 3 chunks).  A range of units holds the chunks that start inside it.
 constexpr int kChunkUnits = 2;
 constexpr int kStartUnits16 = 3;
-constexpr int kStartUnitsE4M3 = 6;
+constexpr int kStartUnits8 = 6;
 constexpr int kMaxStartUnits = 6;
 
 // Kernel families.
@@ -129,13 +129,13 @@ hipError_t launch_append_tokens(const void* key, const void* value, void* key_ca
                                 int row_bytes, int block_size, int num_blocks,
                                 int max_blocks_per_seq, int max_context_len, hipStream_t s);
 
-// Cache write into E4M3 caches: each value x of key/value (dtype src_dtype)
-// is stored as E4M3(fp32(x) * inv_scale).
-hipError_t launch_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
-                                        void* value_cache, const int64_t* slots, int num_tokens,
-                                        int num_kv_heads, int head_dim, int block_size,
-                                        int num_blocks, pa_dtype src_dtype, float k_inv_scale,
-                                        float v_inv_scale, hipStream_t s);
+// Cache write into 8-bit caches: each value x of key/value (dtype src_dtype)
+// is stored as Q(fp32(x) * inv_scale), Q = INT8 (int8) or E4M3 (otherwise).
+hipError_t launch_reshape_and_cache_q8(const void* key, const void* value, void* key_cache,
+                                       void* value_cache, const int64_t* slots, int num_tokens,
+                                       int num_kv_heads, int head_dim, int block_size,
+                                       int num_blocks, pa_dtype src_dtype, bool int8,
+                                       float k_inv_scale, float v_inv_scale, hipStream_t s);
 
 // Verify mode: for every query row r < total_q, the decode row that starts
 // at r -- the block-table row of its sequence, the effective history length

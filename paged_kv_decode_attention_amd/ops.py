@@ -61,6 +61,17 @@ _SIGNATURES = {
     "pa_reshape_and_cache_fp8": (
         _I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, ctypes.c_float, ctypes.c_float,
              _VP]),
+    "pa_paged_attention_decode_i8": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _VP,
+             _I, _I, _I, _I, _I, _I, _I, _I, _I,
+             ctypes.c_float, _I, ctypes.c_float, ctypes.c_float, _I, _VP, ctypes.c_size_t, _VP]),
+    "pa_decode_append_i8": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+             _I, _I, _I, _I, _I, _I, _I, _I, _I,
+             ctypes.c_float, _I, ctypes.c_float, ctypes.c_float, _I, _VP, ctypes.c_size_t, _VP]),
+    "pa_reshape_and_cache_i8": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, ctypes.c_float, ctypes.c_float,
+             _VP]),
     "pa_pool_create": (_VP, [_I, _I]),
     "pa_pool_destroy": (None, [_VP]),
     "pa_pool_add_sequence": (_I, [_VP]),
@@ -160,10 +171,15 @@ def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_siz
 
 
 FP8_CACHE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+INT8_CACHE_DTYPES = (torch.int8,)
+# 8-bit cache formats: accepted cache dtypes and their description
+_CODES = {"fp8": (FP8_CACHE_DTYPES, "FP8 caches must be uint8 or float8_e4m3fn tensors of "
+                                    "E4M3 codes"),
+          "int8": (INT8_CACHE_DTYPES, "INT8 caches must be int8 tensors")}
 
 
 def _decode_args(query, key_cache, value_cache, block_tables, context_lens, scale,
-                 max_context_len, partition_size, out, workspace, kv_fp8=False):
+                 max_context_len, partition_size, out, workspace, kv8=None):
     for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
                  (block_tables, "block_tables"), (context_lens, "context_lens")):
         _gpu(t, n)
@@ -173,9 +189,10 @@ def _decode_args(query, key_cache, value_cache, block_tables, context_lens, scal
     N, H_kv, BS, D2 = key_cache.shape
     if D2 != D:
         raise ValueError("head_dim of query (%d) and caches (%d) differ" % (D, D2))
-    if kv_fp8:
-        if key_cache.dtype not in FP8_CACHE_DTYPES or value_cache.dtype not in FP8_CACHE_DTYPES:
-            raise ValueError("FP8 caches must be uint8 or float8_e4m3fn tensors of E4M3 codes")
+    if kv8 is not None:
+        ok, msg = _CODES[kv8]
+        if key_cache.dtype not in ok or value_cache.dtype not in ok:
+            raise ValueError(msg)
     elif key_cache.dtype != query.dtype or value_cache.dtype != query.dtype:
         raise ValueError("query and caches must share one dtype")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
@@ -369,6 +386,65 @@ def paged_attention_verify(query, key_cache, value_cache, block_tables, context_
     return out
 
 
+def _decode_q8(kv8, query, key_cache, value_cache, block_tables, context_lens, k_scale,
+               v_scale, scale, max_context_len, partition_size, out, workspace):
+    out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
+                                    scale, max_context_len, partition_size, out, workspace,
+                                    kv8=kv8)
+    name = "paged_attention_decode_" + ("fp8" if kv8 == "fp8" else "i8")
+    status = getattr(load_library(), "pa_" + name)(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), *sizes, *_fp8_tail(tail, k_scale, v_scale))
+    _check(status, name)
+    return out
+
+
+def _decode_append_q8(kv8, query, key, value, key_cache, value_cache, block_tables,
+                      context_lens, k_scale, v_scale, scale, max_context_len, partition_size,
+                      out, workspace):
+    out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
+                                    scale, max_context_len, partition_size, out, workspace,
+                                    kv8=kv8)
+    for t, n in ((key, "key"), (value, "value")):
+        _gpu(t, n)
+    S, H_kv, D = query.shape[0], key_cache.shape[1], query.shape[2]
+    if key.shape != (S, H_kv, D) or value.shape != key.shape:
+        raise ValueError("key and value must be [S, H_kv, D]")
+    if key.dtype != query.dtype or value.dtype != query.dtype:
+        raise ValueError("key/value must share the query dtype")
+    name = "decode_append_" + ("fp8" if kv8 == "fp8" else "i8")
+    status = getattr(load_library(), "pa_" + name)(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
+        _ptr(block_tables), _ptr(context_lens), *sizes, *_fp8_tail(tail, k_scale, v_scale))
+    _check(status, name)
+    return out
+
+
+def _reshape_and_cache_q8(kv8, key, value, key_cache, value_cache, slot_mapping, k_scale,
+                          v_scale):
+    for t, n in ((key, "key"), (value, "value"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache"), (slot_mapping, "slot_mapping")):
+        _gpu(t, n)
+    if key.shape != value.shape or key.dim() != 3 or key.dtype != value.dtype:
+        raise ValueError("key and value must be [T, H_kv, D] of one shape and dtype")
+    if key_cache.shape != value_cache.shape or key_cache.dim() != 4:
+        raise ValueError("caches must be [N, H_kv, BS, D] of one shape")
+    ok, msg = _CODES[kv8]
+    if key_cache.dtype not in ok or value_cache.dtype not in ok:
+        raise ValueError(msg)
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
+        raise ValueError("slot_mapping must be [T] int64")
+    T, H_kv, D = key.shape
+    N, H_kv2, BS, D2 = key_cache.shape
+    if (H_kv, D) != (H_kv2, D2):
+        raise ValueError("new tokens and caches disagree in KV heads or head_dim")
+    name = "reshape_and_cache_" + ("fp8" if kv8 == "fp8" else "i8")
+    _check(getattr(load_library(), "pa_" + name)(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T, H_kv,
+        D, BS, N, dtype_code(key.dtype), float(k_scale), float(v_scale),
+        _stream(key.device)), name)
+
+
 def paged_attention_decode_fp8(query, key_cache, value_cache, block_tables, context_lens,
                                k_scale, v_scale, scale=None, *, max_context_len=None,
                                partition_size=0, out=None, workspace=None):
@@ -377,14 +453,8 @@ def paged_attention_decode_fp8(query, key_cache, value_cache, block_tables, cont
     (keys) or * v_scale (values).  query/out bf16 or f16; the shapes of the
     matrix-core kernel (head_dim 64/128/256, block size 8-64, GQA group up to
     16, or 32 at head_dim 64/128)."""
-    out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
-                                    scale, max_context_len, partition_size, out, workspace,
-                                    kv_fp8=True)
-    status = load_library().pa_paged_attention_decode_fp8(
-        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
-        _ptr(context_lens), *sizes, *_fp8_tail(tail, k_scale, v_scale))
-    _check(status, "paged_attention_decode_fp8")
-    return out
+    return _decode_q8("fp8", query, key_cache, value_cache, block_tables, context_lens,
+                      k_scale, v_scale, scale, max_context_len, partition_size, out, workspace)
 
 
 def decode_append_fp8(query, key, value, key_cache, value_cache, block_tables, context_lens,
@@ -392,46 +462,45 @@ def decode_append_fp8(query, key, value, key_cache, value_cache, block_tables, c
                       out=None, workspace=None):
     """decode_append on E4M3 caches: the newest token's key/value (query
     dtype) are quantised with k_scale / v_scale as they are stored."""
-    out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
-                                    scale, max_context_len, partition_size, out, workspace,
-                                    kv_fp8=True)
-    for t, n in ((key, "key"), (value, "value")):
-        _gpu(t, n)
-    S, H_kv, D = query.shape[0], key_cache.shape[1], query.shape[2]
-    if key.shape != (S, H_kv, D) or value.shape != key.shape:
-        raise ValueError("key and value must be [S, H_kv, D]")
-    if key.dtype != query.dtype or value.dtype != query.dtype:
-        raise ValueError("key/value must share the query dtype")
-    status = load_library().pa_decode_append_fp8(
-        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
-        _ptr(block_tables), _ptr(context_lens), *sizes, *_fp8_tail(tail, k_scale, v_scale))
-    _check(status, "decode_append_fp8")
-    return out
+    return _decode_append_q8("fp8", query, key, value, key_cache, value_cache, block_tables,
+                             context_lens, k_scale, v_scale, scale, max_context_len,
+                             partition_size, out, workspace)
 
 
 def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale):
     """Quantise key/value [T, H_kv, D] (f32, f16 or bf16) to E4M3 with the
     given scales and store them at slot_mapping [T] in the uint8 /
     float8_e4m3fn caches [N, H_kv, BS, D]."""
-    for t, n in ((key, "key"), (value, "value"), (key_cache, "key_cache"),
-                 (value_cache, "value_cache"), (slot_mapping, "slot_mapping")):
-        _gpu(t, n)
-    if key.shape != value.shape or key.dim() != 3 or key.dtype != value.dtype:
-        raise ValueError("key and value must be [T, H_kv, D] of one shape and dtype")
-    if key_cache.shape != value_cache.shape or key_cache.dim() != 4:
-        raise ValueError("caches must be [N, H_kv, BS, D] of one shape")
-    if key_cache.dtype not in FP8_CACHE_DTYPES or value_cache.dtype not in FP8_CACHE_DTYPES:
-        raise ValueError("FP8 caches must be uint8 or float8_e4m3fn")
-    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
-        raise ValueError("slot_mapping must be [T] int64")
-    T, H_kv, D = key.shape
-    N, H_kv2, BS, D2 = key_cache.shape
-    if (H_kv, D) != (H_kv2, D2):
-        raise ValueError("new tokens and caches disagree in KV heads or head_dim")
-    _check(load_library().pa_reshape_and_cache_fp8(
-        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T, H_kv,
-        D, BS, N, dtype_code(key.dtype), float(k_scale), float(v_scale),
-        _stream(key.device)), "reshape_and_cache_fp8")
+    _reshape_and_cache_q8("fp8", key, value, key_cache, value_cache, slot_mapping, k_scale,
+                          v_scale)
+
+
+def paged_attention_decode_i8(query, key_cache, value_cache, block_tables, context_lens,
+                              k_scale, v_scale, scale=None, *, max_context_len=None,
+                              partition_size=0, out=None, workspace=None):
+    """paged_attention_decode over caches of signed INT8 codes (int8 [N, H_kv,
+    BS, D]); code c stands for c * k_scale (keys) or c * v_scale (values).
+    Query dtypes and shapes as for paged_attention_decode_fp8."""
+    return _decode_q8("int8", query, key_cache, value_cache, block_tables, context_lens,
+                      k_scale, v_scale, scale, max_context_len, partition_size, out, workspace)
+
+
+def decode_append_i8(query, key, value, key_cache, value_cache, block_tables, context_lens,
+                     k_scale, v_scale, scale=None, *, max_context_len=None, partition_size=0,
+                     out=None, workspace=None):
+    """decode_append on INT8 caches: the newest token's key/value (query
+    dtype) are quantised with k_scale / v_scale as they are stored."""
+    return _decode_append_q8("int8", query, key, value, key_cache, value_cache, block_tables,
+                             context_lens, k_scale, v_scale, scale, max_context_len,
+                             partition_size, out, workspace)
+
+
+def reshape_and_cache_i8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale):
+    """Quantise key/value [T, H_kv, D] (f32, f16 or bf16) to INT8 codes
+    (nearest integer of x / scale, ties to even, clamped to +-127, NaN to 0)
+    and store them at slot_mapping [T] in the int8 caches [N, H_kv, BS, D]."""
+    _reshape_and_cache_q8("int8", key, value, key_cache, value_cache, slot_mapping, k_scale,
+                          v_scale)
 
 
 def copy_blocks(key_cache, value_cache, block_pairs):
