@@ -171,27 +171,32 @@ def cpu_baseline_threads(inp, budget_s, arrays, max_workers=16):
                       % (done, workers, elapsed)}
 
 
-def fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
-                    timed_replay):
-    """The same decode calls on OCP FP8 E4M3 caches (pa_paged_attention_decode_fp8):
-    each pool replica quantised once by the library's own FP8 cache write
+def q8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
+                   timed_replay, fmt="fp8"):
+    """The same decode calls on 8-bit caches: OCP FP8 E4M3 codes
+    (pa_paged_attention_decode_fp8) or INT8 codes (pa_paged_attention_decode_i8).
+    Each pool replica is quantised once by the library's own 8-bit cache write
     (every slot written as one token, per-cache scales), then K decode calls
-    replayed from a HIP graph.  Algorithmic bytes are half the 16-bit ones."""
+    are replayed from a HIP graph.  Algorithmic bytes are half the 16-bit ones."""
     import numpy as np
     import torch
     from paged_kv_decode_attention_amd import ops
 
-    k_scale, v_scale = 1.0 / 64, 1.0 / 64
+    fp8 = fmt == "fp8"
+    # unit-variance pools: E4M3 spans +-448 * 1/64 = +-7, INT8 +-127 * 1/24 = +-5.3
+    k_scale = v_scale = 1.0 / 64 if fp8 else 1.0 / 24
+    write = ops.reshape_and_cache_fp8 if fp8 else ops.reshape_and_cache_i8
+    decode = ops.paged_attention_decode_fp8 if fp8 else ops.paged_attention_decode_i8
     N, H_kv, BS, D = kcs[0].shape
     slots = torch.arange(N * BS, dtype=torch.int64, device=dev)
     k8s, v8s = [], []
     for kc, vc in zip(kcs, vcs):
-        k8 = torch.empty(N, H_kv, BS, D, dtype=torch.uint8, device=dev)
+        k8 = torch.empty(N, H_kv, BS, D, dtype=torch.uint8 if fp8 else torch.int8, device=dev)
         v8 = torch.empty_like(k8)
         # pool rows as tokens: [N, BS, H_kv, D] -> [N*BS, H_kv, D], slot = row
-        ops.reshape_and_cache_fp8(kc.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous(),
-                                  vc.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous(),
-                                  k8, v8, slots, k_scale, v_scale)
+        write(kc.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous(),
+              vc.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous(),
+              k8, v8, slots, k_scale, v_scale)
         k8s.append(k8)
         v8s.append(v8)
     out = torch.empty_like(q)
@@ -201,8 +206,8 @@ def fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, cap
 
     def call(k):
         r = k % len(k8s)
-        ops.paged_attention_decode_fp8(q, k8s[r], v8s[r], bt, cl, k_scale, v_scale, cfg.scale,
-                                       max_context_len=max_ctx, out=out, workspace=ws)
+        decode(q, k8s[r], v8s[r], bt, cl, k_scale, v_scale, cfg.scale,
+               max_context_len=max_ctx, out=out, workspace=ws)
     for k in range(10):
         call(k)
     torch.cuda.synchronize()
@@ -212,7 +217,8 @@ def fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, cap
     t = float(us.mean()) * 1e-6
     alg8 = alg_bytes // 2
     del k8s, v8s
-    return {"kv_format": "OCP FP8 E4M3, per-cache scales", "decode_us_mean": t * 1e6,
+    return {"kv_format": ("OCP FP8 E4M3" if fp8 else "INT8 symmetric") + ", per-cache scales",
+            "decode_us_mean": t * 1e6,
             "decode_tokens_per_s": S / t, "alg_bytes_per_launch": alg8,
             "achieved_gbps": alg8 / t / 1e9, "frac": alg8 / t / 1e9 / HBM_PEAK_GBPS,
             "bound": "hbm"}
@@ -266,10 +272,10 @@ def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture
 
 def shape_sweep(args, dev):
     """Decode-call rate over block sizes 8/16/32/64 and head dims 64/128/256,
-    on 16-bit caches and on FP8 E4M3 caches: the bench batch (64 sequences,
-    28 query / 4 KV heads, the same seeded context lengths), bf16 queries,
-    shuffled tables, random pools on the GPU (the FP8 ones quantised by the
-    library's cache write), pool replicas rotated so the last-level cache
+    on 16-bit caches and on FP8 E4M3 and INT8 caches: the bench batch (64
+    sequences, 28 query / 4 KV heads, the same seeded context lengths), bf16
+    queries, shuffled tables, random pools on the GPU (the 8-bit ones quantised
+    by the library's cache writes), pool replicas rotated so the last-level cache
     cannot hold the working set; K calls replayed from a HIP graph, HIP
     events around each replay."""
     import numpy as np
@@ -282,7 +288,7 @@ def shape_sweep(args, dev):
     S, H, H_kv = base.num_seqs, base.num_heads, base.num_kv_heads
     G = H // H_kv
     K = min(args.steps, 100)
-    k_scale = v_scale = 1.0 / 64
+    scales = {"fp8": 1.0 / 64, "int8": 1.0 / 24}
     rows = []
 
     def timed(call):
@@ -332,9 +338,10 @@ def shape_sweep(args, dev):
                                                            q.dtype), 256),
                              dtype=torch.uint8, device=dev)
             mfma = ops.decode_kernel(D, BS, G, q.dtype) == ops.KERNEL_MFMA
-            for kv in ("bf16", "fp8"):
-                if kv == "fp8" and not mfma:
+            for kv in ("bf16", "fp8", "int8"):
+                if kv != "bf16" and not mfma:
                     continue
+                k_scale = v_scale = scales.get(kv, 1.0)
                 e = 2 if kv == "bf16" else 1
                 pool = N * H_kv * BS * D * e
                 # replicas cycled through: 1.2 GB or more of K/V between two
@@ -344,13 +351,15 @@ def shape_sweep(args, dev):
                 kcs, vcs = [], []
                 for _ in range(2 * R):
                     x = torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(torch.bfloat16)
-                    if kv == "fp8":
+                    if kv != "bf16":
                         # pool rows as tokens: slot pb * BS + off holds row (pb, :, off)
-                        c = torch.empty(N, H_kv, BS, D, dtype=torch.uint8, device=dev)
+                        c = torch.empty(N, H_kv, BS, D, device=dev,
+                                        dtype=torch.uint8 if kv == "fp8" else torch.int8)
                         rows_ = x.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous()
                         slots = torch.arange(N * BS, dtype=torch.int64, device=dev)
-                        ops.reshape_and_cache_fp8(rows_, rows_, c, torch.empty_like(c), slots,
-                                                  k_scale, v_scale)
+                        write = (ops.reshape_and_cache_fp8 if kv == "fp8"
+                                 else ops.reshape_and_cache_i8)
+                        write(rows_, rows_, c, torch.empty_like(c), slots, k_scale, v_scale)
                         x = c
                     (kcs if len(kcs) < R else vcs).append(x)
                 torch.cuda.synchronize()
@@ -361,14 +370,16 @@ def shape_sweep(args, dev):
                                                    max_context_len=max_ctx, out=out,
                                                    workspace=ws)
                 else:
+                    dec = (ops.paged_attention_decode_fp8 if kv == "fp8"
+                           else ops.paged_attention_decode_i8)
+
                     def call(j):
-                        ops.paged_attention_decode_fp8(q, kcs[j % R], vcs[j % R], btd, cld,
-                                                       k_scale, v_scale, max_context_len=max_ctx,
-                                                       out=out, workspace=ws)
+                        dec(q, kcs[j % R], vcs[j % R], btd, cld, k_scale, v_scale,
+                            max_context_len=max_ctx, out=out, workspace=ws)
                 t = timed(call)
                 alg = int(lens.sum()) * H_kv * D * e * 2
                 row = {"head_dim": D, "block_size": BS,
-                       "kv": "bf16" if kv == "bf16" else "fp8 e4m3",
+                       "kv": {"bf16": "bf16", "fp8": "fp8 e4m3", "int8": "int8"}[kv],
                        "kernel": "matrix-core, balanced" if mfma else "vector-ALU, partitions",
                        "decode_us": t * 1e6, "alg_bytes": alg, "achieved_gbps": alg / t / 1e9,
                        "frac": alg / t / 1e9 / HBM_PEAK_GBPS, "decode_tokens_per_s": S / t,
@@ -389,7 +400,7 @@ def shape_sweep(args, dev):
                 r["head_dim"], r["block_size"], r["kv"], r["kernel"], r["decode_us"],
                 r["achieved_gbps"] / 1e3, 100 * r["frac"], r["decode_tokens_per_s"]))
         L += ["", "Algorithmic bytes: sum_b L_b x 4 KV heads x head_dim x element bytes (2 for "
-              "bf16, 1 for FP8 E4M3) x 2 (K and V).  "
+              "bf16, 1 for FP8 E4M3 and INT8) x 2 (K and V).  "
               "Timing: K decode calls replayed from a HIP graph, HIP events around each "
               "replay, mean of 3."]
         with open(args.sweep_out, "w") as fh:
@@ -588,7 +599,7 @@ def main():
 
     # the other operations' figures (not in --decode-only runs, which the
     # hardware-counter passes profile)
-    copy = fp8_kv = verify = None
+    copy = fp8_kv = int8_kv = verify = None
     if not args.decode_only:
         copy = copy_blocks_rate(kcs, vcs, dev)
         verify = verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
@@ -596,8 +607,10 @@ def main():
         verify["q_len_2"] = verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
                                         capture, timed_replay, q_len=2)
         if cfg.dtype in ("bf16", "f16"):
-            fp8_kv = fp8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
-                                     capture, timed_replay)
+            fp8_kv = q8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
+                                    capture, timed_replay, "fp8")
+            int8_kv = q8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes,
+                                     capture, timed_replay, "int8")
 
     dec_s = float(dec_ms.mean()) * 1e-3
     achieved = alg_bytes / dec_s / 1e9
@@ -651,6 +664,7 @@ def main():
         "hbm_read_ceiling_gbps": ceiling_gbps,
         "copy_blocks": copy,
         "fp8_kv": fp8_kv,
+        "int8_kv": int8_kv,
         "verify": verify,
         "kernel_src_sha": kernel_source_hash(),
     }
