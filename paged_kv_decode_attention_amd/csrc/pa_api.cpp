@@ -351,7 +351,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     a.schedule = balanced ? pa::kBalanced : pa::kFixed;
     a.num_wg = balanced ? balanced_workgroups(head_dim) : 0;
     a.col_tiles = col_tiles;
-    // scale * log2(e), and the key scale of an FP8 cache folded into it
+    // scale * log2(e), and the key scale of an 8-bit cache folded into it
     a.scale_log2 = (float)((double)scale * 1.4426950408889634 * (q8 ? (double)k_scale : 1.0));
     a.kv_format = kv_format;
     a.out_scale = q8 ? v_scale : 1.0f;

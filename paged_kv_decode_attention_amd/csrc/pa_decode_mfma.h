@@ -77,7 +77,7 @@ struct Dim {
     static constexpr int VW = D / 16;   // d values a lane holds per V row = PV MFMAs
     static constexpr int RB = D * 2;    // bytes per 16-bit token row
     static constexpr int OS = D + 4;    // padded LDS row of one column (floats)
-    // 32-bit dwords of this lane's slice of a V row: 16-bit / E4M3 storage
+    // 32-bit dwords of this lane's slice of a V row: 16-bit / 8-bit storage
     using VRow = typename std::conditional<
         D == 64, u32x2, typename std::conditional<D == 128, u32x4, u32x8>::type>::type;
     using VRow8 = typename std::conditional<
@@ -155,7 +155,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, bo
 constexpr int kNonTemporal = 2;   // buffer cache-policy bit: nt
 
 // V row slices: 8, 16 or 32 bytes (head_dim 64, 128, 256) of 16-bit values;
-// 4, 8 or 16 bytes of E4M3 codes.
+// 4, 8 or 16 bytes of 8-bit codes.
 __device__ __forceinline__ void load_row(u32x8& x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
     const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNonTemporal);
     const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kNonTemporal);

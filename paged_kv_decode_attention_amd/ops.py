@@ -224,7 +224,7 @@ def _decode_args(query, key_cache, value_cache, block_tables, context_lens, scal
     return out, sizes, tail
 
 
-def _fp8_tail(tail, k_scale, v_scale):
+def _q8_tail(tail, k_scale, v_scale):
     # (scale, dtype, partition_size, ws, ws_len, stream) ->
     # (scale, dtype, k_scale, v_scale, partition_size, ws, ws_len, stream)
     return tail[:2] + (float(k_scale), float(v_scale)) + tail[2:]
@@ -394,7 +394,7 @@ def _decode_q8(kv8, query, key_cache, value_cache, block_tables, context_lens, k
     name = "paged_attention_decode_" + ("fp8" if kv8 == "fp8" else "i8")
     status = getattr(load_library(), "pa_" + name)(
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
-        _ptr(context_lens), *sizes, *_fp8_tail(tail, k_scale, v_scale))
+        _ptr(context_lens), *sizes, *_q8_tail(tail, k_scale, v_scale))
     _check(status, name)
     return out
 
@@ -415,7 +415,7 @@ def _decode_append_q8(kv8, query, key, value, key_cache, value_cache, block_tabl
     name = "decode_append_" + ("fp8" if kv8 == "fp8" else "i8")
     status = getattr(load_library(), "pa_" + name)(
         _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache),
-        _ptr(block_tables), _ptr(context_lens), *sizes, *_fp8_tail(tail, k_scale, v_scale))
+        _ptr(block_tables), _ptr(context_lens), *sizes, *_q8_tail(tail, k_scale, v_scale))
     _check(status, name)
     return out
 
