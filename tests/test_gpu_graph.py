@@ -129,3 +129,39 @@ def test_graph_decode_append_replays_match_eager():
                           workspace=ws)
 
     _replays_match(step, out, ws)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_graph_decode_append_8bit_replays_match_eager(fmt):
+    """The fused step on 8-bit caches (the newest token quantised inside the
+    decode kernel) in a graph.  The caches are restored before each step, so
+    every step writes the same codes."""
+    cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_seqs=16, num_blocks=6000)
+    inp = I.generate(cfg, new_tokens_at="last")
+    d = upload(inp)
+    S, H, D = d["query"].shape
+    N, H_kv, BS, _ = d["key_cache"].shape
+    W = d["block_tables"].shape[1]
+    ks, vs = 1.0 / 24, 1.0 / 20
+    dt = torch.uint8 if fmt == "fp8" else torch.int8
+    k0 = torch.empty(N, H_kv, BS, D, dtype=dt, device=DEV)
+    v0 = torch.empty_like(k0)
+    write = ops.reshape_and_cache_fp8 if fmt == "fp8" else ops.reshape_and_cache_i8
+    slots = torch.arange(N * BS, dtype=torch.int64, device=DEV)
+    write(d["key_cache"].permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous(),
+          d["value_cache"].permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous(),
+          k0, v0, slots, ks, vs)
+    kc, vc = k0.clone(), v0.clone()
+    ws = torch.empty(max(256, ops.decode_workspace_size(S, H, H_kv, D, BS, W * BS, 0,
+                                                        d["query"].dtype)),
+                     dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(d["query"])
+    step_fn = ops.decode_append_fp8 if fmt == "fp8" else ops.decode_append_i8
+
+    def step():
+        kc.copy_(k0)
+        vc.copy_(v0)
+        step_fn(d["query"], d["new_key"], d["new_value"], kc, vc, d["block_tables"],
+                d["context_lens"], ks, vs, out=out, workspace=ws)
+
+    _replays_match(step, out, ws)
