@@ -136,16 +136,17 @@ def test_copy_blocks_rejects_on_host(lib):
     assert f(vp(FAKE), vp(FAKE), vp(FAKE), 3, 2, 64, 16, 0, ops.PA_F32, vp(0)) == INVALID
 
 
-def test_fp8_entry_points_reject_on_host(lib):
+@pytest.mark.parametrize("fmt", ["fp8", "i8"])
+def test_8bit_entry_points_reject_on_host(lib, fmt):
     vp, f32 = ctypes.c_void_p, ctypes.c_float
-    f = lib.pa_reshape_and_cache_fp8
+    f = getattr(lib, "pa_reshape_and_cache_" + fmt)
     args = lambda ks, vs, T=4, D=128: (vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), T, 2, D,
                                        16, 4, ops.PA_BF16, f32(ks), f32(vs), vp(0))
     assert f(*args(1.0, 1.0, T=0)) == OK                       # no tokens
     assert f(*args(0.0, 1.0)) == INVALID                       # scale must be > 0
     assert f(*args(1.0, float("inf"))) == INVALID
     assert f(*args(1.0, 1.0, D=24)) == UNSUPPORTED             # head_dim not a multiple of 16
-    d = lib.pa_paged_attention_decode_fp8
+    d = getattr(lib, "pa_paged_attention_decode_" + fmt)
     base = dict(S=2, H=28, H_kv=4, G=7, D=128, BS=16, dtype=ops.PA_BF16, ks=0.5, vs=0.5)
 
     def call(**kw):
@@ -158,6 +159,11 @@ def test_fp8_entry_points_reject_on_host(lib):
     assert call(G=33, H=132) == UNSUPPORTED                    # matrix-core kernel: group <= 32
     assert call(dtype=ops.PA_F32) == UNSUPPORTED               # f32 queries: vector-ALU only
     assert call(S=0) == OK
+    # the fused append needs the new key and value
+    a = getattr(lib, "pa_decode_append_" + fmt)
+    assert a(vp(FAKE), vp(FAKE), vp(0), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+             2, 28, 4, 7, 128, 16, 64, 16, 256, f32(0.1), ops.PA_BF16, f32(0.5), f32(0.5), 0,
+             vp(FAKE), ctypes.c_size_t(1 << 30), vp(0)) == INVALID
 
 
 def test_decode_kernel_choice(lib):
