@@ -33,6 +33,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attention tokens/s and achieved KV HBM GB/s (% of peak), 1 MI355X"
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_qwen7b_gqa_bf16_traffic.json")
+TRACE_FILE = os.path.join(HERE, "profiles", "decode_qwen7b_gqa_bf16_kernel_trace.json")
 
 
 def parse():
@@ -81,6 +82,31 @@ def load_traffic(config_name, per_launch_alg_bytes):
     if t.get("kernel_src_sha") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+def load_kernel_only(config_name, alg_bytes):
+    """rocprofv3 kernel-only durations of the bench call's two kernels (the
+    16-bit matrix-core decode kernel and its merge kernel) from the committed
+    kernel trace of bench.py, if it was taken on the current kernel sources;
+    else None.  The decode kernel's calls include the hot-cache and
+    single-call figures of the same run; the merge kernel's also those of the
+    FP8, INT8 and verify figures, which launch the same instantiation."""
+    if config_name != "qwen7b_gqa_bf16" or not os.path.exists(TRACE_FILE):
+        return None
+    with open(TRACE_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_src_sha") != kernel_source_hash():
+        return None
+    ks = t.get("kernels", {})
+    dec = ks.get("decode_mfma_balanced<pa::BF16, 16, KvSame, 0, 128, 1>")
+    mrg = ks.get("merge_balanced<pa::BF16, 128, 16>")
+    if not dec or not mrg:
+        return None
+    pick = lambda k: {x: k[x] for x in ("calls", "avg_us", "median_us", "min_us", "max_us")}
+    return {"source": os.path.relpath(TRACE_FILE, HERE),
+            "decode_kernel": pick(dec), "merge_kernel": pick(mrg),
+            "decode_kernel_gbps": alg_bytes / (dec["median_us"] * 1e-6) / 1e9,
+            "decode_kernel_frac": alg_bytes / (dec["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS}
 
 
 def cpu_baseline(inp, budget_s):
@@ -659,6 +685,9 @@ def main():
             "decode_us_max": float(dec_ms.max()) * 1e3,
             "single_call_us_p10_p50_p90": [float(np.percentile(one_us, p)) for p in (10, 50, 90)],
             "hot_cache_decode_us": hot_us,
+            # rocprofv3 kernel-only durations (committed trace of this
+            # command, current sources only), beside the event timings
+            "rocprof_kernel_only": load_kernel_only(args.config, alg_bytes),
         },
         "decode_tokens_per_s": S / dec_s,
         "hbm_read_ceiling_gbps": ceiling_gbps,

@@ -4,7 +4,8 @@
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --copy-bytes N --config NAME --out FILE.json [--command CMD ...]
     python -m paged_kv_decode_attention_amd.counters trace \\
-        --db FILE.db --out FILE.md --title TEXT --command CMD [--note TEXT ...]
+        --db FILE.db --out FILE.md --title TEXT --command CMD [--note TEXT ...] \\
+        [--json FILE.json --sha HASH]
     python -m paged_kv_decode_attention_amd.counters compute \\
         --run DIR --out FILE.md --title TEXT --command CMD [--note TEXT ...]
 
@@ -131,6 +132,25 @@ def compute_main(a):
     return 0
 
 
+def trace_durations(db):
+    """Sorted kernel durations (us) per kernel of a --kernel-trace database."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        rows = con.execute("select name, end - start from kernels").fetchall()
+    finally:
+        con.close()
+    out = {}
+    for name, ns in rows:
+        out.setdefault(short_name(name), []).append(ns / 1e3)
+    return {k: sorted(v) for k, v in out.items()}
+
+
+def median(xs):
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
 def trace_main(a):
     lines = ["# " + a.title, "", "Command (repository root, one MI355X):", "",
              "    " + a.command, "",
@@ -143,6 +163,14 @@ def trace_main(a):
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+    if a.json:
+        # kernel-only durations for bench.py, tied to the decode sources
+        rec = {"kernel_src_sha": a.sha, "command": a.command, "kernels": {
+            k: {"calls": len(v), "avg_us": sum(v) / len(v), "median_us": median(v),
+                "min_us": v[0], "max_us": v[-1]}
+            for k, v in trace_durations(a.db).items()}}
+        with open(a.json, "w") as fh:
+            json.dump(rec, fh, indent=1)
     return 0
 
 
@@ -155,6 +183,8 @@ def main(argv=None):
     tr.add_argument("--title", required=True)
     tr.add_argument("--command", required=True)
     tr.add_argument("--note", action="append", default=[])
+    tr.add_argument("--json", default=None)
+    tr.add_argument("--sha", default=None)
     cp = sub.add_parser("compute", help="instruction counters of the decode kernels")
     cp.add_argument("--run", required=True)
     cp.add_argument("--out", required=True)

@@ -76,6 +76,17 @@ def test_trace_table(tmp_path):
     k, calls, avg, lo, hi, share = table[0]
     assert (calls, avg, lo, hi) == (2, 55.0, 50.0, 60.0)
     assert share == pytest.approx(100.0 * 110 / 115)
+    # the JSON record bench.py reads: per-kernel durations and the source hash
+    out, js = tmp_path / "t.md", tmp_path / "t.json"
+    counters.main(["trace", "--db", str(db), "--out", str(out), "--title", "t",
+                   "--command", "c", "--json", str(js), "--sha", "abc"])
+    rec = json.load(open(js))
+    assert rec["kernel_src_sha"] == "abc"
+    dec = rec["kernels"]["decode_mfma_balanced<pa::BF16, 16>"]
+    assert (dec["calls"], dec["avg_us"], dec["median_us"], dec["min_us"], dec["max_us"]) == \
+        (2, 55.0, 55.0, 50.0, 60.0)
+    assert rec["kernels"]["merge_balanced<pa::BF16>"]["median_us"] == 5.0
+    assert counters.median([1.0, 2.0, 7.0]) == 2.0
 
 
 def test_compute_counter_summary(tmp_path):
