@@ -167,3 +167,22 @@ def test_fp8_full_bench_workload_sampled():
     kdq[blocks] = fp8.dequantize(kq[blocks], K_SCALE)
     vdq[blocks] = fp8.dequantize(vq[blocks], V_SCALE)
     compare(out, oracle_fp8(inp, kdq, vdq, pairs), "bf16", pairs=pairs, what="fp8 bench workload")
+
+
+@pytest.mark.parametrize("D", [48, 256])
+def test_fp8_cache_write_other_head_dims(D):
+    """head_dim 48 (a multiple of 16 that is not a power of two) and 256."""
+    T, H_kv, BS, N = 100, 3, 32, 16
+    g = torch.Generator().manual_seed(D)
+    key = (torch.randn(T, H_kv, D, generator=g) * 3).to(torch.bfloat16)
+    value = (torch.randn(T, H_kv, D, generator=g) * 9).to(torch.bfloat16)
+    slots = np.random.default_rng(D).choice(N * BS, size=T, replace=False).astype(np.int64)
+    kc = torch.full((N, H_kv, BS, D), 0x3C, dtype=torch.uint8)
+    dk, dv = kc.to(DEV), kc.to(DEV)
+    ops.reshape_and_cache_fp8(key.to(DEV), value.to(DEV), dk, dv,
+                              torch.from_numpy(slots).to(DEV), K_SCALE, V_SCALE)
+    torch.cuda.synchronize()
+    rk, rv = fp8.reshape_and_cache_fp8(key.float().numpy(), value.float().numpy(), kc.numpy(),
+                                       kc.numpy(), slots, K_SCALE, V_SCALE)
+    assert np.array_equal(dk.cpu().numpy(), rk)
+    assert np.array_equal(dv.cpu().numpy(), rv)
