@@ -205,3 +205,21 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         ops.paged_attention_decode(q, kc, kc, torch.zeros(2, 1, dtype=torch.int32),
                                    torch.zeros(2, dtype=torch.int32))
+
+
+def test_8bit_bindings_refuse_cpu_tensors():
+    """Every 8-bit binding checks its tensors before calling the library: host
+    tensors are refused on a machine without a GPU as on one with it."""
+    import torch
+    q = torch.zeros(2, 4, 64, dtype=torch.bfloat16)
+    bt, cl = torch.zeros(2, 1, dtype=torch.int32), torch.zeros(2, dtype=torch.int32)
+    kv = torch.zeros(2, 2, 64, dtype=torch.bfloat16)
+    slots = torch.zeros(2, dtype=torch.int64)
+    for fmt, dt in (("fp8", torch.uint8), ("i8", torch.int8)):
+        kc = torch.zeros(8, 2, 16, 64, dtype=dt)
+        with pytest.raises(ValueError):
+            getattr(ops, "paged_attention_decode_" + fmt)(q, kc, kc, bt, cl, 1.0, 1.0)
+        with pytest.raises(ValueError):
+            getattr(ops, "decode_append_" + fmt)(q, kv, kv, kc, kc, bt, cl, 1.0, 1.0)
+        with pytest.raises(ValueError):
+            getattr(ops, "reshape_and_cache_" + fmt)(kv, kv, kc, kc, slots, 1.0, 1.0)
