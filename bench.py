@@ -17,10 +17,12 @@ launch a decode step) and the timed region is one replay, bracketed by a
 device synchronisation on both sides; --eager launches them one by one.
 
 Prints ONE JSON line: throughput (decode tokens/s = sequences per second of
-steps), the decode call's achieved KV bandwidth against the 8 TB/s HBM peak
-(HIP events on the stream the kernels run on, around a replay of K decode
-calls: partition kernel + merge kernel), and the float64 CPU oracle timed on
-a bounded sample of the same workload.
+steps); the decode call's achieved KV bandwidth against the 8 TB/s HBM peak
+(HIP events on the stream the kernels run on, around replays of a graph of
+200 decode calls whatever K is, so that the replay's own start-up is spread
+thin: partition kernel + merge kernel); the same figures for every seeded
+workload; and the float64 CPU oracle timed on bounded samples of the same
+workloads.
 """
 
 import argparse
@@ -34,6 +36,13 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attention tokens/s and achieved KV HBM GB/s (% of peak), 1 MI355X"
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_qwen7b_gqa_bf16_traffic.json")
 TRACE_FILE = os.path.join(HERE, "profiles", "decode_qwen7b_gqa_bf16_kernel_trace.json")
+# decode calls per graph replay behind the call-duration figures (any --steps):
+# a replay's start-up costs tens of microseconds, which a short replay would
+# spread over too few calls
+DECODE_CALLS = 200
+# the seeded workloads, timed one after another in the "workloads" figure
+WORKLOADS = ("tiny_fp32", "qwen7b_gqa_bf16", "llama7b_mha_fp16", "long_ctx_bf16",
+             "mixed_shared_bf16")
 
 
 def parse():
@@ -46,10 +55,14 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--kernel", choices=["auto", "generic", "mfma"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=12.0,
+    ap.add_argument("--cpu-budget-s", type=float, default=8.0,
                     help="wall-time budget of the oracle sample")
     ap.add_argument("--decode-only", action="store_true",
-                    help="time decode calls only (for counter runs)")
+                    help="time decode calls only, on cold pool replicas (for counter and "
+                         "trace runs): no hot-cache, single-call, other-operation or "
+                         "workload figures")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the figures of the other seeded workloads")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step from Python instead of replaying a graph")
     ap.add_argument("--unfused", action="store_true",
@@ -87,10 +100,8 @@ def load_traffic(config_name, per_launch_alg_bytes):
 def load_kernel_only(config_name, alg_bytes):
     """rocprofv3 kernel-only durations of the bench call's two kernels (the
     16-bit matrix-core decode kernel and its merge kernel) from the committed
-    kernel trace of bench.py, if it was taken on the current kernel sources;
-    else None.  The decode kernel's calls include the hot-cache and
-    single-call figures of the same run; the merge kernel's also those of the
-    FP8, INT8 and verify figures, which launch the same instantiation."""
+    kernel trace of `bench.py --decode-only` (every dispatch reads a cold pool
+    replica), if it was taken on the current kernel sources; else None."""
     if config_name != "qwen7b_gqa_bf16" or not os.path.exists(TRACE_FILE):
         return None
     with open(TRACE_FILE) as f:
@@ -109,40 +120,56 @@ def load_kernel_only(config_name, alg_bytes):
             "decode_kernel_frac": alg_bytes / (dec["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS}
 
 
-def cpu_baseline(inp, budget_s):
-    """The oracle (float64 gather + softmax) on the host, one thread: passes
-    over the batch's sequences, one sequence (all heads) at a time, until the
-    wall-time budget is spent (a bounded sample of the same workload)."""
+def _oracle_arrays(inp):
+    """The oracle's inputs: exactly the values the GPU reads, as float32
+    (upcast to float64 inside the oracle), tables as int64."""
     import numpy as np
+    return (inp.query.float().numpy(), inp.key_cache.float().numpy(),
+            inp.value_cache.float().numpy(), inp.block_tables.numpy().astype(np.int64),
+            inp.context_lens.numpy().astype(np.int64))
+
+
+def oracle_rate(arrays, scale, budget_s):
+    """The oracle (float64 gather + softmax) on one host thread: passes over
+    the batch's sequences, one sequence (all heads) at a time, until the
+    wall-time budget is spent (at least one sequence).  Returns (sequence
+    steps, history tokens, seconds)."""
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:
         threadpool_limits = None
     import oracle
 
-    q = inp.query.float().numpy()
-    kc = inp.key_cache.float().numpy()
-    vc = inp.value_cache.float().numpy()
-    bt = inp.block_tables.numpy().astype(np.int64)
-    cl = inp.context_lens.numpy().astype(np.int64)
+    q, kc, vc, bt, cl = arrays
     S, H = q.shape[0], q.shape[1]
-    # float64 K and V bytes of one history token (all KV heads): the gathered
-    # rows the oracle reduces
-    kv_row_bytes = 2 * kc.shape[1] * kc.shape[3] * 8
     done, tokens, elapsed = 0, 0, 0.0
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     try:
-        while elapsed < budget_s:
+        while elapsed < budget_s or done == 0:
             b = done % S
             t0 = time.perf_counter()
-            oracle.decode_contiguous(q, kc, vc, bt, cl, inp.cfg.scale,
-                                     pairs=[(b, h) for h in range(H)])
+            oracle.decode_contiguous(q, kc, vc, bt, cl, scale, pairs=[(b, h) for h in range(H)])
             elapsed += time.perf_counter() - t0
             done += 1
             tokens += int(cl[b])
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
+    return done, tokens, elapsed
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle on the host: one thread (the reported value), and every
+    core of the process's affinity set as a pool of worker processes over
+    sequences (all_cores), each for about budget_s of wall time on a bounded
+    sample of the workload."""
+    arrays = _oracle_arrays(inp)
+    q, kc = arrays[0], arrays[1]
+    S, H = q.shape[0], q.shape[1]
+    # float64 K and V bytes of one history token (all KV heads): the gathered
+    # rows the oracle reduces
+    kv_row_bytes = 2 * kc.shape[1] * kc.shape[3] * 8
+    done, tokens, elapsed = oracle_rate(arrays, inp.cfg.scale, budget_s)
     return {
         "value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
         "sample": "float64 oracle (contiguous gather + softmax), %d sequence-steps "
@@ -153,48 +180,172 @@ def cpu_baseline(inp, budget_s):
         "cpu_model": _cpu_model(),
         "host_cpus": os.cpu_count(),
         "affinity_cpus": len(os.sched_getaffinity(0)),
-        "all_cores": cpu_baseline_threads(inp, budget_s, (q, kc, vc, bt, cl)),
+        "all_cores": cpu_baseline_pool(arrays, inp.cfg.scale, budget_s),
     }
 
 
-def cpu_baseline_threads(inp, budget_s, arrays, max_workers=16):
-    """The same oracle on a thread pool over sequences, one BLAS thread per
-    worker, for about budget_s of wall time (NumPy releases the interpreter
-    lock inside its array operations; the speed-up measured is what this
-    host gives)."""
-    import concurrent.futures as cf
+_POOL = {}
+
+
+def _pool_init(d):
+    """Worker start-up: map the oracle's inputs read-only from files (shared
+    page cache, nothing pickled) and hold BLAS to one thread."""
+    import numpy as np
     try:
         from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
     except ImportError:
-        threadpool_limits = None
+        pass
+    for k in ("q", "kc", "vc", "bt", "cl"):
+        _POOL[k] = np.load(os.path.join(d, k + ".npy"), mmap_mode="r")
+    with open(os.path.join(d, "scale")) as f:
+        _POOL["scale"] = float(f.read())
+
+
+def _pool_seq(b):
+    """One sequence (all heads) through the oracle in a worker process."""
     import oracle
+    P = _POOL
+    H = P["q"].shape[1]
+    oracle.decode_contiguous(P["q"], P["kc"], P["vc"], P["bt"], P["cl"], P["scale"],
+                             pairs=[(b, h) for h in range(H)])
+    return int(P["cl"][b])
+
+
+def cpu_baseline_pool(arrays, scale, budget_s, max_workers=16):
+    """The oracle on a pool of worker processes (one per core of the affinity
+    set, at most max_workers, each with one BLAS thread), fed whole passes
+    over the batch's sequences for about budget_s of wall time.  Workers are
+    started fresh (spawn: no GPU state inherited) and map the inputs from
+    temporary files."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+    import numpy as np
 
     q, kc, vc, bt, cl = arrays
-    S, H = q.shape[0], q.shape[1]
+    S = q.shape[0]
     workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
-
-    def one(b):
-        oracle.decode_contiguous(q, kc, vc, bt, cl, inp.cfg.scale,
-                                 pairs=[(b, h) for h in range(H)])
-        return 1
-
-    done, tokens = 0, 0
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    d = tempfile.mkdtemp(prefix="pa_oracle_")
     try:
-        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        for k, v in zip(("q", "kc", "vc", "bt", "cl"), arrays):
+            np.save(os.path.join(d, k + ".npy"), v)
+        with open(os.path.join(d, "scale"), "w") as f:
+            f.write(repr(float(scale)))
+        with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn"),
+                                    initializer=_pool_init, initargs=(d,)) as ex:
+            list(ex.map(_pool_seq, [b % S for b in range(workers)]))     # workers up
+            done, tokens = 0, 0
             t0 = time.perf_counter()
             while time.perf_counter() - t0 < budget_s:
-                done += sum(ex.map(one, range(S)))               # one pass
-                tokens += int(cl.sum())
+                tokens += sum(ex.map(_pool_seq, range(S)))              # one pass
+                done += S
             elapsed = time.perf_counter() - t0
     finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
+        shutil.rmtree(d, ignore_errors=True)
     kv_row_bytes = 2 * kc.shape[1] * kc.shape[3] * 8
     return {"value": done / elapsed, "unit": "tokens/s", "cores": workers,
             "fp64_gbps": tokens * kv_row_bytes / elapsed / 1e9,
-            "sample": "%d sequence-steps (whole passes over the batch) on %d threads in %.1f s"
-                      % (done, workers, elapsed)}
+            "sample": "%d sequence-steps (whole passes over the batch) on %d worker processes "
+                      "in %.1f s" % (done, workers, elapsed)}
+
+
+def unique_kv_bytes(cfg, block_tables, context_lens):
+    """K+V bytes of the distinct (physical block, slot) token rows a decode
+    call reads: a block shared by several sequences' tables (the shared
+    prefixes of the mixed workload) counts once."""
+    import numpy as np
+    from paged_kv_decode_attention_amd.inputs import ELEM_BYTES
+    bt = np.asarray(block_tables, dtype=np.int64)
+    cl = np.asarray(context_lens, dtype=np.int64)
+    BS = cfg.block_size
+    rows = [bt[b, np.arange(int(cl[b])) // BS] * BS + np.arange(int(cl[b])) % BS
+            for b in range(bt.shape[0])]
+    n = np.unique(np.concatenate(rows)).size if rows else 0
+    return int(n) * cfg.num_kv_heads * cfg.head_dim * ELEM_BYTES[cfg.dtype] * 2
+
+
+def graph_call_us(capture, timed_replay, call, n_calls, reps=3):
+    """Mean, min and max duration (us) of one call over `reps` replays of a
+    graph of n_calls calls (an untimed replay first)."""
+    import numpy as np
+    import torch
+    for k in range(min(10, n_calls)):
+        call(k)
+    torch.cuda.synchronize()
+    g = capture(lambda: [call(k) for k in range(n_calls)])
+    g.replay()
+    us = np.array([timed_replay(g)[1] / n_calls * 1e6 for _ in range(reps)])
+    del g
+    return float(us.mean()), float(us.min()), float(us.max())
+
+
+def workload_rates(dev, capture, timed_replay, oracle_budget_s):
+    """Decode-call figures of every seeded workload (decode calls only, pool
+    replicas rotated so that at least 1.5 GB of K/V pass between two reads of
+    the same bytes), and the oracle on one host thread on a bounded sample
+    of each (none when oracle_budget_s is None)."""
+    import numpy as np
+    import torch
+    from paged_kv_decode_attention_amd import inputs as I
+    from paged_kv_decode_attention_amd import ops
+
+    res = {}
+    for name in WORKLOADS:
+        cfg = I.CONFIGS[name]
+        inp = I.generate(cfg)
+        lens = inp.context_lens.numpy()
+        alg = I.kv_bytes_read(cfg, lens)
+        q = inp.query.to(dev)
+        bt = inp.block_tables.to(dev)
+        cl = inp.context_lens.to(dev)
+        S, H, D = q.shape
+        N, H_kv, BS, _ = inp.key_cache.shape
+        W = bt.shape[1]
+        pool = 2 * inp.key_cache.numel() * inp.key_cache.element_size()
+        R = int(min(8, max(2, np.ceil(1.5e9 / pool))))
+        kcs = [inp.key_cache.to(dev) for _ in range(R)]
+        vcs = [inp.value_cache.to(dev) for _ in range(R)]
+        out = torch.empty_like(q)
+        max_ctx = W * BS
+        ws = torch.zeros(max(ops.decode_workspace_size(S, H, H_kv, D, BS, max_ctx, 0, q.dtype),
+                             256), dtype=torch.uint8, device=dev)
+
+        def call(k):
+            ops.paged_attention_decode(q, kcs[k % R], vcs[k % R], bt, cl, cfg.scale,
+                                       max_context_len=max_ctx, out=out, workspace=ws)
+        # about 20 ms of calls per replay (at about 6 TB/s)
+        n_calls = int(min(DECODE_CALLS, max(20, 2e7 // max(1, alg // 6000))))
+        mean, lo, hi = graph_call_us(capture, timed_replay, call, n_calls)
+        t = mean * 1e-6
+        row = {"call_us_mean": mean, "call_us_min": lo, "call_us_max": hi,
+               "calls_per_replay": n_calls, "pool_replicas": R,
+               "decode_tokens_per_s": S / t, "alg_bytes_per_call": alg,
+               "achieved_gbps": alg / t / 1e9, "frac": alg / t / 1e9 / HBM_PEAK_GBPS,
+               "kernel": "matrix-core, balanced" if ops.decode_kernel(
+                   D, BS, H // H_kv, q.dtype) == ops.KERNEL_MFMA else "vector-ALU, partitions",
+               "dtype": cfg.dtype}
+        if name == "tiny_fp32":
+            row["note"] = "launch-bound (133 KB of K/V): no roofline claim"
+        if name == "mixed_shared_bf16":
+            u = unique_kv_bytes(cfg, inp.block_tables.numpy(), lens)
+            row["unique_bytes_per_call"] = u
+            row["unique_gbps"] = u / t / 1e9
+            row["note"] = ("frac counts logical bytes (every sequence's history, shared "
+                           "prefix blocks once per sequence); unique_gbps counts each "
+                           "distinct token row once")
+        del kcs, vcs, q, bt, cl, out, ws
+        torch.cuda.empty_cache()
+        if oracle_budget_s is not None:
+            arrays = _oracle_arrays(inp)
+            done, tokens, el = oracle_rate(arrays, cfg.scale, oracle_budget_s)
+            row["oracle_1core"] = {"tokens_per_s": done / el, "sequence_steps": done,
+                                   "history_tokens": tokens, "seconds": el}
+            del arrays
+        res[name] = row
+        del inp
+    return res
 
 
 def q8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture,
@@ -237,9 +388,9 @@ def q8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capt
     for k in range(10):
         call(k)
     torch.cuda.synchronize()
-    g = capture(lambda: [call(k) for k in range(args.steps)])
+    g = capture(lambda: [call(k) for k in range(DECODE_CALLS)])
     g.replay()
-    us = np.array([timed_replay(g)[1] / args.steps * 1e6 for _ in range(3)])
+    us = np.array([timed_replay(g)[1] / DECODE_CALLS * 1e6 for _ in range(3)])
     t = float(us.mean()) * 1e-6
     alg8 = alg_bytes // 2
     del k8s, v8s
@@ -279,9 +430,9 @@ def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture
     for k in range(10):
         call(k)
     torch.cuda.synchronize()
-    g = capture(lambda: [call(k) for k in range(args.steps)])
+    g = capture(lambda: [call(k) for k in range(DECODE_CALLS)])
     g.replay()
-    us = np.array([timed_replay(g)[1] / args.steps * 1e6 for _ in range(3)])
+    us = np.array([timed_replay(g)[1] / DECODE_CALLS * 1e6 for _ in range(3)])
     del g
     t = float(us.mean()) * 1e-6
     G = H // H_kv
@@ -588,29 +739,35 @@ def main():
         dec_ms = np.array([s.elapsed_time(e) for s, e in events])
     else:
         g_step = capture(lambda: [step(k) for k in range(args.steps)])
-        g_dec = capture(lambda: [step(k, decode_only=True) for k in range(args.steps)])
         g_step.replay()          # untimed replay: first-launch costs out of the way
         wall, _ = timed_replay(g_step)
-        # decode call duration: K back-to-back decode calls, HIP events around them
-        dec_ms = np.array([timed_replay(g_dec)[1] / args.steps * 1e3 for _ in range(3)])
-    # hot-cache figure, labelled as such: every call reads the same pool
-    # replica, so whatever of it the 256 MB last-level cache keeps is reused
-    g_hot = capture(lambda: [step(k * R, decode_only=True) for k in range(args.steps)])
-    g_hot.replay()
-    hot_us = timed_replay(g_hot)[1] / args.steps * 1e6
-    del g_hot
-
-    # distribution of single decode calls: HIP events around each of 100
-    # calls launched one by one (launch gaps excluded, each call timed alone)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(100)]
-    for k in range(100):
-        step(k, ev[k], decode_only=True)
-    torch.cuda.synchronize()
-    one_us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+        del g_step
+        # decode call duration: DECODE_CALLS back-to-back decode calls, HIP
+        # events around each of 3 replays
+        g_dec = capture(lambda: [step(k, decode_only=True) for k in range(DECODE_CALLS)])
+        g_dec.replay()
+        dec_ms = np.array([timed_replay(g_dec)[1] / DECODE_CALLS * 1e3 for _ in range(3)])
+        del g_dec
+    hot_us = None
+    one_us = None
+    if not args.decode_only:
+        # hot-cache figure, labelled as such: every call reads the same pool
+        # replica, so whatever of it the 256 MB last-level cache keeps is reused
+        g_hot = capture(lambda: [step(k * R, decode_only=True) for k in range(DECODE_CALLS)])
+        g_hot.replay()
+        hot_us = timed_replay(g_hot)[1] / DECODE_CALLS * 1e6
+        del g_hot
+        # distribution of single decode calls: HIP events around each of 100
+        # calls launched one by one (launch gaps excluded, each call timed alone)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(100)]
+        for k in range(100):
+            step(k, ev[k], decode_only=True)
+        torch.cuda.synchronize()
+        one_us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
 
     # practical streaming-read ceiling of this GPU (hand-written kernel)
-    rd = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    rd = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
     sink = torch.empty(16 * 65536, dtype=torch.uint8, device=dev)
     ops.stream_read(rd, sink)
     torch.cuda.synchronize()
@@ -683,7 +840,9 @@ def main():
             "decode_us_mean": float(dec_ms.mean()) * 1e3,
             "decode_us_min": float(dec_ms.min()) * 1e3,
             "decode_us_max": float(dec_ms.max()) * 1e3,
-            "single_call_us_p10_p50_p90": [float(np.percentile(one_us, p)) for p in (10, 50, 90)],
+            "decode_calls_per_replay": DECODE_CALLS,
+            "single_call_us_p10_p50_p90": None if one_us is None else
+                [float(np.percentile(one_us, p)) for p in (10, 50, 90)],
             "hot_cache_decode_us": hot_us,
             # rocprofv3 kernel-only durations (committed trace of this
             # command, current sources only), beside the event timings
@@ -691,12 +850,18 @@ def main():
         },
         "decode_tokens_per_s": S / dec_s,
         "hbm_read_ceiling_gbps": ceiling_gbps,
+        "frac_of_read_ceiling": achieved / ceiling_gbps,
         "copy_blocks": copy,
         "fp8_kv": fp8_kv,
         "int8_kv": int8_kv,
         "verify": verify,
         "kernel_src_sha": kernel_source_hash(),
     }
+    if not args.decode_only and not args.no_workloads:
+        del kcs, vcs
+        torch.cuda.empty_cache()
+        result["workloads"] = workload_rates(dev, capture, timed_replay,
+                                             None if args.no_cpu_baseline else 1.5)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget_s)
     print(json.dumps(result), flush=True)

@@ -498,9 +498,12 @@ int pa_decode_kernel(int head_dim, int block_size, int gqa_group_size, pa_dtype 
 /*
  * Measurement helpers (not part of the decode path).
  *
- * pa_bench_stream_read -- read `bytes` (multiple of 16) from `src` with 16-byte
- *   coalesced loads and write one 16-byte value per workgroup to `sink`
- *   (at least 16 * 65536 bytes); gives the practical HBM read ceiling.
+ * pa_bench_stream_read -- read `bytes` (multiple of 16) from `src` once, one
+ *   workgroup per compute unit streaming a contiguous region with 16-byte
+ *   coalesced nontemporal loads, and write the XOR of the 16-byte words each
+ *   workgroup read to sink[workgroup] (sink: at least 16 * 65536 bytes; the
+ *   entries past the workgroup count are not written).  Gives the practical
+ *   HBM read ceiling.
  * pa_bench_copy -- copy `bytes` (multiple of 16) from src to dst; a kernel of
  *   known traffic, used to calibrate hardware byte counters.
  */
