@@ -34,8 +34,9 @@ import time
 HERE = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBPS = 8000.0
 METRIC = "decode attention tokens/s and achieved KV HBM GB/s (% of peak), 1 MI355X"
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_qwen7b_gqa_bf16_traffic.json")
-TRACE_FILE = os.path.join(HERE, "profiles", "decode_qwen7b_gqa_bf16_kernel_trace.json")
+# committed rocprofv3 summaries of `bench.py --config NAME --decode-only`
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "decode_%s_traffic.json")
+TRACE_FILE = os.path.join(HERE, "profiles", "decode_%s_kernel_trace.json")
 # decode calls per graph replay behind the call-duration figures (any --steps):
 # a replay's start-up costs tens of microseconds, which a short replay would
 # spread over too few calls
@@ -61,6 +62,8 @@ def parse():
                     help="time decode calls only, on cold pool replicas (for counter and "
                          "trace runs): no hot-cache, single-call, other-operation or "
                          "workload figures")
+    ap.add_argument("--decode-calls", type=int, default=DECODE_CALLS,
+                    help="decode calls per graph replay behind the call-duration figures")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the figures of the other seeded workloads")
     ap.add_argument("--eager", action="store_true",
@@ -88,9 +91,10 @@ def kernel_source_hash():
 def load_traffic(config_name, per_launch_alg_bytes):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel sources; else None."""
-    if config_name != "qwen7b_gqa_bf16" or not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILE % config_name
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
     if t.get("kernel_src_sha") != kernel_source_hash():
         return None
@@ -102,19 +106,23 @@ def load_kernel_only(config_name, alg_bytes):
     16-bit matrix-core decode kernel and its merge kernel) from the committed
     kernel trace of `bench.py --decode-only` (every dispatch reads a cold pool
     replica), if it was taken on the current kernel sources; else None."""
-    if config_name != "qwen7b_gqa_bf16" or not os.path.exists(TRACE_FILE):
+    path = TRACE_FILE % config_name
+    if not os.path.exists(path):
         return None
-    with open(TRACE_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
     if t.get("kernel_src_sha") != kernel_source_hash():
         return None
     ks = t.get("kernels", {})
-    dec = ks.get("decode_mfma_balanced<pa::BF16, 16, KvSame, 0, 128, 1>")
-    mrg = ks.get("merge_balanced<pa::BF16, 128, 16>")
+    # the run's decode and merge kernels: the most-called of each
+    most = lambda key: max(((k, v) for k, v in ks.items() if key in k),
+                           key=lambda kv: kv[1]["calls"], default=(None, None))[1]
+    dec = most("decode_")
+    mrg = most("merge_")
     if not dec or not mrg:
         return None
     pick = lambda k: {x: k[x] for x in ("calls", "avg_us", "median_us", "min_us", "max_us")}
-    return {"source": os.path.relpath(TRACE_FILE, HERE),
+    return {"source": os.path.relpath(path, HERE),
             "decode_kernel": pick(dec), "merge_kernel": pick(mrg),
             "decode_kernel_gbps": alg_bytes / (dec["median_us"] * 1e-6) / 1e9,
             "decode_kernel_frac": alg_bytes / (dec["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS}
@@ -388,9 +396,9 @@ def q8_decode_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capt
     for k in range(10):
         call(k)
     torch.cuda.synchronize()
-    g = capture(lambda: [call(k) for k in range(DECODE_CALLS)])
+    g = capture(lambda: [call(k) for k in range(args.decode_calls)])
     g.replay()
-    us = np.array([timed_replay(g)[1] / DECODE_CALLS * 1e6 for _ in range(3)])
+    us = np.array([timed_replay(g)[1] / args.decode_calls * 1e6 for _ in range(3)])
     t = float(us.mean()) * 1e-6
     alg8 = alg_bytes // 2
     del k8s, v8s
@@ -430,9 +438,9 @@ def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture
     for k in range(10):
         call(k)
     torch.cuda.synchronize()
-    g = capture(lambda: [call(k) for k in range(DECODE_CALLS)])
+    g = capture(lambda: [call(k) for k in range(args.decode_calls)])
     g.replay()
-    us = np.array([timed_replay(g)[1] / DECODE_CALLS * 1e6 for _ in range(3)])
+    us = np.array([timed_replay(g)[1] / args.decode_calls * 1e6 for _ in range(3)])
     del g
     t = float(us.mean()) * 1e-6
     G = H // H_kv
@@ -744,18 +752,18 @@ def main():
         del g_step
         # decode call duration: DECODE_CALLS back-to-back decode calls, HIP
         # events around each of 3 replays
-        g_dec = capture(lambda: [step(k, decode_only=True) for k in range(DECODE_CALLS)])
+        g_dec = capture(lambda: [step(k, decode_only=True) for k in range(args.decode_calls)])
         g_dec.replay()
-        dec_ms = np.array([timed_replay(g_dec)[1] / DECODE_CALLS * 1e3 for _ in range(3)])
+        dec_ms = np.array([timed_replay(g_dec)[1] / args.decode_calls * 1e3 for _ in range(3)])
         del g_dec
     hot_us = None
     one_us = None
     if not args.decode_only:
         # hot-cache figure, labelled as such: every call reads the same pool
         # replica, so whatever of it the 256 MB last-level cache keeps is reused
-        g_hot = capture(lambda: [step(k * R, decode_only=True) for k in range(DECODE_CALLS)])
+        g_hot = capture(lambda: [step(k * R, decode_only=True) for k in range(args.decode_calls)])
         g_hot.replay()
-        hot_us = timed_replay(g_hot)[1] / DECODE_CALLS * 1e6
+        hot_us = timed_replay(g_hot)[1] / args.decode_calls * 1e6
         del g_hot
         # distribution of single decode calls: HIP events around each of 100
         # calls launched one by one (launch gaps excluded, each call timed alone)
@@ -840,7 +848,7 @@ def main():
             "decode_us_mean": float(dec_ms.mean()) * 1e3,
             "decode_us_min": float(dec_ms.min()) * 1e3,
             "decode_us_max": float(dec_ms.max()) * 1e3,
-            "decode_calls_per_replay": DECODE_CALLS,
+            "decode_calls_per_replay": args.decode_calls,
             "single_call_us_p10_p50_p90": None if one_us is None else
                 [float(np.percentile(one_us, p)) for p in (10, 50, 90)],
             "hot_cache_decode_us": hot_us,

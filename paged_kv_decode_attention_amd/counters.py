@@ -174,6 +174,32 @@ def trace_main(a):
     return 0
 
 
+def write_traffic_md(rec, path, title):
+    """Markdown summary of a traffic record: commands, calibration, per-kernel
+    readings and the bytes per call against the algorithmic bytes."""
+    lines = ["# " + title, "",
+             "Commands (repository root, one MI355X; each counter in a run of its own):", ""]
+    lines += ["    " + c for c in rec["commands"]]
+    lines += ["",
+              "Calibration: a plain %d-byte copy (reads and writes that many bytes) gives "
+              "%.1f bytes per FETCH_SIZE KiB and %.1f bytes per WRITE_SIZE KiB." % (
+                  rec["copy_calibration_bytes"], rec["fetch_factor_bytes_per_kib"],
+                  rec["write_factor_bytes_per_kib"]), "",
+              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | "
+              "written bytes |", "|---|---|---|---|---|---|"]
+    for k, v in rec["kernels"].items():
+        lines.append("| %s | %d | %.1f | %.1f | %.0f | %.0f |" % (
+            k, v["dispatches"], v["fetch_kib"], v["write_kib"], v["fetch_bytes"],
+            v["write_bytes"]))
+    lines += ["", "Kernels counted: those whose name holds %s.  Per call: %.1f MB moved against "
+              "%.1f MB of algorithmic K/V bytes (ratio %.3f).  Decode sources: kernel_src_sha "
+              "%s." % (" or ".join(repr(k) for k in rec["kernel_filter"]),
+                       rec["hbm_bytes_per_launch"] / 1e6, rec["alg_bytes_per_launch"] / 1e6,
+                       rec["traffic_over_alg"], rec["kernel_src_sha"])]
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def main(argv=None):
     top = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = top.add_subparsers(dest="cmd", required=True)
@@ -198,7 +224,15 @@ def main(argv=None):
     ap.add_argument("--copy-write", required=True)
     ap.add_argument("--copy-bytes", type=int, required=True)
     ap.add_argument("--config", default="qwen7b_gqa_bf16")
+    ap.add_argument("--kernels", action="append", default=[],
+                    help="count only kernels whose name holds one of these (repeatable; "
+                         "default: every decode and merge kernel)")
+    ap.add_argument("--alg-factor", type=float, default=1.0,
+                    help="algorithmic bytes relative to the config's 16-bit K/V "
+                         "(0.5 for 8-bit caches)")
     ap.add_argument("--out", required=True)
+    ap.add_argument("--md", default=None, help="also write this markdown summary")
+    ap.add_argument("--title", default=None)
     ap.add_argument("--command", action="append", default=[],
                     help="a command the readings came from (repeatable)")
     a = top.parse_args(argv)
@@ -212,8 +246,9 @@ def main(argv=None):
 
     f_fetch = calibration(a.copy_fetch, "FETCH_SIZE", a.copy_bytes)
     f_write = calibration(a.copy_write, "WRITE_SIZE", a.copy_bytes)
-    fetch = per_dispatch(read_counter(a.fetch, "FETCH_SIZE"), DECODE_KERNELS)
-    write = per_dispatch(read_counter(a.write, "WRITE_SIZE"), DECODE_KERNELS)
+    keys = tuple(a.kernels) or DECODE_KERNELS
+    fetch = per_dispatch(read_counter(a.fetch, "FETCH_SIZE"), keys)
+    write = per_dispatch(read_counter(a.write, "WRITE_SIZE"), keys)
     if not fetch or set(fetch) != set(write):
         raise ValueError("decode kernels differ between runs: %s vs %s"
                          % (sorted(fetch), sorted(write)))
@@ -226,9 +261,10 @@ def main(argv=None):
                       "write_kib": write[k][0], "fetch_bytes": fb, "write_bytes": wb}
         total += fb + wb
     cfg = I.CONFIGS[a.config]
-    alg = I.kv_bytes_read(cfg, I.draw_context_lens(cfg))
+    alg = int(I.kv_bytes_read(cfg, I.draw_context_lens(cfg)) * a.alg_factor)
     rec = {
         "config": a.config,
+        "kernel_filter": list(keys),
         "kernel_src_sha": decode_source_hash(),
         "hbm_bytes_per_launch": total,
         "alg_bytes_per_launch": alg,
@@ -242,6 +278,8 @@ def main(argv=None):
     with open(a.out, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
+    if a.md:
+        write_traffic_md(rec, a.md, a.title or "HBM traffic of the decode call, " + a.config)
     print(json.dumps({"hbm_bytes_per_launch": total, "alg": alg, "ratio": total / alg,
                       "fetch_factor": f_fetch, "write_factor": f_write}))
     return 0
