@@ -156,6 +156,39 @@ int pa_paged_attention_decode(void* out, const void* query,
                               size_t workspace_bytes, void* hip_stream);
 
 /*
+ * pa_paged_attention_decode_noalloc -- pa_paged_attention_decode with no
+ * workspace argument and no device allocation, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.
+ *
+ * Same arguments, results (bit for bit), supported shapes and errors as
+ * pa_paged_attention_decode, minus workspace / workspace_bytes.  The
+ * workspace is a device array of pa_noalloc_scratch_bytes() bytes (40 MiB)
+ * that the library holds, one per GPU, from the first call made with that
+ * GPU current until the process ends.  Nothing in it needs to start at zero:
+ * every call writes what it reads.  Sizes whose
+ * pa_decode_workspace_size() exceeds that return PA_ERR_WORKSPACE (use
+ * pa_paged_attention_decode with a workspace of your own); the balanced
+ * schedule of the matrix-core kernel needs at most about 34 MB, so every call
+ * on it fits.  All calls on one GPU share its array: calls that overlap in
+ * time on one GPU (different streams, or several host threads) race and
+ * give wrong results -- serialise them.  PA_ERR_HIP if the array's device
+ * address cannot be found (no current device).
+ */
+int pa_paged_attention_decode_noalloc(void* out, const void* query,
+                                      const void* key_cache, const void* value_cache,
+                                      const int32_t* block_tables,
+                                      const int32_t* context_lens,
+                                      int num_seqs, int num_heads, int num_kv_heads,
+                                      int gqa_group_size, int head_dim, int block_size,
+                                      int num_blocks, int max_blocks_per_seq,
+                                      int max_context_len, float scale, pa_dtype dtype,
+                                      int partition_size, void* hip_stream);
+
+/* Bytes of the per-GPU device array pa_paged_attention_decode_noalloc works in. */
+size_t pa_noalloc_scratch_bytes(void);
+
+/*
  * pa_decode_append -- one decode step: append each sequence's newest token to
  * its paged history, then attend over the whole history (the step of
  * [MiniPaged-Qwen] §8.1 -- append_token gives the new token's slot, the

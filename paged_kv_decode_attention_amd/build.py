@@ -33,6 +33,7 @@ SOURCES = [
     "pa_cache.hip",
     "pa_bench.hip",
     "pa_pool.cpp",
+    "pa_noalloc.hip",
 ]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

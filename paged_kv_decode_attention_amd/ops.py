@@ -36,6 +36,11 @@ _SIGNATURES = {
         _I, [_VP, _VP, _VP, _VP, _VP, _VP,
              _I, _I, _I, _I, _I, _I, _I, _I, _I,
              ctypes.c_float, _I, _I, _VP, ctypes.c_size_t, _VP]),
+    "pa_paged_attention_decode_noalloc": (
+        _I, [_VP, _VP, _VP, _VP, _VP, _VP,
+             _I, _I, _I, _I, _I, _I, _I, _I, _I,
+             ctypes.c_float, _I, _I, _VP]),
+    "pa_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "pa_decode_append": (
         _I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
              _I, _I, _I, _I, _I, _I, _I, _I, _I,
@@ -179,7 +184,8 @@ _CODES = {"fp8": (FP8_CACHE_DTYPES, "FP8 caches must be uint8 or float8_e4m3fn t
 
 
 def _decode_args(query, key_cache, value_cache, block_tables, context_lens, scale,
-                 max_context_len, partition_size, out, workspace, kv8=None):
+                 max_context_len, partition_size, out, workspace, kv8=None,
+                 workspace_from_library=False):
     for t, n in ((query, "query"), (key_cache, "key_cache"), (value_cache, "value_cache"),
                  (block_tables, "block_tables"), (context_lens, "context_lens")):
         _gpu(t, n)
@@ -212,8 +218,8 @@ def _decode_args(query, key_cache, value_cache, block_tables, context_lens, scal
         _gpu(out, "out")
         if out.shape != query.shape or out.dtype != query.dtype:
             raise ValueError("out must match query in shape and dtype")
-    ws_bytes = decode_workspace_size(S, H, H_kv, D, BS, max_context_len, partition_size,
-                                     query.dtype)
+    ws_bytes = 0 if workspace_from_library else decode_workspace_size(
+        S, H, H_kv, D, BS, max_context_len, partition_size, query.dtype)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=query.device)
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
@@ -246,6 +252,23 @@ def paged_attention_decode(query, key_cache, value_cache, block_tables, context_
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
         _ptr(context_lens), *sizes, *tail)
     _check(status, "paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_noalloc(query, key_cache, value_cache, block_tables, context_lens,
+                                   scale=None, *, max_context_len=None, partition_size=0,
+                                   out=None):
+    """paged_attention_decode with the library's own per-GPU device array as
+    the workspace (pa_paged_attention_decode_noalloc): no allocation by the
+    library; `out` given, nothing is allocated at all.  Calls that overlap in
+    time on one GPU must not be made (they share the array)."""
+    out, sizes, tail = _decode_args(query, key_cache, value_cache, block_tables, context_lens,
+                                    scale, max_context_len, partition_size, out, None,
+                                    workspace_from_library=True)
+    scale_, dt, P, _, _, stream = tail
+    _check(load_library().pa_paged_attention_decode_noalloc(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), *sizes, scale_, dt, P, stream), "paged_attention_decode_noalloc")
     return out
 
 

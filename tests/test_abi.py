@@ -86,6 +86,30 @@ def test_decode_rejects_on_host(lib, kw, status):
     assert lib.pa_last_error() != b""
 
 
+def test_noalloc_decode_rejects_on_host(lib):
+    """The no-allocation decode: its device array's size, and sizes that are
+    invalid or need more workspace than the array holds are refused before
+    any HIP call (the array's address is looked up only for a call that runs)."""
+    vp = ctypes.c_void_p
+    assert lib.pa_noalloc_scratch_bytes() == 40 << 20
+
+    def call(**kw):
+        a = dict(S=2, H=28, H_kv=4, G=7, D=128, BS=16, N=100, W=8, max_ctx=128, P=0,
+                 dtype=ops.PA_BF16)
+        a.update(kw)
+        return lib.pa_paged_attention_decode_noalloc(
+            vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), a["S"], a["H"],
+            a["H_kv"], a["G"], a["D"], a["BS"], a["N"], a["W"], a["max_ctx"], 0.088,
+            a["dtype"], a["P"], vp(0))
+    assert call(H=30) == INVALID                       # H % H_kv != 0
+    assert call(D=96) == INVALID                       # no workspace size for this shape
+    # fixed partitions of 32 tokens over 2048 sequences x 64 heads x 4096 tokens:
+    # 2048 * 64 * 128 * 129 * 4 bytes of partial states, beyond 40 MiB
+    assert call(S=2048, H=64, H_kv=8, G=8, W=256, max_ctx=4096, P=32) == WORKSPACE
+    assert b"workspace" in lib.pa_last_error()
+    assert lib.pa_decode_workspace_size(2048, 64, 8, 128, 16, 4096, 32, ops.PA_BF16) > 40 << 20
+
+
 def test_decode_empty_batch_is_noop(lib):
     assert _decode(lib, S=0, out=0, query=0) == OK
 
