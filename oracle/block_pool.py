@@ -2,40 +2,51 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-What is modelled ([vLLM-paging] "Copy-on-write 是共享的正确性边界" and its
-"最小分页与 COW 模拟" simulation; [MiniPaged-Qwen] §9 "差异 3" and §10.1
-name the same features -- shared prefixes, branch sharing, reference
-counting, copy-on-write):
+Rules, as the pages state them in prose ([vLLM-paging] "Copy-on-write 是共享的
+正确性边界"; [MiniPaged-Qwen] §9 "差异 3" and §10.1 name the same features --
+shared prefixes, branch sharing, reference counting, copy-on-write):
 
-* a pool of physical blocks with a free list; a block is taken from the end
-  of the free list and starts with reference count 1;
-* a sequence is a block table (a list of physical blocks) whose blocks hold
-  its tokens in order, block_size per block, the last one possibly partial;
-* forking a sequence gives a second table naming the same blocks, and every
-  block named gains one reference;
-* appending a token: if the table is empty or its last block is full, a
-  fresh block is taken and the token is its first; if the last block is
-  partial but shared (more than one reference), the sequence may not write
-  into it -- it drops its reference, takes a fresh block holding a copy of
-  the shared block's tokens, and writes the token there; otherwise the token
-  goes into the last block in place;
-* releasing a sequence drops one reference of each of its blocks; a block
-  with no reference left returns to the free list.
+* a sequence owns a block table; token p of its history lives in block
+  table[p // block_size] at offset p % block_size ([MiniPaged-Qwen] §6.2);
+* a block's reference count is the number of live tables that name it, and
+  a block no table names is free;
+* forking a sequence gives the new sequence the same history and a table
+  naming the same blocks (the blocks gain a reference each);
+* a sequence may write only into a block no other table names: appending
+  token p at offset 0 needs a fresh block; at a non-zero offset the block
+  already exists, and if another table names it too, the sequence first
+  takes a fresh block holding a copy of the shared one (the copy the device
+  must make) and writes there;
+* releasing a sequence drops its table.
 
-Each token's slot is block * block_size + position in the block, the linear
-slot the cache write takes ([MiniPaged-Qwen] §8.1).  Token values are
-tracked per block, so ``read`` returns exactly what the blocks hold.
+The model is declarative: the state is each live sequence's token list and
+table, plus the order of the free blocks.  Reference counts and block
+contents are derived from them whenever asked (a block holds, slot by slot,
+the tokens of any sequence naming it; sequences sharing a block agree on
+it).  Fresh blocks come from the end of the free list and freed blocks go to
+its end, in table order -- the allocation order of the pages' simulation,
+under which its printed example names the blocks it does.
 
-Parity status: pinned by the worked example of the simulation (golden file
-tests/golden/block_pool_cow.json) and by invariants under random operation
-sequences (tests/test_block_pool_oracle.py).
+A batch of appends is taken in list order, each seeing the tables as the
+earlier ones left them (of sequences sharing a partial block, every writer
+but the last copies it); a batch that cannot get all its fresh blocks
+changes nothing.
+
+Each token's slot is block * block_size + offset, the linear slot the cache
+write takes ([MiniPaged-Qwen] §8.1).
+
+Parity status: pinned by the worked example of the page's simulation
+(tests/golden/block_pool_cow.json) and by invariants under random operation
+sequences, among them a simulated device cache that applies every copy and
+slot write and must read back every sequence's history
+(tests/test_block_pool_oracle.py).
 """
 
 import numpy as np
 
 
 class PoolExhausted(Exception):
-    """No free block is left (the simulation raises MemoryError)."""
+    """No free block is left for an append (the simulation raises MemoryError)."""
 
 
 class BlockPool:
@@ -44,62 +55,84 @@ class BlockPool:
             raise ValueError("pool sizes must be positive")
         self.num_blocks = num_blocks
         self.block_size = block_size
-        self.free = list(range(num_blocks))
-        self.tokens = {}       # block -> list of token values it holds
-        self.refs = {}         # block -> number of tables naming it
+        self.free = list(range(num_blocks))   # fresh blocks come from the end
+        self.history = {}                     # sequence id -> list of tokens
+        self.tables = {}                      # sequence id -> list of blocks
+        self._next = 0
 
-    # -- blocks --------------------------------------------------------
-    def _take(self, initial=()):
-        if not self.free:
-            raise PoolExhausted("KV pool exhausted")
-        b = self.free.pop()
-        self.tokens[b] = list(initial)
-        self.refs[b] = 1
-        return b
+    # -- derived quantities ---------------------------------------------
+    def refcount(self, block):
+        """Number of live tables naming the block."""
+        return sum(t.count(block) for t in self.tables.values())
 
-    def _drop(self, b):
-        self.refs[b] -= 1
-        if self.refs[b] == 0:
-            del self.refs[b]
-            del self.tokens[b]
-            self.free.append(b)
+    def contents(self, block):
+        """Tokens the block holds, read from a sequence that names it."""
+        for s, t in self.tables.items():
+            if block in t:
+                j = t.index(block)
+                return self.history[s][j * self.block_size:(j + 1) * self.block_size]
+        return []
 
-    # -- sequences -------------------------------------------------------
-    def fork(self, table):
-        for b in table:
-            self.refs[b] += 1
-        return list(table)
+    def read(self, seq):
+        return list(self.history[seq])
 
-    def append(self, table, token):
-        """Returns (new table, slot of the token, copy) with copy = (src,
-        dst) when a shared partial block was copied, else None."""
-        table = list(table)
-        copy = None
-        if not table or len(self.tokens[table[-1]]) == self.block_size:
-            table.append(self._take())
-        elif self.refs[table[-1]] > 1:
-            src = table[-1]
-            dst = self._take(self.tokens[src])
-            self.refs[src] -= 1            # still held by another table
-            table[-1] = dst
-            copy = (src, dst)
-        last = table[-1]
-        slot = last * self.block_size + len(self.tokens[last])
-        self.tokens[last].append(token)
-        return table, slot, copy
+    def length(self, seq):
+        return len(self.history[seq])
 
-    def release(self, table):
-        for b in table:
-            self._drop(b)
+    def table(self, seq):
+        return list(self.tables[seq])
 
-    def read(self, table):
-        out = []
-        for b in table:
-            out.extend(self.tokens[b])
-        return out
+    # -- operations -----------------------------------------------------
+    def add_sequence(self):
+        s = self._next
+        self._next += 1
+        self.history[s] = []
+        self.tables[s] = []
+        return s
 
-    def length(self, table):
-        return sum(len(self.tokens[b]) for b in table)
+    def fork(self, seq):
+        s = self.add_sequence()
+        self.history[s] = list(self.history[seq])
+        self.tables[s] = list(self.tables[seq])
+        return s
+
+    def append(self, seqs, tokens):
+        """Append tokens[i] to sequence seqs[i], in list order.  Returns
+        (slots, copies): the slot of each token, and the (src, dst) block
+        copies to make first, in order.  Raises PoolExhausted, changing
+        nothing, when the fresh blocks do not suffice."""
+        if len(set(seqs)) != len(seqs):
+            raise ValueError("a sequence is listed twice")
+        tables = {s: list(t) for s, t in self.tables.items()}
+        free = list(self.free)
+        slots, copies = [], []
+        for s, tok in zip(seqs, tokens):
+            p = len(self.history[s])
+            j, off = divmod(p, self.block_size)
+            t = tables[s]
+            if off == 0:
+                if not free:
+                    raise PoolExhausted("KV pool exhausted")
+                t.append(free.pop())
+            elif sum(u.count(t[j]) for u in tables.values()) > 1:
+                if not free:
+                    raise PoolExhausted("KV pool exhausted")
+                fresh = free.pop()
+                copies.append((t[j], fresh))
+                t[j] = fresh
+            slots.append(t[j] * self.block_size + off)
+        # every append fits: commit
+        self.tables, self.free = tables, free
+        for s, tok in zip(seqs, tokens):
+            self.history[s].append(tok)
+        return slots, copies
+
+    def release(self, seq):
+        t = self.tables.pop(seq)
+        del self.history[seq]
+        for b in t:
+            if self.refcount(b) == 0:
+                self.free.append(b)
 
 
 def copy_blocks(key_cache, value_cache, pairs):

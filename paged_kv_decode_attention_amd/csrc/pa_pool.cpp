@@ -10,6 +10,10 @@
 
 #include "pa_internal.h"
 
+// Token p of a sequence sits in block table[p / block_size] at offset
+// p % block_size, so a sequence of length L names ceil(L / block_size) blocks
+// and its last block holds L - (blocks - 1) * block_size tokens: the fill of
+// a block follows from the lengths and is not stored.
 struct pa_block_pool {
     struct Sequence {
         std::vector<int32_t> table;
@@ -19,26 +23,23 @@ struct pa_block_pool {
     int num_blocks = 0;
     int block_size = 0;
     std::vector<int32_t> free_list;   // taken from the back
-    std::vector<int32_t> refs;        // references per block, 0 = free
-    std::vector<int32_t> fill;        // tokens each held block contains
+    std::vector<int32_t> refs;        // tables naming each block, 0 = free
     std::vector<Sequence> seqs;
 
     int32_t take() {
         const int32_t b = free_list.back();
         free_list.pop_back();
         refs[b] = 1;
-        fill[b] = 0;
         return b;
     }
     void drop(int32_t b) {
-        if (--refs[b] == 0) {
-            fill[b] = 0;
-            free_list.push_back(b);
-        }
+        if (--refs[b] == 0) free_list.push_back(b);
     }
     bool valid(int seq) const {
         return seq >= 0 && seq < (int)seqs.size() && seqs[seq].live;
     }
+    // Offset the sequence's next token takes in its block; 0 opens a block.
+    int next_offset(int seq) const { return (int)(seqs[seq].length % block_size); }
 };
 
 namespace {
@@ -79,7 +80,6 @@ pa_block_pool* pa_pool_create(int num_blocks, int block_size) {
         p->free_list.resize(num_blocks);
         for (int b = 0; b < num_blocks; ++b) p->free_list[b] = b;
         p->refs.assign(num_blocks, 0);
-        p->fill.assign(num_blocks, 0);
     } catch (const std::bad_alloc&) {
         delete p;
         pa::report_error(PA_ERR_INVALID_ARG, "out of host memory");
@@ -123,56 +123,63 @@ int pa_pool_append(pa_block_pool* pool, const int* seqs, int n, int64_t* slots,
     if (n == 0) return PA_OK;
     const int BS = pool->block_size;
 
-    // Validate ids and count the blocks the appends take, applying the same
-    // rules to a scratch copy of the reference counts they change (a shared
-    // tail loses the reference of each sequence that copies it).  Tables that
-    // grow get their room here, so that nothing below can fail half-way:
-    // the batch is applied whole or not at all.
-    int64_t need = 0;
+    // Plan.  A token at offset 0 opens a fresh block.  A token at a later
+    // offset goes into the sequence's last block, which it may write only
+    // if no other table names it.  Taken in list order, the k-th listed
+    // writer of a partial block that h tables name copies it while the
+    // earlier writers' copies still leave other holders, i.e. unless
+    // k == h: the block is written in place only by the last of its writers,
+    // and only when every holder is listed.  So writers[b] (how many listed
+    // sequences end in partial block b) settles every copy up front, and the
+    // fresh blocks the batch takes are counted before anything changes: the
+    // batch is applied whole or not at all.  Tables that open a block get
+    // their room here, so that nothing below can fail.
+    std::unordered_map<int32_t, int32_t> writers;
+    int64_t fresh = 0;
     try {
         std::unordered_map<int, int> seen;
-        std::unordered_map<int32_t, int32_t> tail_refs;
         for (int i = 0; i < n; ++i) {
             const int s = seqs[i];
             if (!pool->valid(s)) return invalid("unknown sequence %lld", s);
             if (!seen.emplace(s, i).second) return invalid("sequence %lld listed twice", s);
             std::vector<int32_t>& t = pool->seqs[s].table;
-            if (t.empty() || pool->fill[t.back()] == BS) {
+            if (pool->next_offset(s) == 0) {
                 t.reserve(t.size() + 1);
-                ++need;
-                continue;
-            }
-            auto it = tail_refs.find(t.back());
-            int32_t& r = it != tail_refs.end()
-                             ? it->second
-                             : tail_refs.emplace(t.back(), pool->refs[t.back()]).first->second;
-            if (r > 1) {
-                --r;
-                ++need;
+                ++fresh;
+            } else {
+                ++writers[t.back()];
             }
         }
     } catch (const std::bad_alloc&) {
         return pa::report_error(PA_ERR_INVALID_ARG, "out of host memory");
     }
-    if (need > (int64_t)pool->free_list.size())
+    for (const auto& w : writers)
+        fresh += w.second == pool->refs[w.first] ? w.second - 1 : w.second;
+    if (fresh > (int64_t)pool->free_list.size())
         return pa::report_error(PA_ERR_POOL_EXHAUSTED, "KV pool exhausted");
+
+    // Apply, in list order (the order fresh blocks leave the free list).
     for (int i = 0; i < n; ++i) {
-        pa_block_pool::Sequence& q = pool->seqs[seqs[i]];
-        if (q.table.empty() || pool->fill[q.table.back()] == BS) {
+        const int s = seqs[i];
+        pa_block_pool::Sequence& q = pool->seqs[s];
+        const int off = pool->next_offset(s);
+        if (off == 0) {
             q.table.push_back(pool->take());      // capacity reserved above
-        } else if (pool->refs[q.table.back()] > 1) {
-            const int32_t src = q.table.back();
-            const int32_t dst = pool->take();
-            pool->fill[dst] = pool->fill[src];
-            --pool->refs[src];        // other sequences still hold it
-            q.table.back() = dst;
-            copy_pairs[2 * *num_copies] = src;
-            copy_pairs[2 * *num_copies + 1] = dst;
-            ++*num_copies;
+        } else {
+            const int32_t held = q.table.back();
+            int32_t& left = writers.find(held)->second;   // counted above
+            const bool in_place = left == 1 && pool->refs[held] == 1;
+            --left;
+            if (!in_place) {
+                const int32_t dst = pool->take();
+                --pool->refs[held];               // other tables still name it
+                q.table.back() = dst;
+                copy_pairs[2 * *num_copies] = held;
+                copy_pairs[2 * *num_copies + 1] = dst;
+                ++*num_copies;
+            }
         }
-        const int32_t last = q.table.back();
-        slots[i] = (int64_t)last * BS + pool->fill[last];
-        ++pool->fill[last];
+        slots[i] = (int64_t)q.table.back() * BS + off;
         ++q.length;
     }
     return PA_OK;

@@ -32,12 +32,12 @@ def test_printed_cow_example_through_the_library():
     assert slots.tolist() == [t_b[-1] * g["block_size"] + 1]
 
 
-def compare(lib_pool, ref, tables, ids):
-    for k, t in tables.items():
-        assert list(lib_pool.table(ids[k])) == t
-        assert lib_pool.length(ids[k]) == ref.length(t)
+def compare(lib_pool, ref, ids):
+    for r, l in ids.items():
+        assert list(lib_pool.table(l)) == ref.table(r)
+        assert lib_pool.length(l) == ref.length(r)
     for b in range(ref.num_blocks):
-        assert lib_pool.refcount(b) == ref.refs.get(b, 0)
+        assert lib_pool.refcount(b) == ref.refcount(b)
     assert lib_pool.free_blocks() == len(ref.free)
 
 
@@ -48,55 +48,37 @@ def test_random_operations_match_the_oracle(seed):
     nb = int(rng.integers(4, 80))
     ref = oracle.BlockPool(nb, bs)
     lib_pool = ops.BlockPool(nb, bs)
-    tables, ids = {}, {}          # key -> oracle table, key -> library id
-    key, tok = 0, 0
+    ids = {}                      # oracle sequence id -> library sequence id
+    tok = 0
     for step in range(200):
         op = rng.choice(["new", "append", "append", "fork", "release"])
-        if op == "new" or not tables:
-            tables[key], ids[key] = [], lib_pool.add_sequence()
-            key += 1
+        if op == "new" or not ids:
+            ids[ref.add_sequence()] = lib_pool.add_sequence()
         elif op == "append":
-            keys = list(tables)
-            batch = list(rng.choice(keys, size=int(rng.integers(1, len(keys) + 1)),
-                                    replace=False))
-            # the oracle, one append after another in list order
-            trial = oracle.BlockPool(nb, bs)
-            trial.free, trial.tokens, trial.refs = (list(ref.free),
-                                                    {b: list(v) for b, v in ref.tokens.items()},
-                                                    dict(ref.refs))
-            want_slots, want_pairs, new_tables = [], [], {}
+            live = list(ids)
+            batch = [int(r) for r in rng.choice(live, size=int(rng.integers(1, len(live) + 1)),
+                                                replace=False)]
             try:
-                for k in batch:
-                    t, slot, copy = trial.append(new_tables.get(k, tables[k]), tok + len(want_slots))
-                    new_tables[k] = t
-                    want_slots.append(slot)
-                    if copy is not None:
-                        want_pairs.append(list(copy))
-                exhausted = False
+                want_slots, want_pairs = ref.append(batch, list(range(tok, tok + len(batch))))
             except oracle.PoolExhausted:
-                exhausted = True
-            if exhausted:
                 with pytest.raises(RuntimeError, match="exhausted"):
-                    lib_pool.append([ids[k] for k in batch])
+                    lib_pool.append([ids[r] for r in batch])
             else:
-                slots, pairs = lib_pool.append([ids[k] for k in batch])
+                slots, pairs = lib_pool.append([ids[r] for r in batch])
                 assert slots.tolist() == want_slots
-                assert pairs.tolist() == want_pairs
-                ref = trial
-                tables.update(new_tables)
+                assert pairs.tolist() == [list(p) for p in want_pairs]
                 tok += len(batch)
         elif op == "fork":
-            k = int(rng.choice(list(tables)))
-            tables[key], ids[key] = ref.fork(tables[k]), lib_pool.fork(ids[k])
-            key += 1
+            r = int(rng.choice(list(ids)))
+            ids[ref.fork(r)] = lib_pool.fork(ids[r])
         else:
-            k = int(rng.choice(list(tables)))
-            ref.release(tables.pop(k))
-            lib_pool.release(ids.pop(k))
-        compare(lib_pool, ref, tables, ids)
-    for k in list(tables):
-        lib_pool.release(ids.pop(k))
-        ref.release(tables.pop(k))
+            r = int(rng.choice(list(ids)))
+            ref.release(r)
+            lib_pool.release(ids.pop(r))
+        compare(lib_pool, ref, ids)
+    for r in list(ids):
+        lib_pool.release(ids.pop(r))
+        ref.release(r)
     assert lib_pool.free_blocks() == nb
 
 

@@ -1,78 +1,59 @@
 """Plant plausible mistakes in the block-pool oracle (on the CPU) and check
-that the pins catch each one."""
+that the pins catch each one.  Each mutant is the oracle's source with one
+edit, compiled into a module of its own."""
+
+import inspect
+import types
 
 import pytest
 
 import test_block_pool_oracle as pins
 from oracle import block_pool as bp
 
-
-class NoCopyOnWrite(bp.BlockPool):
-    """Writes into a shared partial block instead of copying it."""
-    def append(self, table, token):
-        table = list(table)
-        if not table or len(self.tokens[table[-1]]) == self.block_size:
-            table.append(self._take())
-        last = table[-1]
-        slot = last * self.block_size + len(self.tokens[last])
-        self.tokens[last].append(token)
-        return table, slot, None
-
-
-class CopyWithoutData(bp.BlockPool):
-    """Takes a fresh block on copy-on-write but does not copy the tokens."""
-    def _take(self, initial=()):
-        return super()._take(())
-
-
-class CopyKeepsReference(bp.BlockPool):
-    """Does not drop the branch's reference to the shared block."""
-    def append(self, table, token):
-        shared = bool(table) and len(self.tokens[table[-1]]) < self.block_size and \
-            self.refs[table[-1]] > 1
-        src = table[-1] if shared else None
-        out = super().append(table, token)
-        if shared:
-            self.refs[src] += 1
-        return out
-
-
-class ForkWithoutReferences(bp.BlockPool):
-    def fork(self, table):
-        return list(table)
+MUTANTS = {
+    # writes into a shared partial block instead of copying it
+    "no_copy_on_write": ("elif sum(u.count(t[j]) for u in tables.values()) > 1:", "elif False:"),
+    # copies a partial block even when no other table names it
+    "copy_unshared": ("for u in tables.values()) > 1:", "for u in tables.values()) >= 1:"),
+    # counts holders before the batch, so every writer of a shared block copies
+    "stale_counts_in_batch": ("for u in tables.values()) > 1:", "for u in self.tables.values()) > 1:"),
+    # takes the fresh block but does not report the copy
+    "copy_not_reported": ("copies.append((t[j], fresh))", "pass"),
+    # the fork shares the parent's history list instead of copying it
+    "fork_aliases_history": ("self.history[s] = list(self.history[seq])",
+                             "self.history[s] = self.history[seq]"),
+    # the fork starts with an empty table
+    "fork_without_blocks": ("self.tables[s] = list(self.tables[seq])", "self.tables[s] = []"),
+    # takes fresh blocks from the front of the free list
+    "front_of_free_list": ("free.pop()", "free.pop(0)"),
+    # frees every block of a released table, shared or not
+    "release_frees_shared": ("if self.refcount(b) == 0:", "if True:"),
+    # never returns blocks to the free list
+    "release_leaks": ("if self.refcount(b) == 0:", "if False:"),
+    # the slot is one past the token's place
+    "slot_off_by_one": ("slots.append(t[j] * self.block_size + off)",
+                        "slots.append(t[j] * self.block_size + off + 1)"),
+    # the slot uses the logical block index instead of the physical block
+    "slot_logical_block": ("slots.append(t[j] * self.block_size + off)",
+                           "slots.append(j * self.block_size + off)"),
+    # a batch that runs out of blocks keeps the appends made before it ran out
+    "partial_batch": ("tables = {s: list(t) for s, t in self.tables.items()}\n        free = list(self.free)",
+                      "tables = self.tables\n        free = self.free"),
+}
 
 
-class FrontOfFreeList(bp.BlockPool):
-    """Takes blocks from the front of the free list."""
-    def _take(self, initial=()):
-        if not self.free:
-            raise bp.PoolExhausted("KV pool exhausted")
-        b = self.free.pop(0)
-        self.tokens[b] = list(initial)
-        self.refs[b] = 1
-        return b
+def mutant_module(name):
+    old, new = MUTANTS[name]
+    src = inspect.getsource(bp)
+    assert old in src, name
+    mod = types.ModuleType("block_pool_" + name)
+    exec(compile(src.replace(old, new), mod.__name__, "exec"), mod.__dict__)
+    return mod
 
 
-class ReleaseFreesShared(bp.BlockPool):
-    """Frees every block of a released table, shared or not."""
-    def release(self, table):
-        for b in table:
-            self.refs[b] = 1
-            self._drop(b)
-
-
-class SlotOffByOne(bp.BlockPool):
-    def append(self, table, token):
-        t, slot, copy = super().append(table, token)
-        return t, slot + 1, copy
-
-
-MUTANTS = [NoCopyOnWrite, CopyWithoutData, CopyKeepsReference, ForkWithoutReferences,
-           FrontOfFreeList, ReleaseFreesShared, SlotOffByOne]
-
-
-def _pins_fail(monkeypatch, cls):
-    monkeypatch.setattr(pins, "BlockPool", cls)
+def _pins_fail(monkeypatch, mod):
+    monkeypatch.setattr(pins, "BlockPool", mod.BlockPool)
+    monkeypatch.setattr(pins, "PoolExhausted", mod.PoolExhausted)
     failures = 0
     for pin in [pins.test_printed_cow_example] + \
                [lambda s=s: pins.test_random_operation_sequences(s) for s in range(6)]:
@@ -83,10 +64,12 @@ def _pins_fail(monkeypatch, cls):
     return failures
 
 
-@pytest.mark.parametrize("cls", MUTANTS, ids=lambda c: c.__name__)
-def test_mutant_is_caught(monkeypatch, cls):
-    assert _pins_fail(monkeypatch, cls) > 0, cls.__name__
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(monkeypatch, name):
+    assert _pins_fail(monkeypatch, mutant_module(name)) > 0, name
 
 
 def test_unmutated_pool_passes(monkeypatch):
-    assert _pins_fail(monkeypatch, bp.BlockPool) == 0
+    mod = types.ModuleType("block_pool_plain")
+    exec(compile(inspect.getsource(bp), mod.__name__, "exec"), mod.__dict__)
+    assert _pins_fail(monkeypatch, mod) == 0

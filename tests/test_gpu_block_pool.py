@@ -48,7 +48,7 @@ def test_copy_on_write_end_to_end():
     dk, dv = kc.to(DEV), vc.to(DEV)
     rk, rv = bits(kc), bits(vc)                 # oracle caches, raw bits
     rows_k, rows_v = [], []                     # K/V row of every token ever appended
-    seqs, tables = [], []                       # library ids, oracle tables
+    seqs, rids = [], []                         # library ids, oracle ids
 
     def append(which):
         nonlocal rk, rv
@@ -60,25 +60,22 @@ def test_copy_on_write_end_to_end():
             ops.copy_blocks(dk, dv, torch.from_numpy(pairs).to(DEV))
         ops.reshape_and_cache(new_k.to(DEV), new_v.to(DEV), dk, dv,
                               torch.from_numpy(slots).to(DEV))
-        want_pairs, want_slots = [], []
-        for j, i in enumerate(which):
-            tables[i], slot, copy = ref.append(tables[i], len(rows_k))
-            rows_k.append(new_k[j])
-            rows_v.append(new_v[j])
-            want_slots.append(slot)
-            if copy is not None:
-                want_pairs.append(list(copy))
-        assert slots.tolist() == want_slots and pairs.tolist() == want_pairs
+        toks = list(range(len(rows_k), len(rows_k) + len(which)))
+        want_slots, want_pairs = ref.append([rids[i] for i in which], toks)
+        rows_k.extend(new_k)
+        rows_v.extend(new_v)
+        assert slots.tolist() == want_slots
+        assert pairs.tolist() == [list(p) for p in want_pairs]
         rk, rv = oracle.copy_blocks(rk, rv, want_pairs)
         rk, rv = oracle.reshape_and_cache(bits(new_k), bits(new_v), rk, rv, slots)
 
     def fork(i):
         seqs.append(pool.fork(seqs[i]))
-        tables.append(ref.fork(tables[i]))
+        rids.append(ref.fork(rids[i]))
 
     for _ in range(3):
         seqs.append(pool.add_sequence())
-        tables.append([])
+        rids.append(ref.add_sequence())
     for step in range(40):                      # prompts of 40 tokens
         append([0, 1, 2])
     fork(0)                                     # 40 % 16 = 8: shared partial tail
@@ -97,11 +94,11 @@ def test_copy_on_write_end_to_end():
 
     S = len(seqs)
     lens = [pool.length(s) for s in seqs]
-    W = max(len(t) for t in tables)
+    W = max(len(ref.table(r)) for r in rids)
     bt = np.full((S, W), -1, dtype=np.int32)
     for b, s in enumerate(seqs):
         t = pool.table(s)
-        assert list(t) == tables[b]
+        assert list(t) == ref.table(rids[b])
         bt[b, :len(t)] = t
     q = torch.randn(S, H, D).to(dtype)
     out = ops.paged_attention_decode(q.to(DEV), dk, dv, torch.from_numpy(bt).to(DEV),
@@ -112,7 +109,7 @@ def test_copy_on_write_end_to_end():
     ref_out = np.zeros((S, H, D))
     scale = 1.0 / np.sqrt(D)
     for b in range(S):
-        toks = ref.read(tables[b])
+        toks = ref.read(rids[b])
         assert len(toks) == lens[b]
         K = torch.stack([rows_k[t] for t in toks]).double().numpy()    # [L, H_kv, D]
         V = torch.stack([rows_v[t] for t in toks]).double().numpy()
