@@ -257,6 +257,18 @@ int pa_reshape_and_cache(const void* key, const void* value,
                          void* hip_stream);
 
 /*
+ * pa_check_slot_mapping -- host-side check of a cache write's slot mapping
+ * against the preconditions above (the write kernels do not check them).
+ *   slot_mapping   HOST [num_tokens] int64
+ *   num_slots      num_blocks * block_size of the caches the write targets
+ * Returns PA_OK when every non-negative slot is below num_slots and no two
+ * tokens share a slot; otherwise PA_ERR_INVALID_ARG, and pa_last_error()
+ * names the first offending token (past the pool) or slot (given twice).
+ * Negative slots are padding and pass.  Reads only; O(n log n) host time.
+ */
+int pa_check_slot_mapping(const int64_t* slot_mapping, int num_tokens, int64_t num_slots);
+
+/*
  * pa_paged_attention_verify -- decode with several new query tokens per
  * sequence: the verify step of speculative decoding, or multi-token decode
  * ([vLLM-paging] "Kernel metadata": each sequence's query range and the

@@ -33,6 +33,7 @@ SOURCES = [
     "pa_cache.hip",
     "pa_bench.hip",
     "pa_pool.cpp",
+    "pa_check.cpp",
     "pa_noalloc.hip",
 ]
 

@@ -11,6 +11,7 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
@@ -87,6 +88,7 @@ _SIGNATURES = {
     "pa_pool_table": (_I, [_VP, _I, _VP, _I]),
     "pa_pool_refcount": (_I, [_VP, _I]),
     "pa_pool_free_blocks": (_I, [_VP]),
+    "pa_check_slot_mapping": (_I, [_VP, _I, ctypes.c_int64]),
     "pa_bench_stream_read": (_I, [_VP, ctypes.c_size_t, _VP, _VP]),
     "pa_bench_copy": (_I, [_VP, _VP, ctypes.c_size_t, _VP]),
 }
@@ -294,9 +296,29 @@ def decode_append(query, key, value, key_cache, value_cache, block_tables, conte
     return out
 
 
-def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
+def check_slot_mapping(slot_mapping, num_slots):
+    """Raise RuntimeError unless every non-negative slot of slot_mapping (a
+    tensor on any device, or an array; int64 [T]) is below num_slots and no
+    two tokens share one.  Copies the mapping to the host (synchronising)."""
+    if isinstance(slot_mapping, torch.Tensor):
+        slot_mapping = slot_mapping.detach().cpu().numpy()
+    host = np.ascontiguousarray(slot_mapping, dtype=np.int64).reshape(-1)
+    _check(load_library().pa_check_slot_mapping(host.ctypes.data_as(ctypes.c_void_p), host.size,
+                                                int(num_slots)), "check_slot_mapping")
+
+
+def _checking_slots(check_slots):
+    """check_slots if given, else whether PAGEDATTN_CHECK_SLOTS=1 is set."""
+    if check_slots is None:
+        return os.environ.get("PAGEDATTN_CHECK_SLOTS") == "1"
+    return bool(check_slots)
+
+
+def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping, *, check_slots=None):
     """Store key/value [T, H_kv, D] into the caches at slot_mapping [T] (int64;
-    negative = skip).  In place on the caches."""
+    negative = skip).  In place on the caches.  With check_slots (default:
+    the PAGEDATTN_CHECK_SLOTS=1 environment setting), the mapping is first
+    checked on the host by check_slot_mapping."""
     for t, n in ((key, "key"), (value, "value"), (key_cache, "key_cache"),
                  (value_cache, "value_cache"), (slot_mapping, "slot_mapping")):
         _gpu(t, n)
@@ -312,6 +334,8 @@ def reshape_and_cache(key, value, key_cache, value_cache, slot_mapping):
         raise ValueError("key, value and caches must share one dtype")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be int64 [T]")
+    if _checking_slots(check_slots):
+        check_slot_mapping(slot_mapping, N * BS)
     status = load_library().pa_reshape_and_cache(
         _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping),
         T, H_kv, D, BS, N, dtype_code(key.dtype), _stream(key.device))
@@ -444,7 +468,7 @@ def _decode_append_q8(kv8, query, key, value, key_cache, value_cache, block_tabl
 
 
 def _reshape_and_cache_q8(kv8, key, value, key_cache, value_cache, slot_mapping, k_scale,
-                          v_scale):
+                          v_scale, check_slots):
     for t, n in ((key, "key"), (value, "value"), (key_cache, "key_cache"),
                  (value_cache, "value_cache"), (slot_mapping, "slot_mapping")):
         _gpu(t, n)
@@ -461,6 +485,8 @@ def _reshape_and_cache_q8(kv8, key, value, key_cache, value_cache, slot_mapping,
     N, H_kv2, BS, D2 = key_cache.shape
     if (H_kv, D) != (H_kv2, D2):
         raise ValueError("new tokens and caches disagree in KV heads or head_dim")
+    if _checking_slots(check_slots):
+        check_slot_mapping(slot_mapping, N * BS)
     name = "reshape_and_cache_" + ("fp8" if kv8 == "fp8" else "i8")
     _check(getattr(load_library(), "pa_" + name)(
         _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), T, H_kv,
@@ -490,12 +516,14 @@ def decode_append_fp8(query, key, value, key_cache, value_cache, block_tables, c
                              partition_size, out, workspace)
 
 
-def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale):
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale, *,
+                          check_slots=None):
     """Quantise key/value [T, H_kv, D] (f32, f16 or bf16) to E4M3 with the
     given scales and store them at slot_mapping [T] in the uint8 /
-    float8_e4m3fn caches [N, H_kv, BS, D]."""
+    float8_e4m3fn caches [N, H_kv, BS, D].  check_slots as for
+    reshape_and_cache."""
     _reshape_and_cache_q8("fp8", key, value, key_cache, value_cache, slot_mapping, k_scale,
-                          v_scale)
+                          v_scale, check_slots)
 
 
 def paged_attention_decode_i8(query, key_cache, value_cache, block_tables, context_lens,
@@ -518,12 +546,14 @@ def decode_append_i8(query, key, value, key_cache, value_cache, block_tables, co
                              partition_size, out, workspace)
 
 
-def reshape_and_cache_i8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale):
+def reshape_and_cache_i8(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale, *,
+                         check_slots=None):
     """Quantise key/value [T, H_kv, D] (f32, f16 or bf16) to INT8 codes
     (nearest integer of x / scale, ties to even, clamped to +-127, NaN to 0)
-    and store them at slot_mapping [T] in the int8 caches [N, H_kv, BS, D]."""
+    and store them at slot_mapping [T] in the int8 caches [N, H_kv, BS, D].
+    check_slots as for reshape_and_cache."""
     _reshape_and_cache_q8("int8", key, value, key_cache, value_cache, slot_mapping, k_scale,
-                          v_scale)
+                          v_scale, check_slots)
 
 
 def copy_blocks(key_cache, value_cache, block_pairs):
@@ -549,7 +579,6 @@ class BlockPool:
     Arrays cross the boundary as NumPy host arrays."""
 
     def __init__(self, num_blocks, block_size):
-        import numpy as np
         self._np = np
         lib = load_library()
         self._lib = lib

@@ -42,6 +42,35 @@ def test_cache_write_bit_exact(dtype, H_kv, D, BS):
     assert np.array_equal(bits(vc), rv)
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "int8"])
+def test_slot_check_rejects_before_writing(kind, monkeypatch):
+    # with the check on, a duplicate slot or one past the pool raises before
+    # any launch: the caches keep their bits; with it off (the default) the
+    # same distinct-slot write goes through
+    N, H_kv, BS, D, T = 8, 2, 16, 64, 5
+    code = {"bf16": torch.bfloat16, "fp8": torch.uint8, "int8": torch.int8}[kind]
+    kc = torch.zeros(N, H_kv, BS, D, dtype=code, device=DEV)
+    vc = torch.zeros_like(kc)
+    key = torch.randn(T, H_kv, D, dtype=torch.bfloat16, device=DEV)
+    val = torch.randn_like(key)
+    write = {"bf16": lambda sm, **kw: ops.reshape_and_cache(key, val, kc, vc, sm, **kw),
+             "fp8": lambda sm, **kw: ops.reshape_and_cache_fp8(key, val, kc, vc, sm, 0.05, 0.05, **kw),
+             "int8": lambda sm, **kw: ops.reshape_and_cache_i8(key, val, kc, vc, sm, 0.05, 0.05, **kw)}[kind]
+    dup = torch.tensor([3, 40, -1, 9, 40], dtype=torch.int64, device=DEV)
+    past = torch.tensor([3, 4, N * BS, 9, 10], dtype=torch.int64, device=DEV)
+    with pytest.raises(RuntimeError, match="slot 40 given to tokens 1 and 4"):
+        write(dup, check_slots=True)
+    monkeypatch.setenv("PAGEDATTN_CHECK_SLOTS", "1")
+    with pytest.raises(RuntimeError, match="past the pool"):
+        write(past)
+    torch.cuda.synchronize()
+    assert not kc.view(torch.uint8).any() and not vc.view(torch.uint8).any()
+    monkeypatch.delenv("PAGEDATTN_CHECK_SLOTS")
+    write(torch.tensor([3, 40, -1, 9, 41], dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    assert kc.view(torch.uint8)[40 // BS, :, 40 % BS].any()
+
+
 def test_write_then_attend_tiny():
     """The append flow: each sequence's next token goes to position L_b (a
     free block when L_b is a multiple of the block size), then decode attends
