@@ -75,11 +75,21 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="only run the block-size x head-dim sweep (one JSON line per shape)")
     ap.add_argument("--sweep-out", default=None,
-                    help="with --sweep: also write the table as markdown to this file")
+                    help="with --sweep or --sweep-lengths: also write the table as markdown to this file")
     ap.add_argument("--sweep-head-dims", default="64,128,256",
                     help="with --sweep: comma-separated head dims")
     ap.add_argument("--sweep-block-sizes", default="8,16,32,64",
                     help="with --sweep: comma-separated block sizes")
+    ap.add_argument("--sweep-lengths", action="store_true",
+                    help="only run the context-length x batch sweep (one JSON line per point)")
+    ap.add_argument("--sweep-lens", default="64,256,1024,4096,16384,65536,131072",
+                    help="with --sweep-lengths: comma-separated history lengths")
+    ap.add_argument("--sweep-seqs", default="1,4,16,64,256,1024,2048",
+                    help="with --sweep-lengths: comma-separated batch sizes")
+    ap.add_argument("--sweep-kv", default="bf16,fp8",
+                    help="with --sweep-lengths: KV formats (bf16, fp8)")
+    ap.add_argument("--sweep-max-tokens", type=int, default=1 << 23,
+                    help="with --sweep-lengths: largest batch history (tokens) swept")
     return ap.parse_args()
 
 
@@ -455,6 +465,36 @@ def verify_rate(args, cfg, q, bt, cl, kcs, vcs, max_ctx, dev, alg_bytes, capture
                     "(%d (token, head) columns of %d)" % (per_pass, per_pass * G, cols)}
 
 
+def graph_time_s(call, K):
+    """Seconds per call(j): K calls captured in one HIP graph (after 5 eager
+    warm-up calls), HIP events around each of 3 replays, the mean."""
+    import numpy as np
+    import torch
+    for j in range(5):
+        call(j)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(gr, stream=st):
+            for j in range(K):
+                call(j)
+    torch.cuda.current_stream().wait_stream(st)
+    gr.replay()
+    torch.cuda.synchronize()
+    us = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3 / K)
+    del gr
+    return float(np.mean(us)) * 1e-6
+
+
 def shape_sweep(args, dev):
     """Decode-call rate over block sizes 8/16/32/64 and head dims 64/128/256,
     on 16-bit caches and on FP8 E4M3 and INT8 caches: the bench batch (64
@@ -477,29 +517,7 @@ def shape_sweep(args, dev):
     rows = []
 
     def timed(call):
-        for j in range(5):
-            call(j)
-        torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        st = torch.cuda.Stream()
-        st.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(st):
-            with torch.cuda.graph(gr, stream=st):
-                for j in range(K):
-                    call(j)
-        torch.cuda.current_stream().wait_stream(st)
-        gr.replay()
-        torch.cuda.synchronize()
-        us = []
-        for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            gr.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            us.append(e0.elapsed_time(e1) * 1e3 / K)
-        del gr
-        return float(np.mean(us)) * 1e-6
+        return graph_time_s(call, K)
 
     for D in [int(x) for x in args.sweep_head_dims.split(",")]:
         for BS in [int(x) for x in args.sweep_block_sizes.split(",")]:
@@ -592,6 +610,132 @@ def shape_sweep(args, dev):
             fh.write("\n".join(L) + "\n")
 
 
+LENGTH_MIXES = {"U[32,255]": (32, 255), "U[256,1023]": (256, 1023)}
+
+
+def length_sweep(args, dev):
+    """Decode-call rate over context length x batch: every history of the
+    batch L tokens long (L from the --sweep-lens list), S sequences (from
+    --sweep-seqs), or L drawn uniformly from a short range (the LENGTH_MIXES
+    rows), at 28 query / 4 KV heads, head_dim 128, block size 16, bf16
+    queries, on bf16 and FP8 E4M3 caches.  Points with more than
+    --sweep-max-tokens history tokens are left out.  Shuffled tables, random
+    pools on the GPU (FP8 quantised by the library's cache write), replicas
+    rotated so that 1.2 GB or more of K/V lies between two reads of the same
+    bytes; K calls replayed from a HIP graph, HIP events around each
+    replay."""
+    import numpy as np
+    import torch
+    from paged_kv_decode_attention_amd import ops
+
+    H, H_kv, D, BS = 28, 4, 128, 16
+    G = H // H_kv
+    scale8 = 1.0 / 64
+    kvs = args.sweep_kv.split(",")
+    points = []
+    for L in [int(x) for x in args.sweep_lens.split(",")]:
+        for S in [int(x) for x in args.sweep_seqs.split(",")]:
+            if S * L <= args.sweep_max_tokens:
+                points.append((str(L), S, np.full(S, L, dtype=np.int64)))
+    for name, (lo, hi) in LENGTH_MIXES.items():
+        for S in (1024, 2048):
+            lens = np.random.default_rng(5).integers(lo, hi + 1, size=S).astype(np.int64)
+            points.append((name, S, lens))
+    rows = []
+    for label, S, lens in points:
+        rng = np.random.default_rng(7)
+        nblk = -(-lens // BS)
+        N = int(nblk.sum()) + 16
+        W = int(nblk.max())
+        perm = rng.permutation(N).astype(np.int32)
+        bt = np.full((S, W), -1, dtype=np.int32)
+        k = 0
+        for b in range(S):
+            bt[b, :nblk[b]] = perm[k:k + nblk[b]]
+            k += nblk[b]
+        g = torch.Generator(device=dev).manual_seed(11)
+        q = torch.randn(S, H, D, generator=g, device=dev).to(torch.bfloat16)
+        btd = torch.from_numpy(bt).to(dev)
+        cld = torch.from_numpy(lens.astype(np.int32)).to(dev)
+        out = torch.empty_like(q)
+        max_ctx = W * BS
+        ws = torch.zeros(max(ops.decode_workspace_size(S, H, H_kv, D, BS, max_ctx, 0, q.dtype),
+                             256), dtype=torch.uint8, device=dev)
+        for kv in kvs:
+            e = 2 if kv == "bf16" else 1
+            pool = N * H_kv * BS * D * e
+            R = max(1, int(np.ceil(1.2e9 / (2 * pool))))
+            kcs, vcs = [], []
+            for _ in range(2 * R):
+                x = torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(torch.bfloat16)
+                if kv != "bf16":
+                    c = torch.empty(N, H_kv, BS, D, device=dev, dtype=torch.uint8)
+                    rows_ = x.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous()
+                    ops.reshape_and_cache_fp8(rows_, rows_, c, torch.empty_like(c),
+                                              torch.arange(N * BS, dtype=torch.int64, device=dev),
+                                              scale8, scale8)
+                    del rows_
+                    x = c
+                (kcs if len(kcs) < R else vcs).append(x)
+            torch.cuda.synchronize()
+            if kv == "bf16":
+                def call(j):
+                    ops.paged_attention_decode(q, kcs[j % R], vcs[j % R], btd, cld,
+                                               max_context_len=max_ctx, out=out, workspace=ws)
+            else:
+                def call(j):
+                    ops.paged_attention_decode_fp8(q, kcs[j % R], vcs[j % R], btd, cld, scale8,
+                                                   scale8, max_context_len=max_ctx, out=out,
+                                                   workspace=ws)
+            alg = int(lens.sum()) * H_kv * D * e * 2
+            # about 0.2 s of calls per point, at least 20, at most 200
+            est = max(alg / 6e12, 8e-6)
+            K = int(min(200, max(20, 0.2 / est)))
+            t = graph_time_s(call, K)
+            row = {"context": label, "seqs": S, "kv": "bf16" if kv == "bf16" else "fp8 e4m3",
+                   "history_tokens": int(lens.sum()), "decode_us": t * 1e6, "alg_bytes": alg,
+                   "achieved_gbps": alg / t / 1e9, "frac": alg / t / 1e9 / HBM_PEAK_GBPS,
+                   "decode_tokens_per_s": S / t, "calls": K, "pool_replicas": R,
+                   "kernel": "matrix-core, balanced"
+                   if ops.decode_kernel(D, BS, G, q.dtype) == ops.KERNEL_MFMA else "vector-ALU"}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+            del kcs, vcs, x
+            torch.cuda.empty_cache()
+    if args.sweep_out:
+        L = ["# Decode call over context length x batch (28/4 heads, head_dim 128, block "
+             "size 16, bf16 queries)", "",
+             "Command (repository root, one MI355X):", "",
+             "    python bench.py --sweep-lengths --sweep-out <file>", "",
+             "Each cell: decode-call time in us, and algorithmic KV bytes per second as % of "
+             "8 TB/s.  Histories of L tokens each (rows), S sequences (columns); the last rows "
+             "draw each history's length uniformly from the range named.", ""]
+        seqs = sorted({r["seqs"] for r in rows})
+        for kv in sorted({r["kv"] for r in rows}):
+            L += ["## KV cache: %s" % kv, "",
+                  "| L \\ S | " + " | ".join(str(x) for x in seqs) + " |",
+                  "|---|" + "---|" * len(seqs)]
+            labels = []
+            for r in rows:
+                if r["kv"] == kv and r["context"] not in labels:
+                    labels.append(r["context"])
+            for lab in labels:
+                cells = []
+                for sq in seqs:
+                    m = [r for r in rows if r["kv"] == kv and r["context"] == lab and
+                         r["seqs"] == sq]
+                    cells.append("%.1f us, %.1f %%" % (m[0]["decode_us"], 100 * m[0]["frac"])
+                                 if m else "")
+                L.append("| %s | " % lab + " | ".join(cells) + " |")
+            L.append("")
+        L += ["Algorithmic bytes: history tokens x 4 KV heads x 128 x element bytes (2 for "
+              "bf16, 1 for FP8) x 2 (K and V).  Timing: K decode calls replayed from a HIP "
+              "graph (K = 20..200, about 0.2 s per point), HIP events around each replay, "
+              "mean of 3.  Small calls are launch-bound: there the percentage says little."]
+        with open(args.sweep_out, "w") as fh:
+            fh.write("\n".join(L) + "\n")
+
+
 def copy_blocks_rate(kcs, vcs, dev, pairs=2048, calls=8):
     """The copy-on-write block copy (pa_copy_blocks) on the same pools:
     `pairs` distinct (src, dst) blocks per call, a fresh set each call and
@@ -654,6 +798,9 @@ def main():
 
     if args.sweep:
         shape_sweep(args, dev)
+        return
+    if args.sweep_lengths:
+        length_sweep(args, dev)
         return
 
     if args.copy_calibration_mib:
