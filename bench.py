@@ -502,7 +502,10 @@ def shape_sweep(args, dev):
     queries, shuffled tables, random pools on the GPU (the 8-bit ones quantised
     by the library's cache writes), pool replicas rotated so the last-level cache
     cannot hold the working set; K calls replayed from a HIP graph, HIP
-    events around each replay."""
+    events around each replay.  Then the shapes the vector-ALU kernel serves
+    (the same batch): fp32 at each head dim, and bf16 with more query heads
+    per KV head than the matrix-core kernel takes (64 at head_dim 128, 32 at
+    head_dim 256: one KV head)."""
     import numpy as np
     import torch
     from paged_kv_decode_attention_amd import inputs as I
@@ -510,8 +513,7 @@ def shape_sweep(args, dev):
 
     base = I.CONFIGS["qwen7b_gqa_bf16"]
     lens = I.draw_context_lens(base).astype(np.int64)
-    S, H, H_kv = base.num_seqs, base.num_heads, base.num_kv_heads
-    G = H // H_kv
+    S = base.num_seqs
     K = min(args.steps, 100)
     scales = {"fp8": 1.0 / 64, "int8": 1.0 / 24}
     rows = []
@@ -519,91 +521,101 @@ def shape_sweep(args, dev):
     def timed(call):
         return graph_time_s(call, K)
 
+    def run(D, BS, H, H_kv, dt, kvs):
+        G = H // H_kv
+        rng = np.random.default_rng(7)
+        nblk = -(-lens // BS)
+        N = int(nblk.sum()) + 64
+        W = -(-4096 // BS)
+        perm = rng.permutation(N).astype(np.int32)
+        bt = np.full((S, W), -1, dtype=np.int32)
+        k = 0
+        for b in range(S):
+            bt[b, :nblk[b]] = perm[k:k + nblk[b]]
+            k += nblk[b]
+        g = torch.Generator(device=dev).manual_seed(11)
+        q = torch.randn(S, H, D, generator=g, device=dev).to(dt)
+        btd = torch.from_numpy(bt).to(dev)
+        cld = torch.from_numpy(lens.astype(np.int32)).to(dev)
+        out = torch.empty_like(q)
+        max_ctx = W * BS
+        ws = torch.zeros(max(ops.decode_workspace_size(S, H, H_kv, D, BS, max_ctx, 0, q.dtype),
+                             256), dtype=torch.uint8, device=dev)
+        mfma = ops.decode_kernel(D, BS, G, q.dtype) == ops.KERNEL_MFMA
+        for kv in kvs:
+            if kv in ("fp8", "int8") and not mfma:
+                continue
+            k_scale = v_scale = scales.get(kv, 1.0)
+            e = {"fp8": 1, "int8": 1}.get(kv, q.element_size())
+            pool = N * H_kv * BS * D * e
+            # replicas cycled through: 1.2 GB or more of K/V between two
+            # reads of the same bytes, well beyond the 256 MB last-level
+            # cache
+            R = max(2, int(np.ceil(1.2e9 / (2 * pool))))
+            kcs, vcs = [], []
+            for _ in range(2 * R):
+                x = torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(dt)
+                if kv in ("fp8", "int8"):
+                    # pool rows as tokens: slot pb * BS + off holds row (pb, :, off)
+                    c = torch.empty(N, H_kv, BS, D, device=dev,
+                                    dtype=torch.uint8 if kv == "fp8" else torch.int8)
+                    rows_ = x.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous()
+                    slots = torch.arange(N * BS, dtype=torch.int64, device=dev)
+                    write = (ops.reshape_and_cache_fp8 if kv == "fp8"
+                             else ops.reshape_and_cache_i8)
+                    write(rows_, rows_, c, torch.empty_like(c), slots, k_scale, v_scale)
+                    x = c
+                (kcs if len(kcs) < R else vcs).append(x)
+            torch.cuda.synchronize()
+
+            if kv in ("fp8", "int8"):
+                dec = (ops.paged_attention_decode_fp8 if kv == "fp8"
+                       else ops.paged_attention_decode_i8)
+
+                def call(j):
+                    dec(q, kcs[j % R], vcs[j % R], btd, cld, k_scale, v_scale,
+                        max_context_len=max_ctx, out=out, workspace=ws)
+            else:
+                def call(j):
+                    ops.paged_attention_decode(q, kcs[j % R], vcs[j % R], btd, cld,
+                                               max_context_len=max_ctx, out=out, workspace=ws)
+            t = timed(call)
+            alg = int(lens.sum()) * H_kv * D * e * 2
+            row = {"head_dim": D, "block_size": BS, "heads": "%d/%d" % (H, H_kv),
+                   "kv": {"fp8": "fp8 e4m3", "int8": "int8"}.get(kv, kv),
+                   "kernel": "matrix-core, balanced" if mfma else "vector-ALU, partitions",
+                   "decode_us": t * 1e6, "alg_bytes": alg, "achieved_gbps": alg / t / 1e9,
+                   "frac": alg / t / 1e9 / HBM_PEAK_GBPS, "decode_tokens_per_s": S / t,
+                   "pool_replicas": R}
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+            del kcs, vcs
+            torch.cuda.empty_cache()
+
+    H, H_kv = base.num_heads, base.num_kv_heads
     for D in [int(x) for x in args.sweep_head_dims.split(",")]:
         for BS in [int(x) for x in args.sweep_block_sizes.split(",")]:
-            rng = np.random.default_rng(7)
-            nblk = -(-lens // BS)
-            N = int(nblk.sum()) + 64
-            W = -(-4096 // BS)
-            perm = rng.permutation(N).astype(np.int32)
-            bt = np.full((S, W), -1, dtype=np.int32)
-            k = 0
-            for b in range(S):
-                bt[b, :nblk[b]] = perm[k:k + nblk[b]]
-                k += nblk[b]
-            g = torch.Generator(device=dev).manual_seed(11)
-            q = torch.randn(S, H, D, generator=g, device=dev).to(torch.bfloat16)
-            btd = torch.from_numpy(bt).to(dev)
-            cld = torch.from_numpy(lens.astype(np.int32)).to(dev)
-            out = torch.empty_like(q)
-            max_ctx = W * BS
-            ws = torch.zeros(max(ops.decode_workspace_size(S, H, H_kv, D, BS, max_ctx, 0,
-                                                           q.dtype), 256),
-                             dtype=torch.uint8, device=dev)
-            mfma = ops.decode_kernel(D, BS, G, q.dtype) == ops.KERNEL_MFMA
-            for kv in ("bf16", "fp8", "int8"):
-                if kv != "bf16" and not mfma:
-                    continue
-                k_scale = v_scale = scales.get(kv, 1.0)
-                e = 2 if kv == "bf16" else 1
-                pool = N * H_kv * BS * D * e
-                # replicas cycled through: 1.2 GB or more of K/V between two
-                # reads of the same bytes, well beyond the 256 MB last-level
-                # cache
-                R = max(2, int(np.ceil(1.2e9 / (2 * pool))))
-                kcs, vcs = [], []
-                for _ in range(2 * R):
-                    x = torch.randn(N, H_kv, BS, D, generator=g, device=dev).to(torch.bfloat16)
-                    if kv != "bf16":
-                        # pool rows as tokens: slot pb * BS + off holds row (pb, :, off)
-                        c = torch.empty(N, H_kv, BS, D, device=dev,
-                                        dtype=torch.uint8 if kv == "fp8" else torch.int8)
-                        rows_ = x.permute(0, 2, 1, 3).reshape(N * BS, H_kv, D).contiguous()
-                        slots = torch.arange(N * BS, dtype=torch.int64, device=dev)
-                        write = (ops.reshape_and_cache_fp8 if kv == "fp8"
-                                 else ops.reshape_and_cache_i8)
-                        write(rows_, rows_, c, torch.empty_like(c), slots, k_scale, v_scale)
-                        x = c
-                    (kcs if len(kcs) < R else vcs).append(x)
-                torch.cuda.synchronize()
-
-                if kv == "bf16":
-                    def call(j):
-                        ops.paged_attention_decode(q, kcs[j % R], vcs[j % R], btd, cld,
-                                                   max_context_len=max_ctx, out=out,
-                                                   workspace=ws)
-                else:
-                    dec = (ops.paged_attention_decode_fp8 if kv == "fp8"
-                           else ops.paged_attention_decode_i8)
-
-                    def call(j):
-                        dec(q, kcs[j % R], vcs[j % R], btd, cld, k_scale, v_scale,
-                            max_context_len=max_ctx, out=out, workspace=ws)
-                t = timed(call)
-                alg = int(lens.sum()) * H_kv * D * e * 2
-                row = {"head_dim": D, "block_size": BS,
-                       "kv": {"bf16": "bf16", "fp8": "fp8 e4m3", "int8": "int8"}[kv],
-                       "kernel": "matrix-core, balanced" if mfma else "vector-ALU, partitions",
-                       "decode_us": t * 1e6, "alg_bytes": alg, "achieved_gbps": alg / t / 1e9,
-                       "frac": alg / t / 1e9 / HBM_PEAK_GBPS, "decode_tokens_per_s": S / t,
-                       "pool_replicas": R}
-                rows.append(row)
-                print(json.dumps(row), flush=True)
-                del kcs, vcs
-                torch.cuda.empty_cache()
+            run(D, BS, H, H_kv, torch.bfloat16, ("bf16", "fp8", "int8"))
+    for D in [int(x) for x in args.sweep_head_dims.split(",")]:
+        run(D, 16, H, H_kv, torch.float32, ("fp32",))
+    if "128" in args.sweep_head_dims.split(","):
+        run(128, 16, 64, 1, torch.bfloat16, ("bf16",))
+    if "256" in args.sweep_head_dims.split(","):
+        run(256, 16, 32, 1, torch.bfloat16, ("bf16",))
     if args.sweep_out:
-        L = ["# Decode shape sweep: block size x head dim x KV format (bf16 queries, "
-             "64 sequences, 28/4 heads, L~U[512,4096] seed 2)", "",
+        L = ["# Decode shape sweep: block size x head dim x KV format (64 sequences, "
+             "L~U[512,4096] seed 2; 28/4 heads unless the row says otherwise)", "",
              "Command (repository root, one MI355X):", "",
              "    python bench.py --sweep --sweep-out <file>", "",
-             "| head_dim | block_size | KV | kernel | decode call us | KV TB/s | % of 8 TB/s | "
-             "decode tokens/s |", "|---|---|---|---|---|---|---|---|"]
+             "| head_dim | block_size | heads (query/KV) | KV | kernel | decode call us | "
+             "KV TB/s | % of 8 TB/s | decode tokens/s |", "|---|---|---|---|---|---|---|---|---|"]
         for r in rows:
-            L.append("| %d | %d | %s | %s | %.1f | %.2f | %.1f | %.0f |" % (
-                r["head_dim"], r["block_size"], r["kv"], r["kernel"], r["decode_us"],
-                r["achieved_gbps"] / 1e3, 100 * r["frac"], r["decode_tokens_per_s"]))
-        L += ["", "Algorithmic bytes: sum_b L_b x 4 KV heads x head_dim x element bytes (2 for "
-              "bf16, 1 for FP8 E4M3 and INT8) x 2 (K and V).  "
+            L.append("| %d | %d | %s | %s | %s | %.1f | %.2f | %.1f | %.0f |" % (
+                r["head_dim"], r["block_size"], r["heads"], r["kv"], r["kernel"],
+                r["decode_us"], r["achieved_gbps"] / 1e3, 100 * r["frac"],
+                r["decode_tokens_per_s"]))
+        L += ["", "Algorithmic bytes: sum_b L_b x KV heads x head_dim x element bytes (4 for "
+              "fp32, 2 for bf16, 1 for FP8 E4M3 and INT8) x 2 (K and V).  "
               "Timing: K decode calls replayed from a HIP graph, HIP events around each "
               "replay, mean of 3."]
         with open(args.sweep_out, "w") as fh:

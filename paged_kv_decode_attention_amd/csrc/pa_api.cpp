@@ -179,7 +179,7 @@ int pa_decode_kernel(int head_dim, int block_size, int gqa_group_size, pa_dtype 
         return fail(PA_ERR_UNSUPPORTED, "head_dim %d with block_size %d not built", head_dim,
                     block_size);
     const int kind = g_kernel_kind.load();
-    const bool mfma_ok = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size);
+    const bool mfma_ok = pa::mfma_split(dtype, head_dim, block_size, gqa_group_size) > 0;
     if (kind == pa::kMfma && !mfma_ok)
         return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
     return mfma_ok && kind != pa::kGeneric ? pa::kMfma : pa::kGeneric;
@@ -205,12 +205,13 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
     size_t bytes = fixed_layout(num_seqs, num_heads, head_dim, max_context_len, P).bytes;
     // enough for either kernel family (pa_debug_select_kernel may force one)
     const int group = num_heads / num_kv_heads;
-    const bool mfma = pa::mfma_supported(dtype, head_dim, block_size, group);
-    if (use_balanced(mfma, partition_size, num_seqs, max_context_len)) {
-        // groups of more than 16 heads take two 16-column tiles per slot
-        const size_t bal =
-            balanced_layout(head_dim, group > pa::kMaxGroup ? 2 * pa::kMaxGroup : pa::kMaxGroup)
-                .bytes;
+    const int split = pa::mfma_split(dtype, head_dim, block_size, group);
+    if (use_balanced(split > 0, partition_size, num_seqs, max_context_len)) {
+        // groups (per pass) of more than 16 heads take two 16-column tiles per slot
+        const size_t bal = balanced_layout(head_dim, group / split > pa::kMaxGroup
+                                                         ? 2 * pa::kMaxGroup
+                                                         : pa::kMaxGroup)
+                               .bytes;
         if (bal > bytes) bytes = bal;
     }
     return bytes;
@@ -281,14 +282,19 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                     "and of block_size, at most 64*block_size", partition_size);
 
     const int kind = kernel_kind >= 0 ? kernel_kind : g_kernel_kind.load();
-    const bool mfma_ok = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size);
+    // verify rows (a row map or a fold) take the matrix-core kernel in one pass only
+    const bool rows_mapped = table_rows != nullptr || fold != nullptr;
+    const int split = rows_mapped ? (pa::mfma_supported(dtype, head_dim, block_size,
+                                                        gqa_group_size) ? 1 : 0)
+                                  : pa::mfma_split(dtype, head_dim, block_size, gqa_group_size);
+    const bool mfma_ok = split > 0;
     const bool use_mfma = mfma_ok && kind != pa::kGeneric;
     if (kind == pa::kMfma && !mfma_ok)
         return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
     if (q8 && !use_mfma)
         return fail(PA_ERR_UNSUPPORTED, "8-bit caches are served by the matrix-core kernel only "
-                    "(bf16/f16 queries, head_dim 64/128/256, block_size 8/16/32/64, group <= 16, "
-                    "or <= 32 at head_dim 64/128)");
+                    "(bf16/f16 queries, head_dim 64/128/256, block_size 8/16/32/64, a group that "
+                    "splits into equal passes of <= 16 heads, or <= 32 at head_dim 64/128)");
     // a row map held in memory is read by the fixed schedule's kernels only
     const bool balanced = table_rows == nullptr &&
                           use_balanced(use_mfma, partition_size, num_seqs, max_context_len);
@@ -298,8 +304,17 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     const int P = partition_size ? partition_size
                                  : heuristic_partition(num_seqs, num_kv_heads, block_size,
                                                        max_context_len);
+    // a group too large for one pass runs as `split` passes of smaller ones
+    const int kv_split = use_mfma ? split : 1;
+    const int pass_group = gqa_group_size / kv_split;
+    // the passes of a split group all read the newest token, so its append
+    // runs in a kernel of its own first -- built for 16-bit and f32 rows only
+    if (append && q8 && kv_split > 1)
+        return fail(PA_ERR_UNSUPPORTED, "the fused append into 8-bit caches needs a group of at "
+                    "most 16 heads (32 at head_dim 64/128); store the token with "
+                    "pa_reshape_and_cache_fp8/_i8, then call the 8-bit decode");
     // groups of more than 16 heads always take two column tiles
-    if (use_mfma && gqa_group_size > pa::kMaxGroup) col_tiles = 2;
+    if (use_mfma && pass_group > pa::kMaxGroup) col_tiles = 2;
     if (col_tiles != 1 && !(col_tiles == 2 && use_mfma && head_dim <= 128))
         return fail(PA_ERR_INVALID_ARG, "two column tiles serve the matrix-core kernel at "
                     "head_dim 64/128 only");
@@ -339,8 +354,10 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                     : nullptr;
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
-    a.num_kv_heads = num_kv_heads;
-    a.group = gqa_group_size;
+    a.num_kv_heads = num_kv_heads * kv_split;
+    a.group = pass_group;
+    a.kv_split = kv_split;
+    a.kv_heads_mem = num_kv_heads;
     a.head_dim = head_dim;
     a.block_size = block_size;
     a.num_blocks = num_blocks;
@@ -360,8 +377,10 @@ static int decode_impl(void* out, const void* query, const void* new_key,
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = hipSuccess;
-    if (append && use_mfma) {
-        // the matrix-core kernel stores each newest token itself
+    if (append && use_mfma && kv_split == 1) {
+        // the matrix-core kernel stores each newest token itself (with a
+        // split group, several passes read that token: a kernel of its own
+        // stores it first)
         a.new_key = new_key;
         a.new_value = new_value;
     } else if (append) {

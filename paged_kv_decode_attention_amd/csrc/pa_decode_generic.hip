@@ -102,28 +102,47 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
         for (int e = 0; e < VEC; ++e) o[g][e] = 0.0f;
     }
 
+    // Each token group takes tokens t0, t0 + NG, ..., U at a time: their K and
+    // V rows are loaded together (nontemporal: streamed once), then folded
+    // in token order, so that U rows per lane are in flight instead of one.
+    // Loads past the partition's end re-read its last token and are not
+    // folded.
+    typedef __attribute__((address_space(1))) const u32x4 GlobalRow;
+    constexpr int U = 8;
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
-    for (int t = t_begin + grp; t < t_end; t += NG) {
-        const int pb = sm_pb[(t - t_begin) / BS];
-        const uint64_t byte = (kv_row(pb, kvh, t % BS, a.num_kv_heads, BS) * D + c * VEC) * E;
-        float kf[VEC], vf[VEC];
-        to_float(Tag(), load16(kbase + byte), kf);
-        to_float(Tag(), load16(vbase + byte), vf);
+    for (int t0 = t_begin + grp; t0 < t_end; t0 += NG * U) {
+        u32x4 kr[U], vr[U];
 #pragma unroll
-        for (int g = 0; g < GT; ++g) {
-            float dot = 0.0f;
+        for (int u = 0; u < U; ++u) {
+            const int t = min(t0 + u * NG, t_end - 1);
+            const int pb = sm_pb[(t - t_begin) / BS];
+            const uint64_t byte =
+                (kv_row(pb, kvh, t % BS, a.num_kv_heads, BS) * D + c * VEC) * E;
+            kr[u] = __builtin_nontemporal_load((GlobalRow*)(kbase + byte));
+            vr[u] = __builtin_nontemporal_load((GlobalRow*)(vbase + byte));
+        }
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) dot += qf[g][e] * kf[e];
+        for (int u = 0; u < U; ++u) {
+            if (t0 + u * NG >= t_end) break;   // the same for every lane of a token group
+            float kf[VEC], vf[VEC];
+            to_float(Tag(), kr[u], kf);
+            to_float(Tag(), vr[u], vf);
 #pragma unroll
-            for (int s = 1; s < TG; s <<= 1) dot += __shfl_xor(dot, s);
-            const float m_new = fmaxf(m[g], dot);
-            const float al = fast_exp2(m[g] - m_new);
-            const float pe = fast_exp2(dot - m_new);
-            l[g] = l[g] * al + pe;
+            for (int g = 0; g < GT; ++g) {
+                float dot = 0.0f;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) o[g][e] = o[g][e] * al + pe * vf[e];
-            m[g] = m_new;
+                for (int e = 0; e < VEC; ++e) dot += qf[g][e] * kf[e];
+#pragma unroll
+                for (int s = 1; s < TG; s <<= 1) dot += __shfl_xor(dot, s);
+                const float m_new = fmaxf(m[g], dot);
+                const float al = fast_exp2(m[g] - m_new);
+                const float pe = fast_exp2(dot - m_new);
+                l[g] = l[g] * al + pe;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) o[g][e] = o[g][e] * al + pe * vf[e];
+                m[g] = m_new;
+            }
         }
     }
 

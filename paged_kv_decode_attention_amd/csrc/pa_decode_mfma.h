@@ -455,10 +455,12 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, const ConstI32
     if ((unsigned)pb >= (unsigned)a.num_blocks || lane >= 2 * LP) return;
     const bool is_k = lane < LP;
     const int c = lane % LP;
+    // (calls that split a group append in a kernel of their own: here the
+    // virtual head is the caches' head)
     const char* from = reinterpret_cast<const char*>(is_k ? a.new_key : a.new_value) +
-                       (((uint64_t)b * a.num_kv_heads + kvh) * D + c * 8) * 2;
+                       (((uint64_t)b * a.kv_heads_mem + kvh) * D + c * 8) * 2;
     char* to = reinterpret_cast<char*>(const_cast<void*>(is_k ? a.key_cache : a.value_cache));
-    const uint64_t r = kv_row(pb, kvh, pos % BS, a.num_kv_heads, BS);
+    const uint64_t r = kv_row(pb, kvh, pos % BS, a.kv_heads_mem, BS);
     const u32x4 x = load16(from);
     if constexpr (Kv::k8) {
         // both scales as register values first: a per-lane choice between
@@ -624,6 +626,9 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>*
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     const float sl2 = a.scale_log2;
+    // the caches' KV head of (virtual) head kvh
+    const int H_mem = a.kv_heads_mem;
+    kvh = a.kv_split == 1 ? kvh : kvh / a.kv_split;
     // tile 1 of chunk c is live when it holds history tokens
     auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
     if constexpr (D == 256) {
@@ -631,7 +636,7 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>*
         for (int k = 0; k < K; ++k) {
             KvRegs<Kv, D> buf;
             load_chunk<BS, D>(buf, kbase, vbase, ids, tile_row<BS>(chunk_of(k)), true,
-                              tile1_live(k), kvh, a.num_kv_heads, koff, voff);
+                              tile1_live(k), kvh, H_mem, koff, voff);
             ids = chunk_blocks<BS>(row, chunk_of(k + 1), L, a.num_blocks, bad);
             compute<Tag, Kv, kCols, D, NT>(st, buf, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
                                        t_lo, q);
@@ -641,7 +646,7 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>*
         BlockIds<BS> idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
         BlockIds<BS> idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
         load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true,
-                          tile1_live(0), kvh, a.num_kv_heads, koff, voff);
+                          tile1_live(0), kvh, H_mem, koff, voff);
         int k = 0;
         // The scheduling barriers keep each phase's loads after the previous
         // chunk's math and before this chunk's: the load counter is in
@@ -652,7 +657,7 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>*
         for (;;) {
             __builtin_amdgcn_sched_barrier(0);
             load_chunk<BS, D>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
-                              k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
+                              k + 1 < K && tile1_live(k + 1), kvh, H_mem, koff, voff);
             idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
             compute<Tag, Kv, kCols, D, NT>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
@@ -660,7 +665,7 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>*
             if (++k >= K) break;
             __builtin_amdgcn_sched_barrier(0);
             load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
-                              k + 1 < K && tile1_live(k + 1), kvh, a.num_kv_heads, koff, voff);
+                              k + 1 < K && tile1_live(k + 1), kvh, H_mem, koff, voff);
             idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
             __builtin_amdgcn_sched_barrier(0);
             compute<Tag, Kv, kCols, D, NT>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,

@@ -13,6 +13,20 @@ bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group) {
            group >= 1 && (group <= kMaxGroup || (group <= 2 * kMaxGroup && head_dim <= 128));
 }
 
+// A larger group is split into the fewest passes of equal groups that one
+// pass serves, at most kMaxSplit: each pass reads the KV head's history once
+// more, still cheaper than the vector-ALU kernel, which re-reads it for
+// every 8 heads.  (A group with no such split -- a prime above 32 -- stays
+// on the vector-ALU kernel.)
+constexpr int kMaxSplit = 4;
+
+int mfma_split(pa_dtype dt, int head_dim, int block_size, int group) {
+    if (group < 1) return 0;
+    for (int sp = 1; sp <= kMaxSplit && sp <= group; ++sp)
+        if (group % sp == 0 && mfma_supported(dt, head_dim, block_size, group / sp)) return sp;
+    return 0;
+}
+
 // Workgroups of the balanced schedule per compute unit: one (4 wavefronts,
 // one per SIMD).  One wavefront's two chunk buffers per SIMD already keep the
 // compute unit at its share of the HBM bandwidth; more, smaller ranges only

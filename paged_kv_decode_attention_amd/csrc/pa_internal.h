@@ -40,7 +40,14 @@ struct DecodeArgs {
     float* ws_lse;             // [S, H, num_parts] float32 (log2 units)
     float* ws_out;             // [S, H, num_parts, D] float32
     int* ws_meta;              // balanced schedule: [num_wg][4] tail-segment records
+    // num_kv_heads and group are the kernel's (virtual) KV heads and their
+    // query heads: a group too large for one pass of the matrix-core kernel
+    // is served as kv_split passes, KV head h standing for kv_split virtual
+    // heads h kv_split + j of group / kv_split consecutive query heads each
+    // (query head = virtual head * group + column, as without a split); the
+    // caches are addressed with KV head virtual / kv_split of kv_heads_mem.
     int num_seqs, num_heads, num_kv_heads, group, head_dim, block_size;
+    int kv_split, kv_heads_mem;
     int num_blocks, max_blocks_per_seq, max_context_len;
     int part_len;              // tokens per context partition (fixed schedule)
     int num_parts;             // ceil(max_context_len / part_len)
@@ -105,6 +112,10 @@ constexpr int kMaxStartUnits = 6;
 enum KernelKind { kAuto = 0, kGeneric = 1, kMfma = 2 };
 
 bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group);
+// Passes the matrix-core kernel serves a group of `group` query heads per KV
+// head in (1: directly; the fewest passes of equal, small enough groups
+// otherwise), or 0 if it cannot.
+int mfma_split(pa_dtype dt, int head_dim, int block_size, int group);
 // Workgroups of the matrix-core kernel resident per compute unit.
 int mfma_workgroups_per_cu(int head_dim);
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);

@@ -180,7 +180,14 @@ def test_8bit_entry_points_reject_on_host(lib, fmt):
                  f32(a["ks"]), f32(a["vs"]), 0, vp(FAKE), ctypes.c_size_t(1 << 30), vp(0))
     assert call(ks=-1.0) == INVALID
     assert call(vs=float("nan")) == INVALID
-    assert call(G=33, H=132) == UNSUPPORTED                    # matrix-core kernel: group <= 32
+    assert call(G=37, H=148) == UNSUPPORTED                    # 37: no split into <= 4 passes
+    # the fused 8-bit append takes groups of one pass only
+    a8 = getattr(lib, "pa_decode_append_" + fmt)
+    assert a8(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+              2, 64, 1, 64, 128, 16, 64, 16, 256, f32(0.1), ops.PA_BF16, f32(0.5), f32(0.5), 0,
+              vp(FAKE), ctypes.c_size_t(1 << 30), vp(0)) == UNSUPPORTED
+    assert b"fused append" in lib.pa_last_error()
+    assert call(G=33, H=132, S=0) == OK                        # 33 = 3 passes of 11 heads
     assert call(dtype=ops.PA_F32) == UNSUPPORTED               # f32 queries: vector-ALU only
     assert call(S=0) == OK
     # the fused append needs the new key and value
@@ -198,10 +205,17 @@ def test_decode_kernel_choice(lib):
     assert f(64, 64, 16, ops.PA_F16) == MFMA
     assert f(128, 8, 7, ops.PA_BF16) == MFMA
     assert f(256, 16, 7, ops.PA_BF16) == MFMA
+    # groups beyond one pass: equal passes of <= 32 heads (<= 16 at head_dim 256)
+    assert f(128, 16, 64, ops.PA_BF16) == MFMA
+    assert f(64, 16, 48, ops.PA_F16) == MFMA
+    assert f(256, 16, 32, ops.PA_BF16) == MFMA
+    assert f(128, 16, 37, ops.PA_BF16) == GEN                  # prime: no split into <= 4 passes
+    assert f(128, 16, 160, ops.PA_BF16) == GEN                 # 5 passes of 32: too many
+    assert f(256, 16, 17, ops.PA_BF16) == GEN
     assert f(128, 16, 17, ops.PA_BF16) == MFMA       # groups of 17..32: two column tiles
     assert f(64, 8, 32, ops.PA_F16) == MFMA
-    assert f(128, 16, 33, ops.PA_BF16) == GEN        # group > 32
-    assert f(256, 16, 17, ops.PA_BF16) == GEN        # group > 16 at head_dim 256
+    assert f(128, 16, 33, ops.PA_BF16) == MFMA       # 33 = three passes of 11
+    assert f(256, 16, 18, ops.PA_BF16) == MFMA       # two passes of 9 at head_dim 256
     assert f(128, 16, 7, ops.PA_F32) == GEN
     assert f(96, 16, 7, ops.PA_BF16) == UNSUPPORTED
     assert f(128, 16, 0, ops.PA_BF16) == INVALID
@@ -211,7 +225,7 @@ def test_decode_kernel_choice(lib):
         assert f(128, 16, 7, ops.PA_BF16) == GEN
         lib.pa_debug_select_kernel(2)
         assert f(128, 16, 7, ops.PA_BF16) == MFMA
-        assert f(128, 8, 33, ops.PA_BF16) == UNSUPPORTED
+        assert f(128, 8, 37, ops.PA_BF16) == UNSUPPORTED
     finally:
         lib.pa_debug_select_kernel(prev)
 

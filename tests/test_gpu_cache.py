@@ -123,11 +123,16 @@ def test_tiny_config_cache_write():
     ("qwen7b_gqa_bf16", ops.KERNEL_GENERIC, 0),    # vector ALU: append kernel + decode
     ("long_ctx_bf16", ops.KERNEL_AUTO, 0),
     ("tiny_fp32", ops.KERNEL_AUTO, 0),
+    ("qwen7b_gqa_bf16:mqa64", ops.KERNEL_AUTO, 0),   # 64 heads on 1 KV head: two passes
+    ("qwen7b_gqa_bf16:mqa64", ops.KERNEL_MFMA, 256),
 ])
 def test_decode_append_equals_write_then_decode(name, kernel, partition_size):
     """The fused step gives bit for bit the caches and output of
     reshape_and_cache at each sequence's last position followed by decode."""
-    cfg = I.CONFIGS[name]
+    base, _, variant = name.partition(":")
+    cfg = I.CONFIGS[base]
+    if variant == "mqa64":
+        cfg = I.with_overrides(cfg, num_seqs=16, num_heads=64, num_kv_heads=1)
     inp = I.generate(cfg, new_tokens_at="last")
     prev = ops.select_kernel(kernel)
     try:

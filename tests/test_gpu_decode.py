@@ -51,8 +51,14 @@ SMALL_CASES = [
     ("bf16", 1, 32, 128, 32, ops.KERNEL_MFMA),
     ("f16", 2, 17, 64, 16, ops.KERNEL_MFMA),
     ("bf16", 1, 24, 128, 8, ops.KERNEL_MFMA),
-    ("bf16", 1, 40, 128, 16, ops.KERNEL_AUTO),      # G > 32: vector-ALU kernel
-    ("bf16", 1, 20, 256, 16, ops.KERNEL_AUTO),      # G > 16 at head_dim 256: vector ALU
+    ("bf16", 1, 40, 128, 16, ops.KERNEL_AUTO),      # G > 32: two passes of 20 heads
+    ("bf16", 1, 20, 256, 16, ops.KERNEL_AUTO),      # G > 16 at head_dim 256: two passes of 10
+    ("bf16", 1, 64, 128, 16, ops.KERNEL_MFMA),      # two passes of 32 (two column tiles)
+    ("f16", 2, 48, 64, 32, ops.KERNEL_MFMA),        # two passes of 24
+    ("bf16", 1, 32, 256, 8, ops.KERNEL_MFMA),       # two passes of 16 at head_dim 256
+    ("bf16", 2, 96, 128, 16, ops.KERNEL_MFMA),      # three passes of 32
+    ("bf16", 1, 37, 128, 16, ops.KERNEL_AUTO),      # 37 heads: vector-ALU kernel
+    ("bf16", 1, 64, 128, 16, ops.KERNEL_GENERIC),
     ("f16", 2, 3, 64, 16, ops.KERNEL_AUTO),         # head_dim 64: matrix-core kernel
     ("bf16", 2, 5, 64, 32, ops.KERNEL_GENERIC),
     ("bf16", 2, 7, 64, 16, ops.KERNEL_MFMA),
