@@ -13,10 +13,39 @@
 //   m' = max(m, s),  l' = l 2^(m-m') + 2^(s-m'),  o' = o 2^(m-m') + 2^(s-m') v
 // and the groups' states are merged at the end (same update rule applied to
 // whole states), first across lanes, then across wavefronts in LDS.
+#include <type_traits>
+
 #include "pa_finalize.h"
 
 namespace pa {
 namespace {
+
+// Sum of x over the TG lanes of this lane's token group (TG a power of two
+// up to 64, groups aligned to TG lanes), in every lane of the group.  The
+// partners are those of a butterfly (lanes 1, 2, 4, ... apart), so the sum is
+// the same in every lane and the same as pairwise xor exchanges give; within
+// a row of 16 lanes they are DPP moves (quad permutes, then the half-row and
+// row mirrors, which pair each quad with the next and each half-row with
+// the other), across rows lane permutes.
+template <int TG>
+__device__ __forceinline__ float group_sum(float x) {
+    auto dpp = [](float v, auto ctrl) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
+                                                                  decltype(ctrl)::value, 0xF,
+                                                                  0xF, false));
+    };
+    using Q1 = std::integral_constant<int, 0xB1>;     // quad_perm [1, 0, 3, 2]
+    using Q2 = std::integral_constant<int, 0x4E>;     // quad_perm [2, 3, 0, 1]
+    using HM = std::integral_constant<int, 0x141>;    // row_half_mirror
+    using RM = std::integral_constant<int, 0x140>;    // row_mirror
+    if constexpr (TG >= 2) x += dpp(x, Q1{});
+    if constexpr (TG >= 4) x += dpp(x, Q2{});
+    if constexpr (TG >= 8) x += dpp(x, HM{});
+    if constexpr (TG >= 16) x += dpp(x, RM{});
+    if constexpr (TG >= 32) x += __shfl_xor(x, 16);
+    if constexpr (TG >= 64) x += __shfl_xor(x, 32);
+    return x;
+}
 
 template <typename Tag, int D, int BS, int GT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeArgs a) {
@@ -104,11 +133,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
 
     // Each token group takes tokens t0, t0 + NG, ..., U at a time: their K and
     // V rows are loaded together (nontemporal: streamed once), then folded
-    // in token order, so that U rows per lane are in flight instead of one.
+    // in token order, so that U rows per lane are in flight instead of one
+    // (U = 8 float32 rows or 4 16-bit rows: 128 bytes of K and V per lane).
     // Loads past the partition's end re-read its last token and are not
     // folded.
     typedef __attribute__((address_space(1))) const u32x4 GlobalRow;
-    constexpr int U = 8;
+    constexpr int U = VEC == 4 ? 8 : 4;    // 16-bit rows: half the registers' worth
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     for (int t0 = t_begin + grp; t0 < t_end; t0 += NG * U) {
@@ -133,8 +163,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
                 float dot = 0.0f;
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) dot += qf[g][e] * kf[e];
-#pragma unroll
-                for (int s = 1; s < TG; s <<= 1) dot += __shfl_xor(dot, s);
+                dot = group_sum<TG>(dot);
                 const float m_new = fmaxf(m[g], dot);
                 const float al = fast_exp2(m[g] - m_new);
                 const float pe = fast_exp2(dot - m_new);
