@@ -35,15 +35,32 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
 // range count and the columns a decode row can have: G, or u G for verify
 // rows), so that the compiler preloads them into scalar registers and the
 // loads leave without a round trip for the kernel arguments.
+// A history of more than kSpec pieces (long histories on few sequences:
+// 64 pieces each for one sequence of 131072 tokens) is folded by nsub
+// subsets of the workgroup's threads at once -- the threads past the
+// columns' would otherwise idle -- subset j taking pieces j, j + nsub, ...,
+// kSubBatch per memory round trip; the subsets' states are then combined in
+// LDS, in subset order (the same order on every call).
+constexpr int kMaxSub = 8;
+constexpr int kSubBatch = 16;
+
 template <typename Tag, int D, int NC>
 __global__ __launch_bounds__(NC * D / 4) void merge_balanced(
     const int4* __restrict__ ws_meta, const float* __restrict__ ws_out,
     const float* __restrict__ ws_lse, int nwg, int max_cols, DecodeArgs a) {
     constexpr int kSpec = 3;
+    constexpr int D4 = D / 4;
+    __shared__ float sub_m[NC * D4], sub_den[NC * D4];
+    __shared__ f32x4 sub_num[NC * D4];
+    __shared__ int sub_nan[NC * D4];
     const int w = blockIdx.x;
-    const int g = threadIdx.x / (D / 4);
-    const int d = (threadIdx.x % (D / 4)) * 4;
-    if (g >= max_cols) return;            // a column no decode row has: load nothing
+    const int items = max_cols * D4;                // one thread per (column, 4 d)
+    const int nsub = max(1, min((int)(NC * D4) / items, kMaxSub));
+    const int j = threadIdx.x / items;              // this thread's piece subset
+    const int it = threadIdx.x - j * items;
+    const int g = it / D4;
+    const int d = (it % D4) * 4;
+    if (j >= nsub) return;                          // no subset: load nothing
     auto slot_row = [&](int slot) { return (uint64_t)slot * NC + g; };
     const int4 meta = ws_meta[w];
     f32x4 o[kSpec];
@@ -71,10 +88,68 @@ __global__ __launch_bounds__(NC * D / 4) void merge_balanced(
     const int64_t T = (int64_t)(uint32_t)meta.z | ((int64_t)meta.w << 32);
     const int b = key / H_kv;
     const int kvh = key - b * H_kv;
-    if (g >= ntok * G) return;     // g: column of the decode row
     // every range is non-empty when T >= num_wg: pieces are then [w][1],
     // [w+1][0], ..., [w1][0]
     const int npieces = w1 - w + 1;
+    const bool active = g < ntok * G;    // g: column of the decode row
+    if (T >= nwg && npieces > kSpec && nsub > 1) {
+        float M = -INFINITY, den = 0.0f;
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
+        bool has_nan = false;
+        if (active) {
+            for (int p0 = j; p0 < npieces; p0 += nsub * kSubBatch) {
+                f32x4 ob[kSubBatch];
+                float lb[kSubBatch];
+#pragma unroll
+                for (int k = 0; k < kSubBatch; ++k) {
+                    const int p = min(p0 + k * nsub, npieces - 1);
+                    const int slot = p == 0 ? 2 * w + 1 : 2 * (w + p);
+                    ob[k] = *reinterpret_cast<const f32x4*>(ws_out + slot_row(slot) * D + d);
+                    lb[k] = p0 + k * nsub < npieces ? ws_lse[slot_row(slot)] : -INFINITY;
+                }
+                float mb = M;
+#pragma unroll
+                for (int k = 0; k < kSubBatch; ++k) {
+                    has_nan |= (lb[k] != lb[k]);
+                    mb = fmaxf(mb, lb[k]);
+                }
+                const float keep = rescale_weight(M, mb);
+                den *= keep;
+                num *= keep;
+#pragma unroll
+                for (int k = 0; k < kSubBatch; ++k) {
+                    const float wgt = rescale_weight(lb[k], mb);
+                    den += wgt;
+                    num += wgt * ob[k];
+                }
+                M = mb;
+            }
+        }
+        sub_m[threadIdx.x] = M;
+        sub_den[threadIdx.x] = den;
+        sub_num[threadIdx.x] = num;
+        sub_nan[threadIdx.x] = has_nan;
+        __syncthreads();
+        if (!active || j != 0) return;
+        float Mt = -INFINITY;
+        for (int q = 0; q < nsub; ++q) Mt = fmaxf(Mt, sub_m[q * items + it]);
+        float dt = 0.0f;
+        f32x4 nt = {0.f, 0.f, 0.f, 0.f};
+        bool nan_any = false;
+        for (int q = 0; q < nsub; ++q) {
+            const float wgt = rescale_weight(sub_m[q * items + it], Mt);
+            dt += wgt * sub_den[q * items + it];
+            nt += wgt * sub_num[q * items + it];
+            nan_any |= sub_nan[q * items + it] != 0;
+        }
+        const uint64_t out0 = col_row(a, b, kvh, g) * D + d;
+        store4(Tag(), a.out, out0,
+               nan_any ? (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                 __builtin_nanf("")}
+                       : a.out_scale * (nt / dt));
+        return;
+    }
+    if (!active || j != 0) return;
     float M = -INFINITY, den = 0.0f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     bool has_nan = false;

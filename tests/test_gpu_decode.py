@@ -259,6 +259,24 @@ def test_long_context_ragged_tails():
         compare(out, ref, "bf16", pairs=pairs, what="long ragged P=%d" % P)
 
 
+@pytest.mark.parametrize("G,L", [(7, 65536 - 5), (4, 131072), (16, 40000)])
+def test_one_long_sequence(G, L):
+    """One sequence with a long history: on the balanced schedule each of its
+    KV heads' histories is cut into tens of pieces (64 at 131072 tokens over
+    4 KV heads), which the merge folds in several thread subsets at once;
+    checked against the oracle on sampled heads."""
+    H_kv = 4 if G != 16 else 2
+    cfg = I.with_overrides(I.CONFIGS["long_ctx_bf16"], num_seqs=1, num_heads=H_kv * G,
+                           num_kv_heads=H_kv, block_size=16,
+                           num_blocks=L // 16 + 64, max_blocks_per_seq=L // 16 + 16)
+    inp = I.poison_unread(I.generate(cfg, lens=[L]))
+    d = upload(inp)
+    pairs = [(0, h) for h in range(0, H_kv * G, max(1, G // 3))]
+    ref = oracle_ref(inp, pairs)
+    out = run_decode(d)
+    compare(out, ref, "bf16", pairs=pairs, what="one sequence of %d tokens, G=%d" % (L, G))
+
+
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("S", [2048, 2049])
 def test_many_sequences_balanced_limit(S, D):
