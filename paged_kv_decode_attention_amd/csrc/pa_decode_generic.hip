@@ -50,8 +50,13 @@ __device__ __forceinline__ float group_sum(float x) {
 template <typename Tag, int D, int BS, int GT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeArgs a) {
     constexpr int E = Tag::kBytes;
-    constexpr int VEC = 16 / E;                  // elements per lane
-    constexpr int TG = D * E / 16;               // lanes per token row
+    // Each lane holds VEC elements of a token row: 16 bytes, or 32 of a
+    // float32 row at head_dim 128 and up, so that a row is at most 16 lanes
+    // wide up to head_dim 128 and a head's dot product is reduced with DPP
+    // moves within a row of lanes.
+    constexpr int VEC = (E == 4 && D >= 128) ? 8 : 16 / E;   // elements per lane
+    constexpr int W = VEC * E / 16;              // 16-byte words per lane and row
+    constexpr int TG = D / VEC;                  // lanes per token row
     constexpr int NG = kDecodeThreads / TG;      // token groups per workgroup
     constexpr int NW = kDecodeThreads / 64;
     constexpr int kMaxBlocks = 64;               // part_len <= 64 * BS
@@ -113,7 +118,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
         if (g < nh) {
             const char* qp = reinterpret_cast<const char*>(a.query) +
                              (((uint64_t)b * a.num_heads + head0 + g) * D + c * VEC) * E;
-            to_float(Tag(), load16(qp), qf[g]);
+#pragma unroll
+            for (int w = 0; w < W; ++w) to_float(Tag(), load16(qp + 16 * w), qf[g] + (16 / E) * w);
 #pragma unroll
             for (int e = 0; e < VEC; ++e) qf[g][e] *= a.scale_log2;
         } else {
@@ -134,30 +140,36 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
     // Each token group takes tokens t0, t0 + NG, ..., U at a time: their K and
     // V rows are loaded together (nontemporal: streamed once), then folded
     // in token order, so that U rows per lane are in flight instead of one
-    // (U = 8 float32 rows or 4 16-bit rows: 128 bytes of K and V per lane).
+    // (64 to 128 bytes of K and V per lane).
     // Loads past the partition's end re-read its last token and are not
     // folded.
     typedef __attribute__((address_space(1))) const u32x4 GlobalRow;
-    constexpr int U = VEC == 4 ? 8 : 4;    // 16-bit rows: half the registers' worth
+    constexpr int U = W == 1 && E == 4 ? 8 : 4;   // rows per lane in flight
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
     const char* vbase = reinterpret_cast<const char*>(a.value_cache);
     for (int t0 = t_begin + grp; t0 < t_end; t0 += NG * U) {
-        u32x4 kr[U], vr[U];
+        u32x4 kr[U][W], vr[U][W];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = min(t0 + u * NG, t_end - 1);
             const int pb = sm_pb[(t - t_begin) / BS];
             const uint64_t byte =
                 (kv_row(pb, kvh, t % BS, a.num_kv_heads, BS) * D + c * VEC) * E;
-            kr[u] = __builtin_nontemporal_load((GlobalRow*)(kbase + byte));
-            vr[u] = __builtin_nontemporal_load((GlobalRow*)(vbase + byte));
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                kr[u][w] = __builtin_nontemporal_load((GlobalRow*)(kbase + byte + 16 * w));
+                vr[u][w] = __builtin_nontemporal_load((GlobalRow*)(vbase + byte + 16 * w));
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (t0 + u * NG >= t_end) break;   // the same for every lane of a token group
             float kf[VEC], vf[VEC];
-            to_float(Tag(), kr[u], kf);
-            to_float(Tag(), vr[u], vf);
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                to_float(Tag(), kr[u][w], kf + (16 / E) * w);
+                to_float(Tag(), vr[u][w], vf + (16 / E) * w);
+            }
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
                 float dot = 0.0f;
