@@ -896,15 +896,16 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, 
     const int n = col0 + (lane & 15);
     const int q = lane >> 4;
     if (n >= ncols) return;
-    const float l = st.acc_l[0];
-    const float vs = a.out_scale;
+    // one division per column, then products (an IEEE division per element
+    // costs about ten instructions, and short histories write rows often)
+    const float scale = a.out_scale / st.acc_l[0];
     char* orow = reinterpret_cast<char*>(a.out) +
                  (column_row<kCols>(a, b, kvh, n) * D + 4 * q * VW) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float o[VW];
 #pragma unroll
-        for (int j = 0; j < VW; ++j) o[j] = bad ? __builtin_nanf("") : vs * (st.acc[j][i] / l);
+        for (int j = 0; j < VW; ++j) o[j] = bad ? __builtin_nanf("") : st.acc[j][i] * scale;
         if constexpr (VW >= 8) {
 #pragma unroll
             for (int j0 = 0; j0 < VW; j0 += 8) {
