@@ -140,9 +140,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
     // Each token group takes tokens t0, t0 + NG, ..., U at a time: their K and
     // V rows are loaded together (nontemporal: streamed once), then folded
     // in token order, so that U rows per lane are in flight instead of one
-    // (64 to 128 bytes of K and V per lane).
-    // Loads past the partition's end re-read its last token and are not
-    // folded.
+    // (64 to 128 bytes of K and V per lane).  Loads past the partition's end
+    // re-read its last token and are not folded.
     typedef __attribute__((address_space(1))) const u32x4 GlobalRow;
     constexpr int U = W == 1 && E == 4 ? 8 : 4;   // rows per lane in flight
     const char* kbase = reinterpret_cast<const char*>(a.key_cache);
@@ -161,6 +160,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
                 vr[u][w] = __builtin_nontemporal_load((GlobalRow*)(vbase + byte + 16 * w));
             }
         }
+        // At head_dim 128 and 256 a scheduling barrier keeps the batch's
+        // loads all issued before its fold, which the compiler would
+        // otherwise interleave (float32 rows: 47 and 52 % of 8 TB/s against
+        // 43 and 45); at 64 the registers it takes would cost a third
+        // wavefront per SIMD.
+        if constexpr (D >= 128) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (t0 + u * NG >= t_end) break;   // the same for every lane of a token group
