@@ -133,11 +133,12 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  * Supported: dtype f32, f16, bf16; head_dim 64, 128 or 256; block_size 8,
  * 16, 32 or 64; any gqa_group_size >= 1 (other head_dim / block_size values
  * return PA_ERR_UNSUPPORTED).  bf16/f16 run on the matrix-core kernel
- * (pa_decode_kernel tells) when gqa_group_size <= 16, or <= 32 at head_dim
- * 64 or 128, in one pass over each KV head's history; a larger group that
- * divides into at most 4 equal parts of that size runs as that many passes
- * (the fewest), each over its part of the heads; the rest, and f32, run on
- * the vector-ALU kernel.  Pointers to query/out/caches must be 16-byte aligned.
+ * (pa_decode_kernel tells): a group of <= 16 heads, or <= 32 at head_dim 64
+ * or 128, in one pass over each KV head's history; a larger group in the
+ * fewest passes of at most that many heads, ceil(G / passes) heads each and
+ * the remainder in the last, each pass over the whole history.  f32 runs on
+ * the vector-ALU kernel.  Pointers to query/out/caches must be 16-byte
+ * aligned.
  *
  * Device-data preconditions and what happens when they are broken:
  *   0 <= L_b <= max_context_len      otherwise out[b] is all NaN
@@ -330,12 +331,11 @@ int pa_paged_attention_verify(void* out, const void* query, const void* key_cach
  *   caches: the attention of each query over the dequantised history.  Same
  *   arguments, plus k_scale and v_scale (finite, > 0); dtype is that of query
  *   and out (bf16 or f16).  Supported: the shapes of the matrix-core kernel
- *   (head_dim 64/128/256, block_size 8/16/32/64, gqa_group_size <= 16, or
- *   <= 32 at head_dim 64/128, or a group that divides into at most 4 equal
- *   parts of that size -- except pa_decode_append_fp8/_i8, which take one
- *   pass only); other shapes return PA_ERR_UNSUPPORTED.  The workspace is
- *   sized by pa_decode_workspace_size
- *   with the query dtype.
+ *   (head_dim 64/128/256, block_size 8/16/32/64, any gqa_group_size; a group
+ *   of more than 16 heads, or 32 at head_dim 64/128, in several passes as
+ *   for pa_paged_attention_decode -- except pa_decode_append_fp8/_i8, which
+ *   take one pass only); other shapes return PA_ERR_UNSUPPORTED.  The
+ *   workspace is sized by pa_decode_workspace_size with the query dtype.
  * pa_decode_append_fp8 -- pa_decode_append over E4M3 caches: each newest
  *   token's key/value (query dtype) is quantised as it is stored.
  * pa_reshape_and_cache_fp8 -- pa_reshape_and_cache into E4M3 caches: key and

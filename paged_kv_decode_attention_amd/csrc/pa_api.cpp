@@ -208,10 +208,9 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
     const int split = pa::mfma_split(dtype, head_dim, block_size, group);
     if (use_balanced(split > 0, partition_size, num_seqs, max_context_len)) {
         // groups (per pass) of more than 16 heads take two 16-column tiles per slot
-        const size_t bal = balanced_layout(head_dim, group / split > pa::kMaxGroup
-                                                         ? 2 * pa::kMaxGroup
-                                                         : pa::kMaxGroup)
-                               .bytes;
+        const int slot_cols =
+            pa::mfma_pass_group(group, split) > pa::kMaxGroup ? 2 * pa::kMaxGroup : pa::kMaxGroup;
+        const size_t bal = balanced_layout(head_dim, slot_cols).bytes;
         if (bal > bytes) bytes = bal;
     }
     return bytes;
@@ -293,8 +292,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
         return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
     if (q8 && !use_mfma)
         return fail(PA_ERR_UNSUPPORTED, "8-bit caches are served by the matrix-core kernel only "
-                    "(bf16/f16 queries, head_dim 64/128/256, block_size 8/16/32/64, a group that "
-                    "splits into equal passes of <= 16 heads, or <= 32 at head_dim 64/128)");
+                    "(bf16/f16 queries, head_dim 64/128/256, block_size 8/16/32/64)");
     // a row map held in memory is read by the fixed schedule's kernels only
     const bool balanced = table_rows == nullptr &&
                           use_balanced(use_mfma, partition_size, num_seqs, max_context_len);
@@ -306,7 +304,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
                                                        max_context_len);
     // a group too large for one pass runs as `split` passes of smaller ones
     const int kv_split = use_mfma ? split : 1;
-    const int pass_group = gqa_group_size / kv_split;
+    const int pass_group = pa::mfma_pass_group(gqa_group_size, kv_split);
     // the passes of a split group all read the newest token, so its append
     // runs in a kernel of its own first -- built for 16-bit and f32 rows only
     if (append && q8 && kv_split > 1)
@@ -358,6 +356,7 @@ static int decode_impl(void* out, const void* query, const void* new_key,
     a.group = pass_group;
     a.kv_split = kv_split;
     a.kv_heads_mem = num_kv_heads;
+    a.group_mem = gqa_group_size;
     a.head_dim = head_dim;
     a.block_size = block_size;
     a.num_blocks = num_blocks;

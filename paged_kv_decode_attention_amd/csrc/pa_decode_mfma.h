@@ -416,12 +416,12 @@ __device__ __forceinline__ uint32_t lane_voff(int n, int q) {
     return Kv::k8 ? (uint32_t)(4 * q * D + VW * n) : (uint32_t)(4 * q * D + VW * n) * 2;
 }
 
-// [S, H] row of column n of decode row b (KV head kvh): query head kvh G + n
-// of row b, or with verify columns (kCols) the (query row, head) pair the
-// column stands for.
+// [S, H] row of column n of decode row b (KV head kvh): query head
+// col_head(kvh, n) of row b, or with verify columns (kCols) the (query row,
+// head) pair the column stands for.
 template <bool kCols>
 __device__ __forceinline__ uint64_t column_row(const DecodeArgs& a, int b, int kvh, int n) {
-    return kCols ? col_row(a, b, kvh, n) : (uint64_t)b * a.num_heads + kvh * a.group + n;
+    return kCols ? col_row(a, b, kvh, n) : (uint64_t)b * a.num_heads + col_head(a, kvh, n);
 }
 
 // Query operand: Q[column n][d] for the d each MFMA step contracts (see the
@@ -705,10 +705,11 @@ __device__ __forceinline__ void tile_columns(const DecodeArgs& a, int b, int kvh
                                              int ntok, int L, int t_end, u32x4* qop,
                                              int* t_col) {
     const int G = a.group;
+    const int ncols = ntok * pass_cols(a, kvh);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int col = t * 16 + n;
-        load_query<Kv, kCols, D>(a, b, kvh, col, q, ntok * G, qop + t * Dim<D>::KD);
+        load_query<Kv, kCols, D>(a, b, kvh, col, q, ncols, qop + t * Dim<D>::KD);
         // verify columns: column col attends the L - (ntok - 1 - col / G)
         // oldest tokens
         t_col[t] = kCols ? min(t_end, L - (ntok - 1 - col / G)) : t_end;
@@ -733,7 +734,6 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
     L = __builtin_amdgcn_readfirstlane(L);
     c0 = __builtin_amdgcn_readfirstlane(c0);
     c1 = __builtin_amdgcn_readfirstlane(c1);
-    const int G = a.group;
     const int ntok = kCols ? row_tokens<kRows>(a, b) : 1;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -786,8 +786,8 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
         stage_acc<D>(sm.o + col * OS, q, st[t]);
     }
     const bool any_bad = __syncthreads_or(bad);
-    finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, NC, NC * OS, OS, b, kvh, 0, ntok * G, any_bad,
-                        part);
+    finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, NC, NC * OS, OS, b, kvh, 0,
+                        ntok * pass_cols(a, kvh), any_bad, part);
     __syncthreads();   // LDS is reused by the next segment
 }
 
@@ -800,7 +800,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
     const int kvh = blockIdx.x;
     const int b = blockIdx.y;
     const int part = blockIdx.z;
-    const int ncols = row_tokens<kRows>(a, b) * a.group;
+    const int ncols = row_tokens<kRows>(a, b) * pass_cols(a, kvh);
     const int L = a.context_lens[b];
     if (L < 0 || L > a.max_context_len) {
         if (part == 0) fill_cols<Tag>(a, b, kvh, 0, ncols, __builtin_nanf(""));
@@ -1132,7 +1132,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
         if (!starts_before && !ends_after) {
 #pragma unroll
             for (int t = 0; t < NT; ++t)
-                write_rows<Tag, kCols, D>(a, b, kvh, ntok * a.group, t * 16, st[t], bad != 0);
+                write_rows<Tag, kCols, D>(a, b, kvh, ntok * pass_cols(a, kvh), t * 16, st[t],
+                                          bad != 0);
         } else {
             const int p = 2 * wave + (starts_before ? 0 : 1);
 #pragma unroll
@@ -1178,7 +1179,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
         const bool head = xf < xb;            // continues from the previous range
         const bool tail = xl >= xe;           // continues into the next range
         const int ntok = ntok_of(b);
-        const int ncols = ntok * a.group;
+        const int ncols = ntok * pass_cols(a, kvh);
         if (!head && !tail) {
             finalize_edges<Tag, kCols, D, NT>(a, edge, mask, b, kvh, ncols, bad != 0, nullptr,
                                               nullptr);

@@ -13,18 +13,17 @@ bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group) {
            group >= 1 && (group <= kMaxGroup || (group <= 2 * kMaxGroup && head_dim <= 128));
 }
 
-// A larger group is split into the fewest passes of equal groups that one
-// pass serves, at most kMaxSplit: each pass reads the KV head's history once
-// more, still cheaper than the vector-ALU kernel, which re-reads it for
-// every 8 heads.  (A group with no such split -- a prime above 32 -- stays
-// on the vector-ALU kernel.)
-constexpr int kMaxSplit = 4;
-
+// A larger group is split into passes over the KV head's history, each
+// serving at most the columns one pass holds (16, or 32 at head_dim 64/128):
+// the fewest such passes, with heads dealt as evenly as ceil() allows (the
+// last pass may hold fewer).  Each pass reads the history once more, still
+// less often than the vector-ALU kernel, which re-reads it for every 8 heads.
 int mfma_split(pa_dtype dt, int head_dim, int block_size, int group) {
-    if (group < 1) return 0;
-    for (int sp = 1; sp <= kMaxSplit && sp <= group; ++sp)
-        if (group % sp == 0 && mfma_supported(dt, head_dim, block_size, group / sp)) return sp;
-    return 0;
+    if (group < 1 || !mfma_supported(dt, head_dim, block_size, 1)) return 0;
+    if (mfma_supported(dt, head_dim, block_size, group)) return 1;
+    const int cap = head_dim <= 128 ? 2 * kMaxGroup : kMaxGroup;
+    const int pg = mfma_pass_group(group, (group + cap - 1) / cap);
+    return (group + pg - 1) / pg;   // every pass, the last included, holds a head
 }
 
 // Workgroups of the balanced schedule per compute unit: one (4 wavefronts,

@@ -22,12 +22,31 @@ __device__ __forceinline__ int row_tokens(const DecodeArgs& a, int b) {
     return __builtin_amdgcn_readfirstlane(((const ConstRow*)a.row_tokens)[b]);
 }
 
+// Columns (query heads) of KV head kvh: the group, or with a group split
+// into passes of a.group heads (kv_split virtual heads per cache head) the
+// heads its pass holds -- a.group, fewer in the last pass of a group that
+// does not split evenly.
+__device__ __forceinline__ int pass_cols(const DecodeArgs& a, int kvh) {
+    if (a.kv_split == 1) return a.group;
+    return min(a.group, a.group_mem - (kvh % a.kv_split) * a.group);
+}
+
+// Query head of column n < pass_cols(a, kvh) of KV head kvh: kvh G + n, or
+// with a split group, head j G' + n of cache head kvh / kv_split's group
+// (j = kvh % kv_split, G' = a.group heads per pass).
+__device__ __forceinline__ int col_head(const DecodeArgs& a, int kvh, int n) {
+    if (a.kv_split == 1) return kvh * a.group + n;
+    const int h = kvh / a.kv_split;
+    return h * a.group_mem + (kvh - h * a.kv_split) * a.group + n;
+}
+
 // [S, H] row index (of out, query and the fixed schedule's partition states)
 // of column n of decode row b, KV head kvh: query row b + n / G, head
-// kvh G + n % G.  Without a row map n < G, so this is b H + kvh G + n.
+// col_head(kvh, n % G).  Without a row map n < G, so this is
+// b H + col_head(kvh, n).  (Row maps come without a split: G = a.group.)
 __device__ __forceinline__ uint64_t col_row(const DecodeArgs& a, int b, int kvh, int n) {
     const int t = n / a.group;
-    return (uint64_t)(b + t) * a.num_heads + kvh * a.group + (n - t * a.group);
+    return (uint64_t)(b + t) * a.num_heads + col_head(a, kvh, n - t * a.group);
 }
 
 // Columns n0 .. n0 + ncols - 1 of decode row b, KV head kvh, set to one value

@@ -40,14 +40,16 @@ struct DecodeArgs {
     float* ws_lse;             // [S, H, num_parts] float32 (log2 units)
     float* ws_out;             // [S, H, num_parts, D] float32
     int* ws_meta;              // balanced schedule: [num_wg][4] tail-segment records
-    // num_kv_heads and group are the kernel's (virtual) KV heads and their
-    // query heads: a group too large for one pass of the matrix-core kernel
-    // is served as kv_split passes, KV head h standing for kv_split virtual
-    // heads h kv_split + j of group / kv_split consecutive query heads each
-    // (query head = virtual head * group + column, as without a split); the
-    // caches are addressed with KV head virtual / kv_split of kv_heads_mem.
+    // num_kv_heads and group are the kernel's (virtual) KV heads and the
+    // query heads each serves at most: a group of group_mem heads too large
+    // for one pass of the matrix-core kernel is served as kv_split passes,
+    // KV head h standing for kv_split virtual heads h kv_split + j, pass j
+    // holding query heads h group_mem + j group + n for n < group (fewer in
+    // the last pass when group_mem is not a multiple of group: pass_cols);
+    // the caches are addressed with KV head virtual / kv_split of
+    // kv_heads_mem.  Without a split kv_split = 1, group = group_mem.
     int num_seqs, num_heads, num_kv_heads, group, head_dim, block_size;
-    int kv_split, kv_heads_mem;
+    int kv_split, kv_heads_mem, group_mem;
     int num_blocks, max_blocks_per_seq, max_context_len;
     int part_len;              // tokens per context partition (fixed schedule)
     int num_parts;             // ceil(max_context_len / part_len)
@@ -113,9 +115,12 @@ enum KernelKind { kAuto = 0, kGeneric = 1, kMfma = 2 };
 
 bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group);
 // Passes the matrix-core kernel serves a group of `group` query heads per KV
-// head in (1: directly; the fewest passes of equal, small enough groups
-// otherwise), or 0 if it cannot.
+// head in (1: directly; otherwise the fewest passes of at most 16 heads, 32
+// at head_dim 64/128), or 0 if it cannot (dtype or shape).
 int mfma_split(pa_dtype dt, int head_dim, int block_size, int group);
+// Query heads per pass of a group served in `split` passes: ceil(group /
+// split); the last pass holds the remainder, at least one head.
+inline int mfma_pass_group(int group, int split) { return (group + split - 1) / split; }
 // Workgroups of the matrix-core kernel resident per compute unit.
 int mfma_workgroups_per_cu(int head_dim);
 hipError_t launch_decode_mfma(const DecodeArgs& a, pa_dtype dt, hipStream_t s);

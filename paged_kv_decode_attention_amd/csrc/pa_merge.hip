@@ -19,7 +19,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_fixed(DecodeArgs a) {
     const int L = a.context_lens[b];
     if (L <= a.part_len || L > a.max_context_len) return;
     const int nparts = (L + a.part_len - 1) / a.part_len;
-    merge_pieces<Tag>(a, b, kvh, row_tokens(a, b) * a.group, nparts);
+    merge_pieces<Tag>(a, b, kvh, row_tokens(a, b) * pass_cols(a, kvh), nparts);
 }
 
 // Balanced schedule.  Workgroup w merges the segment whose first piece
@@ -91,7 +91,9 @@ __global__ __launch_bounds__(NC * D / 4) void merge_balanced(
     // every range is non-empty when T >= num_wg: pieces are then [w][1],
     // [w+1][0], ..., [w1][0]
     const int npieces = w1 - w + 1;
-    const bool active = g < ntok * G;    // g: column of the decode row
+    // g: column of the decode row (G columns per query row, fewer in the
+    // last pass of a split group)
+    const bool active = g < ntok * (a.kv_split == 1 ? G : pass_cols(a, kvh));
     if (T >= nwg && npieces > kSpec && nsub > 1) {
         float M = -INFINITY, den = 0.0f;
         f32x4 num = {0.f, 0.f, 0.f, 0.f};

@@ -128,6 +128,24 @@ def test_workspace_size_arithmetic(lib):
     assert f(2, 4, 2, 128, 16, 128, 40, ops.PA_BF16) == ctypes.c_size_t(-1).value
 
 
+def test_balanced_workspace_follows_the_pass_width(lib):
+    """Balanced-schedule slots hold 16 columns, or 32 when a pass serves more
+    than 16 heads; the pass width is ceil(G / passes) with the fewest passes
+    of <= 32 heads (<= 16 at head_dim 256)."""
+    f = lib.pa_decode_workspace_size
+    up = lambda x: (x + 255) // 256 * 256
+    W = 1024                                   # workgroups the layout is sized for
+
+    def bal(cols, D):
+        rows = W * 2 * cols
+        return up(rows * 4) + up(rows * D * 4) + up(W * 4 * 4)
+    # one sequence of 64 tokens: the fixed layout needs nothing, so the size
+    # is the balanced layout's
+    for G, D, cols in ((7, 128, 16), (24, 128, 32), (33, 128, 32), (37, 128, 32),
+                       (96, 128, 32), (17, 256, 16), (37, 256, 16), (40, 64, 32)):
+        assert f(1, G, 1, D, 16, 64, 0, ops.PA_BF16) == bal(cols, D), (G, D)
+
+
 def test_partition_heuristic_is_valid(lib):
     for S, H_kv, BS, L in ((64, 4, 16, 4096), (32, 32, 16, 4096), (4, 8, 32, 131072),
                            (128, 8, 16, 8192), (4, 2, 16, 64), (1, 1, 32, 1)):
@@ -180,14 +198,15 @@ def test_8bit_entry_points_reject_on_host(lib, fmt):
                  f32(a["ks"]), f32(a["vs"]), 0, vp(FAKE), ctypes.c_size_t(1 << 30), vp(0))
     assert call(ks=-1.0) == INVALID
     assert call(vs=float("nan")) == INVALID
-    assert call(G=37, H=148) == UNSUPPORTED                    # 37: no split into <= 4 passes
+    assert call(G=37, H=148, S=0) == OK                        # 37: passes of 19 and 18 heads
+    assert call(G=160, H=160, H_kv=1, S=0) == OK               # 5 passes of 32
     # the fused 8-bit append takes groups of one pass only
     a8 = getattr(lib, "pa_decode_append_" + fmt)
     assert a8(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
               2, 64, 1, 64, 128, 16, 64, 16, 256, f32(0.1), ops.PA_BF16, f32(0.5), f32(0.5), 0,
               vp(FAKE), ctypes.c_size_t(1 << 30), vp(0)) == UNSUPPORTED
     assert b"fused append" in lib.pa_last_error()
-    assert call(G=33, H=132, S=0) == OK                        # 33 = 3 passes of 11 heads
+    assert call(G=33, H=132, S=0) == OK                        # 33: passes of 17 and 16 heads
     assert call(dtype=ops.PA_F32) == UNSUPPORTED               # f32 queries: vector-ALU only
     assert call(S=0) == OK
     # the fused append needs the new key and value
@@ -205,16 +224,18 @@ def test_decode_kernel_choice(lib):
     assert f(64, 64, 16, ops.PA_F16) == MFMA
     assert f(128, 8, 7, ops.PA_BF16) == MFMA
     assert f(256, 16, 7, ops.PA_BF16) == MFMA
-    # groups beyond one pass: equal passes of <= 32 heads (<= 16 at head_dim 256)
+    # groups beyond one pass: the fewest passes of <= 32 heads (<= 16 at
+    # head_dim 256), the last holding the remainder -- every bf16/f16 group
     assert f(128, 16, 64, ops.PA_BF16) == MFMA
     assert f(64, 16, 48, ops.PA_F16) == MFMA
     assert f(256, 16, 32, ops.PA_BF16) == MFMA
-    assert f(128, 16, 37, ops.PA_BF16) == GEN                  # prime: no split into <= 4 passes
-    assert f(128, 16, 160, ops.PA_BF16) == GEN                 # 5 passes of 32: too many
-    assert f(256, 16, 17, ops.PA_BF16) == GEN
+    assert f(128, 16, 37, ops.PA_BF16) == MFMA       # passes of 19 and 18
+    assert f(128, 16, 160, ops.PA_BF16) == MFMA      # 5 passes of 32
+    assert f(256, 16, 17, ops.PA_BF16) == MFMA       # passes of 9 and 8
+    assert f(256, 8, 257, ops.PA_F16) == MFMA        # 17 passes of 16, the last of 1
     assert f(128, 16, 17, ops.PA_BF16) == MFMA       # groups of 17..32: two column tiles
     assert f(64, 8, 32, ops.PA_F16) == MFMA
-    assert f(128, 16, 33, ops.PA_BF16) == MFMA       # 33 = three passes of 11
+    assert f(128, 16, 33, ops.PA_BF16) == MFMA       # passes of 17 and 16
     assert f(256, 16, 18, ops.PA_BF16) == MFMA       # two passes of 9 at head_dim 256
     assert f(128, 16, 7, ops.PA_F32) == GEN
     assert f(96, 16, 7, ops.PA_BF16) == UNSUPPORTED
@@ -225,7 +246,8 @@ def test_decode_kernel_choice(lib):
         assert f(128, 16, 7, ops.PA_BF16) == GEN
         lib.pa_debug_select_kernel(2)
         assert f(128, 16, 7, ops.PA_BF16) == MFMA
-        assert f(128, 8, 37, ops.PA_BF16) == UNSUPPORTED
+        assert f(128, 8, 37, ops.PA_BF16) == MFMA
+        assert f(128, 8, 7, ops.PA_F32) == UNSUPPORTED      # f32: vector-ALU only
     finally:
         lib.pa_debug_select_kernel(prev)
 

@@ -125,6 +125,7 @@ def test_tiny_config_cache_write():
     ("tiny_fp32", ops.KERNEL_AUTO, 0),
     ("qwen7b_gqa_bf16:mqa64", ops.KERNEL_AUTO, 0),   # 64 heads on 1 KV head: two passes
     ("qwen7b_gqa_bf16:mqa64", ops.KERNEL_MFMA, 256),
+    ("qwen7b_gqa_bf16:g37", ops.KERNEL_AUTO, 0),     # 37 heads per KV head: 19 + 18
 ])
 def test_decode_append_equals_write_then_decode(name, kernel, partition_size):
     """The fused step gives bit for bit the caches and output of
@@ -133,6 +134,8 @@ def test_decode_append_equals_write_then_decode(name, kernel, partition_size):
     cfg = I.CONFIGS[base]
     if variant == "mqa64":
         cfg = I.with_overrides(cfg, num_seqs=16, num_heads=64, num_kv_heads=1)
+    elif variant == "g37":
+        cfg = I.with_overrides(cfg, num_seqs=16, num_heads=74, num_kv_heads=2)
     inp = I.generate(cfg, new_tokens_at="last")
     prev = ops.select_kernel(kernel)
     try:

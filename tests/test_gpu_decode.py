@@ -57,7 +57,12 @@ SMALL_CASES = [
     ("f16", 2, 48, 64, 32, ops.KERNEL_MFMA),        # two passes of 24
     ("bf16", 1, 32, 256, 8, ops.KERNEL_MFMA),       # two passes of 16 at head_dim 256
     ("bf16", 2, 96, 128, 16, ops.KERNEL_MFMA),      # three passes of 32
-    ("bf16", 1, 37, 128, 16, ops.KERNEL_AUTO),      # 37 heads: vector-ALU kernel
+    ("bf16", 1, 37, 128, 16, ops.KERNEL_AUTO),      # passes of 19 and 18 heads
+    ("f16", 2, 33, 64, 16, ops.KERNEL_MFMA),        # passes of 17 and 16
+    ("bf16", 1, 37, 256, 16, ops.KERNEL_MFMA),      # passes of 13, 13 and 11 at head_dim 256
+    ("bf16", 1, 17, 256, 8, ops.KERNEL_AUTO),       # passes of 9 and 8, block size 8
+    ("bf16", 2, 70, 128, 32, ops.KERNEL_MFMA),      # passes of 24, 24 and 22
+    ("f16", 1, 101, 64, 64, ops.KERNEL_AUTO),       # passes of 26, 26, 26 and 23
     ("bf16", 1, 64, 128, 16, ops.KERNEL_GENERIC),
     ("f16", 2, 3, 64, 16, ops.KERNEL_AUTO),         # head_dim 64: matrix-core kernel
     ("bf16", 2, 5, 64, 32, ops.KERNEL_GENERIC),
@@ -275,6 +280,28 @@ def test_one_long_sequence(G, L):
     ref = oracle_ref(inp, pairs)
     out = run_decode(d)
     compare(out, ref, "bf16", pairs=pairs, what="one sequence of %d tokens, G=%d" % (L, G))
+
+
+@pytest.mark.parametrize("G,D", [(37, 128), (37, 256), (100, 64)])
+def test_uneven_passes_on_the_bench_batch(G, D):
+    """A group that splits into unequal passes (19 + 18 heads at head_dim 128,
+    13 + 13 + 11 at 256, 4 x 25 at 64 -- even, for contrast) on the bench
+    batch's 64 histories of 512 to 4096 tokens: every history is cut across
+    workgroups and merged.  Sampled against the oracle at the heads on each
+    side of every pass boundary."""
+    cfg = I.with_overrides(I.CONFIGS["qwen7b_gqa_bf16"], num_heads=2 * G, num_kv_heads=2,
+                           head_dim=D)
+    inp = I.poison_unread(I.generate(cfg))
+    d = upload(inp)
+    cap = 16 if D == 256 else 32
+    passes = -(-G // cap)
+    pg = -(-G // passes)
+    heads = sorted({h for j in range(passes) for h in (j * pg, min(G, (j + 1) * pg) - 1)})
+    rng = np.random.default_rng(G + D)
+    pairs = [(int(b), kvh * G + h) for b in rng.choice(64, 12, replace=False)
+             for kvh in range(2) for h in heads]
+    out = run_decode(d)
+    compare(out, oracle_ref(inp, pairs), "bf16", pairs=pairs, what="G=%d D=%d" % (G, D))
 
 
 @pytest.mark.parametrize("D", [128, 256])

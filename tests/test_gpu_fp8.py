@@ -85,8 +85,10 @@ CASES = [("bf16", 2, 7, 128, 16), ("bf16", 2, 4, 128, 32), ("f16", 2, 4, 128, 16
          ("bf16", 2, 7, 64, 16), ("f16", 2, 4, 64, 32), ("bf16", 1, 16, 64, 64),
          ("bf16", 2, 7, 256, 16), ("f16", 1, 8, 256, 32), ("bf16", 2, 7, 128, 8),
          ("f16", 2, 4, 64, 8), ("bf16", 1, 32, 128, 16), ("f16", 2, 20, 64, 32),
-         # groups split into passes: 2 x 32 heads, 2 x 16 at head_dim 256
-         ("bf16", 1, 64, 128, 16), ("f16", 1, 32, 256, 16)]
+         # groups split into passes: 2 x 32 heads, 2 x 16 at head_dim 256,
+         # uneven: 19 + 18 heads, and 13 + 13 + 11 at head_dim 256
+         ("bf16", 1, 64, 128, 16), ("f16", 1, 32, 256, 16), ("bf16", 1, 37, 128, 16),
+         ("f16", 1, 37, 256, 32)]
 
 
 @pytest.mark.parametrize("partition_size", [0, 64, 256])
