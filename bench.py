@@ -503,9 +503,10 @@ def shape_sweep(args, dev):
     by the library's cache writes), pool replicas rotated so the last-level cache
     cannot hold the working set; K calls replayed from a HIP graph, HIP
     events around each replay.  Then the shapes the vector-ALU kernel serves
-    (the same batch): fp32 at each head dim, and bf16 with more query heads
-    per KV head than the matrix-core kernel takes (64 at head_dim 128, 32 at
-    head_dim 256: one KV head)."""
+    (the same batch): fp32 at each head dim; and bf16 with more query heads
+    per KV head than one matrix-core pass takes, which run as several passes
+    (64 on one KV head at head_dim 128, 32 at 256, and 37 per KV head, two
+    unequal passes, at 128)."""
     import numpy as np
     import torch
     from paged_kv_decode_attention_amd import inputs as I
@@ -581,7 +582,10 @@ def shape_sweep(args, dev):
                                                max_context_len=max_ctx, out=out, workspace=ws)
             t = timed(call)
             alg = int(lens.sum()) * H_kv * D * e * 2
-            row = {"head_dim": D, "block_size": BS, "heads": "%d/%d" % (H, H_kv),
+            cap = 16 if D == 256 else 32
+            passes = -(-G // cap) if mfma else 1     # the matrix-core kernel's passes
+            heads = "%d/%d" % (H, H_kv) + (" (%d passes)" % passes if passes > 1 else "")
+            row = {"head_dim": D, "block_size": BS, "heads": heads, "kv_passes": passes,
                    "kv": {"fp8": "fp8 e4m3", "int8": "int8"}.get(kv, kv),
                    "kernel": "matrix-core, balanced" if mfma else "vector-ALU, partitions",
                    "decode_us": t * 1e6, "alg_bytes": alg, "achieved_gbps": alg / t / 1e9,
@@ -602,6 +606,8 @@ def shape_sweep(args, dev):
         run(128, 16, 64, 1, torch.bfloat16, ("bf16",))
     if "256" in args.sweep_head_dims.split(","):
         run(256, 16, 32, 1, torch.bfloat16, ("bf16",))
+    if "128" in args.sweep_head_dims.split(","):
+        run(128, 16, 148, 4, torch.bfloat16, ("bf16", "fp8"))
     if args.sweep_out:
         L = ["# Decode shape sweep: block size x head dim x KV format (64 sequences, "
              "L~U[512,4096] seed 2; 28/4 heads unless the row says otherwise)", "",
@@ -615,7 +621,8 @@ def shape_sweep(args, dev):
                 r["decode_us"], r["achieved_gbps"] / 1e3, 100 * r["frac"],
                 r["decode_tokens_per_s"]))
         L += ["", "Algorithmic bytes: sum_b L_b x KV heads x head_dim x element bytes (4 for "
-              "fp32, 2 for bf16, 1 for FP8 E4M3 and INT8) x 2 (K and V).  "
+              "fp32, 2 for bf16, 1 for FP8 E4M3 and INT8) x 2 (K and V), read once; a "
+              "group run in several passes reads them once per pass.  "
               "Timing: K decode calls replayed from a HIP graph, HIP events around each "
               "replay, mean of 3."]
         with open(args.sweep_out, "w") as fh:

@@ -9,8 +9,10 @@
 // D*E/16 lanes wide (16 bytes per lane, one coalesced load); the workgroup
 // holds 256/(D*E/16) such token groups, which walk the partition's tokens in
 // an interleaved order.  Each token group keeps its own online-softmax state
-// per head ([MiniPaged-Qwen] §5.2 applied one token at a time):
-//   m' = max(m, s),  l' = l 2^(m-m') + 2^(s-m'),  o' = o 2^(m-m') + 2^(s-m') v
+// per head ([MiniPaged-Qwen] §5.2 applied to the U tokens a group loads at
+// once):
+//   m' = max(m, max_u s_u),  l' = l 2^(m-m') + sum_u 2^(s_u-m'),
+//   o' = o 2^(m-m') + sum_u 2^(s_u-m') v_u
 // and the groups' states are merged at the end (same update rule applied to
 // whole states), first across lanes, then across wavefronts in LDS.
 #include <type_traits>
@@ -47,8 +49,27 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// float32 rows of a workgroup of 8 heads are folded a batch at a time
+// (below) at head_dim 64 and 256.  Measured on the bench batch: 88.8 vs
+// 100.4 us at 64 (7 heads), 299 vs 306 at 256.  At 128 the per-token update
+// is faster (163.5 vs 170 us): the block fold's registers leave one
+// wavefront per SIMD or need a scheduling barrier per head.  With 4 heads
+// or fewer it is slower (76.5 vs 68.4 us at head_dim 64, 4 heads): too few
+// independent heads to cover the latency of each head's chain of scores,
+// maximum and exponentials.
+template <typename Tag, int D, int GT>
+constexpr bool block_fold() { return Tag::kBytes == 4 && GT >= 8 && D != 128; }
+
+// Wavefronts per SIMD the register allocation must leave room for: with the
+// block fold three at head_dim 64 (at most 168 registers), two at 256;
+// otherwise no bound (0: the compiler's default).
+template <typename Tag, int D, int GT>
+constexpr int generic_waves() { return !block_fold<Tag, D, GT>() ? 0 : D == 64 ? 3 : 2; }
+
 template <typename Tag, int D, int BS, int GT>
-__global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads)
+__attribute__((amdgpu_waves_per_eu(generic_waves<Tag, D, GT>(), 0))) void decode_generic_kernel(
+    DecodeArgs a) {
     constexpr int E = Tag::kBytes;
     // Each lane holds VEC elements of a token row: 16 bytes, or 32 of a
     // float32 row at head_dim 128 and up, so that a row is at most 16 lanes
@@ -166,28 +187,90 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_generic_kernel(DecodeAr
         // 43 and 45); at 64 the registers it takes would cost a third
         // wavefront per SIMD.
         if constexpr (D >= 128) __builtin_amdgcn_sched_barrier(0);
+        // float32 rows of a workgroup of 8 heads are folded a batch at a
+        // time (see block_fold): the per-token rescale of every head's
+        // accumulators is what their vector-ALU time goes to.  Otherwise
+        // each token's update is applied on its own, which also skips a
+        // short history's absent tokens (the latency case: a few tokens per
+        // partition).
+        if constexpr (block_fold<Tag, D, GT>()) {
+            // float32 rows need no conversion (the batch's rows are the loaded
+            // registers themselves); which of its tokens lie inside the
+            // partition is the same in every lane of a token group.
+            float kf[U][VEC], vf[U][VEC];
+            bool live[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (t0 + u * NG >= t_end) break;   // the same for every lane of a token group
-            float kf[VEC], vf[VEC];
+            for (int u = 0; u < U; ++u) {
+                live[u] = t0 + u * NG < t_end;
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-                to_float(Tag(), kr[u][w], kf + (16 / E) * w);
-                to_float(Tag(), vr[u][w], vf + (16 / E) * w);
+                for (int w = 0; w < W; ++w) {
+                    to_float(Tag(), kr[u][w], kf[u] + (16 / E) * w);
+                    to_float(Tag(), vr[u][w], vf[u] + (16 / E) * w);
+                }
             }
+            // Head by head, the batch's U scores first, then one update of
+            // the head's state for all of them (the block update above):
+            // one rescale per batch instead of one per token.  Tokens past
+            // the partition (in a later token group of the wavefront) score
+            // -inf and weigh 0; token u = 0 is always inside, so m' is
+            // finite.
 #pragma unroll
             for (int g = 0; g < GT; ++g) {
-                float dot = 0.0f;
+                float sc[U];
+                float m_new = m[g];
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) dot += qf[g][e] * kf[e];
-                dot = group_sum<TG>(dot);
-                const float m_new = fmaxf(m[g], dot);
+                for (int u = 0; u < U; ++u) {
+                    float dot = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) dot += qf[g][e] * kf[u][e];
+                    dot = group_sum<TG>(dot);
+                    sc[u] = live[u] ? dot : -INFINITY;
+                    m_new = fmaxf(m_new, sc[u]);
+                }
                 const float al = fast_exp2(m[g] - m_new);
-                const float pe = fast_exp2(dot - m_new);
-                l[g] = l[g] * al + pe;
+                float ls = 0.0f;
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) o[g][e] = o[g][e] * al + pe * vf[e];
+                for (int e = 0; e < VEC; ++e) o[g][e] *= al;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float pe = fast_exp2(sc[u] - m_new);
+                    ls += pe;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) o[g][e] += pe * vf[u][e];
+                }
+                l[g] = l[g] * al + ls;
                 m[g] = m_new;
+                // one head at a time: interleaving the next head's dot
+                // products with this update takes registers head_dim 256
+                // does not have
+                if constexpr (D >= 128) __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // (16-bit rows are converted one token at a time: converting the
+            // whole batch first would hold U more rows of floats.)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (t0 + u * NG >= t_end) break;   // the same for every lane of a token group
+                float kf[VEC], vf[VEC];
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    to_float(Tag(), kr[u][w], kf + (16 / E) * w);
+                    to_float(Tag(), vr[u][w], vf + (16 / E) * w);
+                }
+#pragma unroll
+                for (int g = 0; g < GT; ++g) {
+                    float dot = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) dot += qf[g][e] * kf[e];
+                    dot = group_sum<TG>(dot);
+                    const float m_new = fmaxf(m[g], dot);
+                    const float al = fast_exp2(m[g] - m_new);
+                    const float pe = fast_exp2(dot - m_new);
+                    l[g] = l[g] * al + pe;
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) o[g][e] = o[g][e] * al + pe * vf[e];
+                    m[g] = m_new;
+                }
             }
         }
     }

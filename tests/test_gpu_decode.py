@@ -73,6 +73,9 @@ SMALL_CASES = [
     ("f32", 2, 1, 64, 16, ops.KERNEL_AUTO),
     ("f32", 2, 4, 128, 32, ops.KERNEL_GENERIC),
     ("f32", 1, 12, 128, 16, ops.KERNEL_GENERIC),
+    ("f32", 2, 7, 64, 16, ops.KERNEL_AUTO),         # 8-head workgroups: block fold
+    ("f32", 1, 8, 256, 32, ops.KERNEL_AUTO),
+    ("f32", 1, 13, 64, 8, ops.KERNEL_AUTO),         # block fold + a 5-head workgroup
     # block sizes 8 and 64, head_dim 256
     ("bf16", 2, 7, 128, 64, ops.KERNEL_MFMA),
     ("f16", 2, 4, 128, 8, ops.KERNEL_AUTO),         # block size 8: matrix-core kernel
