@@ -75,7 +75,11 @@ const char* pa_last_error(void);
 
 /*
  * pa_decode_partition_size -- context partition length (tokens) the decode
- * call uses for these sizes when called with partition_size = 0.
+ * call uses for these sizes when called with partition_size = 0 and it runs
+ * on partitions: a small call (histories of at most 512 tokens, at most 8192
+ * (sequence, KV head pass, 32-token chunk) items) always does, with one
+ * partition covering max_context_len; otherwise the vector-ALU kernel does,
+ * and the matrix-core kernel uses its balanced schedule (no partitions).
  *
  * Long histories are split into partitions that are reduced independently and
  * merged by log-sum-exp ([MiniPaged-Qwen] §10.2 (2): shards reduced locally,
@@ -542,6 +546,9 @@ int pa_debug_select_kernel(int kind);
  * kernel, 2 = matrix-core kernel.  PA_ERR_UNSUPPORTED when no kernel serves
  * the shape (or the matrix-core kernel is forced and does not),
  * PA_ERR_INVALID_ARG for an unknown dtype or gqa_group_size < 1.  Host only.
+ * (Under the automatic setting a float32 call small enough for one
+ * partition -- pa_decode_partition_size covering max_context_len -- runs on
+ * the vector-ALU kernel, whatever this returns for its shape.)
  */
 int pa_decode_kernel(int head_dim, int block_size, int gqa_group_size, pa_dtype dtype);
 

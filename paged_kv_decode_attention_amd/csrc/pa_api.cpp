@@ -74,6 +74,26 @@ bool valid_partition(int P, int block_size) {
     return P > 0 && P % 32 == 0 && P % block_size == 0 && P <= 64 * block_size;
 }
 
+// A small call -- histories of at most 16 chunks (512 tokens) and at most
+// 8192 (sequence, KV head pass, chunk) work items -- runs on the fixed
+// schedule with one partition covering every history: one launch, no merge
+// kernel, one workgroup per (sequence, KV head pass).  The balanced
+// schedule's prologue, edge merge and merge launch cost more than such a
+// call streams.  Measured (bf16, 28/4 heads, head_dim 128; balanced against
+// one partition): 4 x 64-token histories 9.8 vs 3.4 us, 64 x U[32, 255]
+// 12.5 vs 8.7, 256 x U[32, 255] 24.1 vs 22.2, 64 x U[256, 511] 17.2 vs
+// 13.3; past the bounds the balanced schedule wins: 512 x U[32, 255] 37.2
+// vs 38.3, 16 x U[768, 1023] 14.8 vs 18.4.  Returns that partition, or 0.
+int small_call_partition(int num_seqs, int kv_passes, int block_size, int max_context_len) {
+    const int chunks = ceil_div(max_context_len, pa::kChunk);
+    if (max_context_len <= 0 || chunks > 16 ||
+        (int64_t)num_seqs * kv_passes * chunks > 8192)
+        return 0;
+    const int unit = block_size > 32 ? block_size : 32;
+    const int P = ceil_div(max_context_len, unit) * unit;
+    return valid_partition(P, block_size) ? P : 0;
+}
+
 struct Layout {
     int part_len = 0;
     int num_parts = 0;
@@ -127,6 +147,13 @@ int balanced_workgroups(int head_dim) {
     }
     const int wgs = cus * pa::mfma_workgroups_per_cu(head_dim);
     return wgs > pa::kMaxBalancedWg ? pa::kMaxBalancedWg : wgs;
+}
+
+// Verify rows (several query rows of a sequence in one pass) run on the
+// matrix-core kernel with 16-bit rows and a group it serves in one pass; the
+// rest on the vector-ALU kernel.
+bool verify_on_mfma(pa_dtype dt, int head_dim, int block_size, int group) {
+    return dt != PA_F32 && pa::mfma_supported(dt, head_dim, block_size, group);
 }
 
 // The balanced schedule serves the matrix-core kernel when no partition
@@ -190,7 +217,10 @@ int pa_decode_partition_size(int num_seqs, int num_kv_heads, int gqa_group_size,
     if (num_seqs < 0 || num_kv_heads <= 0 || gqa_group_size <= 0 || max_context_len < 0 ||
         !supported_shape(head_dim, block_size) || elem_bytes(dtype) == 0)
         return 0;
-    return heuristic_partition(num_seqs, num_kv_heads, block_size, max_context_len);
+    const int split = pa::mfma_split(dtype, head_dim, block_size, gqa_group_size);
+    const int ps = small_call_partition(num_seqs, num_kv_heads * (split > 0 ? split : 1),
+                                        block_size, max_context_len);
+    return ps > 0 ? ps : heuristic_partition(num_seqs, num_kv_heads, block_size, max_context_len);
 }
 
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
@@ -280,16 +310,31 @@ static int decode_impl(void* out, const void* query, const void* new_key,
         return fail(PA_ERR_INVALID_ARG, "partition_size %d must be a positive multiple of 32 "
                     "and of block_size, at most 64*block_size", partition_size);
 
-    const int kind = kernel_kind >= 0 ? kernel_kind : g_kernel_kind.load();
-    // verify rows (a row map or a fold) take the matrix-core kernel in one pass only
+    int kind = kernel_kind >= 0 ? kernel_kind : g_kernel_kind.load();
+    if (q8 && dtype == PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "8-bit caches take bf16 or f16 queries");
+    // verify rows (a row map or a fold) take the matrix-core kernel in one
+    // pass only, with 16-bit rows
     const bool rows_mapped = table_rows != nullptr || fold != nullptr;
-    const int split = rows_mapped ? (pa::mfma_supported(dtype, head_dim, block_size,
-                                                        gqa_group_size) ? 1 : 0)
-                                  : pa::mfma_split(dtype, head_dim, block_size, gqa_group_size);
+    const int split = rows_mapped
+                          ? (verify_on_mfma(dtype, head_dim, block_size, gqa_group_size) ? 1 : 0)
+                          : pa::mfma_split(dtype, head_dim, block_size, gqa_group_size);
     const bool mfma_ok = split > 0;
-    const bool use_mfma = mfma_ok && kind != pa::kGeneric;
     if (kind == pa::kMfma && !mfma_ok)
         return fail(PA_ERR_UNSUPPORTED, "matrix-core kernel selected but not built for this shape");
+    // A small call left to the library takes one partition covering every
+    // history (see small_call_partition); float32 rows then take the
+    // vector-ALU kernel, whose single launch is the shortest (the tiny
+    // float32 workload: 3.7 against 4.5 us on the matrix cores).
+    if (partition_size == 0 && !rows_mapped) {
+        const int ps = small_call_partition(num_seqs, num_kv_heads * (mfma_ok ? split : 1),
+                                            block_size, max_context_len);
+        if (ps > 0) {
+            partition_size = ps;
+            if (dtype == PA_F32 && kind == pa::kAuto) kind = pa::kGeneric;
+        }
+    }
+    const bool use_mfma = mfma_ok && kind != pa::kGeneric;
     if (q8 && !use_mfma)
         return fail(PA_ERR_UNSUPPORTED, "8-bit caches are served by the matrix-core kernel only "
                     "(bf16/f16 queries, head_dim 64/128/256, block_size 8/16/32/64)");
@@ -376,10 +421,10 @@ static int decode_impl(void* out, const void* query, const void* new_key,
 
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     hipError_t e = hipSuccess;
-    if (append && use_mfma && kv_split == 1) {
+    if (append && use_mfma && kv_split == 1 && dtype != PA_F32) {
         // the matrix-core kernel stores each newest token itself (with a
-        // split group, several passes read that token: a kernel of its own
-        // stores it first)
+        // split group, several passes read that token, and float32 rows
+        // have no in-kernel append: a kernel of its own stores it first)
         a.new_key = new_key;
         a.new_value = new_value;
     } else if (append) {
@@ -592,8 +637,8 @@ int pa_paged_attention_verify(void* out, const void* query, const void* key_cach
     // family is chosen once here, so the grouping and the decode launch
     // agree.
     const int kind = g_kernel_kind.load();
-    const bool mfma = pa::mfma_supported(dtype, head_dim, block_size, gqa_group_size) &&
-                      kind != pa::kGeneric;
+    const bool mfma =
+        verify_on_mfma(dtype, head_dim, block_size, gqa_group_size) && kind != pa::kGeneric;
     const int nt = mfma && head_dim <= 128 &&
                            (int64_t)max_query_len * gqa_group_size > pa::kMaxGroup
                        ? 2

@@ -61,6 +61,17 @@ __device__ __forceinline__ f32x4 mfma16x16x32(F16, u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// Float32 operands: A[m][k] and B[k][n] one value per lane (lane 16 k + m /
+// 16 k + n), K = 4.
+__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Element e of four loaded dwords as a float.  The whole vector is cast: a
+// bit cast of the element expression itself compiles to a read of element 0
+// (seen in the generated code), whatever e is.
+__device__ __forceinline__ float f32_at(u32x4 v, int e) { return __builtin_bit_cast(f32x4, v)[e]; }
+
 // Two 16-bit 1.0 values packed in one dword.
 template <typename Tag>
 constexpr uint32_t kOnePair();
@@ -93,8 +104,8 @@ struct ChunkRegs {
 
 // Physical blocks of chunk c's two 16-token tiles, read from the sequence's
 // table row (wave-uniform scalar loads).  A tile past the end of the history
-// reuses tile 0's block, so its table entry is never read.  Entries outside
-// the pool set `bad` and are replaced by block 0 (never an out-of-bounds read).
+// reuses tile 0's block; its table entry is not used.  Entries outside the
+// pool set `bad` and are replaced by block 0 (never an out-of-bounds read).
 // The block table is read-only for the whole launch: read it through the
 // constant address space, which lets uniform reads become scalar loads.
 typedef __attribute__((address_space(4))) const int32_t ConstI32;
@@ -115,24 +126,44 @@ __device__ __forceinline__ int checked_block(int pb, int num_blocks, int& bad) {
     return pb;
 }
 
+// The table entries chunk c may need (block size 8: four, 16: two, 32 and
+// 64: one), each index clamped to the history's last block, so inside the
+// table row.  The reads are independent and go out together; their values
+// are checked only where the chunk's loads are issued (chunk_blocks), so
+// that the wait for them falls after whatever was issued in between -- at
+// the start of a history, the next chunk's entries too.  Reading an entry
+// only once its tile is known to be live would chain a memory round trip per
+// entry.
 template <int BS>
-__device__ __forceinline__ BlockIds<BS> chunk_blocks(const ConstI32* row, int c, int L,
+__device__ __forceinline__ BlockIds<BS> chunk_entries(const ConstI32* row, int c, int L) {
+    const int j0 = c * kChunk / BS;
+    const int jl = (L - 1) / BS;                 // the history's last block
+    if constexpr (BS == 8)
+        return make_int4(row[j0], row[min(j0 + 1, jl)], row[min(j0 + 2, jl)],
+                         row[min(j0 + 3, jl)]);
+    else if constexpr (BS == 16)
+        return make_int2(row[j0], row[min(j0 + 1, jl)]);
+    else
+        return make_int2(row[j0], 0);
+}
+
+// The physical blocks of chunk c from its entries e: a block past the end of
+// the history reuses the first (its entry is not used).
+template <int BS>
+__device__ __forceinline__ BlockIds<BS> chunk_blocks(BlockIds<BS> e, int c, int L,
                                                      int num_blocks, int& bad) {
     const int j0 = c * kChunk / BS;
-    const int pb0 = checked_block(row[j0], num_blocks, bad);
+    const int jl = (L - 1) / BS;
+    const int pb0 = checked_block(e.x, num_blocks, bad);
     if constexpr (BS == 8) {
-        // a block past the end of the history reuses the first block
-        const int t0 = c * kChunk;
-        const int pb1 = t0 + 8 < L ? checked_block(row[j0 + 1], num_blocks, bad) : pb0;
-        const int pb2 = t0 + 16 < L ? checked_block(row[j0 + 2], num_blocks, bad) : pb0;
-        const int pb3 = t0 + 24 < L ? checked_block(row[j0 + 3], num_blocks, bad) : pb0;
+        const int pb1 = j0 + 1 <= jl ? checked_block(e.y, num_blocks, bad) : pb0;
+        const int pb2 = j0 + 2 <= jl ? checked_block(e.z, num_blocks, bad) : pb0;
+        const int pb3 = j0 + 3 <= jl ? checked_block(e.w, num_blocks, bad) : pb0;
         return make_int4(pb0, pb1, pb2, pb3);
+    } else if constexpr (BS == 16) {
+        return make_int2(pb0, j0 + 1 <= jl ? checked_block(e.y, num_blocks, bad) : pb0);
     } else {
-        int pb1 = pb0;
-        if constexpr (BS == 16) {
-            if (c * kChunk + 16 < L) pb1 = checked_block(row[j0 + 1], num_blocks, bad);
-        }
-        return make_int2(pb0, pb1);
+        return make_int2(pb0, pb0);
     }
 }
 
@@ -200,6 +231,18 @@ __device__ __forceinline__ void load_row_at(u32x2& x, const char* p) {
 }
 __device__ __forceinline__ void load_row_at(uint32_t& x, const char* p) {
     x = __builtin_nontemporal_load((GlobalU32*)p);
+}
+// A float32 V row's slices (KvF32): D/64 16-byte slices, 256 bytes apart.
+template <int H>
+__device__ __forceinline__ void load_row(u32x4 (&x)[H], __amdgpu_buffer_rsrc_t r, uint32_t off) {
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+        x[h] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 256 * h, 0, kNonTemporal);
+}
+template <int H>
+__device__ __forceinline__ void load_row_at(u32x4 (&x)[H], const char* p) {
+#pragma unroll
+    for (int h = 0; h < H; ++h) x[h] = __builtin_nontemporal_load((GlobalU32x4*)(p + 256 * h));
 }
 
 // kRB: bytes per token row; kKLoads 16-byte K loads per tile, kKStep bytes
@@ -286,14 +329,29 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D>& r, const char* kbase, c
 struct KvSame {
     static constexpr bool k8 = false;    // 8-bit codes
     static constexpr bool kI8 = false;   // integer codes
+    static constexpr bool kF32 = false;  // float32 rows (and queries)
 };
 struct KvE4M3 {
     static constexpr bool k8 = true;
     static constexpr bool kI8 = false;
+    static constexpr bool kF32 = false;
 };
 struct KvI8 {
     static constexpr bool k8 = true;
     static constexpr bool kI8 = true;
+    static constexpr bool kF32 = false;
+};
+// KvF32: float32 caches and queries, on the float32 matrix instruction
+// (16x16x4: one value per lane and step, K = 4).  A lane takes 16-byte
+// slices: for K, lane (n, q) holds K[token n][d = 16 kk + 4 q .. +4] and MFMA
+// step (kk, e) contracts d = 16 kk + 4 q + e (the query uses the same d); for
+// V, lane (m, q) holds V[token 4 q + i][d = 64 h + 4 m .. +4], and the PV
+// product's output tile (h, e) holds d = 64 h + 4 m + e in its row m, so
+// no register moves are needed.
+struct KvF32 {
+    static constexpr bool k8 = false;
+    static constexpr bool kI8 = false;
+    static constexpr bool kF32 = true;
 };
 
 // One 32-token chunk of 8-bit codes, as loaded.
@@ -302,6 +360,46 @@ struct ChunkRegs8 {
     u32x4 k0[D / 64], k1[D / 64];            // K tile 0 / 1: row n, d = (D/4) q ..
     typename Dim<D>::VRow8 v[8];             // V rows of this lane's 8 tokens, d = VW n ..
 };
+
+// One 32-token chunk of float32 rows, as loaded (two 16-token tiles; see
+// KvF32): K tile t slice kk, and V rows [4 t + i] slice h.
+template <int D>
+struct ChunkRegsF {
+    u32x4 k0[D / 16], k1[D / 16];
+    u32x4 v[8][D / 64];
+};
+
+// The loads of one float32 chunk (same rules as load_chunk).
+template <int BS, int D>
+__device__ __forceinline__ void load_chunk(ChunkRegsF<D>& r, const char* kbase, const char* vbase,
+                                           BlockIds<BS> pb, int r0, bool live0, bool live1,
+                                           int kvh, int num_kv_heads, uint32_t koff,
+                                           uint32_t voff) {
+    constexpr int RB = D * 4;     // bytes per token row
+    if constexpr (lane_addressed<BS, D>()) {
+        const int lane = threadIdx.x & 63;
+        load_chunk_lanes<BS, RB, D / 16, 64>(r, kbase, vbase, pb, r0, live0, live1, kvh,
+                                             num_kv_heads, koff - (lane & 15) * RB,
+                                             voff - 4 * (lane >> 4) * RB);
+    } else {
+        const uint64_t row0 = kv_row(pb.x, kvh, r0, num_kv_heads, BS) * RB;
+        const uint64_t row1 = kv_row(pb.y, kvh, BS == 16 ? 0 : r0 + 16, num_kv_heads, BS) * RB;
+        const __amdgpu_buffer_rsrc_t k0 = tile_rsrc<16 * RB>(kbase + row0, live0);
+        const __amdgpu_buffer_rsrc_t k1 = tile_rsrc<16 * RB>(kbase + row1, live1);
+        const __amdgpu_buffer_rsrc_t v0 = tile_rsrc<16 * RB>(vbase + row0, live0);
+        const __amdgpu_buffer_rsrc_t v1 = tile_rsrc<16 * RB>(vbase + row1, live1);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            r.k0[kk] = __builtin_amdgcn_raw_buffer_load_b128(k0, koff + kk * 64, 0, kNonTemporal);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            r.k1[kk] = __builtin_amdgcn_raw_buffer_load_b128(k1, koff + kk * 64, 0, kNonTemporal);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_row(r.v[i], v0, voff + i * RB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_row(r.v[4 + i], v1, voff + i * RB);
+    }
+}
 
 // The loads of one 8-bit chunk (same rules as load_chunk: always issued, dead
 // tiles through an empty descriptor, nontemporal).
@@ -403,18 +501,27 @@ __device__ __forceinline__ ChunkRegs<D> expand(const ChunkRegs8<D>& r8) {
 }
 
 template <typename Kv, int D>
-using KvRegs = typename std::conditional<Kv::k8, ChunkRegs8<D>, ChunkRegs<D>>::type;
+using KvRegs = typename std::conditional<
+    Kv::kF32, ChunkRegsF<D>,
+    typename std::conditional<Kv::k8, ChunkRegs8<D>, ChunkRegs<D>>::type>::type;
 
 // Byte offsets of this lane's K and V data inside a tile.
 template <typename Kv, int D>
 __device__ __forceinline__ uint32_t lane_koff(int n, int q) {
+    if constexpr (Kv::kF32) return (uint32_t)(n * D + 4 * q) * 4;
     return Kv::k8 ? (uint32_t)(n * D + (D / 4) * q) : (uint32_t)(n * D + 8 * q) * 2;
 }
 template <typename Kv, int D>
 __device__ __forceinline__ uint32_t lane_voff(int n, int q) {
     constexpr int VW = Dim<D>::VW;
+    if constexpr (Kv::kF32) return (uint32_t)(4 * q * D + 4 * n) * 4;
     return Kv::k8 ? (uint32_t)(4 * q * D + VW * n) : (uint32_t)(4 * q * D + VW * n) * 2;
 }
+
+// 16-byte query slices per column tile: D/32 (16-bit: 8 values per MFMA
+// step), D/16 for float32 rows (4 values, 4 steps each).
+template <typename Kv, int D>
+constexpr int query_slices() { return Kv::kF32 ? D / 16 : Dim<D>::KD; }
 
 // [S, H] row of column n of decode row b (KV head kvh): query head
 // col_head(kvh, n) of row b, or with verify columns (kCols) the (query row,
@@ -430,6 +537,16 @@ template <typename Kv, bool kCols, int D>
 __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int kvh, int n, int q,
                                            int ncols, u32x4* qop) {
     constexpr int KD = Dim<D>::KD;
+    if constexpr (Kv::kF32) {
+        // Q[column n][d = 16 kk + 4 q .. +4]
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qop[kk] = n < ncols ? load16(reinterpret_cast<const char*>(a.query) +
+                                         (column_row<kCols>(a, b, kvh, n) * D + 16 * kk + 4 * q) *
+                                             4)
+                                : (u32x4){0u, 0u, 0u, 0u};
+        return;
+    }
     if (n < ncols) {
         const char* qp = reinterpret_cast<const char*>(a.query) +
                          column_row<kCols>(a, b, kvh, n) * D * 2;
@@ -597,12 +714,96 @@ __device__ __forceinline__ void compute_chunk(WaveState<D>* st, ChunkRegs<D>& r,
     }
 }
 
+// The same chunk math on float32 rows (KvF32; decode rows only, no verify
+// columns): S^T = K Q^T in D/4 steps of the 16x16x4 instruction per tile,
+// the scores in the same lane layout as above, P kept in float32 in the
+// registers the scores came out in (step i of a tile contracts tokens
+// 4 q + i), O^T = V^T P^T per output tile (h, e), and l = P summed on the
+// matrix core as before.
+template <int D, int NT>
+__device__ __forceinline__ void compute_chunk_f32(WaveState<D>* st, ChunkRegsF<D>& r,
+                                                  const u32x4* qop, float sl2, int tc, int t_end,
+                                                  int q) {
+    constexpr int KF = D / 16;      // K / query slices per tile
+    constexpr int VH = D / 64;      // V slices per row
+    float s[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KF; ++kk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float qv = f32_at(qop[t * KF + kk], e);
+                s0 = mfma16x16x4(f32_at(r.k0[kk], e), qv, s0);
+                s1 = mfma16x16x4(f32_at(r.k1[kk], e), qv, s1);
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s[t][i] = s0[i] * sl2;
+            s[t][4 + i] = s1[i] * sl2;
+        }
+    }
+    if (tc + kChunk > t_end) {
+        // tokens at or past the end: score -inf, V row zeroed (as above)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                if (tc + 4 * q + i >= t_end) s[t][i] = -INFINITY;
+                if (tc + 16 + 4 * q + i >= t_end) s[t][4 + i] = -INFINITY;
+            }
+#pragma unroll
+            for (int h = 0; h < VH; ++h) {
+                if (tc + 4 * q + i >= t_end) r.v[i][h] = (u32x4){0u, 0u, 0u, 0u};
+                if (tc + 16 + 4 * q + i >= t_end) r.v[4 + i][h] = (u32x4){0u, 0u, 0u, 0u};
+            }
+        }
+    }
+    float p[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float cmax = fmaxf(fmaxf(fmaxf(s[t][0], s[t][1]), fmaxf(s[t][2], s[t][3])),
+                           fmaxf(fmaxf(s[t][4], s[t][5]), fmaxf(s[t][6], s[t][7])));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        WaveState<D>& w = st[t];
+        if (__any(cmax > w.m_ref + kLazy)) {
+            const float m_new = fmaxf(w.m_ref, cmax);
+            const float alpha = fast_exp2(w.m_ref - m_new);
+#pragma unroll
+            for (int j = 0; j < Dim<D>::VW; ++j) w.acc[j] *= alpha;
+            w.acc_l *= alpha;
+            w.m_ref = m_new;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[t][i] = fast_exp2(s[t][i] - w.m_ref);
+            w.acc_l = mfma16x16x4(1.0f, p[t][i], w.acc_l);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < VH; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = f32_at(r.v[i][h], e);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    st[t].acc[4 * h + e] = mfma16x16x4(v, p[t][i], st[t].acc[4 * h + e]);
+            }
+}
+
 // One chunk's math on either storage format.
 template <typename Tag, typename Kv, bool kCols, int D, int NT>
 __device__ __forceinline__ void compute(WaveState<D>* st, KvRegs<Kv, D>& r, const u32x4* qop,
                                         float sl2, int tc, int t_end, const int* t_col, int t_lo,
                                         int q) {
-    if constexpr (Kv::k8) {
+    if constexpr (Kv::kF32) {
+        static_assert(!kCols, "float32 rows: decode rows only");
+        compute_chunk_f32<D, NT>(st, r, qop, sl2, tc, t_end, q);
+    } else if constexpr (Kv::k8) {
         ChunkRegs<D> ops = expand<Tag, Kv, D>(r);
         compute_chunk<Tag, kCols, D, NT>(st, ops, qop, sl2, tc, t_end, t_col, t_lo, q);
     } else {
@@ -614,9 +815,10 @@ __device__ __forceinline__ void compute(WaveState<D>* st, KvRegs<Kv, D>& r, cons
 // KV head): loads and math.  Two register buffers (head_dim 64 and 128):
 // while chunk k is computed, chunk k+1's loads are in flight and chunk
 // k+2's block numbers are being fetched (scalar loads of the table).  At
-// head_dim 256 a chunk's operands take 128 registers, so there is one
-// buffer; only the next chunk's block numbers are fetched ahead, and the
-// other wavefronts of the compute unit keep its loads in flight.
+// head_dim 256 (float32 rows: 128) a chunk's operands take 128 registers,
+// so there is one buffer; only the next chunk's block numbers are fetched
+// ahead, and the other wavefronts of the compute unit keep its loads in
+// flight.
 template <typename Tag, int BS, typename Kv, bool kCols, int D, int NT, typename ChunkOf>
 __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>* st, int K,
                                               ChunkOf chunk_of, const ConstI32* row, int L,
@@ -631,22 +833,28 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>*
     kvh = a.kv_split == 1 ? kvh : kvh / a.kv_split;
     // tile 1 of chunk c is live when it holds history tokens
     auto tile1_live = [&](int k) { return chunk_of(k) * kChunk + 16 < L; };
-    if constexpr (D == 256) {
-        BlockIds<BS> ids = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
+    const int nb = a.num_blocks;
+    // one chunk buffer where a chunk's operands take 128 registers: 16-bit
+    // rows at head_dim 256, float32 rows at 128
+    constexpr bool kOneBuffer = D * (Kv::kF32 ? 4 : 2) >= 512;
+    if constexpr (kOneBuffer) {
+        BlockIds<BS> e = chunk_entries<BS>(row, chunk_of(0), L);
         for (int k = 0; k < K; ++k) {
             KvRegs<Kv, D> buf;
-            load_chunk<BS, D>(buf, kbase, vbase, ids, tile_row<BS>(chunk_of(k)), true,
-                              tile1_live(k), kvh, H_mem, koff, voff);
-            ids = chunk_blocks<BS>(row, chunk_of(k + 1), L, a.num_blocks, bad);
+            load_chunk<BS, D>(buf, kbase, vbase, chunk_blocks<BS>(e, chunk_of(k), L, nb, bad),
+                              tile_row<BS>(chunk_of(k)), true, tile1_live(k), kvh, H_mem, koff,
+                              voff);
+            e = chunk_entries<BS>(row, chunk_of(k + 1), L);
             compute<Tag, Kv, kCols, D, NT>(st, buf, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
                                        t_lo, q);
         }
     } else {
         KvRegs<Kv, D> bufA, bufB;
-        BlockIds<BS> idsA = chunk_blocks<BS>(row, chunk_of(0), L, a.num_blocks, bad);
-        BlockIds<BS> idsB = chunk_blocks<BS>(row, chunk_of(1), L, a.num_blocks, bad);
-        load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(0)), true,
-                          tile1_live(0), kvh, H_mem, koff, voff);
+        BlockIds<BS> eA = chunk_entries<BS>(row, chunk_of(0), L);
+        BlockIds<BS> eB = chunk_entries<BS>(row, chunk_of(1), L);
+        load_chunk<BS, D>(bufA, kbase, vbase, chunk_blocks<BS>(eA, chunk_of(0), L, nb, bad),
+                          tile_row<BS>(chunk_of(0)), true, tile1_live(0), kvh, H_mem, koff,
+                          voff);
         int k = 0;
         // The scheduling barriers keep each phase's loads after the previous
         // chunk's math and before this chunk's: the load counter is in
@@ -656,17 +864,21 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>*
         // flight.
         for (;;) {
             __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS, D>(bufB, kbase, vbase, idsB, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
+            load_chunk<BS, D>(bufB, kbase, vbase,
+                              chunk_blocks<BS>(eB, chunk_of(k + 1), L, nb, bad),
+                              tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
                               k + 1 < K && tile1_live(k + 1), kvh, H_mem, koff, voff);
-            idsA = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
+            eA = chunk_entries<BS>(row, chunk_of(k + 2), L);
             __builtin_amdgcn_sched_barrier(0);
             compute<Tag, Kv, kCols, D, NT>(st, bufA, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
                                        t_lo, q);
             if (++k >= K) break;
             __builtin_amdgcn_sched_barrier(0);
-            load_chunk<BS, D>(bufA, kbase, vbase, idsA, tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
+            load_chunk<BS, D>(bufA, kbase, vbase,
+                              chunk_blocks<BS>(eA, chunk_of(k + 1), L, nb, bad),
+                              tile_row<BS>(chunk_of(k + 1)), k + 1 < K,
                               k + 1 < K && tile1_live(k + 1), kvh, H_mem, koff, voff);
-            idsB = chunk_blocks<BS>(row, chunk_of(k + 2), L, a.num_blocks, bad);
+            eB = chunk_entries<BS>(row, chunk_of(k + 2), L);
             __builtin_amdgcn_sched_barrier(0);
             compute<Tag, Kv, kCols, D, NT>(st, bufB, qop, sl2, chunk_of(k) * kChunk, t_end, t_col,
                                        t_lo, q);
@@ -676,10 +888,21 @@ __device__ __forceinline__ void stream_chunks(const DecodeArgs& a, WaveState<D>*
 }
 
 // This lane's accumulators (column n = lane % 16, d = VW (4 q + i) + j in
-// acc[j][i]) -> an LDS row of the column (float offsets 4 q VW + VW i + j).
-template <int D>
+// acc[j][i]; float32 rows: d = 64 h + 16 q + 4 i + e in acc[4 h + e][i]) ->
+// an LDS row of the column (float offset d).
+template <int D, bool kF32 = false>
 __device__ __forceinline__ void stage_acc(float* col_row_lds, int q, const WaveState<D>& st) {
     constexpr int VW = Dim<D>::VW;
+    if constexpr (kF32) {
+#pragma unroll
+        for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<f32x4*>(col_row_lds + 64 * h + 16 * q + 4 * i) =
+                    (f32x4){st.acc[4 * h][i], st.acc[4 * h + 1][i], st.acc[4 * h + 2][i],
+                            st.acc[4 * h + 3][i]};
+        return;
+    }
     float* ow = col_row_lds + 4 * q * VW;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -709,7 +932,7 @@ __device__ __forceinline__ void tile_columns(const DecodeArgs& a, int b, int kvh
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int col = t * 16 + n;
-        load_query<Kv, kCols, D>(a, b, kvh, col, q, ncols, qop + t * Dim<D>::KD);
+        load_query<Kv, kCols, D>(a, b, kvh, col, q, ncols, qop + t * query_slices<Kv, D>());
         // verify columns: column col attends the L - (ntok - 1 - col / G)
         // oldest tokens
         t_col[t] = kCols ? min(t_end, L - (ntok - 1 - col / G)) : t_end;
@@ -741,7 +964,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
     const int q = lane >> 4;
     const int t_end = min(c1 * kChunk, L);
     const int t_lo = kCols ? min(t_end, L - (ntok - 1)) : t_end;
-    u32x4 qop[NT * Dim<D>::KD];
+    u32x4 qop[NT * query_slices<Kv, D>()];
     int t_col[NT];
     tile_columns<Kv, kCols, D, NT>(a, b, kvh, n, q, ntok, L, t_end, qop, t_col);
 
@@ -755,10 +978,13 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
     // own later load of the row follows in program order; no other
     // wavefront reads the slot in this launch (the tail block of a sequence
     // being appended to is private to it).
-    if (a.new_key != nullptr) {
-        const int c_last = (L - 1) / kChunk;
-        if (c_last >= c0 && c_last < c1 && (c_last - c0) % kNW == wave)
-            append_token<Tag, Kv, BS, D>(a, row, b, kvh, L - 1, lane);
+    // (float32 rows are appended by a kernel of their own first)
+    if constexpr (!Kv::kF32) {
+        if (a.new_key != nullptr) {
+            const int c_last = (L - 1) / kChunk;
+            if (c_last >= c0 && c_last < c1 && (c_last - c0) % kNW == wave)
+                append_token<Tag, Kv, BS, D>(a, row, b, kvh, L - 1, lane);
+        }
     }
 
     WaveState<D> st[NT];
@@ -783,7 +1009,7 @@ __device__ __forceinline__ void attend_segment(const DecodeArgs& a, SegmentLds<D
             sm.m[col] = st[t].m_ref;
             sm.l[col] = st[t].acc_l[0];
         }
-        stage_acc<D>(sm.o + col * OS, q, st[t]);
+        stage_acc<D, Kv::kF32>(sm.o + col * OS, q, st[t]);
     }
     const bool any_bad = __syncthreads_or(bad);
     finalize_state<Tag>(a, sm.m, sm.l, sm.o, kNW, NC, NC * OS, OS, b, kvh, 0,
@@ -862,7 +1088,7 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int tro
     const int q = lane >> 4;
     const int t_end = min(ce * kChunk, L);
     const int t_lo = kCols ? min(t_end, L - (ntok - 1)) : t_end;
-    u32x4 qop[NT * Dim<D>::KD];
+    u32x4 qop[NT * query_slices<Kv, D>()];
     int t_col[NT];
     tile_columns<Kv, kCols, D, NT>(a, b, kvh, n, q, ntok, L, t_end, qop, t_col);
 
@@ -871,10 +1097,13 @@ __device__ __forceinline__ void attend_piece(const DecodeArgs& a, int b, int tro
     const uint32_t koff = lane_koff<Kv, D>(n, q);
     const uint32_t voff = lane_voff<Kv, D>(n, q);
 
-    if (a.new_key != nullptr) {
-        const int c_last = (L - 1) / kChunk;
-        if (c_last >= cs && c_last < ce)
-            append_token<Tag, Kv, BS, D>(a, row, b, kvh, L - 1, lane);
+    // (float32 rows are appended by a kernel of their own first)
+    if constexpr (!Kv::kF32) {
+        if (a.new_key != nullptr) {
+            const int c_last = (L - 1) / kChunk;
+            if (c_last >= cs && c_last < ce)
+                append_token<Tag, Kv, BS, D>(a, row, b, kvh, L - 1, lane);
+        }
     }
 
     const int K = ce - cs;
@@ -899,24 +1128,40 @@ __device__ __forceinline__ void write_rows(const DecodeArgs& a, int b, int kvh, 
     // one division per column, then products (an IEEE division per element
     // costs about ten instructions, and short histories write rows often)
     const float scale = a.out_scale / st.acc_l[0];
-    char* orow = reinterpret_cast<char*>(a.out) +
-                 (column_row<kCols>(a, b, kvh, n) * D + 4 * q * VW) * 2;
+    if constexpr (std::is_same<Tag, F32>::value) {
+        // float32 rows (layout of stage_acc): d = 64 h + 16 q + 4 i + e
+        float* orow = reinterpret_cast<float*>(a.out) + column_row<kCols>(a, b, kvh, n) * D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float o[VW];
+        for (int h = 0; h < D / 64; ++h)
 #pragma unroll
-        for (int j = 0; j < VW; ++j) o[j] = bad ? __builtin_nanf("") : st.acc[j][i] * scale;
-        if constexpr (VW >= 8) {
+            for (int i = 0; i < 4; ++i) {
+                f32x4 o;
 #pragma unroll
-            for (int j0 = 0; j0 < VW; j0 += 8) {
-                const u32x4 v = {pack2(Tag(), o[j0], o[j0 + 1]), pack2(Tag(), o[j0 + 2], o[j0 + 3]),
-                                 pack2(Tag(), o[j0 + 4], o[j0 + 5]),
-                                 pack2(Tag(), o[j0 + 6], o[j0 + 7])};
-                *reinterpret_cast<u32x4*>(orow + 2 * VW * i + 2 * j0) = v;
+                for (int e = 0; e < 4; ++e)
+                    o[e] = bad ? __builtin_nanf("") : st.acc[4 * h + e][i] * scale;
+                *reinterpret_cast<f32x4*>(orow + 64 * h + 16 * q + 4 * i) = o;
             }
-        } else {
-            const u32x2 v = {pack2(Tag(), o[0], o[1]), pack2(Tag(), o[2], o[3])};
-            *reinterpret_cast<u32x2*>(orow + 2 * VW * i) = v;
+    } else {
+        char* orow = reinterpret_cast<char*>(a.out) +
+                     (column_row<kCols>(a, b, kvh, n) * D + 4 * q * VW) * 2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float o[VW];
+#pragma unroll
+            for (int j = 0; j < VW; ++j) o[j] = bad ? __builtin_nanf("") : st.acc[j][i] * scale;
+            if constexpr (VW >= 8) {
+#pragma unroll
+                for (int j0 = 0; j0 < VW; j0 += 8) {
+                    const u32x4 v = {pack2(Tag(), o[j0], o[j0 + 1]),
+                                     pack2(Tag(), o[j0 + 2], o[j0 + 3]),
+                                     pack2(Tag(), o[j0 + 4], o[j0 + 5]),
+                                     pack2(Tag(), o[j0 + 6], o[j0 + 7])};
+                    *reinterpret_cast<u32x4*>(orow + 2 * VW * i + 2 * j0) = v;
+                }
+            } else {
+                const u32x2 v = {pack2(Tag(), o[0], o[1]), pack2(Tag(), o[2], o[3])};
+                *reinterpret_cast<u32x2*>(orow + 2 * VW * i) = v;
+            }
         }
     }
 }
@@ -973,12 +1218,7 @@ __device__ __forceinline__ void finalize_edges_n(const DecodeArgs& a, const Edge
         if (bad) o = (f32x4){__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                              __builtin_nanf("")};
         if (plse == nullptr) {
-            const f32x4 os = a.out_scale * o;
-            const uint32_t lo = pack2(Tag(), os[0], os[1]);
-            const uint32_t hi = pack2(Tag(), os[2], os[3]);
-            char* dst = reinterpret_cast<char*>(a.out) +
-                        (column_row<kCols>(a, b, kvh, g) * D + d) * 2;
-            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+            store4(Tag(), a.out, column_row<kCols>(a, b, kvh, g) * D + d, a.out_scale * o);
         } else {
             *reinterpret_cast<f32x4*>(po + g * D + d) = o;
             if (d == 0) plse[g] = bad ? __builtin_nanf("") : M + __log2f(den);
@@ -1143,7 +1383,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
                     edge.m[p][col] = st[t].m_ref;
                     edge.l[p][col] = st[t].acc_l[0];
                 }
-                stage_acc<D>(&edge.o[p][col * OS], q, st[t]);
+                stage_acc<D, Kv::kF32>(&edge.o[p][col * OS], q, st[t]);
             }
             if (lane == 0) {
                 edge.key[p] = b * H_kv + kvh;
@@ -1226,11 +1466,16 @@ hipError_t launch_tiles(const DecodeArgs& a, hipStream_t s) {
 
 template <typename Tag, int BS, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
-    if (a.kv_format == kKvE4M3) return launch_tiles<Tag, BS, KvE4M3, 0, D>(a, s);
-    if (a.kv_format == kKvI8) return launch_tiles<Tag, BS, KvI8, 0, D>(a, s);
-    if (a.table_rows == nullptr && a.query_start == nullptr)
-        return launch_tiles<Tag, BS, KvSame, 0, D>(a, s);
-    return launch_tiles<Tag, BS, KvSame, 1, D>(a, s);
+    if constexpr (std::is_same<Tag, F32>::value) {
+        // float32 rows: decode rows of one column tile (at most 16 heads a pass)
+        return launch_rows<F32, BS, KvF32, 0, D, 1>(a, s);
+    } else {
+        if (a.kv_format == kKvE4M3) return launch_tiles<Tag, BS, KvE4M3, 0, D>(a, s);
+        if (a.kv_format == kKvI8) return launch_tiles<Tag, BS, KvI8, 0, D>(a, s);
+        if (a.table_rows == nullptr && a.query_start == nullptr)
+            return launch_tiles<Tag, BS, KvSame, 0, D>(a, s);
+        return launch_tiles<Tag, BS, KvSame, 1, D>(a, s);
+    }
 }
 
 template <typename Tag, int D>

@@ -5,12 +5,17 @@
 namespace pa {
 
 // Groups of up to 16 heads fill one column tile; up to 32 take two (head_dim
-// 64 and 128, whose edge LDS then still fits a compute unit).
+// 64 and 128, whose edge LDS then still fits a compute unit).  float32 rows
+// (the float32 matrix instruction) at head_dim 64 and 128, one column tile:
+// at 256 a 32-token chunk of float32 rows would take 256 registers.
 bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group) {
+    const bool bs_ok =
+        block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64;
+    if (dt == PA_F32)
+        return (head_dim == 64 || head_dim == 128) && bs_ok && group >= 1 && group <= kMaxGroup;
     return (dt == PA_BF16 || dt == PA_F16) &&
-           (head_dim == 64 || head_dim == 128 || head_dim == 256) &&
-           (block_size == 8 || block_size == 16 || block_size == 32 || block_size == 64) &&
-           group >= 1 && (group <= kMaxGroup || (group <= 2 * kMaxGroup && head_dim <= 128));
+           (head_dim == 64 || head_dim == 128 || head_dim == 256) && bs_ok && group >= 1 &&
+           (group <= kMaxGroup || (group <= 2 * kMaxGroup && head_dim <= 128));
 }
 
 // A larger group is split into passes over the KV head's history, each
@@ -21,7 +26,7 @@ bool mfma_supported(pa_dtype dt, int head_dim, int block_size, int group) {
 int mfma_split(pa_dtype dt, int head_dim, int block_size, int group) {
     if (group < 1 || !mfma_supported(dt, head_dim, block_size, 1)) return 0;
     if (mfma_supported(dt, head_dim, block_size, group)) return 1;
-    const int cap = head_dim <= 128 ? 2 * kMaxGroup : kMaxGroup;
+    const int cap = head_dim <= 128 && dt != PA_F32 ? 2 * kMaxGroup : kMaxGroup;
     const int pg = mfma_pass_group(group, (group + cap - 1) / cap);
     return (group + pg - 1) / pg;   // every pass, the last included, holds a head
 }

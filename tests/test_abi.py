@@ -116,8 +116,8 @@ def test_decode_empty_batch_is_noop(lib):
 
 def test_workspace_size_arithmetic(lib):
     f = lib.pa_decode_workspace_size
-    # one partition: no workspace
-    assert f(4, 2, 2, 64, 16, 64, 0, ops.PA_F32) == 0
+    # one partition of the vector-ALU kernel (float32 at head_dim 256): no workspace
+    assert f(4, 2, 2, 256, 16, 64, 0, ops.PA_F32) == 0
     # S=2, H=4, P=32, max 128 -> 4 partitions: lse 2*4*4 floats, out
     # 2*4*4*D floats, each region 256-byte aligned
     up = lambda x: (x + 255) // 256 * 256
@@ -144,6 +144,9 @@ def test_balanced_workspace_follows_the_pass_width(lib):
     for G, D, cols in ((7, 128, 16), (24, 128, 32), (33, 128, 32), (37, 128, 32),
                        (96, 128, 32), (17, 256, 16), (37, 256, 16), (40, 64, 32)):
         assert f(1, G, 1, D, 16, 64, 0, ops.PA_BF16) == bal(cols, D), (G, D)
+    # float32 rows: passes of at most 16 heads, one column tile
+    for G, D in ((7, 128), (24, 128), (33, 64)):
+        assert f(1, G, 1, D, 16, 64, 0, ops.PA_F32) == bal(16, D), (G, D)
 
 
 def test_partition_heuristic_is_valid(lib):
@@ -207,7 +210,7 @@ def test_8bit_entry_points_reject_on_host(lib, fmt):
               vp(FAKE), ctypes.c_size_t(1 << 30), vp(0)) == UNSUPPORTED
     assert b"fused append" in lib.pa_last_error()
     assert call(G=33, H=132, S=0) == OK                        # 33: passes of 17 and 16 heads
-    assert call(dtype=ops.PA_F32) == UNSUPPORTED               # f32 queries: vector-ALU only
+    assert call(dtype=ops.PA_F32) == UNSUPPORTED               # 8-bit codes: 16-bit queries
     assert call(S=0) == OK
     # the fused append needs the new key and value
     a = getattr(lib, "pa_decode_append_" + fmt)
@@ -237,7 +240,10 @@ def test_decode_kernel_choice(lib):
     assert f(64, 8, 32, ops.PA_F16) == MFMA
     assert f(128, 16, 33, ops.PA_BF16) == MFMA       # passes of 17 and 16
     assert f(256, 16, 18, ops.PA_BF16) == MFMA       # two passes of 9 at head_dim 256
-    assert f(128, 16, 7, ops.PA_F32) == GEN
+    assert f(128, 16, 7, ops.PA_F32) == MFMA         # float32 rows: 16x16x4 f32 MFMA
+    assert f(64, 8, 16, ops.PA_F32) == MFMA
+    assert f(128, 16, 17, ops.PA_F32) == MFMA        # passes of 9 and 8 (16 columns)
+    assert f(256, 16, 7, ops.PA_F32) == GEN          # head_dim 256: vector ALU
     assert f(96, 16, 7, ops.PA_BF16) == UNSUPPORTED
     assert f(128, 16, 0, ops.PA_BF16) == INVALID
     assert f(128, 16, 7, 9) == INVALID
@@ -247,7 +253,7 @@ def test_decode_kernel_choice(lib):
         lib.pa_debug_select_kernel(2)
         assert f(128, 16, 7, ops.PA_BF16) == MFMA
         assert f(128, 8, 37, ops.PA_BF16) == MFMA
-        assert f(128, 8, 7, ops.PA_F32) == UNSUPPORTED      # f32: vector-ALU only
+        assert f(256, 8, 7, ops.PA_F32) == UNSUPPORTED      # f32 at 256: vector-ALU only
     finally:
         lib.pa_debug_select_kernel(prev)
 

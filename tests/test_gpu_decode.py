@@ -70,12 +70,17 @@ SMALL_CASES = [
     ("bf16", 3, 1, 64, 32, ops.KERNEL_MFMA),
     ("f16", 1, 16, 64, 64, ops.KERNEL_MFMA),
     ("bf16", 2, 8, 64, 16, ops.KERNEL_MFMA),
-    ("f32", 2, 1, 64, 16, ops.KERNEL_AUTO),
+    ("f32", 2, 1, 64, 16, ops.KERNEL_AUTO),         # float32 rows: f32 matrix cores
+    ("f32", 2, 7, 128, 16, ops.KERNEL_MFMA),
+    ("f32", 1, 16, 64, 8, ops.KERNEL_MFMA),         # block size 8: per-lane addresses
+    ("f32", 2, 4, 128, 64, ops.KERNEL_AUTO),
+    ("f32", 1, 20, 128, 32, ops.KERNEL_AUTO),       # passes of 10 heads
+    ("f32", 3, 5, 64, 32, ops.KERNEL_MFMA),
     ("f32", 2, 4, 128, 32, ops.KERNEL_GENERIC),
     ("f32", 1, 12, 128, 16, ops.KERNEL_GENERIC),
-    ("f32", 2, 7, 64, 16, ops.KERNEL_AUTO),         # 8-head workgroups: block fold
-    ("f32", 1, 8, 256, 32, ops.KERNEL_AUTO),
-    ("f32", 1, 13, 64, 8, ops.KERNEL_AUTO),         # block fold + a 5-head workgroup
+    ("f32", 2, 7, 64, 16, ops.KERNEL_GENERIC),      # 8-head workgroups: block fold
+    ("f32", 1, 8, 256, 32, ops.KERNEL_AUTO),        # head_dim 256: vector ALU, block fold
+    ("f32", 1, 13, 64, 8, ops.KERNEL_GENERIC),      # block fold + a 5-head workgroup
     # block sizes 8 and 64, head_dim 256
     ("bf16", 2, 7, 128, 64, ops.KERNEL_MFMA),
     ("f16", 2, 4, 128, 8, ops.KERNEL_AUTO),         # block size 8: matrix-core kernel
@@ -116,7 +121,8 @@ def test_kernels_agree():
 def test_single_token_history_is_v0_exactly():
     for dtype, D, kernel in (("bf16", 128, ops.KERNEL_MFMA), ("f16", 128, ops.KERNEL_MFMA),
                              ("bf16", 64, ops.KERNEL_MFMA), ("bf16", 256, ops.KERNEL_MFMA),
-                             ("f32", 64, ops.KERNEL_GENERIC),
+                             ("f32", 64, ops.KERNEL_GENERIC), ("f32", 128, ops.KERNEL_MFMA),
+                             ("f32", 64, ops.KERNEL_MFMA),
                              ("bf16", 128, ops.KERNEL_GENERIC)):
         inp = I.generate(small_config(dtype, 2, 4, D, 16, (1, 1, 1)))
         out = run_decode(upload(inp), kernel).cpu()
@@ -197,6 +203,24 @@ def test_balanced_workspace_reuse_and_all_empty():
             assert torch.all(out == 0)
         else:
             compare(out, oracle_ref(inp), "bf16", what="after an empty batch")
+
+
+@pytest.mark.parametrize("dtype,G,D,BS,lens", [
+    ("bf16", 7, 128, 16, (1, 15, 16, 17, 100, 500)),     # one fixed partition of 512
+    ("f16", 4, 64, 8, (3, 64, 65, 200)),
+    ("bf16", 20, 128, 32, (31, 32, 33, 250)),             # two column tiles
+    ("bf16", 37, 256, 16, (5, 130, 256)),                 # three passes
+    ("f32", 7, 128, 16, (1, 40, 300)),                    # float32: vector ALU
+])
+def test_small_call_single_partition(dtype, G, D, BS, lens):
+    """Calls whose histories fit 512 tokens take one fixed partition covering
+    every history (one launch, no merge); against the oracle."""
+    inp = I.poison_unread(I.generate(small_config(dtype, 2, G, D, BS, lens)))
+    P = ops.decode_partition_size(len(lens), 2, G, D, BS, inp.block_tables.shape[1] * BS,
+                                  inp.query.dtype)
+    assert P >= inp.block_tables.shape[1] * BS
+    out = run_decode(upload(inp), ops.KERNEL_AUTO, 0)
+    compare(out, oracle_ref(inp), dtype, what="small call %s G=%d D=%d" % (dtype, G, D))
 
 
 def test_partition_size_invariance():
@@ -312,14 +336,17 @@ def test_uneven_passes_on_the_bench_batch(G, D):
 def test_many_sequences_balanced_limit(S, D):
     """The balanced schedule's prefix table (dynamic LDS, S + 1 ints) at its
     largest, next to 134 KB of edge LDS at head_dim 256; one sequence more
-    takes the fixed schedule.  Short ragged histories, some empty."""
+    takes the fixed schedule.  Short ragged histories, some empty, and one of
+    600 tokens (a call whose histories all fit 512 tokens would take one
+    fixed partition)."""
     rng = np.random.default_rng(S + D)
     lens = rng.integers(0, 48, S)
     lens[::97] = 0
+    lens[1] = 600
     cfg = small_config("bf16", 1, 4, D, 16, tuple(int(x) for x in lens), extra_blocks=4)
     inp = I.poison_unread(I.generate(cfg))
     out = run_decode(upload(inp), ops.KERNEL_MFMA)
-    rows = rng.choice(S, 64, replace=False)
+    rows = np.concatenate([[1], rng.choice(np.arange(2, S), 63, replace=False)])
     pairs = [(int(b), h) for b in rows for h in range(4)]
     compare(out, oracle_ref(inp, pairs), "bf16", pairs=pairs, what="S=%d D=%d" % (S, D))
     assert torch.all(out[torch.from_numpy(lens == 0)] == 0)
