@@ -1060,6 +1060,58 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_fixed(DecodeArgs a
 // the previous range) or [w][1] (continues into the next) for the merge
 // kernel.
 
+// Output rows a wavefront stages in LDS before writing them (balanced
+// schedule, 16-bit decode rows at head_dim 64 and 128): what the compute
+// unit's 160 KB leave beside the edge pieces and the largest prefix table
+// (2 * 2048 + 1 ints) -- 200 rows at head_dim 64 (26 KB a wavefront), 75 at
+// 128 (19.5 KB), checked where the stage is declared.
+template <int D>
+constexpr int stage_rows() { return D == 64 ? 200 : 75; }
+
+// write_rows into LDS: the same packed 16-bit values, row n of the history
+// (n < ncols) at stage_o + n * D / 8 (16-byte words), its [S, H] row index
+// at stage_r[n]; written to the output later by flush_stage.
+template <typename Tag, int D>
+__device__ __forceinline__ void stage_rows_of(const DecodeArgs& a, int b, int kvh, int ncols,
+                                              const WaveState<D>& st, bool bad, u32x4* stage_o,
+                                              uint32_t* stage_r) {
+    constexpr int VW = Dim<D>::VW;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    const int q = lane >> 4;
+    if (n >= ncols) return;
+    const float scale = a.out_scale / st.acc_l[0];
+    // this lane's 4 VW values of row n, d = 4 q VW .. +4 VW: VW / 2 words
+    uint32_t w[2 * VW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < VW; j += 2)
+            w[(VW * i + j) / 2] =
+                pack2(Tag(), bad ? __builtin_nanf("") : st.acc[j][i] * scale,
+                      bad ? __builtin_nanf("") : st.acc[j + 1][i] * scale);
+    u32x4* dst = stage_o + n * (D / 8) + q * (VW / 2);
+#pragma unroll
+    for (int k = 0; k < VW / 2; ++k)
+        dst[k] = (u32x4){w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+    if (q == 0) stage_r[n] = (uint32_t)((uint64_t)b * a.num_heads + col_head(a, kvh, n));
+}
+
+// The staged rows (count rows) to the output, 16 bytes a lane.  Rows are a
+// wavefront's own: its LDS writes above come first in its instruction order.
+template <int D>
+__device__ __forceinline__ void flush_stage(const DecodeArgs& a, const u32x4* stage_o,
+                                            const uint32_t* stage_r, int count) {
+    constexpr int W = D / 8;    // 16-byte words a row
+    const int lane = threadIdx.x & 63;
+    for (int u = lane; u < count * W; u += 64) {
+        const int r = u / W;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.out) +
+                                  ((uint64_t)stage_r[r] * D) * 2 + (u - r * W) * 16) =
+            stage_o[u];
+    }
+}
+
 // Edge pieces of the workgroup's wavefronts, in work-list order: piece
 // 2 v + 0 is the segment wavefront v starts inside (or its only piece),
 // 2 v + 1 the one it ends inside.  key: sequence * num_kv_heads + KV head of
@@ -1269,6 +1321,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
     constexpr int NC = 16 * NT;   // columns per slot
     __shared__ EdgeLds<D, NT> edge;
     __shared__ int wsum[kNW];
+    // Whole histories' output rows are staged and written after the
+    // wavefront's last piece: output writes that reach memory while the
+    // K/V stream is being read slow it far beyond their size (2048 x
+    // U[32, 255] tokens: 137 us with the rows stored as each history ends,
+    // 114 us with the same stores all aimed at a few cached lines).  16-bit
+    // decode rows at head_dim 64 and 128, one column tile; a stage that is
+    // full, or another case, stores directly.
+    constexpr bool kStage = D <= 128 && NT == 1 && kRows == 0 && !Kv::kF32;
+    constexpr int SR = kStage ? stage_rows<D>() : 1;
+    __shared__ u32x4 stage_o[kStage ? kNW * SR * (D / 8) : 1];
+    __shared__ uint32_t stage_r[kStage ? kNW * SR : 1];
+    static_assert(!kStage || sizeof(edge) + sizeof(wsum) + sizeof(stage_o) + sizeof(stage_r) +
+                                     (2 * kMaxBalancedSeqs + 1) * sizeof(int) <=
+                                 160 * 1024,
+                  "staged rows, edge pieces and prefix table exceed the compute unit's LDS");
     // this thread's first entries, loaded before anything waits
     const int t0 = threadIdx.x;
     const int v0 = t0 < n0 + (kRows == 1 ? 1 : 0) ? p0[t0] : 0;
@@ -1339,6 +1406,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
     const int64_t ws = xb + wave * (xe - xb) / kNW;       // this wavefront's range
     const int64_t we = xb + (wave + 1) * (xe - xb) / kNW;
     if (lane < 2) edge.key[2 * wave + lane] = -1;
+    int staged = 0;     // rows in this wavefront's stage
 
     for (int64_t x = ws; x < we;) {
         const int b = find_seq(pref, a.num_seqs, H_kv, x);
@@ -1370,10 +1438,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
         const bool starts_before = c0 > 0;    // the segment began before this range
         const bool ends_after = c1 < nb;      // it continues past this range
         if (!starts_before && !ends_after) {
+            const int ncols = ntok * pass_cols(a, kvh);
+            bool kept = false;
+            if constexpr (kStage) {
+                if (staged + ncols <= SR) {
+                    stage_rows_of<Tag, D>(a, b, kvh, ncols, st[0], bad != 0,
+                                          &stage_o[(wave * SR + staged) * (D / 8)],
+                                          &stage_r[wave * SR + staged]);
+                    staged += ncols;
+                    kept = true;
+                }
+            }
+            if (!kept) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                write_rows<Tag, kCols, D>(a, b, kvh, ntok * pass_cols(a, kvh), t * 16, st[t],
-                                          bad != 0);
+                for (int t = 0; t < NT; ++t)
+                    write_rows<Tag, kCols, D>(a, b, kvh, ncols, t * 16, st[t], bad != 0);
+            }
         } else {
             const int p = 2 * wave + (starts_before ? 0 : 1);
 #pragma unroll
@@ -1389,6 +1469,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
                 edge.key[p] = b * H_kv + kvh;
                 edge.bad[p] = bad;
             }
+        }
+    }
+    if constexpr (kStage) {
+        if (staged > 0) {
+            // (the wavefront's own LDS writes, read back by other lanes)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            flush_stage<D>(a, &stage_o[wave * SR * (D / 8)], &stage_r[wave * SR], staged);
         }
     }
     __syncthreads();
