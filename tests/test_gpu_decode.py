@@ -331,6 +331,29 @@ def test_uneven_passes_on_the_bench_batch(G, D):
     compare(out, oracle_ref(inp, pairs), "bf16", pairs=pairs, what="G=%d D=%d" % (G, D))
 
 
+@pytest.mark.parametrize("D,H_kv", [(128, 4), (64, 8)])
+def test_staged_rows_overflow(D, H_kv):
+    """Whole histories' output rows go to a per-wavefront LDS stage (75 rows
+    at head_dim 128, 200 at 64) and out after the wavefront's last piece;
+    with 16 heads a history and 2048 short histories per KV head a
+    wavefront finishes more histories than its stage holds, so the rows
+    past it are stored directly.  Every sequence checked on two heads, and
+    empty histories give zero rows."""
+    rng = np.random.default_rng(D + H_kv)
+    lens = rng.integers(1, 40, 2048)
+    lens[::61] = 0
+    lens[3] = 600            # keeps the call off the one-partition path
+    cfg = small_config("bf16", H_kv, 16, D, 16, tuple(int(x) for x in lens), extra_blocks=4)
+    inp = I.poison_unread(I.generate(cfg))
+    out = run_decode(upload(inp), ops.KERNEL_MFMA)
+    H = H_kv * 16
+    pairs = [(b, int(h)) for b in range(2048) if lens[b] > 0
+             for h in rng.choice(H, 2, replace=False)]
+    compare(out, oracle_ref(inp, pairs), "bf16", pairs=pairs,
+            what="staged rows D=%d H_kv=%d" % (D, H_kv))
+    assert torch.all(out[torch.from_numpy(lens == 0)] == 0)
+
+
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("S", [2048, 2049])
 def test_many_sequences_balanced_limit(S, D):
