@@ -1338,7 +1338,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
                   "staged rows, edge pieces and prefix table exceed the compute unit's LDS");
     // this thread's first entries, loaded before anything waits
     const int t0 = threadIdx.x;
-    const int v0 = t0 < n0 + (kRows == 1 ? 1 : 0) ? p0[t0] : 0;
+    // (decode rows: the first row of this thread's block in unit_prefix)
+    const int i00 = kRows == 1 ? t0 : unit_prefix_row(t0, n0);
+    const int v0 = i00 < n0 + (kRows == 1 ? 1 : 0) ? p0[i00] : 0;
     const int v1 = kRows == 1 && t0 < n0 ? p1[t0] : 0;
     constexpr int kSU = Kv::k8 ? kStartUnits8 : kStartUnits16;
     int* pref = balanced_pref;
@@ -1365,7 +1367,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
             return v.len;
         }, pref, lens, wsum);
     } else {
-        unit_prefix(a, kSU, [&](int r) { return r == t0 ? v0 : p0[r]; }, pref, lens, wsum);
+        unit_prefix(a, kSU, [&](int r) { return r == i00 ? v0 : p0[r]; }, pref, lens, wsum);
     }
     // query rows decode row b carries, and its block-table row (b is uniform)
     auto ntok_of = [&](int b) {
@@ -1379,15 +1381,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_balanced(
     const int w = blockIdx.x;
 
     // Output rows of decode rows with no history to attend: zeros for an
-    // empty one, NaN for an invalid length (rows w, w + num_wg, ...).
-    for (int r = w; r < a.num_seqs; r += a.num_wg) {
-        const int L = lens[r];
-        if (L > 0 && L <= a.max_context_len) continue;
-        const float v = L == 0 ? 0.0f : __builtin_nanf("");
-        const int64_t count = (int64_t)ntok_of(r) * a.num_heads * D;
-        const uint64_t base = (uint64_t)r * a.num_heads * D;
-        for (int64_t i = threadIdx.x; i < count; i += blockDim.x)
-            store_elem(Tag(), a.out, base + i, v);
+    // empty one, NaN for an invalid length (rows w, w + num_wg, ...: every
+    // wavefront tests 64 of them at once, and the workgroup writes those
+    // found).
+    const int nmine = a.num_seqs > w ? (a.num_seqs - w + a.num_wg - 1) / a.num_wg : 0;
+    for (int k0 = 0; k0 < nmine; k0 += 64) {
+        const int k = k0 + (threadIdx.x & 63);
+        const int Lk = k < nmine ? lens[w + k * a.num_wg] : 1;
+        uint64_t todo = __ballot(!(Lk > 0 && Lk <= a.max_context_len));
+        while (todo != 0) {
+            const int r = w + (k0 + __builtin_ctzll(todo)) * a.num_wg;
+            todo &= todo - 1;
+            const float v = lens[r] == 0 ? 0.0f : __builtin_nanf("");
+            const int64_t count = (int64_t)ntok_of(r) * a.num_heads * D;
+            const uint64_t base = (uint64_t)r * a.num_heads * D;
+            for (int64_t i = threadIdx.x; i < count; i += blockDim.x)
+                store_elem(Tag(), a.out, base + i, v);
+        }
     }
 
     // record of the segment whose first piece this range leaves in [w][1]
