@@ -156,6 +156,35 @@ def test_invalid_device_data_gives_nan_rows(BS):
         assert torch.isfinite(out[0]).all()
 
 
+def test_balanced_prologue_many_rows_empty_and_invalid():
+    """The balanced schedule with 700 decode rows (the prologue's prefix table
+    takes three rows a thread): rows with no history give zeros and rows with
+    an invalid length NaN, also past the first 256 rows (each workgroup tests
+    rows w, w + 256, ... together); the other rows against the oracle."""
+    S = 700
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 48, S)
+    lens[1] = 600                         # not a small call: the balanced schedule
+    zero_rows = [0, 255, 256, 300, 511, 699]
+    bad_rows = [5, 257, 512, 698]
+    lens[zero_rows] = 0
+    cfg = small_config("bf16", 1, 4, 128, 16, tuple(int(x) for x in lens), extra_blocks=4)
+    inp = I.poison_unread(I.generate(cfg))
+    good = [r for r in range(S) if r not in zero_rows and r not in bad_rows]
+    rows = [1] + [int(r) for r in rng.choice(good[2:], 40, replace=False)]
+    pairs = [(b, h) for b in rows for h in range(4)]
+    ref = oracle_ref(inp, pairs)
+    for i, r in enumerate(bad_rows):
+        inp.context_lens[r] = 10_000 if i % 2 == 0 else -3
+    out = run_decode(upload(inp), ops.KERNEL_MFMA)
+    host = out.cpu().float()
+    for r in zero_rows:
+        assert torch.all(host[r] == 0), "row %d" % r
+    for r in bad_rows:
+        assert torch.isnan(host[r]).all(), "row %d" % r
+    compare(out, ref, "bf16", pairs=pairs, what="700 rows, empty and invalid ones among them")
+
+
 def test_permutation_and_block_size_invariance_bitwise():
     inp = I.generate(small_config("bf16", 2, 7, 128, 16, RAGGED, seed=11))
     base = run_decode(upload(inp), ops.KERNEL_MFMA, 256).cpu()
