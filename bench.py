@@ -284,6 +284,18 @@ def unique_kv_bytes(cfg, block_tables, context_lens):
     return int(n) * cfg.num_kv_heads * cfg.head_dim * ELEM_BYTES[cfg.dtype] * 2
 
 
+def kernel_label(S, H_kv, G, D, BS, max_ctx, dtype):
+    """The kernel family and schedule a decode call of this shape takes: calls
+    small enough for one fixed partition per history (the library's
+    pa_decode_partition_size) run one launch, float32 ones on the vector ALU."""
+    fam = ops.decode_kernel(D, BS, G, dtype)
+    P = ops.decode_partition_size(S, H_kv, G, D, BS, max_ctx, dtype)
+    if P >= max_ctx:
+        mfma = fam == ops.KERNEL_MFMA and dtype != torch.float32
+        return ("matrix-core" if mfma else "vector-ALU") + ", one partition per history"
+    return "matrix-core, balanced" if fam == ops.KERNEL_MFMA else "vector-ALU, partitions"
+
+
 def graph_call_us(capture, timed_replay, call, n_calls, reps=3):
     """Mean, min and max duration (us) of one call over `reps` replays of a
     graph of n_calls calls (an untimed replay first)."""
@@ -341,11 +353,10 @@ def workload_rates(dev, capture, timed_replay, oracle_budget_s):
                "calls_per_replay": n_calls, "pool_replicas": R,
                "decode_tokens_per_s": S / t, "alg_bytes_per_call": alg,
                "achieved_gbps": alg / t / 1e9, "frac": alg / t / 1e9 / HBM_PEAK_GBPS,
-               "kernel": "matrix-core, balanced" if ops.decode_kernel(
-                   D, BS, H // H_kv, q.dtype) == ops.KERNEL_MFMA else "vector-ALU, partitions",
+               "kernel": kernel_label(S, H_kv, H // H_kv, D, BS, max_ctx, q.dtype),
                "dtype": cfg.dtype}
         if name == "tiny_fp32":
-            row["note"] = "launch-bound (133 KB of K/V): no roofline claim"
+            row["note"] = "launch-bound (%.0f KB of K/V): no roofline claim" % (alg / 1e3)
         if name == "mixed_shared_bf16":
             u = unique_kv_bytes(cfg, inp.block_tables.numpy(), lens)
             row["unique_bytes_per_call"] = u
@@ -715,8 +726,7 @@ def length_sweep(args, dev):
                    "history_tokens": int(lens.sum()), "decode_us": t * 1e6, "alg_bytes": alg,
                    "achieved_gbps": alg / t / 1e9, "frac": alg / t / 1e9 / HBM_PEAK_GBPS,
                    "decode_tokens_per_s": S / t, "calls": K, "pool_replicas": R,
-                   "kernel": "matrix-core, balanced"
-                   if ops.decode_kernel(D, BS, G, q.dtype) == ops.KERNEL_MFMA else "vector-ALU"}
+                   "kernel": kernel_label(S, H_kv, G, D, BS, max_ctx, q.dtype)}
             rows.append(row)
             print(json.dumps(row), flush=True)
             del kcs, vcs, x
