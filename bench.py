@@ -288,6 +288,9 @@ def kernel_label(S, H_kv, G, D, BS, max_ctx, dtype):
     """The kernel family and schedule a decode call of this shape takes: calls
     small enough for one fixed partition per history (the library's
     pa_decode_partition_size) run one launch, float32 ones on the vector ALU."""
+    import torch
+    from paged_kv_decode_attention_amd import ops
+
     fam = ops.decode_kernel(D, BS, G, dtype)
     P = ops.decode_partition_size(S, H_kv, G, D, BS, max_ctx, dtype)
     if P >= max_ctx:
